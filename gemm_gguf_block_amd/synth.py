@@ -1,0 +1,266 @@
+"""Seeded synthetic inputs for the quantized GEMV / mmq path.
+
+This module is the only code that the HIP path's callers (bench, tests) and the
+CPU oracle's callers share.  It makes *inputs*: f32 tensors drawn from seeded
+normals, weight matrices quantized from them into GGUF blocks, fully random
+block bytes, and MoE routing tables.  It holds none of the path's arithmetic:
+it never quantizes activations to Q8_1, never dequantizes and never dots.
+
+Weight quantization here is data generation only -- the path consumes weights
+that are already quantized.  The fitting rules are the plainest ones the
+workload descriptions support (GGUF byte layouts, since the pages name the
+types -- blazr README, "Model Formats > GGUF" -- but give no layout):
+
+* Q8_0: per 32 values, d = amax/127, q = round(w/d).
+* Q4_K: per 32-value sub-block, lo = min(0, min w), hi = max w,
+  scale = (hi-lo)/15, min = -lo; d = max(scale)/63, dmin = max(min)/63;
+  6-bit sc = round(scale/d), m = round(min/dmin); q = round((w + dmin*m)/(d*sc))
+  clamped to [0, 15], using the fp16-rounded d and dmin.
+* Q6_K: per 16-value sub-block, scale = amax/31; d = max(scale)/127;
+  int8 sc = round(scale/d); q = round(w/(d*sc)) + 32 clamped to [0, 63].
+
+"round" is half away from zero.  Shapes and distributions of the five
+workloads (``WORKLOADS``) follow the workload descriptions: weights N(0, 0.02),
+activations N(0, 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES = 34, 36, 144, 210
+BLOCK_BYTES = {"q8_0": Q8_0_BYTES, "q8_1": Q8_1_BYTES, "q4_k": Q4_K_BYTES, "q6_k": Q6_K_BYTES}
+BLOCK_ELEMS = {"q8_0": 32, "q8_1": 32, "q4_k": 256, "q6_k": 256}
+
+# tensor ids within a workload seed
+T_W, T_X, T_ROUTE, T_WDOWN = 0, 1, 2, 3
+
+WORKLOADS = {
+    # name: shape parameters, seed
+    "q8_0_gemv": dict(fmt="q8_0", n=4096, k=4096, seed=1000),
+    "q4_k_gemv": dict(fmt="q4_k", n=14336, k=4096, seed=1001),
+    "q6_k_gemv": dict(fmt="q6_k", n=128256, k=4096, seed=1002),
+    "q4_k_mmq": dict(fmt="q4_k", m=512, n=4096, k=4096, seed=1003),
+    "moe_q4_k": dict(fmt="q4_k", n_expert=128, n_ff=768, n_embd=2048, n_tok=16, top_k=8, seed=1004),
+}
+
+
+def row_bytes(fmt: str, k: int) -> int:
+    return (k // BLOCK_ELEMS[fmt]) * BLOCK_BYTES[fmt]
+
+
+def rng(seed: int, tensor: int) -> np.random.Generator:
+    return np.random.default_rng([seed, tensor])
+
+
+def normal(seed: int, tensor: int, shape, std: float = 1.0) -> np.ndarray:
+    x = rng(seed, tensor).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def _round_away(v: np.ndarray) -> np.ndarray:
+    t = np.trunc(v)
+    return t + np.where(np.abs(v - t) >= 0.5, np.sign(v), 0).astype(v.dtype)
+
+
+def _div(a, b):
+    """a / b where b != 0, else 0 (no warnings)."""
+    out = np.zeros(np.broadcast(a, b).shape, dtype=np.float32)
+    np.divide(a, b, out=out, where=(b != 0))
+    return out
+
+
+def _f16_bytes(v: np.ndarray) -> np.ndarray:
+    """float32 array [...] -> uint8 [..., 2] little-endian binary16 (RNE)."""
+    return np.ascontiguousarray(v.astype(np.float16)).view(np.uint8).reshape(v.shape + (2,))
+
+
+def _f16_val(v: np.ndarray) -> np.ndarray:
+    return v.astype(np.float16).astype(np.float32)
+
+
+# ------------------------------------------------------------ weight quantizers
+def _rows_in_chunks(W, per_row_fn, out_row_bytes, chunk_rows=4096):
+    n = W.shape[0]
+    out = np.empty((n, out_row_bytes), np.uint8)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        out[r0:r1] = per_row_fn(np.asarray(W[r0:r1], dtype=np.float32)).reshape(r1 - r0, out_row_bytes)
+    return out
+
+
+def quantize_weights_q8_0(W: np.ndarray) -> np.ndarray:
+    n, k = W.shape
+    assert k % 32 == 0
+
+    def conv(X):
+        X = X.reshape(-1, 32)
+        amax = np.abs(X).max(axis=1)
+        d = amax / np.float32(127)
+        q = np.clip(_round_away(_div(X, d[:, None])), -127, 127).astype(np.int8)
+        blk = np.empty((X.shape[0], Q8_0_BYTES), np.uint8)
+        blk[:, 0:2] = _f16_bytes(d)
+        blk[:, 2:] = q.view(np.uint8)
+        return blk
+
+    return _rows_in_chunks(W, conv, row_bytes("q8_0", k))
+
+
+def pack_q4_k(d16: np.ndarray, dmin16: np.ndarray, sc: np.ndarray, m: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q4_K fields into 144-byte superblocks.
+
+    d16, dmin16: uint16 bit patterns [B]; sc, m: 6-bit ints [B][8];
+    q: 4-bit codes [B][256] in element order.
+    """
+    B = q.shape[0]
+    sc = sc.astype(np.uint8)
+    m = m.astype(np.uint8)
+    blk = np.zeros((B, Q4_K_BYTES), np.uint8)
+    blk[:, 0:2] = d16.astype(np.uint16).view(np.uint8).reshape(B, 2)
+    blk[:, 2:4] = dmin16.astype(np.uint16).view(np.uint8).reshape(B, 2)
+    s = blk[:, 4:16]
+    s[:, 0:4] = (sc[:, 0:4] & 63) | ((sc[:, 4:8] >> 4) << 6)
+    s[:, 4:8] = (m[:, 0:4] & 63) | ((m[:, 4:8] >> 4) << 6)
+    s[:, 8:12] = (sc[:, 4:8] & 15) | ((m[:, 4:8] & 15) << 4)
+    qq = q.astype(np.uint8).reshape(B, 4, 2, 32)  # [group][low/high half][l]
+    blk[:, 16:] = (qq[:, :, 0, :] | (qq[:, :, 1, :] << 4)).reshape(B, 128)
+    return blk
+
+
+def quantize_weights_q4_k(W: np.ndarray) -> np.ndarray:
+    n, k = W.shape
+    assert k % 256 == 0
+
+    def conv(X):
+        X = X.reshape(-1, 8, 32)
+        lo = np.minimum(X.min(axis=2), 0)
+        hi = X.max(axis=2)
+        scale = (hi - lo) / np.float32(15)
+        minv = -lo
+        d = scale.max(axis=1) / np.float32(63)
+        dmin = minv.max(axis=1) / np.float32(63)
+        sc = np.clip(_round_away(_div(scale, d[:, None])), 0, 63)
+        m = np.clip(_round_away(_div(minv, dmin[:, None])), 0, 63)
+        eff = _f16_val(d)[:, None] * sc
+        mm = _f16_val(dmin)[:, None] * m
+        q = np.clip(_round_away(_div(X + mm[:, :, None], eff[:, :, None])), 0, 15)
+        return pack_q4_k(d.astype(np.float16).view(np.uint16), dmin.astype(np.float16).view(np.uint16),
+                         sc.astype(np.int32), m.astype(np.int32), q.reshape(-1, 256).astype(np.int32))
+
+    return _rows_in_chunks(W, conv, row_bytes("q4_k", k))
+
+
+def pack_q6_k(d16: np.ndarray, sc: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q6_K fields into 210-byte superblocks.
+
+    d16: uint16 bit patterns [B]; sc: int8 scales [B][16]; q: 6-bit codes
+    [B][256] in element order (element 128h + 32g + l).
+    """
+    B = q.shape[0]
+    q = q.astype(np.uint8).reshape(B, 2, 4, 32)  # [h][g][l]
+    blk = np.zeros((B, Q6_K_BYTES), np.uint8)
+    ql = blk[:, 0:128].reshape(B, 2, 2, 32)  # [h][which 32-byte run][l]
+    ql[:, :, 0, :] = (q[:, :, 0, :] & 15) | ((q[:, :, 2, :] & 15) << 4)
+    ql[:, :, 1, :] = (q[:, :, 1, :] & 15) | ((q[:, :, 3, :] & 15) << 4)
+    qh = blk[:, 128:192].reshape(B, 2, 32)
+    qh[:] = ((q[:, :, 0, :] >> 4) | ((q[:, :, 1, :] >> 4) << 2) |
+             ((q[:, :, 2, :] >> 4) << 4) | ((q[:, :, 3, :] >> 4) << 6))
+    blk[:, 192:208] = sc.astype(np.int8).view(np.uint8)
+    blk[:, 208:210] = d16.astype(np.uint16).view(np.uint8).reshape(B, 2)
+    return blk
+
+
+def quantize_weights_q6_k(W: np.ndarray) -> np.ndarray:
+    n, k = W.shape
+    assert k % 256 == 0
+
+    def conv(X):
+        X = X.reshape(-1, 16, 16)
+        amax = np.abs(X).max(axis=2)
+        scale = amax / np.float32(31)
+        d = scale.max(axis=1) / np.float32(127)
+        sc = np.clip(_round_away(_div(scale, d[:, None])), 0, 127)
+        eff = _f16_val(d)[:, None] * sc
+        q = np.clip(_round_away(_div(X, eff[:, :, None])) + 32, 0, 63)
+        return pack_q6_k(d.astype(np.float16).view(np.uint16), sc.astype(np.int32),
+                         q.reshape(-1, 256).astype(np.int32))
+
+    return _rows_in_chunks(W, conv, row_bytes("q6_k", k))
+
+
+QUANTIZE_WEIGHTS = {"q8_0": quantize_weights_q8_0, "q4_k": quantize_weights_q4_k, "q6_k": quantize_weights_q6_k}
+
+
+def weights(fmt: str, n: int, k: int, seed: int, tensor: int = T_W, std: float = 0.02,
+            chunk_rows: int = 8192) -> np.ndarray:
+    """N(0, std) f32 [n][k] quantized to `fmt`, drawn and quantized row-chunk by
+    row-chunk (the draw order is the same as one [n][k] draw)."""
+    g = rng(seed, tensor)
+    out = np.empty((n, row_bytes(fmt, k)), np.uint8)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        W = g.standard_normal((r1 - r0, k), dtype=np.float32) * np.float32(std)
+        out[r0:r1] = QUANTIZE_WEIGHTS[fmt](W)
+    return out
+
+
+# ------------------------------------------------------------ random block bytes
+def random_f16_bits(g: np.random.Generator, size, lo_exp: int = -24, hi_exp: int = 15) -> np.ndarray:
+    """Random finite binary16 bit patterns (either sign, exponents within range)."""
+    x = g.uniform(0.5, 1.0, size) * np.exp2(g.integers(lo_exp, hi_exp + 1, size))
+    x *= np.where(g.integers(0, 2, size) == 0, 1.0, -1.0)
+    h = x.astype(np.float16)
+    h[~np.isfinite(h)] = np.float16(1.0)
+    return h.view(np.uint16)
+
+
+def random_blocks(fmt: str, rows: int, k: int, seed: int, tensor: int = T_W,
+                  lo_exp: int = -20, hi_exp: int = 4) -> np.ndarray:
+    """Uniformly random block bytes with every fp16 field set to a random finite
+    value (exponents 2^lo_exp..2^hi_exp, either sign, subnormals included)."""
+    g = rng(seed, tensor)
+    nb = k // BLOCK_ELEMS[fmt]
+    blk = g.integers(0, 256, (rows * nb, BLOCK_BYTES[fmt]), dtype=np.uint8)
+    offs = {"q8_0": [0], "q8_1": [0, 2], "q4_k": [0, 2], "q6_k": [208]}[fmt]
+    for o in offs:
+        bits = random_f16_bits(g, rows * nb, lo_exp, hi_exp)
+        blk[:, o:o + 2] = bits.view(np.uint8).reshape(-1, 2)
+    return blk.reshape(rows, nb * BLOCK_BYTES[fmt])
+
+
+# ---------------------------------------------------------------------- routing
+def routing(seed: int, n_tok: int, n_expert: int, top_k: int):
+    """Per token: top_k distinct experts drawn uniformly without replacement,
+    and softmax weights over top_k N(0,1) logits (selection ignores logits)."""
+    g = rng(seed, T_ROUTE)
+    ids = np.empty((n_tok, top_k), np.int32)
+    w = np.empty((n_tok, top_k), np.float32)
+    for t in range(n_tok):
+        ids[t] = g.choice(n_expert, top_k, replace=False)
+        logits = g.standard_normal(top_k)
+        e = np.exp(logits - logits.max())
+        w[t] = (e / e.sum()).astype(np.float32)
+    return ids, w
+
+
+# ------------------------------------------------------------ whole workloads
+def workload(name: str, **override):
+    """Inputs of one named workload as numpy arrays (host memory)."""
+    p = dict(WORKLOADS[name])
+    p.update(override)
+    seed = p["seed"]
+    if name.endswith("_gemv"):
+        return dict(p, w=weights(p["fmt"], p["n"], p["k"], seed),
+                    x=normal(seed, T_X, (p["k"],)))
+    if name == "q4_k_mmq":
+        return dict(p, w=weights("q4_k", p["n"], p["k"], seed),
+                    a=normal(seed, T_X, (p["m"], p["k"])))
+    if name == "moe_q4_k":
+        E, F, H = p["n_expert"], p["n_ff"], p["n_embd"]
+        w_gu = weights("q4_k", E * 2 * F, H, seed, T_W)
+        w_dn = weights("q4_k", E * H, F, seed, T_WDOWN)
+        ids, rw = routing(seed, p["n_tok"], E, p["top_k"])
+        return dict(p, w_gu=w_gu.reshape(E, -1), w_down=w_dn.reshape(E, -1),
+                    x=normal(seed, T_X, (p["n_tok"], H)), ids=ids, weights=rw)
+    raise KeyError(name)

@@ -1,0 +1,432 @@
+"""Pins of the CPU oracle against facts fixed independently of it.
+
+Nothing here is the oracle's formula retyped: each test compares the oracle
+with a library routine (numpy binary16), a hand-computed fixture, a closed
+form evaluated exactly, an invariant, or a second, differently-structured
+computation that a dropped term / wrong index / transposed operand would break.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from _util import read_golden
+from gemm_gguf_block_amd import synth
+
+
+# --------------------------------------------------------------- binary16 codec
+def test_f16_decode_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.f16_bits_to_f32(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_encode_rne_matches_numpy(orc):
+    g = np.random.default_rng(5)
+    parts = [
+        g.standard_normal(200000).astype(np.float32),
+        (g.standard_normal(200000) * 1e-5).astype(np.float32),      # subnormal range
+        (g.standard_normal(200000) * 3e4).astype(np.float32),       # near overflow
+        g.uniform(-65536, 65536, 100000).astype(np.float32),
+        np.exp2(g.uniform(-30, 17, 200000)).astype(np.float32) * np.where(g.random(200000) < 0.5, -1, 1),
+    ]
+    # exact ties: odd multiples of half an ulp, at normal and subnormal scales
+    ties = []
+    for e in range(-24, 16):
+        ulp = 2.0 ** (max(e, -14) - 10)
+        for k in range(1, 40, 2):
+            ties.append((2.0 ** e + k * ulp / 2))
+    special = [0.0, -0.0, 65504.0, 65519.996, 65520.0, 65536.0, 1e30, -1e30, 2.0 ** -25, 3 * 2.0 ** -25,
+               2.0 ** -24, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, np.inf, -np.inf]
+    x = np.concatenate(parts + [np.array(ties, np.float32), np.array(special, np.float32)])
+    got = orc.f32_to_f16_bits(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    assert orc.f32_to_f16_bits(np.array([np.nan], np.float32))[0] & 0x7c00 == 0x7c00
+
+
+# ------------------------------------------------------------------ Q8_1
+def _q8_1_cases():
+    fx = read_golden("q8_1_vectors.txt")
+    for xs, bs in zip(fx["x"], fx["bytes"]):
+        x = np.array([float.fromhex(t) for t in xs.split()], np.float32)
+        yield x, bytes.fromhex(bs)
+
+
+def test_quantize_q8_1_hand_vectors(orc):
+    cases = list(_q8_1_cases())
+    assert len(cases) == 4
+    for x, want in cases:
+        assert orc.quantize_q8_1(x[None, :]).tobytes() == want
+    # all four blocks as one row of 128 values
+    x = np.concatenate([c[0] for c in cases])[None, :]
+    assert orc.quantize_q8_1(x).tobytes() == b"".join(c[1] for c in cases)
+
+
+def test_quantize_q8_1_roundtrip_bound(orc):
+    g = np.random.default_rng(11)
+    x = np.concatenate([g.standard_normal((64, 256)), g.standard_normal((64, 256)) * 1e-6,
+                        g.standard_normal((64, 256)) * 1e4]).astype(np.float32)
+    xq = orc.quantize_q8_1(x)
+    blk = xq.reshape(-1, 36)
+    xb = x.reshape(-1, 32).astype(np.float64)
+    q = blk[:, 4:].view(np.int8).astype(np.float64)
+    d16 = blk[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    d32 = (np.abs(x.reshape(-1, 32)).max(axis=1) / np.float32(127)).astype(np.float64)
+    # bound: |x - f(d16) q| <= d/2 + 127 |d - f(d16)|  (q from the fp32 d)
+    err = np.abs(xb - d16[:, None] * q).max(axis=1)
+    bound = d32 / 2 * (1 + 1e-6) + 127 * np.abs(d32 - d16)
+    assert np.all(err <= bound)
+    assert np.all(np.abs(q) <= 127)
+    # s = fp16(d * sum q), an exactly-checkable invariant of the block header
+    s16 = blk[:, 2:4].copy().view(np.float16).ravel()
+    with np.errstate(over="ignore"):
+        want = (d32.astype(np.float32) * q.sum(axis=1).astype(np.float32)).astype(np.float16)
+    assert np.array_equal(s16.view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------- hand-built weight blocks
+def _fixture_block(name):
+    fx = read_golden(name)
+    return fx, np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+
+
+def _ints(s):
+    return np.array([int(t) for t in s.split()], np.int64)
+
+
+def test_q4_k_hand_block_fields_and_values(orc):
+    fx, blk = _fixture_block("q4_k_superblock.txt")
+    assert blk.size == 144
+    d, dmin, sc, m, q = orc.unpack_q4_k(blk)
+    assert d == 2.0 ** -4 and dmin == 2.0 ** -5
+    assert np.array_equal(sc, _ints(fx["sc"][0])) and np.array_equal(m, _ints(fx["m"][0]))
+    assert np.array_equal(q, _ints(fx["q"][0]))
+    w = orc.dequant("q4_k", blk, 1, 256)[0]
+    qq, scc, mm = _ints(fx["q"][0]), _ints(fx["sc"][0]), _ints(fx["m"][0])
+    want = [Fraction(1, 16) * scc[i // 32] * qq[i] - Fraction(1, 32) * mm[i // 32] for i in range(256)]
+    assert [Fraction(v) for v in w] == want
+
+
+def test_q6_k_hand_block_fields_and_values(orc):
+    fx, blk = _fixture_block("q6_k_superblock.txt")
+    assert blk.size == 210
+    d, sc, q = orc.unpack_q6_k(blk)
+    assert d == 2.0 ** -8
+    assert np.array_equal(sc, _ints(fx["scales"][0]))
+    assert np.array_equal(q, _ints(fx["q"][0]))
+    w = orc.dequant("q6_k", blk, 1, 256)[0]
+    qq, scc = _ints(fx["q"][0]), _ints(fx["scales"][0])
+    want = [Fraction(1, 256) * scc[i // 16] * (qq[i] - 32) for i in range(256)]
+    assert [Fraction(v) for v in w] == want
+
+
+def test_q8_0_hand_block_values(orc):
+    fx, blk = _fixture_block("q8_0_block.txt")
+    w = orc.dequant("q8_0", blk, 1, 32)[0]
+    assert [Fraction(v) for v in w] == [Fraction(i - 16, 4) for i in range(32)]
+
+
+# ------------------------------------- generator packer vs oracle decoder
+def test_q4_k_pack_unpack_bijection(orc):
+    g = np.random.default_rng(3)
+    raw = g.integers(0, 256, (200, 144), dtype=np.uint8)
+    for blk in raw:
+        d, dmin, sc, m, q = orc.unpack_q4_k(blk)
+        d16 = blk[0:2].copy().view(np.uint16)
+        dm16 = blk[2:4].copy().view(np.uint16)
+        re = synth.pack_q4_k(d16, dm16, sc[None], m[None], q[None])[0]
+        assert np.array_equal(re, blk)
+    # fields -> bytes -> fields
+    sc = g.integers(0, 64, (50, 8))
+    mn = g.integers(0, 64, (50, 8))
+    qq = g.integers(0, 16, (50, 256))
+    blks = synth.pack_q4_k(np.full(50, 0x3C00, np.uint16), np.full(50, 0x3800, np.uint16), sc, mn, qq)
+    for i in range(50):
+        d, dmin, s2, m2, q2 = orc.unpack_q4_k(blks[i])
+        assert (d, dmin) == (1.0, 0.5)
+        assert np.array_equal(s2, sc[i]) and np.array_equal(m2, mn[i]) and np.array_equal(q2, qq[i])
+
+
+def test_q6_k_pack_unpack_bijection(orc):
+    g = np.random.default_rng(4)
+    raw = g.integers(0, 256, (200, 210), dtype=np.uint8)
+    for blk in raw:
+        d, sc, q = orc.unpack_q6_k(blk)
+        re = synth.pack_q6_k(blk[208:210].copy().view(np.uint16), sc[None], q[None])[0]
+        assert np.array_equal(re, blk)
+
+
+# ------------------------------------------------ identity-selection weights
+def _select_rows(n, k):
+    """Row r selects column (r * 37) % k: a permutation-like pattern."""
+    return np.array([(r * 37) % k for r in range(n)])
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+def test_selection_matrix_gives_activation_entries(orc, fmt):
+    """Weights that dequantize to one-hot rows must return exactly the selected
+    dequantized activation entries: catches transposed operands, wrong block or
+    element indexing, dropped scale factors and sign errors."""
+    n, k = 40, 512
+    cols = _select_rows(n, k)
+    if fmt == "q8_0":
+        blk = np.zeros((n, k // 32, 34), np.uint8)
+        blk[:, :, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+        for r, c in enumerate(cols):
+            blk[r, c // 32, 2 + c % 32] = 1
+        w = blk.reshape(n, -1)
+    elif fmt == "q4_k":
+        ns = k // 256
+        sc = np.ones((n * ns, 8), np.int64)
+        mm = np.zeros((n * ns, 8), np.int64)
+        q = np.zeros((n * ns, 256), np.int64)
+        for r, c in enumerate(cols):
+            q[r * ns + c // 256, c % 256] = 1
+        w = synth.pack_q4_k(np.full(n * ns, 0x3C00, np.uint16), np.zeros(n * ns, np.uint16), sc, mm, q)
+        w = w.reshape(n, -1)
+    else:
+        ns = k // 256
+        sc = np.ones((n * ns, 16), np.int64)
+        q = np.full((n * ns, 256), 32, np.int64)
+        for r, c in enumerate(cols):
+            q[r * ns + c // 256, c % 256] = 33
+        w = synth.pack_q6_k(np.full(n * ns, 0x3C00, np.uint16), sc, q).reshape(n, -1)
+    x = np.random.default_rng(9).standard_normal(k).astype(np.float32)
+    xq = orc.quantize_q8_1(x[None])
+    xhat = orc.dequant("q8_1", xq, 1, k)[0]
+    y = orc.qgemv(fmt, w, xq, n, k)
+    assert np.array_equal(y, xhat[cols])
+    assert np.array_equal(orc.qgemv_factored(fmt, w, xq, n, k), xhat[cols])
+
+
+# ---------------------------------------------- integer dots vs float dequant
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+def test_integer_block_dots_agree_with_dequant_dot(orc, fmt):
+    """The factored sum over exact int32 block dots equals the plain double
+    dequant-and-dot on fully random block bytes (finite fp16 fields)."""
+    for n, k in [(1, 256), (3, 512), (65, 256)]:
+        w = synth.random_blocks(fmt, n, k, seed=100 + n, lo_exp=-14, hi_exp=2)
+        xq = synth.random_blocks("q8_1", 1, k, seed=200 + n, lo_exp=-14, hi_exp=2)
+        plain = orc.qgemv(fmt, w, xq, n, k)
+        fact = orc.qgemv_factored(fmt, w, xq, n, k)
+        scale = np.max(np.abs(plain)) + 1e-300
+        assert np.max(np.abs(plain - fact)) <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+def test_block_dots_brute_force_from_decoded_codes(orc, fmt):
+    """Block dots from the oracle's blockdots routine vs numpy dots of the codes
+    the (separately written) field decoder returns, on random bytes."""
+    n, k = 5, 512
+    w = synth.random_blocks(fmt, n, k, seed=7)
+    xq = synth.random_blocks("q8_1", 1, k, seed=8)
+    qa = xq.reshape(-1, 36)[:, 4:].view(np.int8).astype(np.int64).ravel()
+    if fmt == "q8_0":
+        D = orc.blockdots("q8_0", w, xq, n, k)
+        codes = w.reshape(n, -1, 34)[:, :, 2:].view(np.int8).astype(np.int64).reshape(n, k)
+        want = (codes * qa[None]).reshape(n, -1, 32).sum(axis=2)
+        assert np.array_equal(D, want)
+    elif fmt == "q4_k":
+        D, S = orc.blockdots("q4_k", w, xq, n, k)
+        codes = np.stack([np.concatenate([orc.unpack_q4_k(b)[4] for b in row.reshape(-1, 144)])
+                          for row in w])
+        want = (codes * qa[None]).reshape(n, -1, 32).sum(axis=2)
+        assert np.array_equal(D, want)
+        assert np.array_equal(S, qa.reshape(-1, 32).sum(axis=1))
+    else:
+        D = orc.blockdots("q6_k", w, xq, n, k)
+        codes = np.stack([np.concatenate([orc.unpack_q6_k(b)[2] for b in row.reshape(-1, 210)])
+                          for row in w])
+        want = ((codes - 32) * qa[None]).reshape(n, -1, 16).sum(axis=2)
+        assert np.array_equal(D, want)
+
+
+# ------------------------------------------ single hand-computed superblock dot
+def _hand_activation(k, d_exp=-3):
+    """Q8_1 activation with d = 2^d_exp and q_a[i] = (i mod 7) - 3 (s unused)."""
+    nb = k // 32
+    blk = np.zeros((nb, 36), np.uint8)
+    blk[:, 0:2] = np.frombuffer(np.float16(2.0 ** d_exp).tobytes(), np.uint8)
+    qa = np.array([(i % 7) - 3 for i in range(k)], np.int64)
+    blk[:, 4:] = qa.reshape(nb, 32).astype(np.int8).view(np.uint8)
+    return blk.reshape(1, -1), qa
+
+
+def test_hand_superblock_dot_exact(orc):
+    xq, qa = _hand_activation(256)
+    # Q4_K
+    fx, blk = _fixture_block("q4_k_superblock.txt")
+    q, sc, m = _ints(fx["q"][0]), _ints(fx["sc"][0]), _ints(fx["m"][0])
+    exact = sum((Fraction(1, 16) * sc[i // 32] * q[i] - Fraction(1, 32) * m[i // 32]) * Fraction(1, 8) * qa[i]
+                for i in range(256))
+    assert Fraction(orc.qgemv("q4_k", blk[None], xq, 1, 256)[0]) == exact
+    assert Fraction(orc.qgemv_factored("q4_k", blk[None], xq, 1, 256)[0]) == exact
+    # Q6_K
+    fx, blk = _fixture_block("q6_k_superblock.txt")
+    q, sc = _ints(fx["q"][0]), _ints(fx["scales"][0])
+    exact = sum(Fraction(1, 256) * sc[i // 16] * (q[i] - 32) * Fraction(1, 8) * qa[i] for i in range(256))
+    assert Fraction(orc.qgemv("q6_k", blk[None], xq, 1, 256)[0]) == exact
+    assert Fraction(orc.qgemv_factored("q6_k", blk[None], xq, 1, 256)[0]) == exact
+    # Q8_0: eight copies of the hand block make one 256-wide row
+    fx, blk = _fixture_block("q8_0_block.txt")
+    row = np.tile(blk, 8)[None]
+    exact = sum(Fraction(((i % 32) - 16), 4) * Fraction(1, 8) * qa[i] for i in range(256))
+    assert Fraction(orc.qgemv("q8_0", row, xq, 1, 256)[0]) == exact
+
+
+# --------------------------------------------------- weight quantizers (data)
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+def test_weight_quantizer_roundtrip_bound(orc, fmt):
+    g = np.random.default_rng(21)
+    W = (g.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    wq = synth.QUANTIZE_WEIGHTS[fmt](W)
+    deq = orc.dequant(fmt, wq, 64, 512)
+    err = np.abs(deq - W.astype(np.float64))
+    if fmt == "q8_0":
+        blk = wq.reshape(-1, 34)
+        d16 = blk[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+        d32 = np.abs(W.reshape(-1, 32)).max(axis=1).astype(np.float64) / 127
+        bound = d32 / 2 * (1 + 1e-5) + 127 * np.abs(d32 - d16)
+        assert np.all(err.reshape(-1, 32).max(axis=1) <= bound)
+    elif fmt == "q4_k":
+        effs = []
+        for b in wq.reshape(-1, 144):
+            d, dmin, sc, m, q = orc.unpack_q4_k(b)
+            effs.append(np.repeat(d * sc.astype(np.float64), 32))
+        eff = np.concatenate(effs).reshape(64, 512)
+        frac_bad = np.mean(err > eff / 2 * (1 + 1e-5) + 1e-9)
+        assert frac_bad < 0.01
+        assert np.sqrt(np.mean(err ** 2)) < 0.6 * np.sqrt(np.mean(eff ** 2))
+    else:
+        effs = []
+        for b in wq.reshape(-1, 210):
+            d, sc, q = orc.unpack_q6_k(b)
+            effs.append(np.repeat(d * np.abs(sc.astype(np.float64)), 16))
+        eff = np.concatenate(effs).reshape(64, 512)
+        frac_bad = np.mean(err > eff / 2 * (1 + 1e-5) + 1e-12)
+        assert frac_bad < 0.01
+    # quantization keeps the weights close overall
+    assert np.linalg.norm(deq - W) / np.linalg.norm(W) < 0.12
+
+
+# ------------------------------------------------------------------ mmq oracle
+def test_mmq_rows_equal_gemv(orc):
+    m, n, k = 5, 33, 512
+    w = synth.weights("q4_k", n, k, seed=31)
+    a = synth.normal(31, 1, (m, k))
+    aq = orc.quantize_q8_1(a)
+    C = orc.qgemm_q4_k(w, aq, m, n, k)
+    for i in range(m):
+        y = orc.qgemv("q4_k", w, aq[i], n, k)
+        assert np.max(np.abs(C[i] - y)) <= 1e-12 * np.max(np.abs(y))
+    pairs = np.array([[0, 0], [4, 32], [2, 17], [3, 5]])
+    sel = orc.qgemm_q4_k(w, aq, m, n, k, pairs=pairs)
+    assert np.array_equal(sel, C[pairs[:, 0], pairs[:, 1]])
+    # mmq block dots are the GEMV block dots of each activation row
+    D = orc.blockdots_q4_k_mmq(w, aq, m, n, k)
+    for i in range(m):
+        assert np.array_equal(D[i], orc.blockdots("q4_k", w, aq[i], n, k)[0])
+
+
+def test_mmq_against_numpy_matmul_of_dequantized(orc):
+    m, n, k = 7, 19, 256
+    w = synth.random_blocks("q4_k", n, k, seed=41, lo_exp=-10, hi_exp=0)
+    aq = synth.random_blocks("q8_1", m, k, seed=42, lo_exp=-10, hi_exp=0)
+    C = orc.qgemm_q4_k(w, aq, m, n, k)
+    ref = orc.dequant("q8_1", aq, m, k) @ orc.dequant("q4_k", w, n, k).T
+    assert np.max(np.abs(C - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ MoE oracle
+def _small_moe(seed=51, E=6, F=256, H=512, T=4, K=3):
+    w_gu = synth.weights("q4_k", E * 2 * F, H, seed, 0).reshape(E, -1)
+    w_dn = synth.weights("q4_k", E * H, F, seed, 3).reshape(E, -1)
+    ids, rw = synth.routing(seed, T, E, K)
+    x = synth.normal(seed, 1, (T, H))
+    return dict(w_gu=w_gu, w_dn=w_dn, ids=ids, rw=rw, x=x, E=E, F=F, H=H, T=T, K=K)
+
+
+def test_routing_weights_softmax_and_distinct():
+    ids, rw = synth.routing(1004, 16, 128, 8)
+    assert np.all(np.abs(rw.sum(axis=1) - 1) <= 1e-6) and np.all(rw > 0)
+    assert all(len(set(r)) == 8 for r in ids)
+    assert ids.min() >= 0 and ids.max() < 128
+
+
+def test_moe_equals_composition_of_dense_pieces(orc):
+    """MoE oracle vs an independent composition: numpy matmuls of the
+    dequantized expert weights, the oracle's Q8_1 quantizer for x and h."""
+    c = _small_moe()
+    E, F, H, T, K = c["E"], c["F"], c["H"], c["T"], c["K"]
+    xq = orc.quantize_q8_1(c["x"])
+    res = orc.moe_q4_k(c["w_gu"], c["w_dn"], xq, c["ids"], c["rw"], T, K, E, F, H)
+    xhat = orc.dequant("q8_1", xq, T, H)
+    want = np.zeros((T, H))
+    for t in range(T):
+        for s in range(K):
+            e = c["ids"][t, s]
+            Wgu = orc.dequant("q4_k", c["w_gu"][e], 2 * F, H)
+            Wdn = orc.dequant("q4_k", c["w_dn"][e], H, F)
+            gu = Wgu @ xhat[t]
+            assert np.max(np.abs(gu - res["gu"][t * K + s])) <= 1e-12 * np.max(np.abs(gu))
+            g, u = gu[:F], gu[F:]
+            h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+            hq = orc.quantize_q8_1(h[None])
+            assert np.array_equal(hq[0], res["hq"][t * K + s])
+            want[t] += float(c["rw"][t, s]) * (Wdn @ orc.dequant("q8_1", hq, 1, F)[0])
+    assert np.max(np.abs(res["out"] - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_moe_top1_unit_weight_is_dense_ffn(orc):
+    c = _small_moe(seed=52)
+    E, F, H, T = c["E"], c["F"], c["H"], c["T"]
+    ids = (np.arange(T) % E).astype(np.int32)[:, None]
+    rw = np.ones((T, 1), np.float32)
+    xq = orc.quantize_q8_1(c["x"])
+    out = orc.moe_q4_k(c["w_gu"], c["w_dn"], xq, ids, rw, T, 1, E, F, H)["out"]
+    for t in range(T):
+        e = ids[t, 0]
+        gu = orc.qgemv("q4_k", c["w_gu"][e], xq[t], 2 * F, H)
+        h = (gu[:F] / (1 + np.exp(-gu[:F])) * gu[F:]).astype(np.float32)
+        y = orc.qgemv("q4_k", c["w_dn"][e], orc.quantize_q8_1(h[None])[0], H, F)
+        assert np.max(np.abs(out[t] - y)) <= 1e-12 * np.max(np.abs(y))
+
+
+def test_moe_out_of_range_ids_contribute_nothing(orc):
+    c = _small_moe(seed=53)
+    E, F, H, T, K = c["E"], c["F"], c["H"], c["T"], c["K"]
+    xq = orc.quantize_q8_1(c["x"])
+    ids = c["ids"].copy()
+    ids[1, 2] = E + 5
+    ids[2, 0] = -1
+    bad = orc.moe_q4_k(c["w_gu"], c["w_dn"], xq, ids, c["rw"], T, K, E, F, H)["out"]
+    rw = c["rw"].copy()
+    rw[1, 2] = 0
+    rw[2, 0] = 0
+    ids2 = ids.copy()
+    ids2[1, 2] = 0
+    ids2[2, 0] = 0
+    ref = orc.moe_q4_k(c["w_gu"], c["w_dn"], xq, ids2, rw, T, K, E, F, H)["out"]
+    assert np.max(np.abs(bad - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_quantization_fidelity_vs_unquantized_ffn(orc):
+    """Informational bound: the quantized FFN stays within a few percent of the
+    same FFN on the unquantized activations."""
+    c = _small_moe(seed=54)
+    E, F, H, T, K = c["E"], c["F"], c["H"], c["T"], c["K"]
+    xq = orc.quantize_q8_1(c["x"])
+    out = orc.moe_q4_k(c["w_gu"], c["w_dn"], xq, c["ids"], c["rw"], T, K, E, F, H)["out"]
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for s in range(K):
+            e = c["ids"][t, s]
+            gu = orc.dequant("q4_k", c["w_gu"][e], 2 * F, H) @ c["x"][t].astype(np.float64)
+            h = gu[:F] / (1 + np.exp(-gu[:F])) * gu[F:]
+            ref[t] += c["rw"][t, s] * (orc.dequant("q4_k", c["w_dn"][e], H, F) @ h)
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) < 0.05
