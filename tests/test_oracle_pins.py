@@ -59,7 +59,7 @@ def _q8_1_cases():
 
 def test_quantize_q8_1_hand_vectors(orc):
     cases = list(_q8_1_cases())
-    assert len(cases) == 4
+    assert len(cases) == 5
     for x, want in cases:
         assert orc.quantize_q8_1(x[None, :]).tobytes() == want
     # all four blocks as one row of 128 values
