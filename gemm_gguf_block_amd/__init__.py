@@ -1,0 +1,234 @@
+"""Python binding of libqgguf.so -- argument marshalling only.
+
+Every entry point has the name of its C-ABI function (declared in
+``include/qgguf.h``) and takes torch tensors that live on the GPU: it checks
+dtypes and sizes, passes ``data_ptr()`` values and the current HIP stream, and
+raises ``QGError`` on a non-zero status.  All work runs in the HIP kernels of
+libqgguf.so; there is no other code path.  If the library has not been built,
+the first call raises -- there is no fallback.
+
+The seeded input generators live in the separate module ``.synth``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgguf.so")
+
+Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES = 34, 36, 144, 210
+_BLOCK = {"q8_0": (32, Q8_0_BYTES), "q8_1": (32, Q8_1_BYTES), "q4_k": (256, Q4_K_BYTES), "q6_k": (256, Q6_K_BYTES)}
+
+STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_ALIGN", 4: "QG_ERR_WORKSPACE",
+          5: "QG_ERR_NO_DEVICE", 6: "QG_ERR_ARCH", 7: "QG_ERR_LAUNCH"}
+
+# C-ABI signatures: name -> argument types (restype is qg_status unless noted)
+_P, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "quantize_q8_1": [_P, _P, _I, _I, _P],
+    "qgemv_q8_0": [_P, _P, _P, _I, _I, _P],
+    "qgemv_q4_k": [_P, _P, _P, _I, _I, _P],
+    "qgemv_q6_k": [_P, _P, _P, _I, _I, _P],
+    "qgemm_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "moe_qgemv_q4_k_workspace_size": [_I, _I, _I, _I, _I],
+    "moe_qgemv_q4_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
+    "qg_status_str": [ctypes.c_int],
+    "qg_blockdots_q8_0": [_P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q4_k": [_P, _P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q6_k": [_P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+}
+
+
+class QGError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgguf.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python __graft_entry__.py build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_qgemv_q4_k_workspace_size.restype = ctypes.c_size_t
+        L.qg_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().qg_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise QGError(fn, status)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, nbytes: int, name: str):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return t.data_ptr()
+
+
+def row_bytes(fmt: str, k: int) -> int:
+    e, b = _BLOCK[fmt]
+    return (k // e) * b
+
+
+def _empty(shape, dtype, like):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ----------------------------------------------------------------- entry points
+def quantize_q8_1(x, xq=None, stream=None):
+    """x: f32 [rows][k] (or [k]) -> Q8_1 bytes uint8 [rows][k/32*36]."""
+    import torch
+    rows, k = (1, x.shape[0]) if x.dim() == 1 else (x.shape[0], x.shape[1])
+    if xq is None:
+        xq = _empty((rows, row_bytes("q8_1", k)), torch.uint8, x)
+    px = _need(x, torch.float32, rows * k * 4, "x")
+    pq = _need(xq, torch.uint8, rows * row_bytes("q8_1", k), "xq")
+    _check("quantize_q8_1", lib().quantize_q8_1(px, pq, rows, k, _stream(stream)))
+    return xq
+
+
+def _gemv(fmt, w, xq, n, k, y, stream):
+    import torch
+    if y is None:
+        y = _empty((n,), torch.float32, w)
+    pw = _need(w, torch.uint8, n * row_bytes(fmt, k), "w")
+    pq = _need(xq, torch.uint8, row_bytes("q8_1", k), "xq")
+    py = _need(y, torch.float32, n * 4, "y")
+    name = "qgemv_" + fmt
+    _check(name, getattr(lib(), name)(pw, pq, py, n, k, _stream(stream)))
+    return y
+
+
+def qgemv_q8_0(w, xq, n, k, y=None, stream=None):
+    return _gemv("q8_0", w, xq, n, k, y, stream)
+
+
+def qgemv_q4_k(w, xq, n, k, y=None, stream=None):
+    return _gemv("q4_k", w, xq, n, k, y, stream)
+
+
+def qgemv_q6_k(w, xq, n, k, y=None, stream=None):
+    return _gemv("q6_k", w, xq, n, k, y, stream)
+
+
+def qgemm_q4_k_mmq(w, aq, m, n, k, c=None, stream=None):
+    import torch
+    if c is None:
+        c = _empty((m, n), torch.float32, w)
+    pw = _need(w, torch.uint8, n * row_bytes("q4_k", k), "w")
+    pa = _need(aq, torch.uint8, m * row_bytes("q8_1", k), "aq")
+    pc = _need(c, torch.float32, m * n * 4, "c")
+    _check("qgemm_q4_k_mmq", lib().qgemm_q4_k_mmq(pw, pa, pc, m, n, k, _stream(stream)))
+    return c
+
+
+def moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd) -> int:
+    return int(lib().moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd))
+
+
+def moe_qgemv_q4_k(w_gate_up, w_down, xq, ids, weights, n_tok, top_k, n_expert, n_ff, n_embd,
+                   out=None, workspace=None, stream=None):
+    import torch
+    ws_bytes = moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd)
+    if out is None:
+        out = _empty((n_tok, n_embd), torch.float32, xq)
+    if workspace is None:
+        workspace = _empty((max(ws_bytes, 1),), torch.uint8, xq)
+    pgu = _need(w_gate_up, torch.uint8, n_expert * 2 * n_ff * row_bytes("q4_k", n_embd), "w_gate_up")
+    pdn = _need(w_down, torch.uint8, n_expert * n_embd * row_bytes("q4_k", n_ff), "w_down")
+    pq = _need(xq, torch.uint8, n_tok * row_bytes("q8_1", n_embd), "xq")
+    pid = _need(ids, torch.int32, n_tok * top_k * 4, "ids")
+    pwt = _need(weights, torch.float32, n_tok * top_k * 4, "weights")
+    po = _need(out, torch.float32, n_tok * n_embd * 4, "out")
+    pws = _need(workspace, torch.uint8, ws_bytes, "workspace")
+    _check("moe_qgemv_q4_k", lib().moe_qgemv_q4_k(pgu, pdn, pq, pid, pwt, po, n_tok, top_k, n_expert, n_ff, n_embd,
+                                                  pws, workspace.numel(), _stream(stream)))
+    return out
+
+
+def moe_workspace_regions(workspace, n_tok, top_k, n_ff, n_embd):
+    """Views of the MoE workspace regions: (h^ Q8_1 [P][n_ff/32*36] uint8,
+    g|u f32 [P][2*n_ff], weighted down f32 [P][n_embd]) -- the documented layout."""
+    import torch
+
+    def up(v):
+        return (v + 255) & ~255
+
+    P = n_tok * top_k
+    hq_bytes = P * row_bytes("q8_1", n_ff)
+    gu_off = up(hq_bytes)
+    z_off = gu_off + up(P * 2 * n_ff * 4)
+    hq = workspace[:hq_bytes].view(P, row_bytes("q8_1", n_ff))
+    gu = workspace[gu_off:gu_off + P * 2 * n_ff * 4].view(torch.float32).view(P, 2 * n_ff)
+    z = workspace[z_off:z_off + P * n_embd * 4].view(torch.float32).view(P, n_embd)
+    return hq, gu, z
+
+
+# ------------------------------------------------------- per-block dots (tests)
+def blockdots_q8_0(w, xq, n, k, stream=None):
+    import torch
+    D = _empty((n, k // 32), torch.int32, w)
+    _check("qg_blockdots_q8_0", lib().qg_blockdots_q8_0(
+        _need(w, torch.uint8, n * row_bytes("q8_0", k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
+        _need(D, torch.int32, D.numel() * 4, "D"), n, k, _stream(stream)))
+    return D
+
+
+def blockdots_q4_k(w, xq, n, k, stream=None):
+    import torch
+    D = _empty((n, k // 32), torch.int32, w)
+    S = _empty((k // 32,), torch.int32, w)
+    _check("qg_blockdots_q4_k", lib().qg_blockdots_q4_k(
+        _need(w, torch.uint8, n * row_bytes("q4_k", k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
+        _need(D, torch.int32, D.numel() * 4, "D"), _need(S, torch.int32, S.numel() * 4, "S"), n, k,
+        _stream(stream)))
+    return D, S
+
+
+def blockdots_q6_k(w, xq, n, k, stream=None):
+    import torch
+    D = _empty((n, k // 16), torch.int32, w)
+    _check("qg_blockdots_q6_k", lib().qg_blockdots_q6_k(
+        _need(w, torch.uint8, n * row_bytes("q6_k", k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
+        _need(D, torch.int32, D.numel() * 4, "D"), n, k, _stream(stream)))
+    return D
+
+
+def blockdots_q4_k_mmq(w, aq, m, n, k, stream=None):
+    import torch
+    D = _empty((m, n, k // 32), torch.int32, w)
+    _check("qg_blockdots_q4_k_mmq", lib().qg_blockdots_q4_k_mmq(
+        _need(w, torch.uint8, n * row_bytes("q4_k", k), "w"), _need(aq, torch.uint8, m * row_bytes("q8_1", k), "aq"),
+        _need(D, torch.int32, D.numel() * 4, "D"), m, n, k, _stream(stream)))
+    return D

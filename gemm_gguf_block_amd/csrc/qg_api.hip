@@ -1,0 +1,196 @@
+// qg_api.hip -- the C ABI of libqgguf.so (declared in include/qgguf.h).
+//
+// Every entry point validates its arguments before touching the HIP runtime:
+// on any error nothing is launched and nothing is written.  Then it checks
+// once per device that the current device is gfx950 and enqueues its kernels
+// on the caller's stream.  The status codes mirror the pages' habit of one
+// distinct, named error per failure class (blazr 0.4.0 release notes,
+// "Changed": model lookup / load / out-of-memory errors).
+#include <atomic>
+#include <string.h>
+
+#include "../../include/qgguf.h"
+#include "qg_launch.h"
+
+#define QG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other arch
+std::atomic<int> g_arch[kMaxDevices];
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+qg_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return QG_ERR_NO_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QG_ERR_NO_DEVICE;
+  if (dev >= kMaxDevices) return QG_ERR_ARCH;
+  int state = g_arch[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QG_ERR_NO_DEVICE;
+    state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? QG_OK : QG_ERR_ARCH;
+}
+
+qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH; }
+
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+// fmt 0 = Q8_0 (k % 32), 1 = Q4_K, 2 = Q6_K (k % 256)
+qg_status check_gemv(int fmt, const void *w, const void *xq, const void *out, int64_t n, int64_t k) {
+  if (!w || !xq || !out) return QG_ERR_NULL;
+  if (n < 0 || k < 0 || n > kMaxRows || k > kMaxK) return QG_ERR_SHAPE;
+  if (k % (fmt == 0 ? 32 : 256) != 0) return QG_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+qg_status run_gemv(int fmt, const void *w, const void *xq, float *y, int32_t *D, int32_t *S, int64_t n, int64_t k,
+                   hipStream_t stream) {
+  if (n == 0) return QG_OK;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_qgemv(fmt, w, xq, y, D, S, n, k, stream));
+}
+
+qg_status check_mmq(const void *w, const void *aq, const void *out, int64_t m, int64_t n, int64_t k) {
+  if (!w || !aq || !out) return QG_ERR_NULL;
+  if (m < 0 || n < 0 || k < 0 || m > kMaxRows || n > kMaxRows || k > kMaxK || k % 256 != 0) return QG_ERR_SHAPE;
+  if (((m + 63) / 64) * ((n + 63) / 64) > kMaxRows) return QG_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(aq, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+}  // namespace
+
+QG_EXPORT const char *qg_status_str(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "a required pointer is NULL";
+    case QG_ERR_SHAPE: return "invalid shape (negative, not a multiple of the block size, or too large)";
+    case QG_ERR_ALIGN: return "pointer not aligned (block buffers and f32 inputs 16 B, outputs 4 B)";
+    case QG_ERR_WORKSPACE: return "workspace too small";
+    case QG_ERR_NO_DEVICE: return "no HIP device available";
+    case QG_ERR_ARCH: return "current device is not gfx950";
+    case QG_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+QG_EXPORT qg_status quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t k, hipStream_t stream) {
+  if (!x || !xq) return QG_ERR_NULL;
+  if (rows < 0 || k < 0 || k % 32 != 0 || k > (int64_t(1) << 30)) return QG_ERR_SHAPE;
+  if (rows > 0 && k > 0 && rows > (int64_t(1) << 40) / k) return QG_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(xq, 16)) return QG_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QG_OK;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_quantize_q8_1(x, xq, rows, k, stream));
+}
+
+QG_EXPORT qg_status qgemv_q8_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv(0, w, xq, y, n, k);
+  return st != QG_OK ? st : run_gemv(0, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemv_q4_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv(1, w, xq, y, n, k);
+  return st != QG_OK ? st : run_gemv(1, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv(2, w, xq, y, n, k);
+  return st != QG_OK ? st : run_gemv(2, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  qg_status st = check_mmq(w, aq, c, m, n, k);
+  if (st != QG_OK) return st;
+  if (m == 0 || n == 0) return QG_OK;
+  st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_qgemm_q4_k_mmq(w, aq, c, nullptr, m, n, k, stream));
+}
+
+QG_EXPORT size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
+                                               int64_t n_embd) {
+  (void)n_expert;
+  if (n_tok < 0 || top_k < 0 || n_ff < 0 || n_embd < 0) return 0;
+  return qg::moe_layout(n_tok, top_k, n_ff, n_embd).total;
+}
+
+QG_EXPORT qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                                   const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
+                                   int64_t n_ff, int64_t n_embd, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!w_gate_up || !w_down || !xq || !ids || !weights || !out || !workspace) return QG_ERR_NULL;
+  if (n_tok < 0 || top_k < 1 || top_k > 64 || n_expert < 1 || n_expert > (1 << 16) || n_ff < 0 || n_embd < 0)
+    return QG_ERR_SHAPE;
+  if (n_ff % 256 != 0 || n_embd % 256 != 0 || n_ff > (1 << 20) || n_embd > (1 << 20)) return QG_ERR_SHAPE;
+  if (n_tok * top_k > (1 << 20)) return QG_ERR_SHAPE;
+  if (n_ff == 0 || n_embd == 0) return QG_ERR_SHAPE;
+  if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(xq, 16) || !aligned(ids, 4) ||
+      !aligned(weights, 4) || !aligned(out, 4) || !aligned(workspace, 256))
+    return QG_ERR_ALIGN;
+  const qg::MoeLayout lay = qg::moe_layout(n_tok, top_k, n_ff, n_embd);
+  if (workspace_bytes < lay.total) return QG_ERR_WORKSPACE;
+  if (n_tok == 0) return QG_OK;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  qg::MoeArgs a;
+  a.w_gu = w_gate_up;
+  a.w_down = w_down;
+  a.xq = xq;
+  a.ids = ids;
+  a.weights = weights;
+  a.out = out;
+  a.n_tok = n_tok;
+  a.top_k = top_k;
+  a.n_expert = n_expert;
+  a.n_ff = n_ff;
+  a.n_embd = n_embd;
+  a.ws_hq = ws + lay.hq_off;
+  a.ws_gu = reinterpret_cast<float *>(ws + lay.gu_off);
+  a.ws_z = reinterpret_cast<float *>(ws + lay.z_off);
+  return launched(qg::launch_moe_q4_k(a, stream));
+}
+
+QG_EXPORT qg_status qg_blockdots_q8_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k,
+                                      hipStream_t stream) {
+  qg_status st = check_gemv(0, w, xq, D, n, k);
+  return st != QG_OK ? st : run_gemv(0, w, xq, nullptr, D, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q4_k(const void *w, const void *xq, int32_t *D, int32_t *S, int64_t n, int64_t k,
+                                      hipStream_t stream) {
+  if (!S) return QG_ERR_NULL;
+  if (!aligned(S, 4)) return QG_ERR_ALIGN;
+  qg_status st = check_gemv(1, w, xq, D, n, k);
+  return st != QG_OK ? st : run_gemv(1, w, xq, nullptr, D, S, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q6_k(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k,
+                                      hipStream_t stream) {
+  qg_status st = check_gemv(2, w, xq, D, n, k);
+  return st != QG_OK ? st : run_gemv(2, w, xq, nullptr, D, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q4_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  qg_status st = check_mmq(w, aq, D, m, n, k);
+  if (st != QG_OK) return st;
+  if (m > 0 && n > 0 && k > 0 && m * n > (int64_t(1) << 28) / (k / 32)) return QG_ERR_SHAPE;
+  if (m == 0 || n == 0) return QG_OK;
+  st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_qgemm_q4_k_mmq(w, aq, nullptr, D, m, n, k, stream));
+}

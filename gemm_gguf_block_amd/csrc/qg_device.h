@@ -1,0 +1,91 @@
+// qg_device.h -- device helpers shared by the gfx950 kernels of libqgguf.
+//
+// Block layouts are GGUF's (the pages name the types only -- blazr README,
+// "Model Formats > GGUF"):
+//   Q8_0 34 B = fp16 d | int8 qs[32]
+//   Q8_1 36 B = fp16 d | fp16 s | int8 qs[32]     (qs is dword-aligned in a block)
+//   Q4_K 144 B = fp16 d | fp16 dmin | scales[12] | qs[128]   (9 x 16 B, aligned)
+//   Q6_K 210 B = ql[128] | qh[64] | int8 scales[16] | fp16 d
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kQ8_0Bytes = 34;
+constexpr int kQ8_1Bytes = 36;
+constexpr int kQ4KBytes = 144;
+constexpr int kQ6KBytes = 210;
+
+// 16 bytes at a 4-byte aligned address: global_load_dwordx4 needs only dword
+// alignment, and this type tells the compiler exactly that.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ u32x2 ld8(const uint8_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+__device__ __forceinline__ uint32_t ld2(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
+
+// binary16 bits (low 16 bits of `h`) -> f32, exact.
+__device__ __forceinline__ float h2f(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+}
+
+// f32 -> binary16 bits, round to nearest even (v_cvt_f16_f32 in the default
+// rounding mode, with fp16 denormals preserved).
+__device__ __forceinline__ uint32_t f2h(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Signed int8x4 dot product with int32 accumulate (v_dot4c_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Sum of the four signed bytes of `a`, added to c.
+__device__ __forceinline__ int bsum4(uint32_t a, int c) { return dot4(a, 0x01010101u, c); }
+
+// ({hi,lo} >> 8*shift)[31:0] for shift in 0..3 (v_alignbyte_b32).
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t shift) {
+  return __builtin_amdgcn_alignbyte(hi, lo, shift);
+}
+
+// 16 bytes starting at a 2-byte aligned address p inside a buffer, read as
+// dword loads only: five dwords from p & ~3, realigned.  Reads at most the 4
+// bytes following the 16 (and none before p & ~3); callers keep p+20 inside
+// the buffer.
+__device__ __forceinline__ void ld16_a2(const uint8_t *p, uint32_t out[4]) {
+  const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint8_t *a = p - sh;
+  u32x4 v = ld16(a);
+  uint32_t e = ld4(a + 16);
+  out[0] = align_bytes(v.y, v.x, sh);
+  out[1] = align_bytes(v.z, v.y, sh);
+  out[2] = align_bytes(v.w, v.z, sh);
+  out[3] = align_bytes(e, v.w, sh);
+}
+
+// Butterfly sum over aligned groups of L lanes (L a power of two <= 64).
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ int group_isum(int v) {
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace qg

@@ -1,0 +1,36 @@
+// qg_launch.h -- internal launchers (validated arguments only; called by the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+hipError_t launch_quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t k, hipStream_t stream);
+
+// fmt: 0 = Q8_0, 1 = Q4_K, 2 = Q6_K.  D/S non-null selects the per-block dot
+// dump instead of y.
+hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_t *D, int32_t *S, int64_t n,
+                        int64_t k, hipStream_t stream);
+
+hipError_t launch_qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,
+                                 int64_t k, hipStream_t stream);
+
+struct MoeArgs {
+  const void *w_gu, *w_down, *xq;
+  const int32_t *ids;
+  const float *weights;
+  float *out;
+  int64_t n_tok, top_k, n_expert, n_ff, n_embd;
+  uint8_t *ws_hq;   // Q8_1 h^ per pair
+  float *ws_gu;     // g|u per pair
+  float *ws_z;      // weighted down projection per pair
+};
+hipError_t launch_moe_q4_k(const MoeArgs &a, hipStream_t stream);
+
+// Workspace region offsets for the MoE call (each 256-byte aligned).
+struct MoeLayout {
+  size_t hq_off, gu_off, z_off, total;
+};
+MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd);
+
+}  // namespace qg

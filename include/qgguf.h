@@ -1,0 +1,159 @@
+/*
+ * qgguf.h -- C ABI of libqgguf.so: dequantize-fused quantized-weight GEMV and
+ * small-batch / prefill matrix products on AMD Instinct MI355X (gfx950).
+ *
+ * Weights are GGUF Q8_0, Q4_K or Q6_K blocks, dotted against activations
+ * quantized to Q8_1 blocks.  The pages this library follows name these types
+ * as the ones with dedicated integer-dot GPU kernels (blazr README, "Model
+ * Formats > GGUF"), describe in-shader dequantization feeding an integer mmq
+ * path (infr page, "models"), and MoE expert calls (infr page, "Per-op device
+ * profiling": the expert_gateup role; "Paged experts").  They give no byte
+ * layout; the layouts below are GGUF's published ones, little-endian:
+ *
+ *   Q8_0 (32 values, 34 B):  fp16 d | int8 qs[32]               w = d*qs[i]
+ *   Q8_1 (32 values, 36 B):  fp16 d | fp16 s | int8 qs[32]      x = d*qs[i],
+ *                            s = d*sum(qs) (informational; not read by dots)
+ *   Q4_K (256 values, 144 B): fp16 d | fp16 dmin | u8 scales[12] | u8 qs[128]
+ *        sub-block j = i/32 has 6-bit scale sc_j and min m_j packed in
+ *        scales[]; w = d*sc_j*q - dmin*m_j with q the 4-bit code.
+ *   Q6_K (256 values, 210 B): u8 ql[128] | u8 qh[64] | int8 scales[16] | fp16 d
+ *        w = d*scales[i/16]*(q - 32) with q the 6-bit code.
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major.  A weight matrix of n rows and k columns is n
+ *     rows of k/block_elems blocks, rows contiguous.
+ *   - All pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates and frees nothing.  Block buffers (weights, Q8_1) and float
+ *     inputs must be 16-byte aligned; float / int32 outputs 4-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     and return; they never synchronize.  Launch errors are reported from
+ *     hipGetLastError right after the enqueue; device faults surface at the
+ *     caller's next synchronization.
+ *   - Arguments are validated before any HIP call.  On any error nothing is
+ *     launched and nothing is written.  Outputs are overwritten, not
+ *     accumulated.  Empty problems (n == 0 or m == 0) return QG_OK and launch
+ *     nothing; k == 0 writes zeros.
+ *   - Devices other than gfx950 are refused with QG_ERR_ARCH.
+ *   - Calls on one stream are ordered; calls on different streams that write
+ *     the same buffers race, as for any HIP kernel.
+ */
+#ifndef QGGUF_H
+#define QGGUF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULL = 1,      /* a required pointer is NULL */
+    QG_ERR_SHAPE = 2,     /* negative size, k not a multiple of the block, size too large */
+    QG_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+    QG_ERR_WORKSPACE = 4, /* MoE workspace smaller than moe_qgemv_q4_k_workspace_size() */
+    QG_ERR_NO_DEVICE = 5, /* no HIP device is visible */
+    QG_ERR_ARCH = 6,      /* the current device is not gfx950 */
+    QG_ERR_LAUNCH = 7     /* the kernel launch failed */
+} qg_status;
+
+/* Static description of a status code (never NULL). */
+const char *qg_status_str(qg_status s);
+
+/*
+ * quantize_q8_1 -- activations f32 -> Q8_1 (the activation side of every dot).
+ * Per block of 32 values: amax = max|x|; d = amax/127 (fp32, correctly
+ * rounded); q = round-half-away-from-zero(x/d), computed from the fp32 d and
+ * clamped to [-127, 127]; s = d*sum(q) as an fp32 product.  d and s are stored
+ * rounded once to fp16 (round to nearest even, subnormals kept).  A block whose
+ * values are all zero stores d = s = 0 and q = 0.
+ *   x   : f32 [rows][k], 16-byte aligned
+ *   xq  : Q8_1 [rows][k/32] (36 B each), 16-byte aligned, written
+ *   k   : multiple of 32, <= 2^30;  rows * k <= 2^40
+ */
+qg_status quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t k, hipStream_t stream);
+
+/*
+ * qgemv_q8_0 / qgemv_q4_k / qgemv_q6_k -- batch-1 decode GEMV, y = W . x^.
+ * y[r] = sum_j w^[r][j] * x^[j] with w^ dequantized from the weight blocks and
+ * x^ from the Q8_1 activation.  Computed from exact per-block int32 dots
+ * (Q8_0 and Q4_K: per 32 values; Q6_K: per 16 values) scaled in fp32.
+ *   w   : weight blocks [n][k/block_elems]
+ *   xq  : Q8_1 [k/32] (one activation row)
+ *   y   : f32 [n], written
+ *   k   : multiple of 32 (Q8_0) or 256 (Q4_K, Q6_K), <= 2^24;  n <= 2^31 - 1
+ */
+qg_status qgemv_q8_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
+qg_status qgemv_q4_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
+qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
+
+/*
+ * qgemm_q4_k_mmq -- prefill product on int8 matrix cores.
+ * c[i][r] = sum_j a^[i][j] * w^[r][j]: each 32-wide slice of k is one int8
+ * 32x32x32 MFMA tile of exact per-block dots, rescaled in fp32 by d*sc_j*d_a
+ * with the min term -dmin*m_j*d_a*sum(qa) of that Q8_1 block.
+ *   w   : Q4_K [n][k/256]
+ *   aq  : Q8_1 [m][k/32] (m activation rows, e.g. tokens)
+ *   c   : f32 [m][n] row-major, written
+ *   k   : multiple of 256, <= 2^24;  m, n <= 2^31 - 1
+ */
+qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream);
+
+/*
+ * MoE expert FFN with Q4_K experts (the expert_gateup + down calls of an MoE
+ * layer).  For token t and each routed slot i with expert e = ids[t][i]:
+ *   g = Wgu[e][0:n_ff] . x^_t, u = Wgu[e][n_ff:2n_ff] . x^_t       (fp32)
+ *   h = silu(g) * u, silu(g) = g / (1 + exp(-g))                   (fp32)
+ *   h^ = Q8_1(h) exactly as quantize_q8_1
+ *   out[t] = sum_i weights[t][i] * (Wdown[e] . h^)                  (fp32)
+ * The routing table is an input; ids outside [0, n_expert) contribute nothing.
+ * Each touched expert's weights are read once for all of its tokens.
+ *   w_gate_up : Q4_K [n_expert][2*n_ff][n_embd/256]; rows 0..n_ff-1 gate,
+ *               n_ff..2n_ff-1 up
+ *   w_down    : Q4_K [n_expert][n_embd][n_ff/256]
+ *   xq        : Q8_1 [n_tok][n_embd/32]
+ *   ids       : int32 [n_tok][top_k];  weights : f32 [n_tok][top_k]
+ *   out       : f32 [n_tok][n_embd], written
+ *   workspace : device scratch of at least moe_qgemv_q4_k_workspace_size()
+ *               bytes, 256-byte aligned, owned by the caller.  Layout, for
+ *               P = n_tok*top_k pairs p = t*top_k + i:
+ *                 [0, P*(n_ff/32)*36)            h^ per pair, Q8_1
+ *                 then f32 [P][2*n_ff]           g | u per pair
+ *                 then f32 [P][n_embd]           weights[p] * (Wdown . h^)
+ *               each region starting on a 256-byte boundary.
+ *   n_embd, n_ff : multiples of 256, <= 2^20;  top_k in [1, 64];
+ *   n_tok * top_k <= 2^20;  n_expert in [1, 2^16]
+ */
+size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
+                                     int64_t n_embd);
+qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                         const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
+                         int64_t n_ff, int64_t n_embd, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Test access to the exact per-block int32 dots, computed by the same device
+ * unpack and dot code the products above run (not for production use).
+ *   qg_blockdots_q8_0 : D int32 [n][k/32],  D[r][b] = sum_i qw*qa over block b
+ *   qg_blockdots_q4_k : D int32 [n][k/32] (4-bit codes times qa per 32 values),
+ *                       S int32 [k/32] = sum of qa per activation block
+ *   qg_blockdots_q6_k : D int32 [n][k/16],  sum over 16 values of (q-32)*qa
+ *   qg_blockdots_q4_k_mmq : D int32 [m][n][k/32] from the int8 MFMA tiles of
+ *                       qgemm_q4_k_mmq; m*n*(k/32) <= 2^28
+ * Same validation rules and limits as the corresponding products.
+ */
+qg_status qg_blockdots_q8_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
+qg_status qg_blockdots_q4_k(const void *w, const void *xq, int32_t *D, int32_t *S, int64_t n, int64_t k,
+                            hipStream_t stream);
+qg_status qg_blockdots_q6_k(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
+qg_status qg_blockdots_q4_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGGUF_H */
