@@ -1,0 +1,377 @@
+"""Benchmark of the quantized GEMV / mmq hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input:
+quantize the activations to Q8_1 on the GPU, then run the product on the
+quantized weights.  Default workload: the Q4_K decode GEMV at a Llama-3-8B FFN
+shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
+q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each).
+
+Inputs are resident in HBM before timing starts.  The weights are replicated
+into enough copies (>= 512 MB in total) that consecutive steps read different
+copies, so the 256 MB Infinity Cache cannot serve them (--warm disables this).
+
+Printed per workload: one JSON line with the step throughput (`value`), the
+dominant kernel's roofline position measured with HIP events on the launch
+stream, and the CPU oracle's throughput on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMV HBM GB/s (% of peak) and tokens/s-equivalent; mmq TOPS at M=512"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
+COLD_BYTES = 512 << 20       # rotate weight copies until at least this much
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def q81_bytes(k):
+    return (k // 32) * 36
+
+
+def _cpu_threads():
+    v = os.environ.get("OMP_NUM_THREADS")
+    return int(v) if v and v.isdigit() else (os.cpu_count() or 1)
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, if one exists
+    for this kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration factor recorded beside them)."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    return None if not rec else rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads
+class Workload:
+    """Holds device inputs and issues one step; subclasses define the work."""
+
+    name = ""
+    dominant = ""        # kernel name the roofline refers to
+
+    def step(self, i):
+        raise NotImplementedError
+
+    def dominant_call(self, i):
+        raise NotImplementedError
+
+
+class Gemv(Workload):
+    def __init__(self, qg, torch, name, warm):
+        from gemm_gguf_block_amd import synth
+        p = synth.WORKLOADS[name]
+        self.name, self.fmt, self.n, self.k = name, p["fmt"], p["n"], p["k"]
+        self.seed = p["seed"]
+        self.qg, self.torch = qg, torch
+        dev = torch.device("cuda:0")
+        w = synth.weights(self.fmt, self.n, self.k, self.seed)
+        self.w_host = w
+        self.x_host = synth.normal(self.seed, synth.T_X, (self.k,))
+        wbytes = w.nbytes
+        self.copies = 1 if warm else max(1, math.ceil(COLD_BYTES / wbytes))
+        W0 = torch.from_numpy(w).to(dev)
+        self.W = [W0] + [W0.clone() for _ in range(self.copies - 1)]
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.xq = torch.empty(q81_bytes(self.k), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(self.n, dtype=torch.float32, device=dev)
+        self.fn = getattr(qg, "qgemv_" + self.fmt)
+        self.dominant = "gemv_" + self.fmt.replace("_", "")
+        # algorithmic bytes: every weight byte once, the activation, the output
+        self.kernel_bytes = wbytes + q81_bytes(self.k) + 4 * self.n
+        self.step_bytes = self.kernel_bytes + 4 * self.k + q81_bytes(self.k)  # + quantize's f32 read / Q8_1 write
+        self.tokens_per_step = 1
+        self.unit, self.bound = "GB/s", "hbm"
+
+    def step(self, i):
+        self.qg.quantize_q8_1(self.x, self.xq)
+        self.fn(self.W[i % self.copies], self.xq, self.n, self.k, y=self.y)
+
+    def dominant_call(self, i):
+        self.fn(self.W[i % self.copies], self.xq, self.n, self.k, y=self.y)
+
+    def value(self, sec_per_step):
+        return self.step_bytes / sec_per_step / 1e9
+
+    def kernel_rate(self, sec):
+        return self.kernel_bytes / sec / 1e9
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle
+        xq = oracle.quantize_q8_1(self.x_host[None])[0]
+        rows, t = 64, 0.0
+        while True:
+            sel = np.arange(min(rows, self.n), dtype=np.int64)
+            t0 = time.perf_counter()
+            oracle.qgemv(self.fmt, self.w_host, xq, self.n, self.k, rows=sel)
+            t = time.perf_counter() - t0
+            if t >= budget_s / 4 or rows >= self.n:
+                break
+            rows = min(self.n, rows * 4)
+        nb = sel.size * (self.w_host.shape[1]) + q81_bytes(self.k) + 4 * sel.size
+        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
+                    sample=f"rows 0..{sel.size - 1} of {self.n} (plain double dequant-and-dot), {t:.2f} s")
+
+
+class Mmq(Workload):
+    def __init__(self, qg, torch, warm):
+        from gemm_gguf_block_amd import synth
+        p = synth.WORKLOADS["q4_k_mmq"]
+        self.name, self.m, self.n, self.k = "q4_k_mmq", p["m"], p["n"], p["k"]
+        self.qg, self.torch = qg, torch
+        dev = torch.device("cuda:0")
+        w = synth.weights("q4_k", self.n, self.k, p["seed"])
+        self.w_host = w
+        self.a_host = synth.normal(p["seed"], synth.T_X, (self.m, self.k))
+        self.copies = 1 if warm else max(1, math.ceil(COLD_BYTES / w.nbytes))
+        W0 = torch.from_numpy(w).to(dev)
+        self.W = [W0] + [W0.clone() for _ in range(self.copies - 1)]
+        self.a = torch.from_numpy(self.a_host).to(dev)
+        self.aq = torch.empty((self.m, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
+        self.c = torch.empty((self.m, self.n), dtype=torch.float32, device=dev)
+        self.dominant = "mmq_q4k"
+        self.ops = 2.0 * self.m * self.n * self.k
+        self.kernel_bytes = w.nbytes + self.m * q81_bytes(self.k) + 4 * self.m * self.n
+        self.tokens_per_step = self.m
+        self.unit, self.bound = "TOPS", "mfma"
+
+    def step(self, i):
+        self.qg.quantize_q8_1(self.a, self.aq)
+        self.qg.qgemm_q4_k_mmq(self.W[i % self.copies], self.aq, self.m, self.n, self.k, c=self.c)
+
+    def dominant_call(self, i):
+        self.qg.qgemm_q4_k_mmq(self.W[i % self.copies], self.aq, self.m, self.n, self.k, c=self.c)
+
+    def value(self, sec_per_step):
+        return self.ops / sec_per_step / 1e12
+
+    def kernel_rate(self, sec):
+        return self.ops / sec / 1e12
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle
+        aq = oracle.quantize_q8_1(self.a_host)
+        g = np.random.default_rng(0)
+        cnt, t = 256, 0.0
+        while True:
+            pairs = np.stack([g.integers(0, self.m, cnt), g.integers(0, self.n, cnt)], 1)
+            t0 = time.perf_counter()
+            oracle.qgemm_q4_k(self.w_host, aq, self.m, self.n, self.k, pairs=pairs)
+            t = time.perf_counter() - t0
+            if t >= budget_s / 4 or cnt >= self.m * self.n:
+                break
+            cnt *= 4
+        return dict(value=2.0 * cnt * self.k / t / 1e12, unit="TOPS", cores=_cpu_threads(), kind="oracle",
+                    sample=f"{cnt} random entries of C[{self.m}][{self.n}] (plain double dequant-and-dot), {t:.2f} s")
+
+
+class Moe(Workload):
+    def __init__(self, qg, torch, warm):
+        import numpy as np
+
+        from gemm_gguf_block_amd import synth
+        p = synth.WORKLOADS["moe_q4_k"]
+        self.name = "moe_q4_k"
+        self.E, self.F, self.H, self.T, self.K = p["n_expert"], p["n_ff"], p["n_embd"], p["n_tok"], p["top_k"]
+        self.qg, self.torch = qg, torch
+        dev = torch.device("cuda:0")
+        inp = synth.workload("moe_q4_k")
+        self.inp = inp
+        wbytes = inp["w_gu"].nbytes + inp["w_down"].nbytes
+        self.copies = 1 if warm else max(1, math.ceil(COLD_BYTES / wbytes))
+        gu0, dn0 = torch.from_numpy(inp["w_gu"]).to(dev), torch.from_numpy(inp["w_down"]).to(dev)
+        self.Wgu = [gu0] + [gu0.clone() for _ in range(self.copies - 1)]
+        self.Wdn = [dn0] + [dn0.clone() for _ in range(self.copies - 1)]
+        self.x = torch.from_numpy(inp["x"]).to(dev)
+        self.ids = torch.from_numpy(inp["ids"]).to(dev)
+        self.rw = torch.from_numpy(inp["weights"]).to(dev)
+        self.xq = torch.empty((self.T, q81_bytes(self.H)), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((self.T, self.H), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(qg.moe_qgemv_q4_k_workspace_size(self.T, self.K, self.E, self.F, self.H),
+                              dtype=torch.uint8, device=dev)
+        self.distinct = int(np.unique(inp["ids"]).size)
+        per_expert = wbytes // self.E
+        self.dominant = "moe (4 kernels)"
+        self.kernel_bytes = self.distinct * per_expert + self.T * q81_bytes(self.H) + 4 * self.T * self.H
+        self.step_bytes = self.kernel_bytes + 4 * self.T * self.H + self.T * q81_bytes(self.H)
+        self.tokens_per_step = self.T
+        self.unit, self.bound = "GB/s", "hbm"
+
+    def _moe(self, i):
+        c = i % self.copies
+        self.qg.moe_qgemv_q4_k(self.Wgu[c], self.Wdn[c], self.xq, self.ids, self.rw, self.T, self.K, self.E, self.F,
+                               self.H, out=self.out, workspace=self.ws)
+
+    def step(self, i):
+        self.qg.quantize_q8_1(self.x, self.xq)
+        self._moe(i)
+
+    def dominant_call(self, i):
+        self._moe(i)
+
+    def value(self, sec_per_step):
+        return self.step_bytes / sec_per_step / 1e9
+
+    def kernel_rate(self, sec):
+        return self.kernel_bytes / sec / 1e9
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        inp = self.inp
+        T = 1
+        while True:
+            xq = oracle.quantize_q8_1(inp["x"][:T])
+            t0 = time.perf_counter()
+            oracle.moe_q4_k(inp["w_gu"], inp["w_down"], xq, inp["ids"][:T], inp["weights"][:T], T, self.K, self.E,
+                            self.F, self.H)
+            t = time.perf_counter() - t0
+            if t >= budget_s / 4 or T >= self.T:
+                break
+            T = min(self.T, T * 2)
+        import numpy as np
+        dist = int(np.unique(inp["ids"][:T]).size)
+        nb = dist * (inp["w_gu"].nbytes + inp["w_down"].nbytes) // self.E
+        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
+                    sample=f"first {T} of {self.T} tokens ({dist} distinct experts), {t:.2f} s")
+
+
+def make(name, qg, torch, warm):
+    if name.endswith("_gemv"):
+        return Gemv(qg, torch, name, warm)
+    if name == "q4_k_mmq":
+        return Mmq(qg, torch, warm)
+    if name == "moe_q4_k":
+        return Moe(qg, torch, warm)
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ---------------------------------------------------------------- timing
+def run(wl, steps, warmup, torch):
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    # whole steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        wl.step(warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # dominant kernel: back-to-back launches between two events on its stream
+    for i in range(warmup):
+        wl.dominant_call(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        wl.dominant_call(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_kernel = e0.elapsed_time(e1) / steps
+    return ms_step, ms_kernel
+
+
+def bench_one(name, args, qg, torch):
+    t_setup = time.time()
+    wl = make(name, qg, torch, args.warm)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    ms_step, ms_kernel = run(wl, args.steps, args.warmup, torch)
+    value = wl.value(ms_step / 1e3)
+    achieved = wl.kernel_rate(ms_kernel / 1e3)
+    peak = HBM_PEAK_GBS if wl.unit == "GB/s" else INT8_PEAK_TOPS
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": wl.unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": name},
+        "tokens_per_s_equiv": round(wl.tokens_per_step / (ms_step / 1e3), 1),
+        "roofline": {
+            "bound": wl.bound,
+            "kernel": wl.dominant,
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "GB/s" if wl.unit == "GB/s" else "TOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": _traffic(name),
+            "ms_per_launch": round(ms_kernel, 6),
+            "algorithmic_per_launch": wl.kernel_bytes if wl.unit == "GB/s" else wl.ops,
+        },
+    }
+    if wl.unit == "GB/s":
+        rec["pct_of_hbm_peak"] = round(100.0 * value / HBM_PEAK_GBS, 2)
+    cfg = rec["config"]
+    for key in ("fmt", "m", "n", "k", "E", "F", "H", "T", "K"):
+        if hasattr(wl, key):
+            cfg[key] = getattr(wl, key)
+    cfg["weight_copies"] = wl.copies
+    if name == "moe_q4_k":
+        cfg["distinct_experts"] = wl.distinct
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
+    print(f"[bench] {name}: setup {setup_s:.1f} s, step {ms_step * 1e3:.2f} us, "
+          f"{wl.dominant} {ms_kernel * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q4_k_gemv",
+                    help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, or all")
+    ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gemm_gguf_block_amd as qg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    names = (["q4_k_gemv", "q8_0_gemv", "q6_k_gemv", "q4_k_mmq", "moe_q4_k"]
+             if args.workload == "all" else [args.workload])
+    for name in names:
+        rec = bench_one(name, args, qg, torch)
+        print(json.dumps(rec), flush=True)
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

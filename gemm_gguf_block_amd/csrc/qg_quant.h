@@ -34,7 +34,11 @@ __device__ __forceinline__ void quantize_block_q8_1(float4 v, uint8_t *blk, int 
                             ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
     *reinterpret_cast<uint32_t *>(blk + 4 + 4 * j) = packed;
     if (j == 0) {
-      const float s = d * (float)sum;
+      // s is the fp32 product, rounded to fp16 afterwards.  The empty asm pins
+      // the product in a VGPR so it cannot be fused with the conversion into
+      // one v_fma_mix that would round only once.
+      float s = d * (float)sum;
+      asm volatile("" : "+v"(s));
       *reinterpret_cast<uint32_t *>(blk) = f2h(d) | (f2h(s) << 16);
     }
   }

@@ -193,15 +193,32 @@ QUANTIZE_WEIGHTS = {"q8_0": quantize_weights_q8_0, "q4_k": quantize_weights_q4_k
 
 
 def weights(fmt: str, n: int, k: int, seed: int, tensor: int = T_W, std: float = 0.02,
-            chunk_rows: int = 8192) -> np.ndarray:
-    """N(0, std) f32 [n][k] quantized to `fmt`, drawn and quantized row-chunk by
-    row-chunk (the draw order is the same as one [n][k] draw)."""
+            chunk_rows: int = 4096, threads: int = 0) -> np.ndarray:
+    """N(0, std) f32 [n][k] quantized to `fmt`.  Row chunks are drawn in order
+    from one generator (the values equal one [n][k] draw) and quantized in a
+    thread pool; the result does not depend on the thread count."""
+    import concurrent.futures as cf
+    import os
+
     g = rng(seed, tensor)
     out = np.empty((n, row_bytes(fmt, k)), np.uint8)
-    for r0 in range(0, n, chunk_rows):
-        r1 = min(n, r0 + chunk_rows)
-        W = g.standard_normal((r1 - r0, k), dtype=np.float32) * np.float32(std)
-        out[r0:r1] = QUANTIZE_WEIGHTS[fmt](W)
+    workers = threads or min(16, os.cpu_count() or 1)
+    conv = QUANTIZE_WEIGHTS[fmt]
+
+    def job(r0, W):
+        out[r0:r0 + W.shape[0]] = conv(W)
+
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = []
+        for r0 in range(0, n, chunk_rows):
+            r1 = min(n, r0 + chunk_rows)
+            W = g.standard_normal((r1 - r0, k), dtype=np.float32)
+            W *= np.float32(std)
+            pending.append(ex.submit(job, r0, W))
+            if len(pending) >= 2 * workers:  # bound the chunks held in memory
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
     return out
 
 

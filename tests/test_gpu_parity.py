@@ -1,0 +1,356 @@
+"""GPU parity: every HIP entry point against the CPU oracle on the same seeded
+inputs.  Q8_1 bytes and per-block int32 dots must match exactly; f32 outputs
+within REL_TOL under the max(|r|, rms(r))-floored relative metric."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from _util import REL_TOL, read_golden, rel_err
+from gemm_gguf_block_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+GEMV = {"q8_0": "qgemv_q8_0", "q4_k": "qgemv_q4_k", "q6_k": "qgemv_q6_k"}
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import gemm_gguf_block_amd as qg
+    import oracle
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    return qg, oracle, torch, dev
+
+
+def _gpu(torch, dev, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------- quantize
+def test_quantize_q8_1_hand_vectors(env):
+    qg, orc, torch, dev = env
+    fx = read_golden("q8_1_vectors.txt")
+    for xs, bs in zip(fx["x"], fx["bytes"]):
+        x = np.array([float.fromhex(t) for t in xs.split()], np.float32)
+        got = _host(qg.quantize_q8_1(_gpu(torch, dev, x)))
+        assert got.tobytes() == bytes.fromhex(bs)
+
+
+# A block whose s = d*sum(q) (d = fl(2.4586923/127), sum = 729) is an fp32
+# product that sits exactly on a binary16 tie: rounding it to fp32 first and
+# then to fp16 gives 14.11, one fused rounding would give 14.12.
+DOUBLE_ROUNDING_BLOCK = ("0x1.3ab66ep+1 " + " ".join(["0x1.78a9f8p-2"] * 5) + " " +
+                         " ".join(["0x1.8c7d04p-2", "0x1.78a9f8p-2"] * 13))
+
+
+def test_quantize_q8_1_s_rounds_the_fp32_product(env):
+    qg, orc, torch, dev = env
+    x = np.array([float.fromhex(t) for t in DOUBLE_ROUNDING_BLOCK.split()], np.float32)
+    assert x.size == 32
+    got = _host(qg.quantize_q8_1(_gpu(torch, dev, x)))[0]
+    want = orc.quantize_q8_1(x[None])[0]
+    q = want[4:].view(np.int8).astype(np.int64)
+    d = np.float32(np.abs(x).max() / np.float32(127))
+    assert q.sum() == 729
+    s16 = np.float32(d * np.float32(q.sum())).astype(np.float16)
+    assert want[2:4].copy().view(np.float16)[0] == s16
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("rows,k,scale", [(1, 32, 1.0), (1, 4096, 1.0), (3, 768, 1.0), (7, 4096, 1e-6),
+                                          (5, 2048, 3e4), (33, 96, 1.0), (512, 4096, 1.0), (16, 2048, 1.0)])
+def test_quantize_q8_1_bytes_exact(env, rows, k, scale):
+    qg, orc, torch, dev = env
+    x = synth.normal(300 + rows, 1, (rows, k), std=scale)
+    x[0, :32] = 0.0                       # an all-zero block
+    if k >= 64:
+        x[-1, 32:64] = np.float32(1e-30)  # amax far below binary16 range
+    got = _host(qg.quantize_q8_1(_gpu(torch, dev, x)))
+    want = orc.quantize_q8_1(x)
+    assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------- GEMV block dots
+SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (257, 2048), (64, 4096), (33, 14336)]
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("data", ["random_bytes", "weights"])
+def test_gemv_block_dots_exact(env, fmt, n, k, data):
+    qg, orc, torch, dev = env
+    if data == "random_bytes":
+        w = synth.random_blocks(fmt, n, k, seed=n * 7 + k)
+        xq = synth.random_blocks("q8_1", 1, k, seed=n + k)
+    else:
+        w = synth.weights(fmt, n, k, seed=n + 3 * k)
+        xq = orc.quantize_q8_1(synth.normal(n + k, 1, (1, k)))
+    W, X = _gpu(torch, dev, w), _gpu(torch, dev, xq)
+    if fmt == "q4_k":
+        D, S = qg.blockdots_q4_k(W, X, n, k)
+        Dr, Sr = orc.blockdots("q4_k", w, xq, n, k)
+        assert np.array_equal(_host(S), Sr)
+    else:
+        D = getattr(qg, "blockdots_" + fmt)(W, X, n, k)
+        Dr = orc.blockdots(fmt, w, xq, n, k)
+    assert np.array_equal(_host(D), Dr)
+
+
+def test_q8_0_block_dots_odd_block_count(env):
+    """Rows of an odd number of 34-byte blocks start at 2-byte offsets."""
+    qg, orc, torch, dev = env
+    for n, k in [(5, 32), (9, 96), (64, 4064), (3, 2080)]:
+        w = synth.random_blocks("q8_0", n, k, seed=k)
+        xq = synth.random_blocks("q8_1", 1, k, seed=k + 1)
+        D = qg.blockdots_q8_0(_gpu(torch, dev, w), _gpu(torch, dev, xq), n, k)
+        assert np.array_equal(_host(D), orc.blockdots("q8_0", w, xq, n, k))
+
+
+# ---------------------------------------------------------------- GEMV values
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("n,k", SHAPES + [(1, 4096), (511, 1024), (1000, 4096)])
+def test_gemv_values(env, fmt, n, k):
+    qg, orc, torch, dev = env
+    w = synth.weights(fmt, n, k, seed=11 * n + k)
+    x = synth.normal(n + 5 * k, 1, (k,))
+    X = qg.quantize_q8_1(_gpu(torch, dev, x))
+    y = getattr(qg, GEMV[fmt])(_gpu(torch, dev, w), X, n, k)
+    xq = orc.quantize_q8_1(x[None])[0]
+    assert np.array_equal(_host(X).ravel(), xq)
+    assert rel_err(_host(y), orc.qgemv(fmt, w, xq, n, k)) <= REL_TOL
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+def test_gemv_values_random_bytes(env, fmt):
+    qg, orc, torch, dev = env
+    n, k = 300, 1024
+    w = synth.random_blocks(fmt, n, k, seed=77, lo_exp=-14, hi_exp=2)
+    xq = synth.random_blocks("q8_1", 1, k, seed=78, lo_exp=-14, hi_exp=2)
+    y = getattr(qg, GEMV[fmt])(_gpu(torch, dev, w), _gpu(torch, dev, xq), n, k)
+    assert rel_err(_host(y), orc.qgemv(fmt, w, xq, n, k)) <= REL_TOL
+
+
+def test_q8_0_values_odd_block_count(env):
+    qg, orc, torch, dev = env
+    n, k = 77, 4064
+    w = synth.weights("q8_0", n, k, seed=5)
+    xq = orc.quantize_q8_1(synth.normal(6, 1, (1, k)))
+    y = qg.qgemv_q8_0(_gpu(torch, dev, w), _gpu(torch, dev, xq), n, k)
+    assert rel_err(_host(y), orc.qgemv("q8_0", w, xq[0], n, k)) <= REL_TOL
+
+
+def _hand_activation(k):
+    nb = k // 32
+    blk = np.zeros((nb, 36), np.uint8)
+    blk[:, 0:2] = np.frombuffer(np.float16(0.125).tobytes(), np.uint8)
+    qa = np.array([(i % 7) - 3 for i in range(k)], np.int64)
+    blk[:, 4:] = qa.reshape(nb, 32).astype(np.int8).view(np.uint8)
+    return blk.reshape(1, -1), qa
+
+
+def test_gemv_hand_superblock_exact(env):
+    """Every intermediate is exactly representable in fp32, so y must equal the
+    hand-computed dot bit for bit (any summation order)."""
+    qg, orc, torch, dev = env
+    xq, qa = _hand_activation(256)
+    X = _gpu(torch, dev, xq)
+    fx = read_golden("q4_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["sc"][0].split()]
+    m = [int(t) for t in fx["m"][0].split()]
+    exact = sum((Fraction(1, 16) * sc[i // 32] * q[i] - Fraction(1, 32) * m[i // 32]) * Fraction(1, 8) * qa[i]
+                for i in range(256))
+    y = _host(qg.qgemv_q4_k(_gpu(torch, dev, np.tile(blk, (5, 1))), X, 5, 256))
+    assert all(Fraction(float(v)) == exact for v in y)
+    fx = read_golden("q6_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["scales"][0].split()]
+    exact = sum(Fraction(1, 256) * sc[i // 16] * (q[i] - 32) * Fraction(1, 8) * qa[i] for i in range(256))
+    y = _host(qg.qgemv_q6_k(_gpu(torch, dev, np.tile(blk, (3, 1))), X, 3, 256))
+    assert all(Fraction(float(v)) == exact for v in y)
+    blk = np.frombuffer(bytes.fromhex(read_golden("q8_0_block.txt")["bytes"][0]), np.uint8)
+    exact = sum(Fraction((i % 32) - 16, 4) * Fraction(1, 8) * qa[i] for i in range(256))
+    y = _host(qg.qgemv_q8_0(_gpu(torch, dev, np.tile(blk, (2, 8))), X, 2, 256))
+    assert all(Fraction(float(v)) == exact for v in y)
+
+
+def test_gemv_empty_and_zero_k(env):
+    qg, orc, torch, dev = env
+    X = torch.zeros(288, dtype=torch.uint8, device=dev)
+    y = torch.full((8,), 7.0, device=dev)
+    for fn in (qg.qgemv_q8_0, qg.qgemv_q4_k, qg.qgemv_q6_k):
+        fn(torch.zeros(16, dtype=torch.uint8, device=dev), X, 0, 256, y=y)   # n = 0: nothing written
+        assert np.all(_host(y) == 7.0)
+        fn(torch.zeros(16, dtype=torch.uint8, device=dev), X, 8, 0, y=y)     # k = 0: zeros
+        assert np.all(_host(y) == 0.0)
+        y.fill_(7.0)
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv"])
+def test_gemv_full_size(env, name):
+    """The full workload sizes in the launch configuration the bench times."""
+    qg, orc, torch, dev = env
+    p = synth.WORKLOADS[name]
+    fmt, n, k = p["fmt"], p["n"], p["k"]
+    w = synth.weights(fmt, n, k, p["seed"])
+    x = synth.normal(p["seed"], synth.T_X, (k,))
+    X = qg.quantize_q8_1(_gpu(torch, dev, x))
+    y = _host(getattr(qg, GEMV[fmt])(_gpu(torch, dev, w), X, n, k))
+    xq = orc.quantize_q8_1(x[None])[0]
+    assert np.array_equal(_host(X).ravel(), xq)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                     np.random.default_rng(1).integers(0, n, 4096)]))
+    r = orc.qgemv(fmt, w, xq, n, k, rows=rows)
+    # the floor of the metric is the RMS over the sampled rows
+    assert rel_err(y[rows], r) <= REL_TOL
+    D = getattr(qg, "blockdots_" + fmt)(_gpu(torch, dev, w[rows[:256]]), X, 256, k)
+    D = D[0] if fmt == "q4_k" else D
+    Dr = orc.blockdots(fmt, w[rows[:256]], xq, 256, k)
+    Dr = Dr[0] if fmt == "q4_k" else Dr
+    assert np.array_equal(_host(D), Dr)
+
+
+# ------------------------------------------------------------------------ mmq
+@pytest.mark.parametrize("m,n,k", [(1, 1, 256), (32, 32, 256), (64, 64, 512), (70, 100, 512), (130, 65, 768),
+                                   (3, 200, 1024)])
+def test_mmq_block_dots_exact(env, m, n, k):
+    qg, orc, torch, dev = env
+    w = synth.random_blocks("q4_k", n, k, seed=m + n)
+    aq = synth.random_blocks("q8_1", m, k, seed=m * n + k)
+    D = qg.blockdots_q4_k_mmq(_gpu(torch, dev, w), _gpu(torch, dev, aq), m, n, k)
+    assert np.array_equal(_host(D), orc.blockdots_q4_k_mmq(w, aq, m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 256), (1, 64, 4096), (64, 64, 256), (100, 130, 512), (33, 4096, 256),
+                                   (257, 70, 1024), (512, 256, 4096)])
+def test_mmq_values(env, m, n, k):
+    qg, orc, torch, dev = env
+    w = synth.weights("q4_k", n, k, seed=m + 2 * n + k)
+    a = synth.normal(m + n, 1, (m, k))
+    AQ = qg.quantize_q8_1(_gpu(torch, dev, a))
+    C = _host(qg.qgemm_q4_k_mmq(_gpu(torch, dev, w), AQ, m, n, k))
+    aq = orc.quantize_q8_1(a)
+    assert np.array_equal(_host(AQ), aq)
+    assert rel_err(C, orc.qgemm_q4_k(w, aq, m, n, k)) <= REL_TOL
+
+
+def test_mmq_hand_superblock_exact(env):
+    qg, orc, torch, dev = env
+    fx = read_golden("q4_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["sc"][0].split()]
+    m = [int(t) for t in fx["m"][0].split()]
+    xq, qa = _hand_activation(256)
+    exact = sum((Fraction(1, 16) * sc[i // 32] * q[i] - Fraction(1, 32) * m[i // 32]) * Fraction(1, 8) * qa[i]
+                for i in range(256))
+    C = _host(qg.qgemm_q4_k_mmq(_gpu(torch, dev, np.tile(blk, (70, 1))), _gpu(torch, dev, np.tile(xq, (40, 1))),
+                                40, 70, 256))
+    assert all(Fraction(float(v)) == exact for v in C.ravel())
+
+
+@pytest.mark.big
+def test_mmq_full_size(env):
+    qg, orc, torch, dev = env
+    p = synth.WORKLOADS["q4_k_mmq"]
+    m, n, k = p["m"], p["n"], p["k"]
+    w = synth.weights("q4_k", n, k, p["seed"])
+    a = synth.normal(p["seed"], synth.T_X, (m, k))
+    AQ = qg.quantize_q8_1(_gpu(torch, dev, a))
+    C = _host(qg.qgemm_q4_k_mmq(_gpu(torch, dev, w), AQ, m, n, k))
+    aq = orc.quantize_q8_1(a)
+    assert np.array_equal(_host(AQ), aq)
+    g = np.random.default_rng(3)
+    pairs = np.concatenate([np.stack([g.integers(0, m, 4096), g.integers(0, n, 4096)], 1),
+                            np.stack([np.zeros(n, int), np.arange(n)], 1),          # a full row
+                            np.stack([np.arange(m), np.full(m, n - 1)], 1)])        # a full column
+    r = orc.qgemm_q4_k(w, aq, m, n, k, pairs=pairs)
+    assert rel_err(C[pairs[:, 0], pairs[:, 1]], r) <= REL_TOL
+    D = qg.blockdots_q4_k_mmq(_gpu(torch, dev, w[:96]), AQ[:80].contiguous(), 80, 96, k)
+    assert np.array_equal(_host(D), orc.blockdots_q4_k_mmq(w[:96], aq[:80], 80, 96, k))
+
+
+# ------------------------------------------------------------------------ MoE
+def _moe_case(seed, E, F, H, T, K):
+    w_gu = synth.weights("q4_k", E * 2 * F, H, seed, synth.T_W).reshape(E, -1)
+    w_dn = synth.weights("q4_k", E * H, F, seed, synth.T_WDOWN).reshape(E, -1)
+    ids, rw = synth.routing(seed, T, E, K)
+    x = synth.normal(seed, synth.T_X, (T, H))
+    return w_gu, w_dn, ids, rw, x
+
+
+def _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K):
+    qg, orc, torch, dev = env
+    XQ = qg.quantize_q8_1(_gpu(torch, dev, x))
+    xq = orc.quantize_q8_1(x)
+    assert np.array_equal(_host(XQ), xq)
+    ws = torch.empty(qg.moe_qgemv_q4_k_workspace_size(T, K, E, F, H), dtype=torch.uint8, device=dev)
+    WGU, WDN = _gpu(torch, dev, w_gu), _gpu(torch, dev, w_dn)
+    IDS, RW = _gpu(torch, dev, ids), _gpu(torch, dev, rw)
+    out = _host(qg.moe_qgemv_q4_k(WGU, WDN, XQ, IDS, RW, T, K, E, F, H, workspace=ws))
+    hq_g, gu_g, _ = qg.moe_workspace_regions(ws, T, K, F, H)
+    hq_g, gu_g = _host(hq_g), _host(gu_g)
+    ref = orc.moe_q4_k(w_gu, w_dn, xq, ids, rw, T, K, E, F, H)
+    valid = (ids.ravel() >= 0) & (ids.ravel() < E)
+    # stage 1: gate/up values, and their block dots exactly (same device code)
+    assert rel_err(gu_g[valid], ref["gu"][valid]) <= REL_TOL
+    for p in np.flatnonzero(valid)[:4]:
+        e, t = ids.ravel()[p], p // K
+        D, S = qg.blockdots_q4_k(WGU[e], XQ[t], 2 * F, H)
+        Dr, Sr = orc.blockdots("q4_k", w_gu[e], xq[t], 2 * F, H)
+        assert np.array_equal(_host(D), Dr) and np.array_equal(_host(S), Sr)
+    # stage 2: down projection from the GPU's own h^ -- exact block dots, then out
+    for p in np.flatnonzero(valid)[:4]:
+        e = ids.ravel()[p]
+        D, _ = qg.blockdots_q4_k(WDN[e], _gpu(torch, dev, hq_g[p]), H, F)
+        assert np.array_equal(_host(D), orc.blockdots("q4_k", w_dn[e], hq_g[p], H, F)[0])
+    ref_own = orc.moe_q4_k(w_gu, w_dn, xq, ids, rw, T, K, E, F, H, hq_in=hq_g)
+    assert rel_err(out, ref_own["out"]) <= REL_TOL
+    # end to end against the oracle's own h^ (h^ codes may differ by one at a
+    # rounding boundary: c.f. the count below)
+    flips = int(np.sum(hq_g[valid] != ref["hq"][valid]))
+    assert rel_err(out, ref["out"]) <= REL_TOL, f"h^ byte flips: {flips}"
+    return flips
+
+
+def test_moe_small(env):
+    E, F, H, T, K = 6, 256, 512, 5, 3
+    case = _moe_case(61, E, F, H, T, K)
+    _run_moe_stagewise(env, *case, E, F, H, T, K)
+
+
+def test_moe_invalid_ids_skipped(env):
+    E, F, H, T, K = 5, 256, 768, 4, 2
+    w_gu, w_dn, ids, rw, x = _moe_case(62, E, F, H, T, K)
+    ids = ids.copy()
+    ids[0, 1] = E + 3
+    ids[3, 0] = -7
+    _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
+
+
+def test_moe_shared_experts(env):
+    """Several tokens on one expert: the expert's rows are reused across pairs."""
+    E, F, H, T, K = 3, 512, 256, 9, 2
+    w_gu, w_dn, ids, rw, x = _moe_case(63, E, F, H, T, K)
+    _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
+
+
+@pytest.mark.big
+def test_moe_full_size(env):
+    p = synth.WORKLOADS["moe_q4_k"]
+    E, F, H, T, K = p["n_expert"], p["n_ff"], p["n_embd"], p["n_tok"], p["top_k"]
+    case = _moe_case(p["seed"], E, F, H, T, K)
+    flips = _run_moe_stagewise(env, *case, E, F, H, T, K)
+    print(f"MoE full size: h^ bytes that differ from the oracle's h^: {flips}")
