@@ -57,6 +57,17 @@ def _traffic(kernel_key):
     return None if not rec else rec.get("bytes_per_launch")
 
 
+def _repeat(fn, budget_s):
+    """Run fn() until budget_s seconds have passed (at least once); (reps, secs)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= budget_s:
+            return reps, t
+
+
 # ---------------------------------------------------------------- workloads
 class Workload:
     """Holds device inputs and issues one step; subclasses define the work."""
@@ -115,18 +126,11 @@ class Gemv(Workload):
 
         import oracle
         xq = oracle.quantize_q8_1(self.x_host[None])[0]
-        rows, t = 64, 0.0
-        while True:
-            sel = np.arange(min(rows, self.n), dtype=np.int64)
-            t0 = time.perf_counter()
-            oracle.qgemv(self.fmt, self.w_host, xq, self.n, self.k, rows=sel)
-            t = time.perf_counter() - t0
-            if t >= budget_s / 4 or rows >= self.n:
-                break
-            rows = min(self.n, rows * 4)
-        nb = sel.size * (self.w_host.shape[1]) + q81_bytes(self.k) + 4 * sel.size
+        sel = np.arange(min(self.n, 16384), dtype=np.int64)
+        reps, t = _repeat(lambda: oracle.qgemv(self.fmt, self.w_host, xq, self.n, self.k, rows=sel), budget_s)
+        nb = reps * (sel.size * self.w_host.shape[1] + q81_bytes(self.k) + 4 * sel.size)
         return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"rows 0..{sel.size - 1} of {self.n} (plain double dequant-and-dot), {t:.2f} s")
+                    sample=f"rows 0..{sel.size - 1} of {self.n} (plain double dequant-and-dot) x {reps}, {t:.1f} s")
 
 
 class Mmq(Workload):
@@ -170,17 +174,12 @@ class Mmq(Workload):
         import oracle
         aq = oracle.quantize_q8_1(self.a_host)
         g = np.random.default_rng(0)
-        cnt, t = 256, 0.0
-        while True:
-            pairs = np.stack([g.integers(0, self.m, cnt), g.integers(0, self.n, cnt)], 1)
-            t0 = time.perf_counter()
-            oracle.qgemm_q4_k(self.w_host, aq, self.m, self.n, self.k, pairs=pairs)
-            t = time.perf_counter() - t0
-            if t >= budget_s / 4 or cnt >= self.m * self.n:
-                break
-            cnt *= 4
-        return dict(value=2.0 * cnt * self.k / t / 1e12, unit="TOPS", cores=_cpu_threads(), kind="oracle",
-                    sample=f"{cnt} random entries of C[{self.m}][{self.n}] (plain double dequant-and-dot), {t:.2f} s")
+        cnt = 1 << 18
+        pairs = np.stack([g.integers(0, self.m, cnt), g.integers(0, self.n, cnt)], 1)
+        reps, t = _repeat(lambda: oracle.qgemm_q4_k(self.w_host, aq, self.m, self.n, self.k, pairs=pairs), budget_s)
+        return dict(value=2.0 * reps * cnt * self.k / t / 1e12, unit="TOPS", cores=_cpu_threads(), kind="oracle",
+                    sample=f"{cnt} random entries of C[{self.m}][{self.n}] (plain double dequant-and-dot) x {reps}, "
+                           f"{t:.1f} s")
 
 
 class Moe(Workload):
@@ -236,21 +235,13 @@ class Moe(Workload):
     def cpu_baseline(self, budget_s):
         import oracle
         inp = self.inp
-        T = 1
-        while True:
-            xq = oracle.quantize_q8_1(inp["x"][:T])
-            t0 = time.perf_counter()
-            oracle.moe_q4_k(inp["w_gu"], inp["w_down"], xq, inp["ids"][:T], inp["weights"][:T], T, self.K, self.E,
-                            self.F, self.H)
-            t = time.perf_counter() - t0
-            if t >= budget_s / 4 or T >= self.T:
-                break
-            T = min(self.T, T * 2)
-        import numpy as np
-        dist = int(np.unique(inp["ids"][:T]).size)
-        nb = dist * (inp["w_gu"].nbytes + inp["w_down"].nbytes) // self.E
+        T = self.T
+        xq = oracle.quantize_q8_1(inp["x"])
+        reps, t = _repeat(lambda: oracle.moe_q4_k(inp["w_gu"], inp["w_down"], xq, inp["ids"], inp["weights"], T,
+                                                  self.K, self.E, self.F, self.H), budget_s)
+        nb = reps * self.distinct * (inp["w_gu"].nbytes + inp["w_down"].nbytes) // self.E
         return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"first {T} of {self.T} tokens ({dist} distinct experts), {t:.2f} s")
+                    sample=f"all {T} tokens ({self.distinct} distinct experts) x {reps}, {t:.1f} s")
 
 
 def make(name, qg, torch, warm):
@@ -264,31 +255,49 @@ def make(name, qg, torch, warm):
 
 
 # ---------------------------------------------------------------- timing
-def run(wl, steps, warmup, torch):
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        wl.step(i)
+def _time(fn, first, count, warmup, torch, graph):
+    """Average ms per call of fn(i) over `count` calls, timed with HIP events on
+    the stream the calls launch on.  With graph=True the calls are captured in a
+    HIP graph (after `warmup` eager calls) and the graph is replayed once
+    untimed, then once timed: the device work is identical, host launch
+    overhead is removed."""
+    if not graph:
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(count):
+            fn(first + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / count
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(count):
+                fn(first + i)
     torch.cuda.synchronize()
-    # whole steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        wl.step(warmup + i)
-    t1.record(stream)
+    with torch.cuda.stream(s):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g.replay()
+        e1.record(s)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
-    # dominant kernel: back-to-back launches between two events on its stream
-    for i in range(warmup):
-        wl.dominant_call(i)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        wl.dominant_call(warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_kernel = e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / count
+
+
+def run(wl, steps, warmup, torch, graph):
+    ms_step = _time(wl.step, warmup, steps, warmup, torch, graph)
+    ms_kernel = _time(wl.dominant_call, warmup, steps, warmup, torch, graph)
     return ms_step, ms_kernel
 
 
@@ -297,7 +306,7 @@ def bench_one(name, args, qg, torch):
     wl = make(name, qg, torch, args.warm)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
-    ms_step, ms_kernel = run(wl, args.steps, args.warmup, torch)
+    ms_step, ms_kernel = run(wl, args.steps, args.warmup, torch, not args.no_graph)
     value = wl.value(ms_step / 1e3)
     achieved = wl.kernel_rate(ms_kernel / 1e3)
     peak = HBM_PEAK_GBS if wl.unit == "GB/s" else INT8_PEAK_TOPS
@@ -314,7 +323,7 @@ def bench_one(name, args, qg, torch):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": name},
+        "config": {"workload": name, "hip_graph": not args.no_graph},
         "tokens_per_s_equiv": round(wl.tokens_per_step / (ms_step / 1e3), 1),
         "roofline": {
             "bound": wl.bound,
@@ -352,8 +361,9 @@ def main():
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, or all")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
+    ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work per workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)

@@ -51,19 +51,19 @@ __device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32
   return __builtin_amdgcn_alignbyte(hi, lo, shift);
 }
 
-// 16 bytes starting at a 2-byte aligned address p inside a buffer, read as
-// dword loads only: five dwords from p & ~3, realigned.  Reads at most the 4
-// bytes following the 16 (and none before p & ~3); callers keep p+20 inside
-// the buffer.
-__device__ __forceinline__ void ld16_a2(const uint8_t *p, uint32_t out[4]) {
-  const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint8_t *a = p - sh;
-  u32x4 v = ld16(a);
-  uint32_t e = ld4(a + 16);
-  out[0] = align_bytes(v.y, v.x, sh);
-  out[1] = align_bytes(v.z, v.y, sh);
-  out[2] = align_bytes(v.w, v.z, sh);
-  out[3] = align_bytes(e, v.w, sh);
+// 16 / 8 bytes at a 2-byte aligned address (Q6_K fields, 210-byte blocks).
+// gfx950 under the HSA runtime runs with unaligned memory access enabled, and
+// the compiler emits a single global_load_dwordx4 / dwordx2 for these; only the
+// bytes named are read.
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
+__device__ __forceinline__ u32x4 ld16_a2(const uint8_t *p) {
+  const u32x4_a2 v = *reinterpret_cast<const u32x4_a2 *>(p);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ u32x2 ld8_a2(const uint8_t *p) {
+  const u32x2_a2 v = *reinterpret_cast<const u32x2_a2 *>(p);
+  return u32x2{v.x, v.y};
 }
 
 // Butterfly sum over aligned groups of L lanes (L a power of two <= 64).

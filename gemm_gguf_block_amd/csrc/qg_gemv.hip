@@ -17,210 +17,255 @@
 //        even block count), else one block read with byte realignment.
 //
 // With DUMP the same code writes the exact per-block int32 dots instead of y.
-#include "qg_device.h"
+#include "qg_blocks.h"
 #include "qg_launch.h"
 
 namespace qg {
 
-// 72 bytes = two consecutive Q8_1 blocks: A[0] = d|s of the first, A[1..8] its
-// qs, A[9] = d|s of the second, A[10..17] its qs.
-__device__ __forceinline__ void load_q8_1_pair(const uint8_t *p, uint32_t A[18]) {
-  const u32x4 a0 = ld16(p), a1 = ld16(p + 16), a2 = ld16(p + 32), a3 = ld16(p + 48);
-  const u32x2 a4 = ld8(p + 64);
-  A[0] = a0.x; A[1] = a0.y; A[2] = a0.z; A[3] = a0.w;
-  A[4] = a1.x; A[5] = a1.y; A[6] = a1.z; A[7] = a1.w;
-  A[8] = a2.x; A[9] = a2.y; A[10] = a2.z; A[11] = a2.w;
-  A[12] = a3.x; A[13] = a3.y; A[14] = a3.z; A[15] = a3.w;
-  A[16] = a4.x; A[17] = a4.y;
-}
-
 // ---------------------------------------------------------------- Q4_K
-// Scale/min of sub-blocks 2g and 2g+1 from header dwords y, z, w (the 12
-// packed bytes).  Bytes 0..3 of y/z carry sc/m of sub-blocks 0..3 in their low
-// six bits; sub-blocks 4..7 take a nibble of w plus the spare top two bits.
-__device__ __forceinline__ void q4k_scales(uint32_t hy, uint32_t hz, uint32_t hw, int g, int &sc0, int &sc1,
-                                           int &m0, int &m1) {
-  const uint32_t sc_lo = hy & 0x3F3F3F3Fu;
-  const uint32_t m_lo = hz & 0x3F3F3F3Fu;
-  const uint32_t sc_hi = (hw & 0x0F0F0F0Fu) | ((hy >> 2) & 0x30303030u);
-  const uint32_t m_hi = ((hw >> 4) & 0x0F0F0F0Fu) | ((hz >> 2) & 0x30303030u);
-  const uint32_t scw = g < 2 ? sc_lo : sc_hi;
-  const uint32_t mw = g < 2 ? m_lo : m_hi;
-  const uint32_t sh = (uint32_t)(g & 1) * 16u;
-  sc0 = (int)((scw >> sh) & 0xFFu);
-  sc1 = (int)((scw >> (sh + 8)) & 0xFFu);
-  m0 = (int)((mw >> sh) & 0xFFu);
-  m1 = (int)((mw >> (sh + 8)) & 0xFFu);
-}
-
-template <int L, bool DUMP>
+template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
                                                        float *__restrict__ Y, int32_t *__restrict__ Dd,
                                                        int32_t *__restrict__ Sd, int n, int nsb) {
   constexpr int G = 64 / L;
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L;
-  const bool live = row < n;
+  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const int U = nsb * 4;
-  const uint8_t *wrow = W + row * (int64_t)nsb * kQ4KBytes;
-  float acc = 0.f;
-  if (live) {
+  const int64_t rb = (int64_t)nsb * kQ4KBytes;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  if (row0 < n) {
     for (int u = li; u < U; u += L) {
       const int sb = u >> 2, g = u & 3;
-      const uint8_t *bp = wrow + (int64_t)sb * kQ4KBytes;
-      const u32x4 hdr = ld16(bp);
-      const u32x4 qa = ld16(bp + 16 + 32 * g), qb = ld16(bp + 32 + 32 * g);
+      // weights of this unit for the R rows, all loads issued before any use
+      u32x4 hdr[R], qa[R], qb[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r < n) {
+          const uint8_t *bp = W + (row0 + r) * rb + (int64_t)sb * kQ4KBytes;
+          hdr[r] = ld16(bp);
+          qa[r] = ld16(bp + 16 + 32 * g);
+          qb[r] = ld16(bp + 32 + 32 * g);
+        } else {
+          hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      // the activation slice (two Q8_1 blocks), shared by the R rows
       uint32_t A[18];
       load_q8_1_pair(XQ + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes, A);
-      const uint32_t Q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-      int D0 = 0, D1 = 0, S0 = 0, S1 = 0;
+      int S0 = 0, S1 = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        D0 = dot4(Q[i] & 0x0F0F0F0Fu, A[1 + i], D0);
-        D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A[10 + i], D1);
         S0 = bsum4(A[1 + i], S0);
         S1 = bsum4(A[10 + i], S1);
       }
-      if (DUMP) {
-        Dd[row * (int64_t)(nsb * 8) + 8 * sb + 2 * g] = D0;
-        Dd[row * (int64_t)(nsb * 8) + 8 * sb + 2 * g + 1] = D1;
-        if (row == 0) {
-          Sd[8 * sb + 2 * g] = S0;
-          Sd[8 * sb + 2 * g + 1] = S1;
+      const float da0 = h2f(A[0]), da1 = h2f(A[9]);
+      const float dS0 = da0 * (float)S0, dS1 = da1 * (float)S1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t Q[8] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w, qb[r].x, qb[r].y, qb[r].z, qb[r].w};
+        int D0 = 0, D1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          D0 = dot4(Q[i] & 0x0F0F0F0Fu, A[1 + i], D0);
+          D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A[10 + i], D1);
         }
-      } else {
-        int sc0, sc1, m0, m1;
-        q4k_scales(hdr.y, hdr.z, hdr.w, g, sc0, sc1, m0, m1);
-        const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-        const float da0 = h2f(A[0]), da1 = h2f(A[9]);
-        const float t = da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1);
-        const float mm = da0 * (float)(m0 * S0) + da1 * (float)(m1 * S1);
-        acc += d * t - dmin * mm;
+        if (DUMP) {
+          if (row0 + r < n) {
+            Dd[(row0 + r) * (int64_t)(nsb * 8) + 8 * sb + 2 * g] = D0;
+            Dd[(row0 + r) * (int64_t)(nsb * 8) + 8 * sb + 2 * g + 1] = D1;
+          }
+        } else {
+          int sc0, sc1, m0, m1;
+          q4k_scales(hdr[r].y, hdr[r].z, hdr[r].w, g, sc0, sc1, m0, m1);
+          const float d = h2f(hdr[r].x), dmin = h2f(hdr[r].x >> 16);
+          const float t = da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1);
+          const float mm = dS0 * (float)m0 + dS1 * (float)m1;
+          acc[r] += d * t - dmin * mm;
+        }
+      }
+      if (DUMP && row0 == 0) {
+        Sd[8 * sb + 2 * g] = S0;
+        Sd[8 * sb + 2 * g + 1] = S1;
       }
     }
   }
   if (!DUMP) {
-    acc = group_sum<L>(acc);
-    if (live && li == 0) Y[row] = acc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = group_sum<L>(acc[r]);
+      if (li == 0 && row0 + r < n) Y[row0 + r] = v;
+    }
   }
 }
 
 // ---------------------------------------------------------------- Q6_K
-template <int L, bool DUMP>
+template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
                                                        float *__restrict__ Y, int32_t *__restrict__ Dd, int n,
                                                        int nsb) {
   constexpr int G = 64 / L;
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L;
-  const bool live = row < n;
+  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const int U = nsb * 4;
-  const uint8_t *wrow = W + row * (int64_t)nsb * kQ6KBytes;
-  float acc = 0.f;
-  if (live) {
+  const int64_t rb = (int64_t)nsb * kQ6KBytes;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  if (row0 < n) {
     for (int u = li; u < U; u += L) {
       const int sb = u >> 2, h = (u >> 1) & 1, l = u & 1;
-      const uint8_t *bp = wrow + (int64_t)sb * kQ6KBytes;  // 2-byte aligned
-      uint32_t qlA[4], qlB[4], qh[4];
-      ld16_a2(bp + 64 * h + 16 * l, qlA);
-      ld16_a2(bp + 64 * h + 32 + 16 * l, qlB);
-      ld16_a2(bp + 128 + 32 * h + 16 * l, qh);
-      // scales[8h .. 8h+7]: dwords around them, never past the superblock end
-      const uint8_t *sp = bp + 192 + 8 * h;
-      const uint32_t ssh = (uint32_t)(reinterpret_cast<uintptr_t>(sp) & 3u);
-      const uint8_t *sa = sp - ssh;
-      const uint32_t s0 = ld4(sa), s1 = ld4(sa + 4);
-      const uint32_t s2 = ssh ? ld4(sa + 8) : 0u;
-      const uint32_t scl = align_bytes(s1, s0, ssh), sch = align_bytes(s2, s1, ssh);
-      const float d = h2f(ld2(bp + 208));
-      // sub-block 8h + 2g + l has scale byte 2g + l of scales[8h..]
-      const uint32_t lo8 = 8u * (uint32_t)l;
-      const int sc[4] = {(int)__builtin_amdgcn_sbfe((int)scl, lo8, 8u), (int)__builtin_amdgcn_sbfe((int)scl, 16u + lo8, 8u),
-                         (int)__builtin_amdgcn_sbfe((int)sch, lo8, 8u), (int)__builtin_amdgcn_sbfe((int)sch, 16u + lo8, 8u)};
-      float t = 0.f;
+      u32x4 qlA[R], qlB[R], qh[R];
+      u32x2 sc8[R];
+      uint32_t dh[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r < n) {
+          const uint8_t *bp = W + (row0 + r) * rb + (int64_t)sb * kQ6KBytes;  // 2-byte aligned
+          qlA[r] = ld16_a2(bp + 64 * h + 16 * l);
+          qlB[r] = ld16_a2(bp + 64 * h + 32 + 16 * l);
+          qh[r] = ld16_a2(bp + 128 + 32 * h + 16 * l);
+          sc8[r] = ld8_a2(bp + 192 + 8 * h);  // scales[8h .. 8h+7]
+          dh[r] = ld2(bp + 208);
+        } else {
+          qlA[r] = qlB[r] = qh[r] = u32x4{0u, 0u, 0u, 0u};
+          sc8[r] = u32x2{0u, 0u};
+          dh[r] = 0u;
+        }
+      }
+      // activation: Q8_1 blocks 8sb + 4h + g, bytes 16l..16l+15 of each
+      uint32_t a[4][4];
+      float da[4];
+      int S16[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint8_t *ap = XQ + (int64_t)(8 * sb + 4 * h + g) * kQ8_1Bytes;
-        const float da = h2f(ld4(ap));
+        da[g] = h2f(ld4(ap));
         const u32x4 av = ld16(ap + 4 + 16 * l);
-        const uint32_t a[4] = {av.x, av.y, av.z, av.w};
-        int Dg = 0, Sg = 0;
+        a[g][0] = av.x; a[g][1] = av.y; a[g][2] = av.z; a[g][3] = av.w;
+        int s = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t q;
-          if (g == 0) q = (qlA[i] & 0x0F0F0F0Fu) | ((qh[i] << 4) & 0x30303030u);
-          else if (g == 1) q = (qlB[i] & 0x0F0F0F0Fu) | ((qh[i] << 2) & 0x30303030u);
-          else if (g == 2) q = ((qlA[i] >> 4) & 0x0F0F0F0Fu) | (qh[i] & 0x30303030u);
-          else q = ((qlB[i] >> 4) & 0x0F0F0F0Fu) | ((qh[i] >> 2) & 0x30303030u);
-          Dg = dot4(q, a[i], Dg);  // codes 0..63 are non-negative int8
-          Sg = bsum4(a[i], Sg);
-        }
-        Dg -= 32 * Sg;  // sum (q-32)*qa
-        if (DUMP) {
-          Dd[row * (int64_t)(nsb * 16) + 16 * sb + 8 * h + 2 * g + l] = Dg;
-        } else {
-          t += da * (float)(sc[g] * Dg);
-        }
+        for (int i = 0; i < 4; ++i) s = bsum4(a[g][i], s);
+        S16[g] = 32 * s;
       }
-      acc += d * t;
+      const uint32_t lo8 = 8u * (uint32_t)l;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // sub-block 8h + 2g + l has scale byte 2g + l of scales[8h..]
+        const int sc[4] = {(int)__builtin_amdgcn_sbfe((int)sc8[r].x, lo8, 8u),
+                           (int)__builtin_amdgcn_sbfe((int)sc8[r].x, 16u + lo8, 8u),
+                           (int)__builtin_amdgcn_sbfe((int)sc8[r].y, lo8, 8u),
+                           (int)__builtin_amdgcn_sbfe((int)sc8[r].y, 16u + lo8, 8u)};
+        const uint32_t A4[4] = {qlA[r].x, qlA[r].y, qlA[r].z, qlA[r].w};
+        const uint32_t B4[4] = {qlB[r].x, qlB[r].y, qlB[r].z, qlB[r].w};
+        const uint32_t H4[4] = {qh[r].x, qh[r].y, qh[r].z, qh[r].w};
+        float t = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          int Dg = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t q;
+            if (g == 0) q = (A4[i] & 0x0F0F0F0Fu) | ((H4[i] << 4) & 0x30303030u);
+            else if (g == 1) q = (B4[i] & 0x0F0F0F0Fu) | ((H4[i] << 2) & 0x30303030u);
+            else if (g == 2) q = ((A4[i] >> 4) & 0x0F0F0F0Fu) | (H4[i] & 0x30303030u);
+            else q = ((B4[i] >> 4) & 0x0F0F0F0Fu) | ((H4[i] >> 2) & 0x30303030u);
+            Dg = dot4(q, a[g][i], Dg);  // codes 0..63 are non-negative int8
+          }
+          Dg -= S16[g];  // sum (q-32)*qa
+          if (DUMP) {
+            if (row0 + r < n) Dd[(row0 + r) * (int64_t)(nsb * 16) + 16 * sb + 8 * h + 2 * g + l] = Dg;
+          } else {
+            t += da[g] * (float)(sc[g] * Dg);
+          }
+        }
+        acc[r] += h2f(dh[r]) * t;
+      }
     }
   }
   if (!DUMP) {
-    acc = group_sum<L>(acc);
-    if (live && li == 0) Y[row] = acc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = group_sum<L>(acc[r]);
+      if (li == 0 && row0 + r < n) Y[row0 + r] = v;
+    }
   }
 }
 
 // ---------------------------------------------------------------- Q8_0
 // Rows with an even block count: unit = block pair at a dword-aligned offset.
-template <int L, bool DUMP>
+template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q8_0_pair_kernel(const uint8_t *__restrict__ W,
                                                              const uint8_t *__restrict__ XQ, float *__restrict__ Y,
                                                              int32_t *__restrict__ Dd, int n, int npair) {
   constexpr int G = 64 / L;
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L;
-  const bool live = row < n;
-  const uint8_t *wrow = W + row * (int64_t)npair * (2 * kQ8_0Bytes);
-  float acc = 0.f;
-  if (live) {
+  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+  const int64_t rb = (int64_t)npair * (2 * kQ8_0Bytes);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  if (row0 < n) {
     for (int u = li; u < npair; u += L) {
-      const uint8_t *bp = wrow + (int64_t)u * (2 * kQ8_0Bytes);
-      const u32x4 w0 = ld16(bp), w1 = ld16(bp + 16), w2 = ld16(bp + 32), w3 = ld16(bp + 48);
-      const uint32_t w4 = ld4(bp + 64);
-      const uint32_t Wd[17] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x,
-                               w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w, w4};
+      uint32_t Wd[R][17];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r < n) {
+          const uint8_t *bp = W + (row0 + r) * rb + (int64_t)u * (2 * kQ8_0Bytes);
+          const u32x4 w0 = ld16(bp), w1 = ld16(bp + 16), w2 = ld16(bp + 32), w3 = ld16(bp + 48);
+          Wd[r][0] = w0.x; Wd[r][1] = w0.y; Wd[r][2] = w0.z; Wd[r][3] = w0.w;
+          Wd[r][4] = w1.x; Wd[r][5] = w1.y; Wd[r][6] = w1.z; Wd[r][7] = w1.w;
+          Wd[r][8] = w2.x; Wd[r][9] = w2.y; Wd[r][10] = w2.z; Wd[r][11] = w2.w;
+          Wd[r][12] = w3.x; Wd[r][13] = w3.y; Wd[r][14] = w3.z; Wd[r][15] = w3.w;
+          Wd[r][16] = ld4(bp + 64);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 17; ++i) Wd[r][i] = 0u;
+        }
+      }
       uint32_t A[18];
       load_q8_1_pair(XQ + (int64_t)(2 * u) * kQ8_1Bytes, A);
-      int D0 = 0, D1 = 0;
+      const float da0 = h2f(A[0]), da1 = h2f(A[9]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        D0 = dot4(align_bytes(Wd[i + 1], Wd[i], 2), A[1 + i], D0);  // qs of block 0 at bytes 2..33
-        D1 = dot4(Wd[9 + i], A[10 + i], D1);                         // qs of block 1 at bytes 36..67
-      }
-      if (DUMP) {
-        Dd[row * (int64_t)(2 * npair) + 2 * u] = D0;
-        Dd[row * (int64_t)(2 * npair) + 2 * u + 1] = D1;
-      } else {
-        acc += h2f(Wd[0]) * h2f(A[0]) * (float)D0 + h2f(Wd[8] >> 16) * h2f(A[9]) * (float)D1;
+      for (int r = 0; r < R; ++r) {
+        int D0 = 0, D1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          D0 = dot4(align_bytes(Wd[r][i + 1], Wd[r][i], 2), A[1 + i], D0);  // qs of block 0: bytes 2..33
+          D1 = dot4(Wd[r][9 + i], A[10 + i], D1);                            // qs of block 1: bytes 36..67
+        }
+        if (DUMP) {
+          if (row0 + r < n) {
+            Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * u] = D0;
+            Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * u + 1] = D1;
+          }
+        } else {
+          acc[r] += h2f(Wd[r][0]) * da0 * (float)D0 + h2f(Wd[r][8] >> 16) * da1 * (float)D1;
+        }
       }
     }
   }
   if (!DUMP) {
-    acc = group_sum<L>(acc);
-    if (live && li == 0) Y[row] = acc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = group_sum<L>(acc[r]);
+      if (li == 0 && row0 + r < n) Y[row0 + r] = v;
+    }
   }
 }
 
 // Rows with an odd block count: unit = one block at a 2-byte aligned offset.
-template <int L, bool DUMP>
+// (Not tuned: the common row lengths have an even block count.)
+template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q8_0_single_kernel(const uint8_t *__restrict__ W,
                                                                const uint8_t *__restrict__ XQ,
                                                                float *__restrict__ Y, int32_t *__restrict__ Dd, int n,
                                                                int nb) {
+  static_assert(R == 1, "one row per lane group");
   constexpr int G = 64 / L;
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
@@ -262,67 +307,62 @@ __global__ __launch_bounds__(256) void gemv_q8_0_single_kernel(const uint8_t *__
 }
 
 // ---------------------------------------------------------------- dispatch
-static int lanes_per_row(int64_t units) {
-  int L = 64;
-  while (L > 1 && (units % L) != 0) L >>= 1;
-  return L;
-}
+// Rows per lane group (R): each lane reuses its activation slice across R
+// rows and keeps R rows' worth of weight loads in flight.
+constexpr int kRowsQ8_0 = 2;
+constexpr int kRowsQ4K = 4;
+constexpr int kRowsQ6K = 4;
 
-#define QG_GEMV_CASE(KERNEL, LV, ...)                                                             \
-  case LV:                                                                                        \
-    if (dump)                                                                                     \
-      hipLaunchKernelGGL((KERNEL<LV, true>), grid, dim3(256), 0, stream, __VA_ARGS__);            \
-    else                                                                                          \
-      hipLaunchKernelGGL((KERNEL<LV, false>), grid, dim3(256), 0, stream, __VA_ARGS__);           \
-    break;
+#define QG_LAUNCH(KERNEL, LV, RV, ...)                                                          \
+  do {                                                                                          \
+    if (dump)                                                                                   \
+      hipLaunchKernelGGL((KERNEL<LV, RV, true>), grid, dim3(256), 0, stream, __VA_ARGS__);      \
+    else                                                                                        \
+      hipLaunchKernelGGL((KERNEL<LV, RV, false>), grid, dim3(256), 0, stream, __VA_ARGS__);     \
+  } while (0)
 
-#define QG_GEMV_SWITCH(KERNEL, ...)          \
-  switch (L) {                               \
-    QG_GEMV_CASE(KERNEL, 64, __VA_ARGS__)    \
-    QG_GEMV_CASE(KERNEL, 32, __VA_ARGS__)    \
-    QG_GEMV_CASE(KERNEL, 16, __VA_ARGS__)    \
-    QG_GEMV_CASE(KERNEL, 8, __VA_ARGS__)     \
-    QG_GEMV_CASE(KERNEL, 4, __VA_ARGS__)     \
-    QG_GEMV_CASE(KERNEL, 2, __VA_ARGS__)     \
-    default:                                 \
-      QG_GEMV_CASE_ONE(KERNEL, __VA_ARGS__)  \
+#define QG_GEMV_SWITCH(KERNEL, RV, ...)                         \
+  switch (L) {                                                  \
+    case 64: QG_LAUNCH(KERNEL, 64, RV, __VA_ARGS__); break;     \
+    case 32: QG_LAUNCH(KERNEL, 32, RV, __VA_ARGS__); break;     \
+    case 16: QG_LAUNCH(KERNEL, 16, RV, __VA_ARGS__); break;     \
+    case 8: QG_LAUNCH(KERNEL, 8, RV, __VA_ARGS__); break;       \
+    case 4: QG_LAUNCH(KERNEL, 4, RV, __VA_ARGS__); break;       \
+    case 2: QG_LAUNCH(KERNEL, 2, RV, __VA_ARGS__); break;       \
+    default: QG_LAUNCH(KERNEL, 1, RV, __VA_ARGS__); break;      \
   }
 
-#define QG_GEMV_CASE_ONE(KERNEL, ...)                                                  \
-  if (dump)                                                                            \
-    hipLaunchKernelGGL((KERNEL<1, true>), grid, dim3(256), 0, stream, __VA_ARGS__);    \
-  else                                                                                 \
-    hipLaunchKernelGGL((KERNEL<1, false>), grid, dim3(256), 0, stream, __VA_ARGS__);
+static dim3 gemv_grid(int64_t n, int L, int R) {
+  const int64_t rows_per_block = 4 * (64 / L) * (int64_t)R;
+  return dim3((unsigned)((n + rows_per_block - 1) / rows_per_block));
+}
 
 hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_t *D, int32_t *S, int64_t n,
                         int64_t k, hipStream_t stream) {
   const bool dump = D != nullptr;
   const uint8_t *W = static_cast<const uint8_t *>(w);
   const uint8_t *X = static_cast<const uint8_t *>(xq);
-  int64_t units;
-  bool q8_pair = false;
-  if (fmt == 0) {
-    q8_pair = ((k / 32) % 2) == 0;
-    units = q8_pair ? k / 64 : k / 32;
-  } else {
-    units = (k / 256) * 4;
-  }
-  const int L = lanes_per_row(units);
-  const int64_t rows_per_block = 4 * (64 / L);
-  const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
   const int ni = (int)n;
-  if (fmt == 0 && q8_pair) {
+  if (fmt == 0 && ((k / 32) % 2) == 0) {
     const int npair = (int)(k / 64);
-    QG_GEMV_SWITCH(gemv_q8_0_pair_kernel, W, X, y, D, ni, npair)
+    const int L = lanes_per_row(npair);
+    const dim3 grid = gemv_grid(n, L, kRowsQ8_0);
+    QG_GEMV_SWITCH(gemv_q8_0_pair_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
   } else if (fmt == 0) {
     const int nb = (int)(k / 32);
-    QG_GEMV_SWITCH(gemv_q8_0_single_kernel, W, X, y, D, ni, nb)
+    const int L = lanes_per_row(nb);
+    const dim3 grid = gemv_grid(n, L, 1);
+    QG_GEMV_SWITCH(gemv_q8_0_single_kernel, 1, W, X, y, D, ni, nb)
   } else if (fmt == 1) {
     const int nsb = (int)(k / 256);
-    QG_GEMV_SWITCH(gemv_q4k_kernel, W, X, y, D, S, ni, nsb)
+    const int L = lanes_per_row((int64_t)nsb * 4);
+    const dim3 grid = gemv_grid(n, L, kRowsQ4K);
+    QG_GEMV_SWITCH(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else {
     const int nsb = (int)(k / 256);
-    QG_GEMV_SWITCH(gemv_q6k_kernel, W, X, y, D, ni, nsb)
+    const int L = lanes_per_row((int64_t)nsb * 4);
+    const dim3 grid = gemv_grid(n, L, kRowsQ6K);
+    QG_GEMV_SWITCH(gemv_q6k_kernel, kRowsQ6K, W, X, y, D, ni, nsb)
   }
   return hipGetLastError();
 }

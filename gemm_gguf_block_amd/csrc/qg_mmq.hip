@@ -11,7 +11,7 @@
 // v_mfma_i32_32x32x32_i8 -> the exact int32 dots D of that block for the
 // 32x32 tile, which are then rescaled:
 //   acc += d_a*(d*sc_j)*D - (d_a*S)*(dmin*m_j).
-#include "qg_device.h"
+#include "qg_blocks.h"
 #include "qg_launch.h"
 
 namespace qg {
@@ -98,16 +98,13 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t *__restrict_
         dst[i] = Q[i] & 0x0F0F0F0Fu;             // sub-block 2g, values 0..31
         dst[8 + i] = (Q[i] >> 4) & 0x0F0F0F0Fu;  // sub-block 2g+1
       }
-      const uint32_t sc_lo = hdr.y & 0x3F3F3F3Fu, m_lo = hdr.z & 0x3F3F3F3Fu;
-      const uint32_t sc_hi = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
-      const uint32_t m_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
-      const uint32_t scw = g < 2 ? sc_lo : sc_hi, mw = g < 2 ? m_lo : m_hi;
-      const uint32_t sh = (uint32_t)(g & 1) * 16u;
+      int sc0, sc1, mn0, mn1;
+      q4k_scales(hdr.y, hdr.z, hdr.w, g, sc0, sc1, mn0, mn1);
       const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-      sdsc[2 * g][r] = d * (float)((scw >> sh) & 0xFFu);
-      sdsc[2 * g + 1][r] = d * (float)((scw >> (sh + 8)) & 0xFFu);
-      sdmm[2 * g][r] = dmin * (float)((mw >> sh) & 0xFFu);
-      sdmm[2 * g + 1][r] = dmin * (float)((mw >> (sh + 8)) & 0xFFu);
+      sdsc[2 * g][r] = d * (float)sc0;
+      sdsc[2 * g + 1][r] = d * (float)sc1;
+      sdmm[2 * g][r] = dmin * (float)mn0;
+      sdmm[2 * g + 1][r] = dmin * (float)mn1;
     }
     __syncthreads();
 

@@ -13,60 +13,21 @@
 //   3. down: like 1, over the down weights and each pair's h^, scaled by the
 //      pair's routing weight.
 //   4. combine: out[t] = sum over t's slots in slot order (deterministic).
-#include "qg_device.h"
+#include "qg_blocks.h"
 #include "qg_launch.h"
 #include "qg_quant.h"
 
 namespace qg {
 
-// This lane's share of the dot of Q4_K row `wrow` (nsb superblocks) with Q8_1
-// row `xq`; the L lanes sharing the row sum their shares afterwards.  Unit and
-// scale handling as in the decode GEMV.
-template <int L>
-__device__ __forceinline__ float q4k_row_dot_part(const uint8_t *__restrict__ wrow, const uint8_t *__restrict__ xq,
-                                             int nsb, int li) {
-  const int U = nsb * 4;
-  float acc = 0.f;
-  for (int u = li; u < U; u += L) {
-    const int sb = u >> 2, g = u & 3;
-    const uint8_t *bp = wrow + (int64_t)sb * kQ4KBytes;
-    const u32x4 hdr = ld16(bp);
-    const u32x4 qa = ld16(bp + 16 + 32 * g), qb = ld16(bp + 32 + 32 * g);
-    const uint8_t *ap = xq + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes;
-    const u32x4 a0 = ld16(ap), a1 = ld16(ap + 16), a2 = ld16(ap + 32), a3 = ld16(ap + 48);
-    const u32x2 a4 = ld8(ap + 64);
-    const uint32_t A[18] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w, a2.x,
-                            a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w, a4.x, a4.y};
-    const uint32_t Q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-    int D0 = 0, D1 = 0, S0 = 0, S1 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      D0 = dot4(Q[i] & 0x0F0F0F0Fu, A[1 + i], D0);
-      D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A[10 + i], D1);
-      S0 = bsum4(A[1 + i], S0);
-      S1 = bsum4(A[10 + i], S1);
-    }
-    const uint32_t sc_lo = hdr.y & 0x3F3F3F3Fu, m_lo = hdr.z & 0x3F3F3F3Fu;
-    const uint32_t sc_hi = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
-    const uint32_t m_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
-    const uint32_t scw = g < 2 ? sc_lo : sc_hi, mw = g < 2 ? m_lo : m_hi;
-    const uint32_t sh = (uint32_t)(g & 1) * 16u;
-    const int sc0 = (int)((scw >> sh) & 0xFFu), sc1 = (int)((scw >> (sh + 8)) & 0xFFu);
-    const int m0 = (int)((mw >> sh) & 0xFFu), m1 = (int)((mw >> (sh + 8)) & 0xFFu);
-    const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-    const float da0 = h2f(A[0]), da1 = h2f(A[9]);
-    acc += d * (da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1)) -
-           dmin * (da0 * (float)(m0 * S0) + da1 * (float)(m1 * S1));
-  }
-  return acc;
-}
-
 // Kernels 1 and 3.  blockIdx.x = expert * tiles + row tile; each wave covers
-// 64/L rows of the expert's [rows][nsb] matrix.  For every pair p with ids[p] == expert:
+// (64/L)*R rows of the expert's [rows][nsb] matrix.  The routing table is
+// scanned 64 ids at a time with one vector load and a ballot, so a workgroup
+// whose expert nobody routed to finishes after npairs/64 loads.  For every pair
+// p with ids[p] == expert:
 //   out[p][row] = scale(p) * dot(row, act + act_row(p))
 // with act_row(p) = p / top_k (token rows, kernel 1) or p (h^ rows, kernel 3),
 // scale(p) = 1 (kernel 1) or weights[p] (kernel 3).
-template <int L>
+template <int L, int R>
 __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__restrict__ W,
                                                               const uint8_t *__restrict__ act,
                                                               const int32_t *__restrict__ ids,
@@ -80,16 +41,72 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
   const int tile = (int)(blockIdx.x % (unsigned)tiles);
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int row = (tile * 4 + (threadIdx.x >> 6)) * G + lane / L;
-  const bool live = row < rows;
-  const uint8_t *wrow = W + (int64_t)e * expert_bytes + (int64_t)(live ? row : 0) * nsb * kQ4KBytes;
-  for (int p = 0; p < npairs; ++p) {
-    if (ids[p] != e) continue;  // the same decision for the whole workgroup
-    const int arow = act_per_token ? p / top_k : p;
-    float v = 0.f;
-    if (live) v = q4k_row_dot_part<L>(wrow, act + (int64_t)arow * act_row_bytes, nsb, li);
-    v = group_sum<L>(v);
-    if (live && li == 0) out[(int64_t)p * rows + row] = weights ? weights[p] * v : v;
+  const int row0 = ((tile * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+  const int64_t rb = (int64_t)nsb * kQ4KBytes;
+  const uint8_t *wexp = W + (int64_t)e * expert_bytes;
+  const int U = nsb * 4;
+  for (int c0 = 0; c0 < npairs; c0 += 64) {
+    const int id = c0 + lane < npairs ? ids[c0 + lane] : -1;
+    uint64_t mask = __ballot(id == e);
+    while (mask) {
+      const int p = c0 + __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const uint8_t *xr = act + (int64_t)(act_per_token ? p / top_k : p) * act_row_bytes;
+      float acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+      if (row0 < rows) {
+        for (int u = li; u < U; u += L) {
+          const int sb = u >> 2, g = u & 3;
+          u32x4 hdr[R], qa[R], qb[R];
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (row0 + r < rows) {
+              const uint8_t *bp = wexp + (int64_t)(row0 + r) * rb + (int64_t)sb * kQ4KBytes;
+              hdr[r] = ld16(bp);
+              qa[r] = ld16(bp + 16 + 32 * g);
+              qb[r] = ld16(bp + 32 + 32 * g);
+            } else {
+              hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
+            }
+          }
+          const uint8_t *ap = xr + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes;
+          const u32x4 a0 = ld16(ap), a1 = ld16(ap + 16), a2 = ld16(ap + 32), a3 = ld16(ap + 48);
+          const u32x2 a4 = ld8(ap + 64);
+          const uint32_t A[18] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w, a2.x,
+                                  a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w, a4.x, a4.y};
+          int S0 = 0, S1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            S0 = bsum4(A[1 + i], S0);
+            S1 = bsum4(A[10 + i], S1);
+          }
+          const float da0 = h2f(A[0]), da1 = h2f(A[9]);
+          const float dS0 = da0 * (float)S0, dS1 = da1 * (float)S1;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t Q[8] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w, qb[r].x, qb[r].y, qb[r].z, qb[r].w};
+            int D0 = 0, D1 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              D0 = dot4(Q[i] & 0x0F0F0F0Fu, A[1 + i], D0);
+              D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A[10 + i], D1);
+            }
+            int sc0, sc1, m0, m1;
+            q4k_scales(hdr[r].y, hdr[r].z, hdr[r].w, g, sc0, sc1, m0, m1);
+            const float d = h2f(hdr[r].x), dmin = h2f(hdr[r].x >> 16);
+            acc[r] += d * (da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1)) -
+                      dmin * (dS0 * (float)m0 + dS1 * (float)m1);
+          }
+        }
+      }
+      const float scale = weights ? weights[p] : 1.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = group_sum<L>(acc[r]);
+        if (li == 0 && row0 + r < rows) out[(int64_t)p * rows + row0 + r] = scale * v;
+      }
+    }
   }
 }
 
@@ -139,32 +156,29 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
   out[i] = acc;
 }
 
-static int lanes_for(int64_t units) {
-  int L = 64;
-  while (L > 1 && (units % L) != 0) L >>= 1;
-  return L;
-}
-
-template <int L>
+template <int L, int R>
 static void launch_expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights,
                                float *out, int rows, int nsb, int npairs, int top_k, int act_per_token,
                                int64_t expert_bytes, int64_t act_row_bytes, int n_expert, hipStream_t stream) {
-  const int rows_per_block = 4 * (64 / L);
+  const int rows_per_block = 4 * (64 / L) * R;
   const int tiles = (rows + rows_per_block - 1) / rows_per_block;
   const dim3 grid((unsigned)((int64_t)tiles * n_expert));
-  hipLaunchKernelGGL(moe_expert_gemv_kernel<L>, grid, dim3(256), 0, stream, W, act, ids, weights, out, rows, nsb,
-                     npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles);
+  hipLaunchKernelGGL((moe_expert_gemv_kernel<L, R>), grid, dim3(256), 0, stream, W, act, ids, weights, out, rows,
+                     nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles);
 }
+
+// Rows per lane group for the expert GEMVs (activation reuse, loads in flight).
+constexpr int kMoeRows = 2;
 
 static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights, float *out,
                         int rows, int nsb, int npairs, int top_k, int act_per_token, int64_t act_row_bytes,
                         int n_expert, hipStream_t stream) {
   const int64_t expert_bytes = (int64_t)rows * nsb * kQ4KBytes;
-  switch (lanes_for((int64_t)nsb * 4)) {
-#define QG_MOE_CASE(LV)                                                                                     \
-  case LV:                                                                                                  \
-    launch_expert_gemv<LV>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, \
-                           act_row_bytes, n_expert, stream);                                                \
+  switch (lanes_per_row((int64_t)nsb * 4)) {
+#define QG_MOE_CASE(LV)                                                                                          \
+  case LV:                                                                                                       \
+    launch_expert_gemv<LV, kMoeRows>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token,         \
+                                     expert_bytes, act_row_bytes, n_expert, stream);                             \
     break;
     QG_MOE_CASE(64)
     QG_MOE_CASE(32)

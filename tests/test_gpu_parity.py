@@ -354,3 +354,58 @@ def test_moe_full_size(env):
     case = _moe_case(p["seed"], E, F, H, T, K)
     flips = _run_moe_stagewise(env, *case, E, F, H, T, K)
     print(f"MoE full size: h^ bytes that differ from the oracle's h^: {flips}")
+
+
+# ---------------------------------------------------------------- HIP graphs
+def test_graph_replay_matches_eager(env):
+    """The bench replays captured HIP graphs: every entry point captured in one
+    graph must reproduce the eager results bit for bit on every replay, with
+    other eager work and synchronizations between the replays."""
+    qg, orc, torch, dev = env
+    n, k, m = 300, 1024, 70
+    E, F, H, T, K = 4, 256, 512, 5, 2
+    x = _gpu(torch, dev, synth.normal(91, 1, (k,)))
+    a = _gpu(torch, dev, synth.normal(92, 1, (m, k)))
+    Ws = {f: _gpu(torch, dev, synth.weights(f, n, k, seed=93)) for f in ("q8_0", "q4_k", "q6_k")}
+    w_gu, w_dn, ids, rw, xm = _moe_case(94, E, F, H, T, K)
+    WGU, WDN, IDS, RW, XM = (_gpu(torch, dev, v) for v in (w_gu, w_dn, ids, rw, xm))
+    xq = torch.empty(k // 32 * 36, dtype=torch.uint8, device=dev)
+    aq = torch.empty((m, k // 32 * 36), dtype=torch.uint8, device=dev)
+    xmq = torch.empty((T, H // 32 * 36), dtype=torch.uint8, device=dev)
+    ys = {f: torch.empty(n, device=dev) for f in Ws}
+    c = torch.empty((m, n), device=dev)
+    out = torch.empty((T, H), device=dev)
+    ws = torch.empty(qg.moe_qgemv_q4_k_workspace_size(T, K, E, F, H), dtype=torch.uint8, device=dev)
+
+    def work():
+        qg.quantize_q8_1(x, xq)
+        for f, W in Ws.items():
+            getattr(qg, GEMV[f])(W, xq, n, k, y=ys[f])
+        qg.quantize_q8_1(a, aq)
+        qg.qgemm_q4_k_mmq(Ws["q4_k"], aq, m, n, k, c=c)
+        qg.quantize_q8_1(XM, xmq)
+        qg.moe_qgemv_q4_k(WGU, WDN, xmq, IDS, RW, T, K, E, F, H, out=out, workspace=ws)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (xq, *ys.values(), aq, c, xmq, out)]
+
+    work()
+    eager = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        work()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (xq, *ys.values(), aq, c, xmq, out):
+            t.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for e, r in zip(eager, got):
+            assert torch.equal(e, r), f"replay {rep} differs"
