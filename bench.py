@@ -43,18 +43,37 @@ def _cpu_threads():
     return int(v) if v and v.isdigit() else (os.cpu_count() or 1)
 
 
-def _traffic(kernel_key):
-    """HBM bytes per launch from the committed counter summary, if one exists
-    for this kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
-    calibration factor recorded beside them)."""
+KERNEL_SOURCES = {
+    "q4_k_gemv": ["qg_gemv.hip"], "q8_0_gemv": ["qg_gemv.hip"], "q6_k_gemv": ["qg_gemv.hip"],
+    "q4_k_mmq": ["qg_mmq.hip"], "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
+}
+
+
+def kernel_source_hash(workload):
+    """sha256 over the kernel sources a workload's dominant kernel is built from."""
+    import hashlib
+    csrc = os.path.join(ROOT, "gemm_gguf_block_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[workload] + ["qg_blocks.h", "qg_device.h"]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def _traffic(workload):
+    """HBM bytes per launch of the dominant kernel(s), from the committed
+    counter summary: FETCH_SIZE and WRITE_SIZE, each scaled by what the same
+    counter reads for a plain device copy of known size.  None when there is no
+    summary or the kernel sources changed since the counters were taken."""
     path = os.path.join(PROFILE_DIR, "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel_key)
+        rec = json.load(open(path))["workloads"].get(workload)
     except Exception:
         return None
-    return None if not rec else rec.get("bytes_per_launch")
+    if not rec or rec.get("source_sha256") != kernel_source_hash(workload):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def _repeat(fn, budget_s):
@@ -364,6 +383,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work per workload")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="instead of benchmarking, run 10 plain device copies of MiB mebibytes (a kernel of known "
+                         "traffic, to scale HBM counters by) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
@@ -375,6 +397,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 10}))
+        return
     names = (["q4_k_gemv", "q8_0_gemv", "q6_k_gemv", "q4_k_mmq", "moe_q4_k"]
              if args.workload == "all" else [args.workload])
     for name in names:

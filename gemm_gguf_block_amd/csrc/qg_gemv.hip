@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void gemv_q8_0_single_kernel(const uint8_t *__
 // Rows per lane group (R): each lane reuses its activation slice across R
 // rows and keeps R rows' worth of weight loads in flight.
 constexpr int kRowsQ8_0 = 2;
-constexpr int kRowsQ4K = 4;
+constexpr int kRowsQ4K = 1;
 constexpr int kRowsQ6K = 4;
 
 #define QG_LAUNCH(KERNEL, LV, RV, ...)                                                          \
