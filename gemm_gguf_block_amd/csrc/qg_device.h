@@ -66,11 +66,37 @@ __device__ __forceinline__ u32x2 ld8_a2(const uint8_t *p) {
   return u32x2{v.x, v.y};
 }
 
-// Butterfly sum over aligned groups of L lanes (L a power of two <= 64).
+// Butterfly sum over aligned groups of L lanes (L a power of two <= 64); every
+// lane of a group gets the group's sum.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int off = L / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// DPP controls (gfx9 encoding): row_shr:n = 0x110 + n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Sum over aligned groups of L lanes (L a power of two, 1 <= L <= 64) with DPP
+// adds only (no LDS traffic): the result is exact in the LAST lane of each
+// group (lane % L == L - 1); other lanes hold partial sums.  Rows of 16 lanes
+// are summed by shift-right-and-add (lane i accumulates lanes i-15..i of its
+// row); row totals are then carried across rows with row_bcast.
+template <int L>
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "group of 1..64 lanes, a power of two");
+  if (L >= 2) v += dpp_or_zero<0x111, 0xf>(v);
+  if (L >= 4) v += dpp_or_zero<0x112, 0xf>(v);
+  if (L >= 8) v += dpp_or_zero<0x114, 0xf>(v);
+  if (L >= 16) v += dpp_or_zero<0x118, 0xf>(v);
+  if (L >= 32) v += dpp_or_zero<0x142, 0xa>(v);  // rows 1, 3 += lane 15 of rows 0, 2
+  if (L >= 64) v += dpp_or_zero<0x143, 0x8>(v);  // row 3 += lane 31
   return v;
 }
 

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
   const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const int U = nsb * 4;
   const int64_t rb = (int64_t)nsb * kQ4KBytes;
+  const uint8_t *wrow = W + row0 * rb;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (row0 + r < n) {
-          const uint8_t *bp = W + (row0 + r) * rb + (int64_t)sb * kQ4KBytes;
+          const uint8_t *bp = wrow + r * rb + sb * kQ4KBytes;
           hdr[r] = ld16(bp);
           qa[r] = ld16(bp + 16 + 32 * g);
           qb[r] = ld16(bp + 32 + 32 * g);
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
   if (!DUMP) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float v = group_sum<L>(acc[r]);
-      if (li == 0 && row0 + r < n) Y[row0 + r] = v;
+      const float v = group_sum_last<L>(acc[r]);
+      if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
     }
   }
 }
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
   const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const int U = nsb * 4;
   const int64_t rb = (int64_t)nsb * kQ6KBytes;
+  const uint8_t *wrow = W + row0 * rb;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (row0 + r < n) {
-          const uint8_t *bp = W + (row0 + r) * rb + (int64_t)sb * kQ6KBytes;  // 2-byte aligned
+          const uint8_t *bp = wrow + r * rb + sb * kQ6KBytes;  // 2-byte aligned
           qlA[r] = ld16_a2(bp + 64 * h + 16 * l);
           qlB[r] = ld16_a2(bp + 64 * h + 32 + 16 * l);
           qh[r] = ld16_a2(bp + 128 + 32 * h + 16 * l);
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
   if (!DUMP) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float v = group_sum<L>(acc[r]);
-      if (li == 0 && row0 + r < n) Y[row0 + r] = v;
+      const float v = group_sum_last<L>(acc[r]);
+      if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
     }
   }
 }
@@ -206,6 +208,7 @@ __global__ __launch_bounds__(256) void gemv_q8_0_pair_kernel(const uint8_t *__re
   const int li = lane & (L - 1);
   const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const int64_t rb = (int64_t)npair * (2 * kQ8_0Bytes);
+  const uint8_t *wrow = W + row0 * rb;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void gemv_q8_0_pair_kernel(const uint8_t *__re
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (row0 + r < n) {
-          const uint8_t *bp = W + (row0 + r) * rb + (int64_t)u * (2 * kQ8_0Bytes);
+          const uint8_t *bp = wrow + r * rb + u * (2 * kQ8_0Bytes);
           const u32x4 w0 = ld16(bp), w1 = ld16(bp + 16), w2 = ld16(bp + 32), w3 = ld16(bp + 48);
           Wd[r][0] = w0.x; Wd[r][1] = w0.y; Wd[r][2] = w0.z; Wd[r][3] = w0.w;
           Wd[r][4] = w1.x; Wd[r][5] = w1.y; Wd[r][6] = w1.z; Wd[r][7] = w1.w;
@@ -252,8 +255,8 @@ __global__ __launch_bounds__(256) void gemv_q8_0_pair_kernel(const uint8_t *__re
   if (!DUMP) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float v = group_sum<L>(acc[r]);
-      if (li == 0 && row0 + r < n) Y[row0 + r] = v;
+      const float v = group_sum_last<L>(acc[r]);
+      if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
     }
   }
 }
@@ -301,8 +304,8 @@ __global__ __launch_bounds__(256) void gemv_q8_0_single_kernel(const uint8_t *__
     }
   }
   if (!DUMP) {
-    acc = group_sum<L>(acc);
-    if (live && li == 0) Y[row] = acc;
+    acc = group_sum_last<L>(acc);
+    if (live && li == L - 1) Y[row] = acc;
   }
 }
 

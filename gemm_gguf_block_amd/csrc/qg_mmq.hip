@@ -3,14 +3,19 @@
 //
 // The pages run this step as "in-shader dequant and dp4a mmq" (infr page,
 // "models") and as cooperative-matrix matmul (infr page, "Vulkan-first, Metal
-// too").  Here: a 64x64 output tile per workgroup, four waves of 32x32.  Per
-// 256-wide superblock of k, the workgroup stages A (Q8_1 qs as int8) and B
-// (Q4_K nibbles widened to int8) in LDS together with the fp32 factors
-// d_a, d_a*sum(qa) per activation block and d*sc_j, dmin*m_j per weight
-// sub-block.  Each 32-wide sub-block j is exactly one
-// v_mfma_i32_32x32x32_i8 -> the exact int32 dots D of that block for the
-// 32x32 tile, which are then rescaled:
-//   acc += d_a*(d*sc_j)*D - (d_a*S)*(dmin*m_j).
+// too").  Here a workgroup of 8 waves owns a 64 (tokens) x 128 (weight rows)
+// output tile; each wave owns 32x32.  Per 256-wide superblock of k the
+// workgroup stages in LDS:
+//   A  Q8_1 qs as int8, plus per (row, block) d_a and d_a*sum(qa)
+//   B  Q4_K nibbles widened to int8, plus per (weight row, sub-block) d*sc_j
+//      and -dmin*m_j
+// double-buffered: the global loads of superblock s+1 are in flight while the
+// MFMAs of superblock s run.  Each 32-wide sub-block j is exactly one
+// v_mfma_i32_32x32x32_i8 -> the exact int32 dots D of that block for the wave's
+// 32x32 tile, rescaled in fp32 on the VALU:  acc += (d_a * d*sc_j) * D.
+// The min term -sum_j (d_a*sum qa)_j (dmin*m_j) is a rank-8-per-superblock
+// product of two small fp32 matrices and runs on the matrix core as well
+// (v_mfma_f32_32x32x2_f32 over pairs of sub-blocks) into a second accumulator.
 #include "qg_blocks.h"
 #include "qg_launch.h"
 
@@ -18,115 +23,140 @@ namespace qg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64, kBN = 64;
-constexpr int kRow = 272;  // LDS bytes per staged row: 256 + 16 padding (bank spread)
+constexpr int kBM = 64, kBN = 128;
+constexpr int kRow = 272;  // LDS bytes per staged row: 256 + 16 (spreads rows over banks)
+
+struct MmqStage {
+  uint8_t a[kBM * kRow];
+  uint8_t b[kBN * kRow];
+  float dA[8][kBM];    // d_a per (block j, activation row)
+  float SA[8][kBM];    // d_a * sum(qa)
+  float dsc[8][kBN];   // d * sc_j per (sub-block j, weight row)
+  float ndm[8][kBN];   // -dmin * m_j
+};
+
+// Global -> registers for one superblock: thread t stages activation block
+// (row t/8, block t%8) and weight (row t/4, byte group t%4).
+struct MmqRegs {
+  u32x4 a0, a1;
+  uint32_t a2;
+  u32x4 hdr, qa, qb;
+};
+
+__device__ __forceinline__ void mmq_load(MmqRegs &g, const uint8_t *__restrict__ W, const uint8_t *__restrict__ AQ,
+                                         int M, int N, int nsb, int m0, int n0, int sb, int tid) {
+  const int ar = tid >> 3, ab = tid & 7;
+  const int gm = m0 + ar;
+  if (gm < M) {
+    const uint8_t *ap = AQ + ((int64_t)gm * nsb * 8 + sb * 8 + ab) * kQ8_1Bytes;
+    g.a0 = ld16(ap);
+    g.a1 = ld16(ap + 16);
+    g.a2 = ld4(ap + 32);
+  } else {
+    g.a0 = g.a1 = u32x4{0u, 0u, 0u, 0u};
+    g.a2 = 0u;
+  }
+  const int br = tid >> 2, bg = tid & 3;
+  const int gn = n0 + br;
+  if (gn < N) {
+    const uint8_t *bp = W + ((int64_t)gn * nsb + sb) * kQ4KBytes;
+    g.hdr = ld16(bp);
+    g.qa = ld16(bp + 16 + 32 * bg);
+    g.qb = ld16(bp + 32 + 32 * bg);
+  } else {
+    g.hdr = g.qa = g.qb = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void mmq_store(const MmqRegs &g, MmqStage &s, int tid) {
+  {  // activation block: qs -> int8 row, factors
+    const int ar = tid >> 3, ab = tid & 7;
+    const uint32_t q[8] = {g.a0.y, g.a0.z, g.a0.w, g.a1.x, g.a1.y, g.a1.z, g.a1.w, g.a2};
+    int S = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S = bsum4(q[i], S);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(s.a + ar * kRow + 32 * ab);
+    *reinterpret_cast<u32x4 *>(dst) = u32x4{q[0], q[1], q[2], q[3]};
+    *reinterpret_cast<u32x4 *>(dst + 4) = u32x4{q[4], q[5], q[6], q[7]};
+    const float da = h2f(g.a0.x);
+    s.dA[ab][ar] = da;
+    s.SA[ab][ar] = da * (float)S;
+  }
+  {  // weight group: nibbles -> int8 (sub-block 2g low, 2g+1 high), factors
+    const int br = tid >> 2, bg = tid & 3;
+    const uint32_t Q[8] = {g.qa.x, g.qa.y, g.qa.z, g.qa.w, g.qb.x, g.qb.y, g.qb.z, g.qb.w};
+    uint32_t *dst = reinterpret_cast<uint32_t *>(s.b + br * kRow + 64 * bg);
+    *reinterpret_cast<u32x4 *>(dst) =
+        u32x4{Q[0] & 0x0F0F0F0Fu, Q[1] & 0x0F0F0F0Fu, Q[2] & 0x0F0F0F0Fu, Q[3] & 0x0F0F0F0Fu};
+    *reinterpret_cast<u32x4 *>(dst + 4) =
+        u32x4{Q[4] & 0x0F0F0F0Fu, Q[5] & 0x0F0F0F0Fu, Q[6] & 0x0F0F0F0Fu, Q[7] & 0x0F0F0F0Fu};
+    *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{(Q[0] >> 4) & 0x0F0F0F0Fu, (Q[1] >> 4) & 0x0F0F0F0Fu,
+                                                (Q[2] >> 4) & 0x0F0F0F0Fu, (Q[3] >> 4) & 0x0F0F0F0Fu};
+    *reinterpret_cast<u32x4 *>(dst + 12) = u32x4{(Q[4] >> 4) & 0x0F0F0F0Fu, (Q[5] >> 4) & 0x0F0F0F0Fu,
+                                                 (Q[6] >> 4) & 0x0F0F0F0Fu, (Q[7] >> 4) & 0x0F0F0F0Fu};
+    int sc0, sc1, mn0, mn1;
+    q4k_scales(g.hdr.y, g.hdr.z, g.hdr.w, bg, sc0, sc1, mn0, mn1);
+    const float d = h2f(g.hdr.x), dmin = h2f(g.hdr.x >> 16);
+    s.dsc[2 * bg][br] = d * (float)sc0;
+    s.dsc[2 * bg + 1][br] = d * (float)sc1;
+    s.ndm[2 * bg][br] = -(dmin * (float)mn0);
+    s.ndm[2 * bg + 1][br] = -(dmin * (float)mn1);
+  }
+}
 
 template <bool DUMP>
-__global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ AQ,
+__global__ __launch_bounds__(512) void mmq_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ AQ,
                                                       float *__restrict__ C, int32_t *__restrict__ Dd, int M, int N,
                                                       int nsb) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kRow];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kRow];
-  __shared__ __attribute__((aligned(16))) float sdA[8][kBM];   // d_a per (block j, row)
-  __shared__ __attribute__((aligned(16))) float sSA[8][kBM];   // d_a * sum(qa)
-  __shared__ __attribute__((aligned(16))) float sdsc[8][kBN];  // d * sc_j per (j, weight row)
-  __shared__ __attribute__((aligned(16))) float sdmm[8][kBN];  // dmin * m_j
-
+  __shared__ MmqStage stage[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 2, wn = wv & 3;  // 2 x 4 waves of 32x32
   const int tiles_n = (N + kBN - 1) / kBN;
   const int m0 = (int)(blockIdx.x / tiles_n) * kBM, n0 = (int)(blockIdx.x % tiles_n) * kBN;
   const int lr = lane & 31, lh = lane >> 5;
-  const int nbrow = nsb * 8;  // Q8_1 blocks per activation row
+  const int nbrow = nsb * 8;
 
-  float acc[16];
+  v16f acc, accm;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = accm[r] = 0.f;
+  v16i zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero[r] = 0;
 
+  MmqRegs g;
+  if (nsb > 0) {
+    mmq_load(g, W, AQ, M, N, nsb, m0, n0, 0, tid);
+    mmq_store(g, stage[0], tid);
+  }
+  __syncthreads();
   for (int sb = 0; sb < nsb; ++sb) {
-    // ---- stage A: thread -> activation row r, Q8_1 blocks 2p, 2p+1 of this superblock
-    {
-      const int r = tid >> 2, p = tid & 3;
-      const int gm = m0 + r;
-      uint32_t A[18];
-      if (gm < M) {
-        const uint8_t *ap = AQ + ((int64_t)gm * nbrow + sb * 8 + 2 * p) * kQ8_1Bytes;
-        const u32x4 a0 = ld16(ap), a1 = ld16(ap + 16), a2 = ld16(ap + 32), a3 = ld16(ap + 48);
-        const u32x2 a4 = ld8(ap + 64);
-        A[0] = a0.x; A[1] = a0.y; A[2] = a0.z; A[3] = a0.w; A[4] = a1.x; A[5] = a1.y;
-        A[6] = a1.z; A[7] = a1.w; A[8] = a2.x; A[9] = a2.y; A[10] = a2.z; A[11] = a2.w;
-        A[12] = a3.x; A[13] = a3.y; A[14] = a3.z; A[15] = a3.w; A[16] = a4.x; A[17] = a4.y;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 18; ++i) A[i] = 0u;
-      }
-      int S0 = 0, S1 = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        S0 = bsum4(A[1 + i], S0);
-        S1 = bsum4(A[10 + i], S1);
-      }
-      uint32_t *dst = reinterpret_cast<uint32_t *>(sA + r * kRow + 64 * p);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dst[i] = A[1 + i];
-        dst[8 + i] = A[10 + i];
-      }
-      const float da0 = h2f(A[0]), da1 = h2f(A[9]);
-      sdA[2 * p][r] = da0;
-      sdA[2 * p + 1][r] = da1;
-      sSA[2 * p][r] = da0 * (float)S0;
-      sSA[2 * p + 1][r] = da1 * (float)S1;
-    }
-    // ---- stage B: thread -> weight row r, byte group g (sub-blocks 2g, 2g+1)
-    {
-      const int r = tid >> 2, g = tid & 3;
-      const int gn = n0 + r;
-      u32x4 hdr = {0u, 0u, 0u, 0u}, qa = {0u, 0u, 0u, 0u}, qb = {0u, 0u, 0u, 0u};
-      if (gn < N) {
-        const uint8_t *bp = W + ((int64_t)gn * nsb + sb) * kQ4KBytes;
-        hdr = ld16(bp);
-        qa = ld16(bp + 16 + 32 * g);
-        qb = ld16(bp + 32 + 32 * g);
-      }
-      const uint32_t Q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-      uint32_t *dst = reinterpret_cast<uint32_t *>(sB + r * kRow + 64 * g);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dst[i] = Q[i] & 0x0F0F0F0Fu;             // sub-block 2g, values 0..31
-        dst[8 + i] = (Q[i] >> 4) & 0x0F0F0F0Fu;  // sub-block 2g+1
-      }
-      int sc0, sc1, mn0, mn1;
-      q4k_scales(hdr.y, hdr.z, hdr.w, g, sc0, sc1, mn0, mn1);
-      const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-      sdsc[2 * g][r] = d * (float)sc0;
-      sdsc[2 * g + 1][r] = d * (float)sc1;
-      sdmm[2 * g][r] = dmin * (float)mn0;
-      sdmm[2 * g + 1][r] = dmin * (float)mn1;
-    }
-    __syncthreads();
+    MmqStage &cur = stage[sb & 1];
+    const bool more = sb + 1 < nsb;
+    if (more) mmq_load(g, W, AQ, M, N, nsb, m0, n0, sb + 1, tid);
 
-    // ---- eight 32x32x32 int8 MFMAs, one per sub-block, each rescaled in fp32
-    const uint8_t *arow = sA + (wm * 32 + lr) * kRow + 16 * lh;
-    const uint8_t *brow = sB + (wn * 32 + lr) * kRow + 16 * lh;
-#pragma unroll 2
+    const uint8_t *arow = cur.a + (wm * 32 + lr) * kRow + 16 * lh;
+    const uint8_t *brow = cur.b + (wn * 32 + lr) * kRow + 16 * lh;
+#pragma unroll 2  // full unrolling keeps all eight MFMA results live and spills
     for (int j = 0; j < 8; ++j) {
       const v4i a = *reinterpret_cast<const v4i *>(arow + 32 * j);
       const v4i b = *reinterpret_cast<const v4i *>(brow + 32 * j);
-      v16i zero;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) zero[r] = 0;
       const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
-      // output register r holds row 8(r/4) + 4*lh + r%4 of the wave tile, column lr
-      const float dsc = sdsc[j][wn * 32 + lr], dmm = sdmm[j][wn * 32 + lr];
+      if (!DUMP && (j & 1) == 0) {
+        // min term for sub-blocks j, j+1: (32 x 2) x (2 x 32) fp32 MFMA;
+        // lane l supplies row/column l%32 at k = l/32
+        const float sa = cur.SA[j + lh][wm * 32 + lr];
+        const float nd = cur.ndm[j + lh][wn * 32 + lr];
+        accm = __builtin_amdgcn_mfma_f32_32x32x2f32(sa, nd, accm, 0, 0, 0);
+      }
+      // output register r holds tile row 8(r/4) + 4*lh + r%4, column lr
+      const float dsc = cur.dsc[j][wn * 32 + lr];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 da4 = *reinterpret_cast<const float4 *>(&sdA[j][wm * 32 + 8 * q + 4 * lh]);
-        const float4 sa4 = *reinterpret_cast<const float4 *>(&sSA[j][wm * 32 + 8 * q + 4 * lh]);
+        const float4 da4 = *reinterpret_cast<const float4 *>(&cur.dA[j][wm * 32 + 8 * q + 4 * lh]);
         const float da[4] = {da4.x, da4.y, da4.z, da4.w};
-        const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * q + i;
@@ -134,11 +164,12 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t *__restrict_
             const int gm = m0 + wm * 32 + 8 * q + 4 * lh + i, gn = n0 + wn * 32 + lr;
             if (gm < M && gn < N) Dd[((int64_t)gm * N + gn) * nbrow + sb * 8 + j] = D[r];
           } else {
-            acc[r] += (da[i] * dsc) * (float)D[r] - sa[i] * dmm;
+            acc[r] += (da[i] * dsc) * (float)D[r];
           }
         }
       }
     }
+    if (more) mmq_store(g, stage[(sb + 1) & 1], tid);
     __syncthreads();
   }
 
@@ -147,7 +178,7 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t *__restrict_
     for (int r = 0; r < 16; ++r) {
       const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
       const int gn = n0 + wn * 32 + lr;
-      if (gm < M && gn < N) C[(int64_t)gm * N + gn] = acc[r];
+      if (gm < M && gn < N) C[(int64_t)gm * N + gn] = acc[r] + accm[r];
     }
   }
 }
@@ -158,9 +189,9 @@ hipError_t launch_qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int32_
   const uint8_t *W = static_cast<const uint8_t *>(w);
   const uint8_t *A = static_cast<const uint8_t *>(aq);
   if (D)
-    hipLaunchKernelGGL(mmq_q4k_kernel<true>, grid, dim3(256), 0, stream, W, A, c, D, (int)m, (int)n, (int)(k / 256));
+    hipLaunchKernelGGL(mmq_q4k_kernel<true>, grid, dim3(512), 0, stream, W, A, c, D, (int)m, (int)n, (int)(k / 256));
   else
-    hipLaunchKernelGGL(mmq_q4k_kernel<false>, grid, dim3(256), 0, stream, W, A, c, D, (int)m, (int)n,
+    hipLaunchKernelGGL(mmq_q4k_kernel<false>, grid, dim3(512), 0, stream, W, A, c, D, (int)m, (int)n,
                        (int)(k / 256));
   return hipGetLastError();
 }

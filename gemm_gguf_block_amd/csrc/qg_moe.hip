@@ -20,14 +20,16 @@
 namespace qg {
 
 // Kernels 1 and 3.  blockIdx.x = expert * tiles + row tile; each wave covers
-// (64/L)*R rows of the expert's [rows][nsb] matrix.  The routing table is
-// scanned 64 ids at a time with one vector load and a ballot, so a workgroup
-// whose expert nobody routed to finishes after npairs/64 loads.  For every pair
-// p with ids[p] == expert:
+// (64/L)*R rows of the expert's [rows][nsb] matrix, a lane the units
+// li, li + L, ... (UPL of them; lanes with nothing to do stay idle).  The
+// routing table is scanned 64 ids per vector load + ballot.  If any pair is
+// routed to the expert, the lane loads its weight units for all R rows into
+// VGPRs once; then, for every pair p with ids[p] == expert,
 //   out[p][row] = scale(p) * dot(row, act + act_row(p))
 // with act_row(p) = p / top_k (token rows, kernel 1) or p (h^ rows, kernel 3),
-// scale(p) = 1 (kernel 1) or weights[p] (kernel 3).
-template <int L, int R>
+// scale(p) = 1 (kernel 1) or weights[p] (kernel 3).  An expert nobody routed
+// to reads no weights; a touched expert's weights are read once.
+template <int L, int R, int UPL>
 __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__restrict__ W,
                                                               const uint8_t *__restrict__ act,
                                                               const int32_t *__restrict__ ids,
@@ -45,9 +47,32 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
   const int64_t rb = (int64_t)nsb * kQ4KBytes;
   const uint8_t *wexp = W + (int64_t)e * expert_bytes;
   const int U = nsb * 4;
+
+  constexpr int NV = UPL > 0 ? UPL : 1;
+  bool loaded = false;
+  u32x4 hdr[NV][R], qa[NV][R], qb[NV][R];
   for (int c0 = 0; c0 < npairs; c0 += 64) {
     const int id = c0 + lane < npairs ? ids[c0 + lane] : -1;
     uint64_t mask = __ballot(id == e);
+    if (UPL > 0 && mask && !loaded) {
+      loaded = true;
+#pragma unroll
+      for (int v = 0; v < UPL; ++v) {
+        const int u = li + v * L;
+        const int sb = u >> 2, g = u & 3;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (u < U && row0 + r < rows) {
+            const uint8_t *bp = wexp + (int64_t)(row0 + r) * rb + (int64_t)sb * kQ4KBytes;
+            hdr[v][r] = ld16(bp);
+            qa[v][r] = ld16(bp + 16 + 32 * g);
+            qb[v][r] = ld16(bp + 32 + 32 * g);
+          } else {
+            hdr[v][r] = qa[v][r] = qb[v][r] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+    }
     while (mask) {
       const int p = c0 + __builtin_ctzll(mask);
       mask &= mask - 1;
@@ -55,26 +80,159 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
       float acc[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = 0.f;
-      if (row0 < rows) {
-        for (int u = li; u < U; u += L) {
-          const int sb = u >> 2, g = u & 3;
-          u32x4 hdr[R], qa[R], qb[R];
+      // UPL > 0: the lane's UPL units were loaded above; UPL == 0: walk the
+      // row's units with stride L, loading each unit's weights here
+      const int nv = UPL > 0 ? UPL : (U - li + L - 1) / L;
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if (row0 + r < rows) {
-              const uint8_t *bp = wexp + (int64_t)(row0 + r) * rb + (int64_t)sb * kQ4KBytes;
-              hdr[r] = ld16(bp);
-              qa[r] = ld16(bp + 16 + 32 * g);
-              qb[r] = ld16(bp + 32 + 32 * g);
-            } else {
-              hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
+      for (int v = 0; v < nv; ++v) {
+        const int u = li + v * L;
+        if (u < U) {
+          const int sb = u >> 2, g = u & 3;
+          if (UPL == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              if (row0 + r < rows) {
+                const uint8_t *bp = wexp + (int64_t)(row0 + r) * rb + (int64_t)sb * kQ4KBytes;
+                hdr[0][r] = ld16(bp);
+                qa[0][r] = ld16(bp + 16 + 32 * g);
+                qb[0][r] = ld16(bp + 32 + 32 * g);
+              } else {
+                hdr[0][r] = qa[0][r] = qb[0][r] = u32x4{0u, 0u, 0u, 0u};
+              }
             }
           }
-          const uint8_t *ap = xr + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes;
-          const u32x4 a0 = ld16(ap), a1 = ld16(ap + 16), a2 = ld16(ap + 32), a3 = ld16(ap + 48);
-          const u32x2 a4 = ld8(ap + 64);
-          const uint32_t A[18] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w, a2.x,
-                                  a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w, a4.x, a4.y};
+          const int vi = UPL > 0 ? v : 0;
+          uint32_t A[18];
+          load_q8_1_pair(xr + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes, A);
+          int S0 = 0, S1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            S0 = bsum4(A[1 + i], S0);
+            S1 = bsum4(A[10 + i], S1);
+          }
+          const float da0 = h2f(A[0]), da1 = h2f(A[9]);
+          const float dS0 = da0 * (float)S0, dS1 = da1 * (float)S1;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t Q[8] = {qa[vi][r].x, qa[vi][r].y, qa[vi][r].z, qa[vi][r].w,
+                                   qb[vi][r].x, qb[vi][r].y, qb[vi][r].z, qb[vi][r].w};
+            int D0 = 0, D1 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              D0 = dot4(Q[i] & 0x0F0F0F0Fu, A[1 + i], D0);
+              D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A[10 + i], D1);
+            }
+            int sc0, sc1, m0, m1;
+            q4k_scales(hdr[vi][r].y, hdr[vi][r].z, hdr[vi][r].w, g, sc0, sc1, m0, m1);
+            const float d = h2f(hdr[vi][r].x), dmin = h2f(hdr[vi][r].x >> 16);
+            acc[r] += d * (da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1)) -
+                      dmin * (dS0 * (float)m0 + dS1 * (float)m1);
+          }
+        }
+      }
+      const float scale = weights ? weights[p] : 1.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = group_sum_last<L>(acc[r]);
+        if (li == L - 1 && row0 + r < rows) out[(int64_t)p * rows + row0 + r] = scale * v;
+      }
+    }
+  }
+}
+
+// Persistent form of kernels 1 and 3 for small routing tables (npairs <=
+// 64*kMaxIdWords, n_expert <= 64*kMaxExpertWords).  Every wave loads the whole
+// routing table into VGPRs once and builds the bitmap of touched experts with
+// ballots; the workgroups then stride over the work items (touched expert x
+// row tile) only, so an untouched expert costs nothing and every resident
+// workgroup is streaming some expert's weights.  Per item the pairs routed to
+// the expert come from ballots over the ids already in registers.
+constexpr int kMaxIdWords = 4;      // up to 256 (token, slot) pairs
+constexpr int kMaxExpertWords = 4;  // up to 256 experts
+
+template <int L, int R>
+__global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
+    const uint8_t *__restrict__ W, const uint8_t *__restrict__ act, const int32_t *__restrict__ ids,
+    const float *__restrict__ weights, float *__restrict__ out, int rows, int nsb, int npairs, int top_k,
+    int act_per_token, int64_t expert_bytes, int64_t act_row_bytes, int tiles, int n_expert) {
+  constexpr int G = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (L - 1);
+  const int64_t rb = (int64_t)nsb * kQ4KBytes;
+  const int U = nsb * 4;
+  // routing table in registers: id[w] = ids[64w + lane]
+  int id[kMaxIdWords];
+#pragma unroll
+  for (int w = 0; w < kMaxIdWords; ++w) {
+    const int p = 64 * w + lane;
+    id[w] = p < npairs ? ids[p] : -1;
+  }
+  // touched[x] bit b  <=>  expert 64x + b has a pair: each lane sets the bits
+  // of its ids, then a butterfly ORs the words over the wave
+  uint64_t touched[kMaxExpertWords];
+#pragma unroll
+  for (int x = 0; x < kMaxExpertWords; ++x) touched[x] = 0;
+#pragma unroll
+  for (int w = 0; w < kMaxIdWords; ++w) {
+    const int e = id[w];
+    const bool ok = e >= 0 && e < n_expert;
+#pragma unroll
+    for (int x = 0; x < kMaxExpertWords; ++x)
+      if (ok && (e >> 6) == x) touched[x] |= 1ull << (e & 63);
+  }
+#pragma unroll
+  for (int x = 0; x < kMaxExpertWords; ++x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) touched[x] |= __shfl_xor(touched[x], off, 64);
+  }
+  int active = 0;
+#pragma unroll
+  for (int x = 0; x < kMaxExpertWords; ++x) active += __builtin_popcountll(touched[x]);
+  const int items = active * tiles;
+
+  const int u = li;  // this lane's unit (L >= U here, so at most one)
+  const int sb = u >> 2, g = u & 3;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    // expert = the (item / tiles)-th touched expert
+    int k = item / tiles, e = -1;
+#pragma unroll
+    for (int x = 0; x < kMaxExpertWords; ++x) {
+      const int c = __builtin_popcountll(touched[x]);
+      if (e < 0 && k < c) {
+        uint64_t m = touched[x];
+        for (int t = 0; t < k; ++t) m &= m - 1;
+        e = 64 * x + __builtin_ctzll(m);
+      } else if (e < 0) {
+        k -= c;
+      }
+    }
+    const int row0 = (((item % tiles) * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+    const uint8_t *wu = W + (int64_t)e * expert_bytes + (int64_t)row0 * rb + sb * kQ4KBytes;
+    u32x4 hdr[R], qa[R], qb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (u < U && row0 + r < rows) {
+        const uint8_t *bp = wu + r * rb;
+        hdr[r] = ld16(bp);
+        qa[r] = ld16(bp + 16 + 32 * g);
+        qb[r] = ld16(bp + 32 + 32 * g);
+      } else {
+        hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < kMaxIdWords; ++w) {
+      uint64_t mask = __ballot(id[w] == e);
+      while (mask) {
+        const int p = 64 * w + __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const uint8_t *xr = act + (int64_t)(act_per_token ? p / top_k : p) * act_row_bytes;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        if (u < U) {
+          uint32_t A[18];
+          load_q8_1_pair(xr + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes, A);
           int S0 = 0, S1 = 0;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -99,12 +257,12 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
                       dmin * (dS0 * (float)m0 + dS1 * (float)m1);
           }
         }
-      }
-      const float scale = weights ? weights[p] : 1.0f;
+        const float scale = weights ? weights[p] : 1.0f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float v = group_sum<L>(acc[r]);
-        if (li == 0 && row0 + r < rows) out[(int64_t)p * rows + row0 + r] = scale * v;
+        for (int r = 0; r < R; ++r) {
+          const float v = group_sum_last<L>(acc[r]);
+          if (li == L - 1 && row0 + r < rows) out[(int64_t)p * rows + row0 + r] = scale * v;
+        }
       }
     }
   }
@@ -156,38 +314,69 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *__restric
   out[i] = acc;
 }
 
-template <int L, int R>
+template <int L, int R, int UPL>
 static void launch_expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights,
                                float *out, int rows, int nsb, int npairs, int top_k, int act_per_token,
                                int64_t expert_bytes, int64_t act_row_bytes, int n_expert, hipStream_t stream) {
   const int rows_per_block = 4 * (64 / L) * R;
   const int tiles = (rows + rows_per_block - 1) / rows_per_block;
   const dim3 grid((unsigned)((int64_t)tiles * n_expert));
-  hipLaunchKernelGGL((moe_expert_gemv_kernel<L, R>), grid, dim3(256), 0, stream, W, act, ids, weights, out, rows,
-                     nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles);
+  hipLaunchKernelGGL((moe_expert_gemv_kernel<L, R, UPL>), grid, dim3(256), 0, stream, W, act, ids, weights, out,
+                     rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles);
 }
 
-// Rows per lane group for the expert GEMVs (activation reuse, loads in flight).
+// Rows per lane group of the expert GEMVs.
 constexpr int kMoeRows = 2;
+// Workgroups of the persistent expert GEMV (four per CU on 256 CUs).
+constexpr int kMoePersistentBlocks = 1024;
+
+// Lanes per row: the smallest power of two >= the row's unit count, capped at
+// 64 (lanes past the last unit idle); each lane then keeps ceil(U/L) units'
+// weights for R rows in VGPRs (up to two units; longer rows reload per pair).
+template <int L, int R>
+static void launch_expert_gemv_persistent(const uint8_t *W, const uint8_t *act, const int32_t *ids,
+                                          const float *weights, float *out, int rows, int nsb, int npairs,
+                                          int top_k, int act_per_token, int64_t expert_bytes,
+                                          int64_t act_row_bytes, int n_expert, hipStream_t stream) {
+  const int rows_per_block = 4 * (64 / L) * R;
+  const int tiles = (rows + rows_per_block - 1) / rows_per_block;
+  const int64_t max_items = (int64_t)tiles * n_expert;
+  const dim3 grid((unsigned)(max_items < kMoePersistentBlocks ? max_items : kMoePersistentBlocks));
+  hipLaunchKernelGGL((moe_expert_gemv_persistent<L, R>), grid, dim3(256), 0, stream, W, act, ids, weights, out,
+                     rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles, n_expert);
+}
 
 static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights, float *out,
                         int rows, int nsb, int npairs, int top_k, int act_per_token, int64_t act_row_bytes,
                         int n_expert, hipStream_t stream) {
   const int64_t expert_bytes = (int64_t)rows * nsb * kQ4KBytes;
-  switch (lanes_per_row((int64_t)nsb * 4)) {
-#define QG_MOE_CASE(LV)                                                                                          \
-  case LV:                                                                                                       \
-    launch_expert_gemv<LV, kMoeRows>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token,         \
-                                     expert_bytes, act_row_bytes, n_expert, stream);                             \
-    break;
-    QG_MOE_CASE(64)
-    QG_MOE_CASE(32)
-    QG_MOE_CASE(16)
-    QG_MOE_CASE(8)
-    default:
-      QG_MOE_CASE(4)
-#undef QG_MOE_CASE
+  const int U = nsb * 4;
+  int L = 4;
+  while (L < U && L < 64) L <<= 1;
+  const int upl = (U + L - 1) / L;
+  if (upl == 1 && npairs <= 64 * kMaxIdWords && n_expert <= 64 * kMaxExpertWords) {
+#define QG_MOE_PERSIST(LV)                                                                                        \
+  launch_expert_gemv_persistent<LV, kMoeRows>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, \
+                                              expert_bytes, act_row_bytes, n_expert, stream)
+    if (L == 4) QG_MOE_PERSIST(4);
+    else if (L == 8) QG_MOE_PERSIST(8);
+    else if (L == 16) QG_MOE_PERSIST(16);
+    else if (L == 32) QG_MOE_PERSIST(32);
+    else QG_MOE_PERSIST(64);
+#undef QG_MOE_PERSIST
+    return;
   }
+#define QG_MOE_LAUNCH(LV, RV, UV)                                                                                 \
+  launch_expert_gemv<LV, RV, UV>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token,             \
+                                 expert_bytes, act_row_bytes, n_expert, stream)
+  if (L == 4) QG_MOE_LAUNCH(4, kMoeRows, 1);
+  else if (L == 8) QG_MOE_LAUNCH(8, kMoeRows, 1);
+  else if (L == 16) QG_MOE_LAUNCH(16, kMoeRows, 1);
+  else if (L == 32) QG_MOE_LAUNCH(32, kMoeRows, 1);
+  else if (upl == 1) QG_MOE_LAUNCH(64, kMoeRows, 1);
+  else if (upl == 2) QG_MOE_LAUNCH(64, 2, 2);
+  else QG_MOE_LAUNCH(64, 1, 0);  // long rows: weights reloaded per pair
+#undef QG_MOE_LAUNCH
 }
 
 MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd) {

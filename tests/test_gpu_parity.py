@@ -409,3 +409,12 @@ def test_graph_replay_matches_eager(env):
         got = snapshot()
         for e, r in zip(eager, got):
             assert torch.equal(e, r), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("F,H", [(256, 4608), (512, 8448)])
+def test_moe_long_rows(env, F, H):
+    """Rows of 72 and 132 lane units: the two-units-per-lane and the reload-per-
+    pair paths of the expert GEMV."""
+    E, T, K = 3, 4, 2
+    case = _moe_case(64 + F, E, F, H, T, K)
+    _run_moe_stagewise(env, *case, E, F, H, T, K)
