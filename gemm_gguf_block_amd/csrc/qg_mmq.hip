@@ -12,10 +12,14 @@
 // double-buffered: the global loads of superblock s+1 are in flight while the
 // MFMAs of superblock s run.  Each 32-wide sub-block j is exactly one
 // v_mfma_i32_32x32x32_i8 -> the exact int32 dots D of that block for the wave's
-// 32x32 tile, rescaled in fp32 on the VALU:  acc += (d_a * d*sc_j) * D.
-// The min term -sum_j (d_a*sum qa)_j (dmin*m_j) is a rank-8-per-superblock
-// product of two small fp32 matrices and runs on the matrix core as well
-// (v_mfma_f32_32x32x2_f32 over pairs of sub-blocks) into a second accumulator.
+// 32x32 tile.  Its fp32 rescale is acc += F * D with F[m][n] = d_a[m] * (d*sc_j)[n],
+// a rank-1 outer product that the matrix core forms as well: d_a (fp16) is
+// exactly the sum of two bf16 parts and d*sc_j is two bf16 parts to 2^-17, so
+// one v_mfma_f32_32x32x8_bf16 over those parts gives F in the MFMA output
+// layout, leaving one convert and one fma per output on the VALU.  The min term
+// -sum_j (d_a*sum qa)_j (dmin*m_j) is a rank-8-per-superblock product of two
+// small fp32 matrices and runs on the matrix core too (v_mfma_f32_32x32x2_f32
+// over pairs of sub-blocks) into a second accumulator.
 #include "qg_blocks.h"
 #include "qg_launch.h"
 
@@ -24,18 +28,31 @@ namespace qg {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 64, kBN = 128;
 constexpr int kRow = 272;  // LDS bytes per staged row: 256 + 16 (spreads rows over banks)
 
+// Per-block factor arrays are [block][row] so that the MFMA operand reads of a
+// wave are contiguous; one spare entry per block row spreads the transposed
+// staging writes over the LDS banks.
 struct MmqStage {
   uint8_t a[kBM * kRow];
   uint8_t b[kBN * kRow];
-  float dA[8][kBM];    // d_a per (block j, activation row)
-  float SA[8][kBM];    // d_a * sum(qa)
-  float dsc[8][kBN];   // d * sc_j per (sub-block j, weight row)
-  float ndm[8][kBN];   // -dmin * m_j
+  uint32_t fa[8][kBM + 1][2];   // bf16 (ah, ah, al, al) of d_a = ah + al, per (block j, activation row)
+  uint32_t fb[8][kBN + 1][2];   // bf16 (dh, dl, dh, dl) of d*sc_j = dh + dl, per (sub-block j, weight row)
+  float SA[8][kBM + 1];         // d_a * sum(qa)
+  float ndm[8][kBN + 1];        // -dmin * m_j
 };
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// x = hi + lo with hi, lo bf16 (exact when x has <= 16 significant bits).
+__device__ __forceinline__ void bf16_split(float x, uint32_t &hi, uint32_t &lo) {
+  const __bf16 h = (__bf16)x;
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = bf16_bits(x - (float)h);
+}
 
 // Global -> registers for one superblock: thread t stages activation block
 // (row t/8, block t%8) and weight (row t/4, byte group t%4).
@@ -81,7 +98,10 @@ __device__ __forceinline__ void mmq_store(const MmqRegs &g, MmqStage &s, int tid
     *reinterpret_cast<u32x4 *>(dst) = u32x4{q[0], q[1], q[2], q[3]};
     *reinterpret_cast<u32x4 *>(dst + 4) = u32x4{q[4], q[5], q[6], q[7]};
     const float da = h2f(g.a0.x);
-    s.dA[ab][ar] = da;
+    uint32_t hi, lo;
+    bf16_split(da, hi, lo);
+    s.fa[ab][ar][0] = hi | (hi << 16);
+    s.fa[ab][ar][1] = lo | (lo << 16);
     s.SA[ab][ar] = da * (float)S;
   }
   {  // weight group: nibbles -> int8 (sub-block 2g low, 2g+1 high), factors
@@ -99,8 +119,11 @@ __device__ __forceinline__ void mmq_store(const MmqRegs &g, MmqStage &s, int tid
     int sc0, sc1, mn0, mn1;
     q4k_scales(g.hdr.y, g.hdr.z, g.hdr.w, bg, sc0, sc1, mn0, mn1);
     const float d = h2f(g.hdr.x), dmin = h2f(g.hdr.x >> 16);
-    s.dsc[2 * bg][br] = d * (float)sc0;
-    s.dsc[2 * bg + 1][br] = d * (float)sc1;
+    uint32_t hi, lo;
+    bf16_split(d * (float)sc0, hi, lo);
+    s.fb[2 * bg][br][0] = s.fb[2 * bg][br][1] = hi | (lo << 16);
+    bf16_split(d * (float)sc1, hi, lo);
+    s.fb[2 * bg + 1][br][0] = s.fb[2 * bg + 1][br][1] = hi | (lo << 16);
     s.ndm[2 * bg][br] = -(dmin * (float)mn0);
     s.ndm[2 * bg + 1][br] = -(dmin * (float)mn1);
   }
@@ -123,8 +146,12 @@ __global__ __launch_bounds__(512) void mmq_q4k_kernel(const uint8_t *__restrict_
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = accm[r] = 0.f;
   v16i zero;
+  v16f fzero;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) zero[r] = 0;
+  for (int r = 0; r < 16; ++r) {
+    zero[r] = 0;
+    fzero[r] = 0.f;
+  }
 
   MmqRegs g;
   if (nsb > 0) {
@@ -151,21 +178,21 @@ __global__ __launch_bounds__(512) void mmq_q4k_kernel(const uint8_t *__restrict_
         const float nd = cur.ndm[j + lh][wn * 32 + lr];
         accm = __builtin_amdgcn_mfma_f32_32x32x2f32(sa, nd, accm, 0, 0, 0);
       }
-      // output register r holds tile row 8(r/4) + 4*lh + r%4, column lr
-      const float dsc = cur.dsc[j][wn * 32 + lr];
+      // 2F for this block: lanes 32-63 (k = 4..7) repeat the four parts of
+      // lanes 0-31, so the MFMA returns exactly twice the outer product
+      const uint32_t *fa = cur.fa[j][wm * 32 + lr];
+      const uint32_t *fb = cur.fb[j][wn * 32 + lr];
+      const v4s fav = __builtin_bit_cast(v4s, u32x2{fa[0], fa[1]});
+      const v4s fbv = __builtin_bit_cast(v4s, u32x2{fb[0], fb[1]});
+      const v16f F2 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fav, fbv, fzero, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 da4 = *reinterpret_cast<const float4 *>(&cur.dA[j][wm * 32 + 8 * q + 4 * lh]);
-        const float da[4] = {da4.x, da4.y, da4.z, da4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q + i;
-          if (DUMP) {
-            const int gm = m0 + wm * 32 + 8 * q + 4 * lh + i, gn = n0 + wn * 32 + lr;
-            if (gm < M && gn < N) Dd[((int64_t)gm * N + gn) * nbrow + sb * 8 + j] = D[r];
-          } else {
-            acc[r] += (da[i] * dsc) * (float)D[r];
-          }
+      for (int r = 0; r < 16; ++r) {
+        // output register r holds tile row 8(r/4) + 4*lh + r%4, column lr
+        if (DUMP) {
+          const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4), gn = n0 + wn * 32 + lr;
+          if (gm < M && gn < N) Dd[((int64_t)gm * N + gn) * nbrow + sb * 8 + j] = D[r];
+        } else {
+          acc[r] += F2[r] * (float)D[r];
         }
       }
     }
@@ -178,7 +205,7 @@ __global__ __launch_bounds__(512) void mmq_q4k_kernel(const uint8_t *__restrict_
     for (int r = 0; r < 16; ++r) {
       const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
       const int gn = n0 + wn * 32 + lr;
-      if (gm < M && gn < N) C[(int64_t)gm * N + gn] = acc[r] + accm[r];
+      if (gm < M && gn < N) C[(int64_t)gm * N + gn] = 0.5f * acc[r] + accm[r];
     }
   }
 }
