@@ -274,15 +274,22 @@ def make(name, qg, torch, warm):
 
 
 # ---------------------------------------------------------------- timing
-def _time(fn, first, count, warmup, torch, graph):
+def _time(fn, first, count, warmup, torch, graph, spinup):
     """Average ms per call of fn(i) over `count` calls, timed with HIP events on
     the stream the calls launch on.  With graph=True the calls are captured in a
-    HIP graph (after `warmup` eager calls) and the graph is replayed once
-    untimed, then once timed: the device work is identical, host launch
-    overhead is removed."""
+    HIP graph (after `warmup` eager calls) and the graph is replayed untimed,
+    then once timed: the device work is identical, host launch overhead is
+    removed.  The untimed part lasts at least `spinup` seconds of back-to-back
+    work, so the timed calls run at the clock the GPU sustains under load
+    rather than one still ramping up from idle."""
     if not graph:
-        for i in range(warmup):
+        t0 = time.perf_counter()
+        i = 0
+        while i < warmup or time.perf_counter() - t0 < spinup:
             fn(i)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -304,8 +311,12 @@ def _time(fn, first, count, warmup, torch, graph):
                 fn(first + i)
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        g.replay()
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= spinup:
+                break
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         g.replay()
@@ -314,9 +325,9 @@ def _time(fn, first, count, warmup, torch, graph):
     return e0.elapsed_time(e1) / count
 
 
-def run(wl, steps, warmup, torch, graph):
-    ms_step = _time(wl.step, warmup, steps, warmup, torch, graph)
-    ms_kernel = _time(wl.dominant_call, warmup, steps, warmup, torch, graph)
+def run(wl, steps, warmup, torch, graph, spinup):
+    ms_step = _time(wl.step, warmup, steps, warmup, torch, graph, spinup)
+    ms_kernel = _time(wl.dominant_call, warmup, steps, warmup, torch, graph, spinup)
     return ms_step, ms_kernel
 
 
@@ -325,7 +336,7 @@ def bench_one(name, args, qg, torch):
     wl = make(name, qg, torch, args.warm)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
-    ms_step, ms_kernel = run(wl, args.steps, args.warmup, torch, not args.no_graph)
+    ms_step, ms_kernel = run(wl, args.steps, args.warmup, torch, not args.no_graph, args.spinup)
     value = wl.value(ms_step / 1e3)
     achieved = wl.kernel_rate(ms_kernel / 1e3)
     peak = HBM_PEAK_GBS if wl.unit == "GB/s" else INT8_PEAK_TOPS
@@ -342,7 +353,7 @@ def bench_one(name, args, qg, torch):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": name, "hip_graph": not args.no_graph},
+        "config": {"workload": name, "hip_graph": not args.no_graph, "spinup_s": args.spinup},
         "tokens_per_s_equiv": round(wl.tokens_per_step / (ms_step / 1e3), 1),
         "roofline": {
             "bound": wl.bound,
@@ -377,6 +388,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--spinup", type=float, default=1.0,
+                    help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, or all")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
