@@ -17,6 +17,9 @@
 //        even block count), else one block read with byte realignment.
 //
 // With DUMP the same code writes the exact per-block int32 dots instead of y.
+#include <algorithm>
+#include <atomic>
+
 #include "qg_blocks.h"
 #include "qg_launch.h"
 
@@ -102,24 +105,69 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
   }
 }
 
+// ------------------------------------------------------ activations in LDS
+// Every row group reads the whole Q8_1 activation, so a workgroup stages it in
+// LDS once per chunk of kXBlocks blocks: qs as 16-byte-aligned int8 and, per
+// 16-value half block h of block b, rec[2b + h] = {f32 bits of d_a, sum of
+// those 16 qs}.
+constexpr int kXBlocks = 512;
+struct XChunk {
+  uint8_t qs[kXBlocks * 32];
+  u32x2 rec[kXBlocks * 2];
+};
+
+// Stages activation blocks [b0, b0 + nb), nb <= kXBlocks; all threads of the
+// workgroup call it, between barriers.
+__device__ __forceinline__ void stage_x(XChunk &x, const uint8_t *__restrict__ XQ, int64_t b0, int nb) {
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const uint8_t *ap = XQ + (b0 + b) * kQ8_1Bytes;
+    const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
+    const uint32_t v2 = ld4(ap + 32);
+    const u32x4 lo = {v0.y, v0.z, v0.w, v1.x}, hi = {v1.y, v1.z, v1.w, v2};
+    *reinterpret_cast<u32x4 *>(x.qs + 32 * b) = lo;
+    *reinterpret_cast<u32x4 *>(x.qs + 32 * b + 16) = hi;
+    const uint32_t d = __builtin_bit_cast(uint32_t, h2f(v0.x));
+    x.rec[2 * b] = u32x2{d, (uint32_t)bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0))))};
+    x.rec[2 * b + 1] = u32x2{d, (uint32_t)bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x, 0))))};
+  }
+}
+
 // ---------------------------------------------------------------- Q6_K
 template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
                                                        float *__restrict__ Y, int32_t *__restrict__ Dd, int n,
                                                        int nsb) {
+  __shared__ XChunk xs;
   constexpr int G = 64 / L;
+  constexpr int kChunkSb = kXBlocks / 8;
+  constexpr int kGroupRows = 4 * G * R;  // rows per workgroup per group
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
-  const int U = nsb * 4;
   const int64_t rb = (int64_t)nsb * kQ6KBytes;
+  const int64_t ngroups = ((int64_t)n + kGroupRows - 1) / kGroupRows;
+  int staged = -1;  // first superblock of the chunk in xs
+  // persistent: the grid holds what fits on the device and strides over row
+  // groups, so the activation is staged once per workgroup when it fits in
+  // one chunk
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+  const int64_t row0 = ((grp * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const uint8_t *wrow = W + row0 * rb;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  if (row0 < n) {
-    for (int u = li; u < U; u += L) {
-      const int sb = u >> 2, h = (u >> 1) & 1, l = u & 1;
+  for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
+    const int csb = min(kChunkSb, nsb - c0);
+    if (staged != c0) {
+      if (staged >= 0) __syncthreads();  // the previous chunk is no longer read
+      stage_x(xs, XQ, (int64_t)8 * c0, 8 * csb);
+      __syncthreads();
+      staged = c0;
+    }
+    if (row0 >= n) continue;
+    // L divides 4*nsb and 4*kChunkSb, hence the unit count of every chunk
+    for (int u = li; u < 4 * csb; u += L) {
+      const int sbl = u >> 2, h = (u >> 1) & 1, l = u & 1;
+      const int sb = c0 + sbl;
       u32x4 qlA[R], qlB[R], qh[R];
       u32x2 sc8[R];
       uint32_t dh[R];
@@ -138,20 +186,18 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
           dh[r] = 0u;
         }
       }
-      // activation: Q8_1 blocks 8sb + 4h + g, bytes 16l..16l+15 of each
+      // activation: Q8_1 blocks 8sb + 4h + g, values 16l..16l+15 of each
       uint32_t a[4][4];
       float da[4];
       int S16[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const uint8_t *ap = XQ + (int64_t)(8 * sb + 4 * h + g) * kQ8_1Bytes;
-        da[g] = h2f(ld4(ap));
-        const u32x4 av = ld16(ap + 4 + 16 * l);
+        const int blk = 8 * sbl + 4 * h + g;
+        const u32x4 av = *reinterpret_cast<const u32x4 *>(xs.qs + 32 * blk + 16 * l);
+        const u32x2 rec = xs.rec[2 * blk + l];
         a[g][0] = av.x; a[g][1] = av.y; a[g][2] = av.z; a[g][3] = av.w;
-        int s = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = bsum4(a[g][i], s);
-        S16[g] = 32 * s;
+        da[g] = __builtin_bit_cast(float, rec.x);
+        S16[g] = 32 * (int)rec.y;
       }
       const uint32_t lo8 = 8u * (uint32_t)l;
 #pragma unroll
@@ -188,12 +234,13 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
       }
     }
   }
-  if (!DUMP) {
+  if (!DUMP && row0 < n) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float v = group_sum_last<L>(acc[r]);
       if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
     }
+  }
   }
 }
 
@@ -335,6 +382,52 @@ constexpr int kRowsQ6K = 4;
     default: QG_LAUNCH(KERNEL, 1, RV, __VA_ARGS__); break;      \
   }
 
+// Workgroups of `kernel` (256 threads) resident on the current device at
+// once, cached per device.
+template <typename Kern>
+static int64_t resident_blocks(Kern kernel) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+  int v = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
+        cus < 1)
+      cus = 1;
+    v = per_cu * cus;
+    if (dev >= 0) cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Persistent launch: at most the resident workgroups, each striding over the
+// row groups of 4 * (64 / L) * R rows.
+#define QG_LAUNCH_PERSISTENT(KERNEL, LV, RV, ...)                                               \
+  do {                                                                                          \
+    const int64_t groups = (n + 4 * (64 / LV) * RV - 1) / (4 * (64 / LV) * RV);                 \
+    if (dump) {                                                                                 \
+      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, true>));                \
+      hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(256), 0, stream, __VA_ARGS__);  \
+    } else {                                                                                    \
+      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, false>));               \
+      hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(256), 0, stream, __VA_ARGS__); \
+    }                                                                                           \
+  } while (0)
+
+#define QG_GEMV_SWITCH_PERSISTENT(KERNEL, RV, ...)                         \
+  switch (L) {                                                             \
+    case 64: QG_LAUNCH_PERSISTENT(KERNEL, 64, RV, __VA_ARGS__); break;     \
+    case 32: QG_LAUNCH_PERSISTENT(KERNEL, 32, RV, __VA_ARGS__); break;     \
+    case 16: QG_LAUNCH_PERSISTENT(KERNEL, 16, RV, __VA_ARGS__); break;     \
+    case 8: QG_LAUNCH_PERSISTENT(KERNEL, 8, RV, __VA_ARGS__); break;       \
+    case 4: QG_LAUNCH_PERSISTENT(KERNEL, 4, RV, __VA_ARGS__); break;       \
+    case 2: QG_LAUNCH_PERSISTENT(KERNEL, 2, RV, __VA_ARGS__); break;       \
+    default: QG_LAUNCH_PERSISTENT(KERNEL, 1, RV, __VA_ARGS__); break;      \
+  }
+
 static dim3 gemv_grid(int64_t n, int L, int R) {
   const int64_t rows_per_block = 4 * (64 / L) * (int64_t)R;
   return dim3((unsigned)((n + rows_per_block - 1) / rows_per_block));
@@ -364,8 +457,7 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
   } else {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
-    const dim3 grid = gemv_grid(n, L, kRowsQ6K);
-    QG_GEMV_SWITCH(gemv_q6k_kernel, kRowsQ6K, W, X, y, D, ni, nsb)
+    QG_GEMV_SWITCH_PERSISTENT(gemv_q6k_kernel, kRowsQ6K, W, X, y, D, ni, nsb)
   }
   return hipGetLastError();
 }

@@ -80,7 +80,9 @@ def test_quantize_q8_1_bytes_exact(env, rows, k, scale):
 
 
 # ----------------------------------------------------------- GEMV block dots
-SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (257, 2048), (64, 4096), (33, 14336)]
+# (7, 17152) and (5, 33536) span two and three of the 16384-value activation
+# chunks a workgroup stages in LDS, the last one partial
+SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (257, 2048), (64, 4096), (33, 14336), (7, 17152), (5, 33536)]
 
 
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
