@@ -32,6 +32,11 @@ __device__ __forceinline__ float h2f(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
 }
 
+// f32 with the bits of u.  A scalar parameter on purpose: with this compiler
+// __builtin_bit_cast applied directly to an ext-vector element (v.y) reads
+// element 0, so elements must be copied out before the cast.
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
 // f32 -> binary16 bits, round to nearest even (v_cvt_f16_f32 in the default
 // rounding mode, with fp16 denormals preserved).
 __device__ __forceinline__ uint32_t f2h(float f) {

@@ -25,110 +25,169 @@
 
 namespace qg {
 
+// ------------------------------------------------------ activations in LDS
+// Every row group reads the whole Q8_1 activation, so a workgroup stages it in
+// (dynamic) LDS once per chunk of up to kXBlocks blocks.  The kernels read it
+// in units of 64 values (four 16-value pieces) per lane, so it is stored
+// unit-major for Q4_K: with U units in the chunk, piece c of unit u sits at
+// qs[c*U + u] (16 bytes each), and a wave's 64 lanes read 64 consecutive
+// pieces -- no LDS bank conflicts; unit u = blocks 2u, 2u+1 (pieces: halves
+// of 2u, then of 2u+1), with the 16-byte record
+//        rec[u] = {d_a(2u), d_a(2u+1), sum qs(2u), sum qs(2u+1)}.
+// Q6_K keeps the blocks in order (block b at qs bytes 32b) with, per 16-value
+// half h, the 8-byte record {d_a, sum of its 16 qs} at rec word pair 2b + h:
+// its lanes read with bank conflicts, yet this measured faster for that
+// kernel than the unit-major order.
+// d_a is stored as f32 bits, sums as int32.
+constexpr int kXBlocks = 512;
+typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));  // 16-byte aligned: ds_read/write_b128
+
+// Blocks per staged chunk for a row of nb activation blocks, and its LDS
+// bytes: 32 of qs and 16 of records per block.
+__host__ __device__ inline int x_chunk_blocks(int64_t nb) { return nb < kXBlocks ? (int)nb : kXBlocks; }
+inline size_t x_chunk_bytes(int64_t nb) { return (size_t)x_chunk_blocks(nb) * 48; }
+
+struct XView {
+  u32x4n *qs;   // 4U pieces of 16 bytes
+  u32x4n *rec;  // 2U x 16 bytes (Q4_K uses the first U)
+};
+
+// View of a staged chunk of U units (2U blocks) at the start of the dynamic LDS.
+__device__ __forceinline__ XView x_view(uint8_t *lds, int U) {
+  u32x4n *p = reinterpret_cast<u32x4n *>(lds);
+  return XView{p, p + 4 * U};
+}
+
+enum { kXQ4K = 1, kXQ6K = 2 };
+
+// Stages activation blocks [b0, b0 + nb) (nb = 2U <= kXBlocks) in the layout
+// of format FMT; all threads of the workgroup call it, between barriers.
+template <int FMT>
+__device__ __forceinline__ void stage_x(XView x, const uint8_t *__restrict__ XQ, int64_t b0, int nb) {
+  const int U = nb / 2;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const uint8_t *ap = XQ + (b0 + b) * kQ8_1Bytes;
+    const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
+    const uint32_t v2 = ld4(ap + 32);
+    const u32x4n lo = {v0.y, v0.z, v0.w, v1.x}, hi = {v1.y, v1.z, v1.w, v2};
+    const uint32_t d = __builtin_bit_cast(uint32_t, h2f(v0.x));
+    const int slo = bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0))));
+    const int shi = bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x, 0))));
+    uint32_t *ra = reinterpret_cast<uint32_t *>(x.rec);
+    if (FMT == kXQ4K) {
+      const int u = b >> 1, bb = b & 1;
+      x.qs[(2 * bb) * U + u] = lo;
+      x.qs[(2 * bb + 1) * U + u] = hi;
+      ra[4 * u + bb] = d;
+      ra[4 * u + 2 + bb] = (uint32_t)(slo + shi);
+    } else {
+      x.qs[2 * b] = lo;
+      x.qs[2 * b + 1] = hi;
+      ra[4 * b] = d;
+      ra[4 * b + 1] = (uint32_t)slo;
+      ra[4 * b + 2] = d;
+      ra[4 * b + 3] = (uint32_t)shi;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- Q4_K
 template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
                                                        float *__restrict__ Y, int32_t *__restrict__ Dd,
                                                        int32_t *__restrict__ Sd, int n, int nsb) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
+  constexpr int kChunkSb = kXBlocks / 8;
+  constexpr int kGroupRows = 4 * G * R;  // rows per workgroup per group
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
-  const int U = nsb * 4;
   const int64_t rb = (int64_t)nsb * kQ4KBytes;
-  const uint8_t *wrow = W + row0 * rb;
-  float acc[R];
+  const int64_t ngroups = ((int64_t)n + kGroupRows - 1) / kGroupRows;
+  int staged = -1;  // first superblock of the chunk in xs
+  // persistent over row groups, like the Q6_K kernel
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t row0 = ((grp * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+    const uint8_t *wrow = W + row0 * rb;
+    float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  if (row0 < n) {
-    for (int u = li; u < U; u += L) {
-      const int sb = u >> 2, g = u & 3;
-      // weights of this unit for the R rows, all loads issued before any use
-      u32x4 hdr[R], qa[R], qb[R];
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
+      const int csb = min(kChunkSb, nsb - c0);
+      const int U = 4 * csb;
+      const XView xs = x_view(lds, U);
+      // L divides 4*nsb and 4*kChunkSb, so every lane of the workgroup runs
+      // the same number of units per chunk (rows past n included, masked):
+      // the chunk's staging barrier can sit in the first one, after that
+      // unit's weight loads are in flight
+      for (int u = li; u < U; u += L) {
+        const int sbl = u >> 2, g = u & 3;
+        const int sb = c0 + sbl;
+        // weights of this unit for the R rows, all loads issued before any use
+        u32x4 hdr[R], qa[R], qb[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (row0 + r < n) {
-          const uint8_t *bp = wrow + r * rb + sb * kQ4KBytes;
-          hdr[r] = ld16(bp);
-          qa[r] = ld16(bp + 16 + 32 * g);
-          qb[r] = ld16(bp + 32 + 32 * g);
-        } else {
-          hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      // the activation slice (two Q8_1 blocks), shared by the R rows
-      uint32_t A[18];
-      load_q8_1_pair(XQ + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes, A);
-      int S0 = 0, S1 = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        S0 = bsum4(A[1 + i], S0);
-        S1 = bsum4(A[10 + i], S1);
-      }
-      const float da0 = h2f(A[0]), da1 = h2f(A[9]);
-      const float dS0 = da0 * (float)S0, dS1 = da1 * (float)S1;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t Q[8] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w, qb[r].x, qb[r].y, qb[r].z, qb[r].w};
-        int D0 = 0, D1 = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          D0 = dot4(Q[i] & 0x0F0F0F0Fu, A[1 + i], D0);
-          D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A[10 + i], D1);
-        }
-        if (DUMP) {
+        for (int r = 0; r < R; ++r) {
           if (row0 + r < n) {
-            Dd[(row0 + r) * (int64_t)(nsb * 8) + 8 * sb + 2 * g] = D0;
-            Dd[(row0 + r) * (int64_t)(nsb * 8) + 8 * sb + 2 * g + 1] = D1;
+            const uint8_t *bp = wrow + r * rb + sb * kQ4KBytes;
+            hdr[r] = ld16(bp);
+            qa[r] = ld16(bp + 16 + 32 * g);
+            qb[r] = ld16(bp + 32 + 32 * g);
+          } else {
+            hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
           }
-        } else {
-          int sc0, sc1, m0, m1;
-          q4k_scales(hdr[r].y, hdr[r].z, hdr[r].w, g, sc0, sc1, m0, m1);
-          const float d = h2f(hdr[r].x), dmin = h2f(hdr[r].x >> 16);
-          const float t = da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1);
-          const float mm = dS0 * (float)m0 + dS1 * (float)m1;
-          acc[r] += d * t - dmin * mm;
+        }
+        if (staged != c0) {
+          if (staged >= 0) __syncthreads();  // the previous chunk is no longer read
+          stage_x<kXQ4K>(xs, XQ, (int64_t)8 * c0, 8 * csb);
+          __syncthreads();
+          staged = c0;
+        }
+        if (row0 >= n) continue;
+        // the activation slice: Q8_1 blocks 8sb + 2g (low nibbles) and +1
+        // (high nibbles), shared by the R rows
+        const u32x4n x0 = xs.qs[u], x1 = xs.qs[U + u], x2 = xs.qs[2 * U + u], x3 = xs.qs[3 * U + u];
+        const u32x4n rec = xs.rec[u];
+        const uint32_t A0[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const uint32_t A1[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+        const int S0 = (int)rec.z, S1 = (int)rec.w;
+        const float da0 = as_f32(rec.x), da1 = as_f32(rec.y);
+        const float dS0 = da0 * (float)S0, dS1 = da1 * (float)S1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t Q[8] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w, qb[r].x, qb[r].y, qb[r].z, qb[r].w};
+          int D0 = 0, D1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            D0 = dot4(Q[i] & 0x0F0F0F0Fu, A0[i], D0);
+            D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A1[i], D1);
+          }
+          if (DUMP) {
+            if (row0 + r < n) {
+              Dd[(row0 + r) * (int64_t)(nsb * 8) + 8 * sb + 2 * g] = D0;
+              Dd[(row0 + r) * (int64_t)(nsb * 8) + 8 * sb + 2 * g + 1] = D1;
+            }
+          } else {
+            int sc0, sc1, m0, m1;
+            q4k_scales(hdr[r].y, hdr[r].z, hdr[r].w, g, sc0, sc1, m0, m1);
+            const float d = h2f(hdr[r].x), dmin = h2f(hdr[r].x >> 16);
+            const float t = da0 * (float)(sc0 * D0) + da1 * (float)(sc1 * D1);
+            const float mm = dS0 * (float)m0 + dS1 * (float)m1;
+            acc[r] += d * t - dmin * mm;
+          }
+        }
+        if (DUMP && row0 == 0) {
+          Sd[8 * sb + 2 * g] = S0;
+          Sd[8 * sb + 2 * g + 1] = S1;
         }
       }
-      if (DUMP && row0 == 0) {
-        Sd[8 * sb + 2 * g] = S0;
-        Sd[8 * sb + 2 * g + 1] = S1;
+    }
+    if (!DUMP && row0 < n) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = group_sum_last<L>(acc[r]);
+        if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
       }
     }
-  }
-  if (!DUMP) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = group_sum_last<L>(acc[r]);
-      if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
-    }
-  }
-}
-
-// ------------------------------------------------------ activations in LDS
-// Every row group reads the whole Q8_1 activation, so a workgroup stages it in
-// LDS once per chunk of kXBlocks blocks: qs as 16-byte-aligned int8 and, per
-// 16-value half block h of block b, rec[2b + h] = {f32 bits of d_a, sum of
-// those 16 qs}.
-constexpr int kXBlocks = 512;
-struct XChunk {
-  uint8_t qs[kXBlocks * 32];
-  u32x2 rec[kXBlocks * 2];
-};
-
-// Stages activation blocks [b0, b0 + nb), nb <= kXBlocks; all threads of the
-// workgroup call it, between barriers.
-__device__ __forceinline__ void stage_x(XChunk &x, const uint8_t *__restrict__ XQ, int64_t b0, int nb) {
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    const uint8_t *ap = XQ + (b0 + b) * kQ8_1Bytes;
-    const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
-    const uint32_t v2 = ld4(ap + 32);
-    const u32x4 lo = {v0.y, v0.z, v0.w, v1.x}, hi = {v1.y, v1.z, v1.w, v2};
-    *reinterpret_cast<u32x4 *>(x.qs + 32 * b) = lo;
-    *reinterpret_cast<u32x4 *>(x.qs + 32 * b + 16) = hi;
-    const uint32_t d = __builtin_bit_cast(uint32_t, h2f(v0.x));
-    x.rec[2 * b] = u32x2{d, (uint32_t)bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0))))};
-    x.rec[2 * b + 1] = u32x2{d, (uint32_t)bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x, 0))))};
   }
 }
 
@@ -137,7 +196,7 @@ template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
                                                        float *__restrict__ Y, int32_t *__restrict__ Dd, int n,
                                                        int nsb) {
-  __shared__ XChunk xs;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
   constexpr int kChunkSb = kXBlocks / 8;
   constexpr int kGroupRows = 4 * G * R;  // rows per workgroup per group
@@ -157,15 +216,17 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
   for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
     const int csb = min(kChunkSb, nsb - c0);
+    const int U = 4 * csb;
+    const XView xs = x_view(lds, U);
     if (staged != c0) {
       if (staged >= 0) __syncthreads();  // the previous chunk is no longer read
-      stage_x(xs, XQ, (int64_t)8 * c0, 8 * csb);
+      stage_x<kXQ6K>(xs, XQ, (int64_t)8 * c0, 8 * csb);
       __syncthreads();
       staged = c0;
     }
     if (row0 >= n) continue;
     // L divides 4*nsb and 4*kChunkSb, hence the unit count of every chunk
-    for (int u = li; u < 4 * csb; u += L) {
+    for (int u = li; u < U; u += L) {
       const int sbl = u >> 2, h = (u >> 1) & 1, l = u & 1;
       const int sb = c0 + sbl;
       u32x4 qlA[R], qlB[R], qh[R];
@@ -190,13 +251,15 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
       uint32_t a[4][4];
       float da[4];
       int S16[4];
+      const uint8_t *xq = reinterpret_cast<const uint8_t *>(xs.qs);
+      const u32x2 *xr = reinterpret_cast<const u32x2 *>(xs.rec);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int blk = 8 * sbl + 4 * h + g;
-        const u32x4 av = *reinterpret_cast<const u32x4 *>(xs.qs + 32 * blk + 16 * l);
-        const u32x2 rec = xs.rec[2 * blk + l];
+        const u32x4 av = *reinterpret_cast<const u32x4 *>(xq + 32 * blk + 16 * l);
+        const u32x2 rec = xr[2 * blk + l];
         a[g][0] = av.x; a[g][1] = av.y; a[g][2] = av.z; a[g][3] = av.w;
-        da[g] = __builtin_bit_cast(float, rec.x);
+        da[g] = as_f32(rec.x);
         S16[g] = 32 * (int)rec.y;
       }
       const uint32_t lo8 = 8u * (uint32_t)l;
@@ -382,38 +445,37 @@ constexpr int kRowsQ6K = 4;
     default: QG_LAUNCH(KERNEL, 1, RV, __VA_ARGS__); break;      \
   }
 
-// Workgroups of `kernel` (256 threads) resident on the current device at
-// once, cached per device.
+// Workgroups of `kernel` (256 threads, `lds` bytes of dynamic LDS) resident
+// on the current device at once.  Cached per device for the last LDS size
+// asked: (lds << 32 | count) in one word, so readers never see a torn pair.
 template <typename Kern>
-static int64_t resident_blocks(Kern kernel) {
+static int64_t resident_blocks(Kern kernel, size_t lds) {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cached[kMaxDev];
+  static std::atomic<uint64_t> cached[kMaxDev];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
-  int v = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
-  if (v == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
-        cus < 1)
-      cus = 1;
-    v = per_cu * cus;
-    if (dev >= 0) cached[dev].store(v, std::memory_order_relaxed);
-  }
+  const uint64_t c = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (c != 0 && (c >> 32) == (uint64_t)lds) return (int64_t)(c & 0xffffffffu);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
+    cus = 1;
+  const int64_t v = (int64_t)per_cu * cus;
+  if (dev >= 0) cached[dev].store(((uint64_t)lds << 32) | (uint64_t)v, std::memory_order_relaxed);
   return v;
 }
 
 // Persistent launch: at most the resident workgroups, each striding over the
-// row groups of 4 * (64 / L) * R rows.
+// row groups of 4 * (64 / L) * R rows; `xlds` bytes of dynamic LDS.
 #define QG_LAUNCH_PERSISTENT(KERNEL, LV, RV, ...)                                               \
   do {                                                                                          \
     const int64_t groups = (n + 4 * (64 / LV) * RV - 1) / (4 * (64 / LV) * RV);                 \
     if (dump) {                                                                                 \
-      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, true>));                \
-      hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(256), 0, stream, __VA_ARGS__);  \
+      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, true>, xlds));          \
+      hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
     } else {                                                                                    \
-      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, false>));               \
-      hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(256), 0, stream, __VA_ARGS__); \
+      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, false>, xlds));         \
+      hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
     }                                                                                           \
   } while (0)
 
@@ -452,11 +514,12 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
   } else if (fmt == 1) {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
-    const dim3 grid = gemv_grid(n, L, kRowsQ4K);
-    QG_GEMV_SWITCH(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
+    const size_t xlds = x_chunk_bytes(k / 32);
+    QG_GEMV_SWITCH_PERSISTENT(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
+    const size_t xlds = x_chunk_bytes(k / 32);
     QG_GEMV_SWITCH_PERSISTENT(gemv_q6k_kernel, kRowsQ6K, W, X, y, D, ni, nsb)
   }
   return hipGetLastError();
