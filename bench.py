@@ -47,6 +47,11 @@ KERNEL_SOURCES = {
     "q4_k_gemv": ["qg_gemv.hip"], "q8_0_gemv": ["qg_gemv.hip"], "q6_k_gemv": ["qg_gemv.hip"],
     "q4_k_mmq": ["qg_mmq.hip"], "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
 }
+BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8", "q6_k_gemv_b4", "q6_k_gemv_b8"]
+
+
+def _sources(workload):
+    return ["qg_gemv_batch.hip"] if "_gemv_b" in workload else KERNEL_SOURCES[workload]
 
 
 def kernel_source_hash(workload):
@@ -54,7 +59,7 @@ def kernel_source_hash(workload):
     import hashlib
     csrc = os.path.join(ROOT, "gemm_gguf_block_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[workload] + ["qg_blocks.h", "qg_device.h"]:
+    for f in _sources(workload) + ["qg_blocks.h", "qg_device.h"]:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
@@ -150,6 +155,51 @@ class Gemv(Workload):
         nb = reps * (sel.size * self.w_host.shape[1] + q81_bytes(self.k) + 4 * sel.size)
         return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
                     sample=f"rows 0..{sel.size - 1} of {self.n} (plain double dequant-and-dot) x {reps}, {t:.1f} s")
+
+
+class GemvBatch(Gemv):
+    """`<fmt>_gemv_b<B>`: the batch-1 workload's weights against B activation
+    rows (B concurrent decode sequences); weights are read once per step."""
+
+    def __init__(self, qg, torch, name, warm):
+        base, b = name.rsplit("_b", 1)
+        super().__init__(qg, torch, base, warm)
+        from gemm_gguf_block_amd import synth
+        self.name, self.b = name, int(b)
+        dev = torch.device("cuda:0")
+        self.x_host = synth.normal(self.seed, synth.T_X, (self.b, self.k))
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.xq = torch.empty((self.b, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((self.b, self.n), dtype=torch.float32, device=dev)
+        self.fn = getattr(qg, "qgemv_" + self.fmt + "_batch")
+        self.dominant = f"gemv_{self.fmt.replace('_', '')}_b{self.b}"
+        wbytes = self.w_host.nbytes
+        self.kernel_bytes = wbytes + self.b * (q81_bytes(self.k) + 4 * self.n)
+        self.step_bytes = self.kernel_bytes + self.b * (4 * self.k + q81_bytes(self.k))
+        self.tokens_per_step = self.b
+
+    def step(self, i):
+        self.qg.quantize_q8_1(self.x, self.xq)
+        self.fn(self.W[i % self.copies], self.xq, self.b, self.n, self.k, y=self.y)
+
+    def dominant_call(self, i):
+        self.fn(self.W[i % self.copies], self.xq, self.b, self.n, self.k, y=self.y)
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle
+        xq = oracle.quantize_q8_1(self.x_host)
+        sel = np.arange(min(self.n, 16384 // self.b), dtype=np.int64)
+
+        def once():
+            for i in range(self.b):
+                oracle.qgemv(self.fmt, self.w_host, xq[i], self.n, self.k, rows=sel)
+        reps, t = _repeat(once, budget_s)
+        nb = reps * (sel.size * self.w_host.shape[1] + self.b * (q81_bytes(self.k) + 4 * sel.size))
+        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
+                    sample=f"rows 0..{sel.size - 1} of {self.n} against {self.b} activation rows (plain double "
+                           f"dequant-and-dot per row) x {reps}, {t:.1f} s")
 
 
 class Mmq(Workload):
@@ -264,6 +314,8 @@ class Moe(Workload):
 
 
 def make(name, qg, torch, warm):
+    if "_gemv_b" in name:
+        return GemvBatch(qg, torch, name, warm)
     if name.endswith("_gemv"):
         return Gemv(qg, torch, name, warm)
     if name == "q4_k_mmq":
@@ -370,7 +422,7 @@ def bench_one(name, args, qg, torch):
     if wl.unit == "GB/s":
         rec["pct_of_hbm_peak"] = round(100.0 * value / HBM_PEAK_GBS, 2)
     cfg = rec["config"]
-    for key in ("fmt", "m", "n", "k", "E", "F", "H", "T", "K"):
+    for key in ("fmt", "b", "m", "n", "k", "E", "F", "H", "T", "K"):
         if hasattr(wl, key):
             cfg[key] = getattr(wl, key)
     cfg["weight_copies"] = wl.copies
@@ -391,7 +443,8 @@ def main():
     ap.add_argument("--spinup", type=float, default=1.0,
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
-                    help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, or all")
+                    help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
+                         "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -421,8 +474,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 10}))
         return
-    names = (["q4_k_gemv", "q8_0_gemv", "q6_k_gemv", "q4_k_mmq", "moe_q4_k"]
-             if args.workload == "all" else [args.workload])
+    names = (["q4_k_gemv", "q8_0_gemv", "q6_k_gemv", "q4_k_mmq", "moe_q4_k"] if args.workload == "all"
+             else BATCH_WORKLOADS if args.workload == "batch" else [args.workload])
     for name in names:
         rec = bench_one(name, args, qg, torch)
         print(json.dumps(rec), flush=True)

@@ -30,6 +30,9 @@ SIGNATURES = {
     "qgemv_q8_0": [_P, _P, _P, _I, _I, _P],
     "qgemv_q4_k": [_P, _P, _P, _I, _I, _P],
     "qgemv_q6_k": [_P, _P, _P, _I, _I, _P],
+    "qgemv_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemv_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemv_q6_k_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "moe_qgemv_q4_k_workspace_size": [_I, _I, _I, _I, _I],
     "moe_qgemv_q4_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
@@ -140,6 +143,31 @@ def qgemv_q4_k(w, xq, n, k, y=None, stream=None):
 
 def qgemv_q6_k(w, xq, n, k, y=None, stream=None):
     return _gemv("q6_k", w, xq, n, k, y, stream)
+
+
+def _gemv_batch(fmt, w, xq, b, n, k, y, stream):
+    import torch
+    if y is None:
+        y = _empty((b, n), torch.float32, w)
+    pw = _need(w, torch.uint8, n * row_bytes(fmt, k), "w")
+    pq = _need(xq, torch.uint8, b * row_bytes("q8_1", k), "xq")
+    py = _need(y, torch.float32, b * n * 4, "y")
+    name = "qgemv_" + fmt + "_batch"
+    _check(name, getattr(lib(), name)(pw, pq, py, b, n, k, _stream(stream)))
+    return y
+
+
+def qgemv_q8_0_batch(w, xq, b, n, k, y=None, stream=None):
+    """b (<= 8) Q8_1 rows xq [b][k/32*36] against Q8_0 weights -> y f32 [b][n]."""
+    return _gemv_batch("q8_0", w, xq, b, n, k, y, stream)
+
+
+def qgemv_q4_k_batch(w, xq, b, n, k, y=None, stream=None):
+    return _gemv_batch("q4_k", w, xq, b, n, k, y, stream)
+
+
+def qgemv_q6_k_batch(w, xq, b, n, k, y=None, stream=None):
+    return _gemv_batch("q6_k", w, xq, b, n, k, y, stream)
 
 
 def qgemm_q4_k_mmq(w, aq, m, n, k, c=None, stream=None):

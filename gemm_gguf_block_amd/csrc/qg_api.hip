@@ -60,6 +60,27 @@ qg_status run_gemv(int fmt, const void *w, const void *xq, float *y, int32_t *D,
   return launched(qg::launch_qgemv(fmt, w, xq, y, D, S, n, k, stream));
 }
 
+constexpr int64_t kMaxBatch = 8;
+
+qg_status check_gemv_batch(int fmt, const void *w, const void *xq, const void *out, int64_t nb, int64_t n,
+                           int64_t k) {
+  if (!w || !xq || !out) return QG_ERR_NULL;
+  if (nb < 0 || nb > kMaxBatch || n < 0 || k < 0 || n > kMaxRows || k > kMaxK) return QG_ERR_SHAPE;
+  if (nb * n > kMaxRows) return QG_ERR_SHAPE;
+  if (k % (fmt == 0 ? 32 : 256) != 0) return QG_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+qg_status run_gemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
+                         hipStream_t stream) {
+  qg_status st = check_gemv_batch(fmt, w, xq, y, nb, n, k);
+  if (st != QG_OK || nb == 0 || n == 0) return st;  // k == 0 runs: the kernel writes y = 0
+  st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_qgemv_batch(fmt, w, xq, y, nb, n, k, stream));
+}
+
 qg_status check_mmq(const void *w, const void *aq, const void *out, int64_t m, int64_t n, int64_t k) {
   if (!w || !aq || !out) return QG_ERR_NULL;
   if (m < 0 || n < 0 || k < 0 || m > kMaxRows || n > kMaxRows || k > kMaxK || k % 256 != 0) return QG_ERR_SHAPE;
@@ -108,6 +129,21 @@ QG_EXPORT qg_status qgemv_q4_k(const void *w, const void *xq, float *y, int64_t 
 QG_EXPORT qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
   qg_status st = check_gemv(2, w, xq, y, n, k);
   return st != QG_OK ? st : run_gemv(2, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemv_q8_0_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
+                                     hipStream_t stream) {
+  return run_gemv_batch(0, w, xq, y, b, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemv_q4_k_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
+                                     hipStream_t stream) {
+  return run_gemv_batch(1, w, xq, y, b, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemv_q6_k_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
+                                     hipStream_t stream) {
+  return run_gemv_batch(2, w, xq, y, b, n, k, stream);
 }
 
 QG_EXPORT qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,

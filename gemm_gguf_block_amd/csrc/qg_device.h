@@ -48,6 +48,13 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// Signed byte of w starting at bit `bit` (v_bfe_i32).  The builtin's result
+// type is unsigned, so it is cast back to int here: converting it straight to
+// float would read a negative byte as about 4.3e9.
+__device__ __forceinline__ int sbyte(uint32_t w, uint32_t bit) {
+  return (int)__builtin_amdgcn_sbfe((int)w, bit, 8u);
+}
+
 // Sum of the four signed bytes of `a`, added to c.
 __device__ __forceinline__ int bsum4(uint32_t a, int c) { return dot4(a, 0x01010101u, c); }
 

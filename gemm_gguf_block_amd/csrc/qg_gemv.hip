@@ -266,10 +266,8 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         // sub-block 8h + 2g + l has scale byte 2g + l of scales[8h..]
-        const int sc[4] = {(int)__builtin_amdgcn_sbfe((int)sc8[r].x, lo8, 8u),
-                           (int)__builtin_amdgcn_sbfe((int)sc8[r].x, 16u + lo8, 8u),
-                           (int)__builtin_amdgcn_sbfe((int)sc8[r].y, lo8, 8u),
-                           (int)__builtin_amdgcn_sbfe((int)sc8[r].y, 16u + lo8, 8u)};
+        const int sc[4] = {sbyte(sc8[r].x, lo8), sbyte(sc8[r].x, 16u + lo8), sbyte(sc8[r].y, lo8),
+                           sbyte(sc8[r].y, 16u + lo8)};
         const uint32_t A4[4] = {qlA[r].x, qlA[r].y, qlA[r].z, qlA[r].w};
         const uint32_t B4[4] = {qlB[r].x, qlB[r].y, qlB[r].z, qlB[r].w};
         const uint32_t H4[4] = {qh[r].x, qh[r].y, qh[r].z, qh[r].w};

@@ -1,0 +1,362 @@
+// qg_gemv_batch.hip -- small-batch GEMV: b <= 8 Q8_1 activation rows against
+// one read of Q8_0 / Q4_K / Q6_K weight rows, Y[i][r] = w^[r] . x^_i.
+//
+// This is the decode step of several concurrent sequences (the N generation
+// slots of infr page, "Concurrent slots, many models"): every weight byte is
+// fetched once and dotted against all b rows, so the call costs about one
+// batch-1 GEMV of HBM traffic while the integer-dot work grows with b.
+//
+// Decomposition as in the batch-1 kernels: a row is cut into units (Q8_0: one
+// 32-value block; Q4_K: a 64-value group = sub-blocks 2g, 2g+1; Q6_K: the
+// 64-value (half h, l-half) set of four 16-value sub-blocks), L lanes share a
+// row and walk its units.  A lane unpacks its unit's codes once into VGPRs and
+// runs v_dot4 against each of the B activation rows, which the persistent
+// workgroup stages in LDS once per chunk of k.  Rows i >= b of the batch
+// template are staged as zeros and never written.
+//
+// LDS per activation row and chunk of U units: the unit's 16-value pieces
+// unit-major, qs[(i * NP + p) * U + u] (NP = 2 pieces for Q8_0, 4 for the
+// K-quants), so a wave's 64 lanes read consecutive 16-byte pieces, and
+// per-unit records:
+//   Q8_0  recf[i * U + u]  = d_a
+//   Q4_K  rec4[i * U + u]  = {d_a(2u), d_a(2u+1), d_a*sum q (2u), d_a*sum q (2u+1)}
+//   Q6_K  rec4[2(i * U + u)] = d_a of pieces 0..3, [+1] = sum of each piece's 16 qs
+#include <algorithm>
+#include <atomic>
+
+#include "qg_blocks.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+namespace {
+
+typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));  // 16-byte aligned: ds_read/write_b128
+
+constexpr int kThreads = 512;  // 8 waves: one LDS copy of the activations serves more waves
+constexpr int kWaves = kThreads / 64;
+enum { kFmtQ8_0 = 0, kFmtQ4K = 1, kFmtQ6K = 2 };
+
+// Values per unit and 16-value pieces per unit.
+template <int FMT> struct Unit {
+  static constexpr int kValues = FMT == kFmtQ8_0 ? 32 : 64;
+  static constexpr int kPieces = kValues / 16;
+};
+
+// Activation blocks per staged chunk for a batch template of B rows: 1024/B
+// blocks keeps LDS at <= 48 KB (32 B of qs + <= 16 B of records per block).
+template <int B> constexpr int chunk_blocks() { return 1024 / B; }
+
+template <int FMT> __host__ __device__ constexpr int rec_bytes_per_block() {
+  return FMT == kFmtQ8_0 ? 4 : FMT == kFmtQ4K ? 8 : 16;
+}
+
+// LDS bytes for nbk blocks of B rows.
+template <int FMT, int B> size_t batch_lds_bytes(int64_t nbk) {
+  const int64_t cb = std::min<int64_t>(nbk, chunk_blocks<B>());
+  return (size_t)(B * cb * (32 + rec_bytes_per_block<FMT>()));
+}
+
+// Stages blocks [c0, c0 + cb) of every activation row i < nb (rows nb..B-1 as
+// zeros); XQ row i starts at XQ + i * row_bytes.  All threads call it,
+// between barriers.
+template <int FMT, int B>
+__device__ __forceinline__ void stage_batch(uint8_t *lds, const uint8_t *__restrict__ XQ, int64_t row_bytes, int nb,
+                                            int64_t c0, int cb) {
+  constexpr int NP = Unit<FMT>::kPieces;
+  const int U = cb * 32 / Unit<FMT>::kValues;
+  u32x4n *qs = reinterpret_cast<u32x4n *>(lds);
+  uint8_t *rec = lds + (size_t)B * NP * U * 16;
+  for (int t = threadIdx.x; t < B * cb; t += kThreads) {
+    const int i = t / cb, blk = t - i * cb;
+    u32x4n lo = {0u, 0u, 0u, 0u}, hi = lo;
+    float d = 0.f;
+    if (i < nb) {
+      const uint8_t *ap = XQ + i * row_bytes + (c0 + blk) * kQ8_1Bytes;
+      const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
+      const uint32_t v2 = ld4(ap + 32);
+      lo = u32x4n{v0.y, v0.z, v0.w, v1.x};
+      hi = u32x4n{v1.y, v1.z, v1.w, v2};
+      d = h2f(v0.x);
+    }
+    const int slo = bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0))));
+    const int shi = bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x, 0))));
+    if (FMT == kFmtQ8_0) {
+      qs[(i * NP + 0) * U + blk] = lo;
+      qs[(i * NP + 1) * U + blk] = hi;
+      reinterpret_cast<float *>(rec)[i * U + blk] = d;
+    } else if (FMT == kFmtQ4K) {
+      const int u = blk >> 1, bb = blk & 1;
+      qs[(i * NP + 2 * bb) * U + u] = lo;
+      qs[(i * NP + 2 * bb + 1) * U + u] = hi;
+      float *r = reinterpret_cast<float *>(rec) + 4 * (i * U + u);
+      r[bb] = d;
+      r[2 + bb] = d * (float)(slo + shi);
+    } else {
+      const int sbl = blk >> 3, h = (blk >> 2) & 1, g = blk & 3;
+      const int u0 = 4 * sbl + 2 * h;  // unit of half 0; half 1 is u0 + 1
+      qs[(i * NP + g) * U + u0] = lo;
+      qs[(i * NP + g) * U + u0 + 1] = hi;
+      uint32_t *r0 = reinterpret_cast<uint32_t *>(rec) + 8 * (i * U + u0);
+      r0[g] = __builtin_bit_cast(uint32_t, d);
+      r0[4 + g] = (uint32_t)slo;
+      r0[8 + g] = __builtin_bit_cast(uint32_t, d);
+      r0[12 + g] = (uint32_t)shi;
+    }
+  }
+}
+
+// One workgroup of 8 waves strides over groups of 8 * (64/L) * R rows; the
+// activation is staged per chunk of chunk_blocks<B>() Q8_1 blocks (c0 counts
+// blocks for every format).
+template <int FMT, int L, int B, int R>
+__global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__restrict__ W,
+                                                              const uint8_t *__restrict__ XQ, float *__restrict__ Y,
+                                                              int nb, int n, int nblk) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int G = 64 / L;
+  constexpr int NP = Unit<FMT>::kPieces;
+  constexpr int kGroupRows = kWaves * G * R;
+  constexpr int CB = chunk_blocks<B>();  // activation blocks per chunk
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (L - 1);
+  // row bytes and activation row bytes
+  const int64_t rb = FMT == kFmtQ8_0 ? (int64_t)nblk * kQ8_0Bytes
+                                     : (int64_t)(nblk / 8) * (FMT == kFmtQ4K ? kQ4KBytes : kQ6KBytes);
+  const int64_t xrb = (int64_t)nblk * kQ8_1Bytes;
+  const int64_t ngroups = ((int64_t)n + kGroupRows - 1) / kGroupRows;
+  int64_t staged = -1;
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t row0 = ((grp * kWaves + (threadIdx.x >> 6)) * G + lane / L) * R;
+    const uint8_t *wrow = W + row0 * rb;
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < B; ++i) acc[r][i] = 0.f;
+    for (int64_t c0 = 0; c0 < nblk; c0 += CB) {
+      const int cb = (int)std::min<int64_t>(CB, nblk - c0);
+      const int U = cb * 32 / Unit<FMT>::kValues;
+      if (staged != c0) {
+        if (staged >= 0) __syncthreads();  // the previous chunk is no longer read
+        stage_batch<FMT, B>(lds, XQ, xrb, nb, c0, cb);
+        __syncthreads();
+        staged = c0;
+      }
+      if (row0 >= n) continue;
+      const u32x4n *qs = reinterpret_cast<const u32x4n *>(lds);
+      const uint8_t *rec = lds + (size_t)B * NP * U * 16;
+      // L divides the unit count of every chunk (a power of two dividing both
+      // the row's unit count and the full chunk's)
+      for (int u = li; u < U; u += L) {
+        // ---- this unit's codes, once per row: 16 dwords of int8 (Q8_0: 8)
+        uint32_t q[R][16];
+        float f[R][4];  // per-format scale factors
+        int mi[R][2];   // Q4_K mins
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool live = row0 + r < n;
+          if (FMT == kFmtQ8_0) {
+            const uint8_t *bp = wrow + r * rb + (c0 + u) * kQ8_0Bytes;  // 2-byte aligned
+            u32x4 a = {0u, 0u, 0u, 0u}, b = a;
+            uint32_t dh = 0u;
+            if (live) {
+              dh = ld2(bp);
+              a = ld16_a2(bp + 2);
+              b = ld16_a2(bp + 18);
+            }
+            q[r][0] = a.x; q[r][1] = a.y; q[r][2] = a.z; q[r][3] = a.w;
+            q[r][4] = b.x; q[r][5] = b.y; q[r][6] = b.z; q[r][7] = b.w;
+            f[r][0] = h2f(dh);
+          } else if (FMT == kFmtQ4K) {
+            const int sb = (int)(c0 / 8) + (u >> 2), g = u & 3;
+            const uint8_t *bp = wrow + r * rb + (int64_t)sb * kQ4KBytes;
+            u32x4 hdr = {0u, 0u, 0u, 0u}, qa = hdr, qb = hdr;
+            if (live) {
+              hdr = ld16(bp);
+              qa = ld16(bp + 16 + 32 * g);
+              qb = ld16(bp + 32 + 32 * g);
+            }
+            const uint32_t Q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              q[r][j] = Q[j] & 0x0F0F0F0Fu;             // sub-block 2g
+              q[r][8 + j] = (Q[j] >> 4) & 0x0F0F0F0Fu;  // sub-block 2g+1
+            }
+            int sc0, sc1, m0, m1;
+            q4k_scales(hdr.y, hdr.z, hdr.w, g, sc0, sc1, m0, m1);
+            f[r][0] = h2f(hdr.x);        // d
+            f[r][1] = h2f(hdr.x >> 16);  // dmin
+            f[r][2] = (float)sc0;
+            f[r][3] = (float)sc1;
+            mi[r][0] = m0;
+            mi[r][1] = m1;
+          } else {
+            const int sb = (int)(c0 / 8) + (u >> 2), h = (u >> 1) & 1, l = u & 1;
+            const uint8_t *bp = wrow + r * rb + (int64_t)sb * kQ6KBytes;  // 2-byte aligned
+            u32x4 qlA = {0u, 0u, 0u, 0u}, qlB = qlA, qh = qlA;
+            u32x2 sc8 = {0u, 0u};
+            uint32_t dh = 0u;
+            if (live) {
+              qlA = ld16_a2(bp + 64 * h + 16 * l);
+              qlB = ld16_a2(bp + 64 * h + 32 + 16 * l);
+              qh = ld16_a2(bp + 128 + 32 * h + 16 * l);
+              sc8 = ld8_a2(bp + 192 + 8 * h);
+              dh = ld2(bp + 208);
+            }
+            const uint32_t A4[4] = {qlA.x, qlA.y, qlA.z, qlA.w};
+            const uint32_t B4[4] = {qlB.x, qlB.y, qlB.z, qlB.w};
+            const uint32_t H4[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // piece g = 0..3: sub-block 8h + 2g + l
+              q[r][j] = (A4[j] & 0x0F0F0F0Fu) | ((H4[j] << 4) & 0x30303030u);
+              q[r][4 + j] = (B4[j] & 0x0F0F0F0Fu) | ((H4[j] << 2) & 0x30303030u);
+              q[r][8 + j] = ((A4[j] >> 4) & 0x0F0F0F0Fu) | (H4[j] & 0x30303030u);
+              q[r][12 + j] = ((B4[j] >> 4) & 0x0F0F0F0Fu) | ((H4[j] >> 2) & 0x30303030u);
+            }
+            const uint32_t lo8 = 8u * (uint32_t)l;
+            const float d = h2f(dh);
+            f[r][0] = d * (float)sbyte(sc8.x, lo8);
+            f[r][1] = d * (float)sbyte(sc8.x, 16u + lo8);
+            f[r][2] = d * (float)sbyte(sc8.y, lo8);
+            f[r][3] = d * (float)sbyte(sc8.y, 16u + lo8);
+          }
+        }
+        // ---- against each activation row
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          uint32_t a[16];
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const u32x4n v = qs[(i * NP + p) * U + u];
+            a[4 * p] = v.x; a[4 * p + 1] = v.y; a[4 * p + 2] = v.z; a[4 * p + 3] = v.w;
+          }
+          if (FMT == kFmtQ8_0) {
+            const float da = reinterpret_cast<const float *>(rec)[i * U + u];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              int D = 0;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) D = dot4(q[r][j], a[j], D);
+              acc[r][i] += f[r][0] * da * (float)D;
+            }
+          } else if (FMT == kFmtQ4K) {
+            const u32x4n rv = reinterpret_cast<const u32x4n *>(rec)[i * U + u];
+            const float da0 = as_f32(rv.x), da1 = as_f32(rv.y), dS0 = as_f32(rv.z), dS1 = as_f32(rv.w);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              int D0 = 0, D1 = 0;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                D0 = dot4(q[r][j], a[j], D0);
+                D1 = dot4(q[r][8 + j], a[8 + j], D1);
+              }
+              const float t = da0 * (f[r][2] * (float)D0) + da1 * (f[r][3] * (float)D1);
+              const float mm = dS0 * (float)mi[r][0] + dS1 * (float)mi[r][1];
+              acc[r][i] += f[r][0] * t - f[r][1] * mm;
+            }
+          } else {
+            const u32x4n rd = reinterpret_cast<const u32x4n *>(rec)[2 * (i * U + u)];
+            const u32x4n rs = reinterpret_cast<const u32x4n *>(rec)[2 * (i * U + u) + 1];
+            const uint32_t dd[4] = {rd.x, rd.y, rd.z, rd.w};
+            const uint32_t ss[4] = {rs.x, rs.y, rs.z, rs.w};
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              float t = 0.f;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                int Dg = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Dg = dot4(q[r][4 * g + j], a[4 * g + j], Dg);
+                Dg -= 32 * (int)ss[g];  // sum (q-32)*qa
+                t += as_f32(dd[g]) * (f[r][g] * (float)Dg);
+              }
+              acc[r][i] += t;
+            }
+          }
+        }
+      }
+    }
+    if (row0 < n) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          const float v = group_sum_last<L>(acc[r][i]);
+          if (li == L - 1 && row0 + r < n && i < nb) Y[(int64_t)i * n + row0 + r] = v;
+        }
+    }
+  }
+}
+
+// Workgroups of `kernel` resident on the current device, cached per device
+// for the last LDS size asked (lds << 32 | count in one word).
+template <typename Kern>
+int64_t resident(Kern kernel, size_t lds) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<uint64_t> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+  const uint64_t c = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (c != 0 && (c >> 32) == (uint64_t)lds) return (int64_t)(c & 0xffffffffu);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
+    cus = 1;
+  const int64_t v = (int64_t)per_cu * cus;
+  if (dev >= 0) cached[dev].store(((uint64_t)lds << 32) | (uint64_t)v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int FMT> constexpr int rows_per_lane() { return FMT == kFmtQ6K ? 2 : 1; }
+
+template <int FMT, int L, int B>
+hipError_t launch_fmt_lb(const uint8_t *W, const uint8_t *X, float *y, int nb, int64_t n, int nblk,
+                         hipStream_t stream) {
+  constexpr int R = rows_per_lane<FMT>();
+  constexpr int kGroupRows = kWaves * (64 / L) * R;
+  const size_t lds = batch_lds_bytes<FMT, B>(nblk);
+  const int64_t groups = (n + kGroupRows - 1) / kGroupRows;
+  const int64_t g = std::min(groups, resident(gemv_batch_kernel<FMT, L, B, R>, lds));
+  hipLaunchKernelGGL((gemv_batch_kernel<FMT, L, B, R>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, nb,
+                     (int)n, nblk);
+  return hipGetLastError();
+}
+
+template <int FMT, int B>
+hipError_t launch_fmt_b(const uint8_t *W, const uint8_t *X, float *y, int nb, int64_t n, int nblk, int L,
+                        hipStream_t stream) {
+  switch (L) {
+    case 64: return launch_fmt_lb<FMT, 64, B>(W, X, y, nb, n, nblk, stream);
+    case 16: return launch_fmt_lb<FMT, 16, B>(W, X, y, nb, n, nblk, stream);
+    case 4: return launch_fmt_lb<FMT, 4, B>(W, X, y, nb, n, nblk, stream);
+    default: return launch_fmt_lb<FMT, 1, B>(W, X, y, nb, n, nblk, stream);
+  }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const uint8_t *W, const uint8_t *X, float *y, int nb, int64_t n, int nblk, hipStream_t stream) {
+  // lanes per row: the largest of 64, 16, 4, 1 dividing both the row's unit
+  // count and a full chunk's (so every chunk's unit count too)
+  const int units = nblk * 32 / Unit<FMT>::kValues;
+  int L = 64;
+  while (L > 1 && units % L != 0) L /= 4;
+  if (nb <= 2) return launch_fmt_b<FMT, 2>(W, X, y, nb, n, nblk, L, stream);
+  if (nb <= 4) return launch_fmt_b<FMT, 4>(W, X, y, nb, n, nblk, L, stream);
+  return launch_fmt_b<FMT, 8>(W, X, y, nb, n, nblk, L, stream);
+}
+
+}  // namespace
+
+hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
+                              hipStream_t stream) {
+  const uint8_t *W = static_cast<const uint8_t *>(w);
+  const uint8_t *X = static_cast<const uint8_t *>(xq);
+  const int nblk = (int)(k / 32);
+  if (fmt == 0) return launch_fmt<kFmtQ8_0>(W, X, y, (int)nb, n, nblk, stream);
+  if (fmt == 1) return launch_fmt<kFmtQ4K>(W, X, y, (int)nb, n, nblk, stream);
+  return launch_fmt<kFmtQ6K>(W, X, y, (int)nb, n, nblk, stream);
+}
+
+}  // namespace qg

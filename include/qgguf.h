@@ -90,6 +90,26 @@ qg_status qgemv_q4_k(const void *w, const void *xq, float *y, int64_t n, int64_t
 qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
 
 /*
+ * qgemv_q8_0_batch / qgemv_q4_k_batch / qgemv_q6_k_batch -- small-batch GEMV,
+ * b activation rows against one read of the weights (the decode step of b
+ * concurrent sequences: infr page, "Concurrent slots, many models").
+ * y[i][r] = sum_j w^[r][j] * x^_i[j] for i < b, each row computed like the
+ * batch-1 GEMV above from exact per-block int32 dots scaled in fp32 (the fp32
+ * rounding order may differ from qgemv_*, the value is the same to 1e-3).
+ *   w   : weight blocks [n][k/block_elems]
+ *   xq  : Q8_1 [b][k/32], the b rows back to back, 16-byte aligned
+ *   y   : f32 [b][n] row-major, written
+ *   b   : 0..8 (0 and n = 0 do nothing);  b * n <= 2^31 - 1
+ *   k   : multiple of 32 (Q8_0) or 256 (Q4_K, Q6_K), <= 2^24; k = 0 writes y = 0
+ */
+qg_status qgemv_q8_0_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
+                           hipStream_t stream);
+qg_status qgemv_q4_k_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
+                           hipStream_t stream);
+qg_status qgemv_q6_k_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
+                           hipStream_t stream);
+
+/*
  * qgemm_q4_k_mmq -- prefill product on int8 matrix cores.
  * c[i][r] = sum_j a^[i][j] * w^[r][j]: each 32-wide slice of k is one int8
  * 32x32x32 MFMA tile of exact per-block dots, rescaled in fp32 by d*sc_j*d_a

@@ -30,6 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemm_q4_k_mmq",
+                 "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
         assert want in names
 
@@ -90,6 +91,27 @@ def test_gemv_validation(lib, name, kmult):
     assert f(A16, MIS, y, 4, kmult, None) == ALIGN
     assert f(A16, A16b, P((1 << 20) + 2), 4, kmult, None) == ALIGN
     assert f(A16, A16b, y, 0, kmult, None) == OK
+
+
+@pytest.mark.parametrize("name,kmult", [("qgemv_q8_0_batch", 32), ("qgemv_q4_k_batch", 256),
+                                        ("qgemv_q6_k_batch", 256)])
+def test_gemv_batch_validation(lib, name, kmult):
+    f = getattr(lib, name)
+    y = P((1 << 20) + 8192)
+    assert f(None, A16b, y, 2, 4, kmult, None) == NULL
+    assert f(A16, None, y, 2, 4, kmult, None) == NULL
+    assert f(A16, A16b, None, 2, 4, kmult, None) == NULL
+    assert f(A16, A16b, y, 9, 4, kmult, None) == SHAPE      # more than 8 activation rows
+    assert f(A16, A16b, y, -1, 4, kmult, None) == SHAPE
+    assert f(A16, A16b, y, 2, 4, kmult + 16, None) == SHAPE
+    assert f(A16, A16b, y, 2, -1, kmult, None) == SHAPE
+    assert f(A16, A16b, y, 8, 1 << 29, kmult, None) == SHAPE  # b * n beyond 2^31 - 1
+    assert f(A16, A16b, y, 2, 4, kmult * (1 << 25), None) == SHAPE
+    assert f(MIS, A16b, y, 2, 4, kmult, None) == ALIGN
+    assert f(A16, MIS, y, 2, 4, kmult, None) == ALIGN
+    assert f(A16, A16b, P((1 << 20) + 2), 2, 4, kmult, None) == ALIGN
+    assert f(A16, A16b, y, 0, 4, kmult, None) == OK
+    assert f(A16, A16b, y, 3, 0, kmult, None) == OK
 
 
 def test_mmq_validation(lib):

@@ -199,6 +199,111 @@ def test_gemv_empty_and_zero_k(env):
         y.fill_(7.0)
 
 
+# ------------------------------------------------------------ small-batch GEMV
+GEMV_BATCH = {f: g + "_batch" for f, g in GEMV.items()}
+# k = 17152 and 33536 span several activation chunks for every batch template
+BATCH_SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (64, 4096), (33, 14336), (7, 17152), (5, 33536)]
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("b", [1, 2, 5, 8])
+@pytest.mark.parametrize("n,k", BATCH_SHAPES)
+def test_gemv_batch_values(env, fmt, b, n, k):
+    """Each of the b rows against the oracle's batch-1 GEMV of that row."""
+    qg, orc, torch, dev = env
+    w = synth.weights(fmt, n, k, seed=13 * n + k)
+    x = synth.normal(n + 7 * k + b, 1, (b, k))
+    X = qg.quantize_q8_1(_gpu(torch, dev, x))
+    y = _host(getattr(qg, GEMV_BATCH[fmt])(_gpu(torch, dev, w), X, b, n, k))
+    xq = orc.quantize_q8_1(x)
+    assert np.array_equal(_host(X), xq)
+    assert y.shape == (b, n)
+    for i in range(b):
+        assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+def test_gemv_batch_values_random_bytes(env, fmt):
+    qg, orc, torch, dev = env
+    b, n, k = 6, 300, 1024
+    w = synth.random_blocks(fmt, n, k, seed=177, lo_exp=-14, hi_exp=2)
+    xq = synth.random_blocks("q8_1", b, k, seed=178, lo_exp=-14, hi_exp=2)
+    y = _host(getattr(qg, GEMV_BATCH[fmt])(_gpu(torch, dev, w), _gpu(torch, dev, xq), b, n, k))
+    for i in range(b):
+        assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
+
+
+def test_gemv_batch_hand_superblock_exact(env):
+    """Rows with different power-of-two d_a and shifted codes: every
+    intermediate is exact in fp32, so each y[i] equals its hand-computed dot."""
+    qg, orc, torch, dev = env
+    b, k = 5, 256
+    xq = np.zeros((b, k // 32, 36), np.uint8)
+    qa = np.zeros((b, k), np.int64)
+    for i in range(b):
+        xq[i, :, 0:2] = np.frombuffer(np.float16(2.0 ** (i - 3)).tobytes(), np.uint8)
+        qa[i] = [((j + i) % 7) - 3 for j in range(k)]
+        xq[i, :, 4:] = qa[i].reshape(k // 32, 32).astype(np.int8).view(np.uint8)
+    X = _gpu(torch, dev, xq.reshape(b, -1))
+    da = [Fraction(2) ** (i - 3) for i in range(b)]
+    fx = read_golden("q4_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["sc"][0].split()]
+    m = [int(t) for t in fx["m"][0].split()]
+    y = _host(qg.qgemv_q4_k_batch(_gpu(torch, dev, np.tile(blk, (5, 1))), X, b, 5, k))
+    for i in range(b):
+        exact = sum((Fraction(1, 16) * sc[j // 32] * q[j] - Fraction(1, 32) * m[j // 32]) * da[i] * qa[i][j]
+                    for j in range(k))
+        assert all(Fraction(float(v)) == exact for v in y[i])
+    fx = read_golden("q6_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["scales"][0].split()]
+    y = _host(qg.qgemv_q6_k_batch(_gpu(torch, dev, np.tile(blk, (3, 1))), X, b, 3, k))
+    for i in range(b):
+        exact = sum(Fraction(1, 256) * sc[j // 16] * (q[j] - 32) * da[i] * qa[i][j] for j in range(k))
+        assert all(Fraction(float(v)) == exact for v in y[i])
+    blk = np.frombuffer(bytes.fromhex(read_golden("q8_0_block.txt")["bytes"][0]), np.uint8)
+    y = _host(qg.qgemv_q8_0_batch(_gpu(torch, dev, np.tile(blk, (2, 8))), X, b, 2, k))
+    for i in range(b):
+        exact = sum(Fraction((j % 32) - 16, 4) * da[i] * qa[i][j] for j in range(k))
+        assert all(Fraction(float(v)) == exact for v in y[i])
+
+
+def test_gemv_batch_empty_and_zero_k(env):
+    qg, orc, torch, dev = env
+    X = torch.zeros(8 * 288, dtype=torch.uint8, device=dev)
+    y = torch.full((4, 8), 7.0, device=dev)
+    for fmt, fn in GEMV_BATCH.items():
+        f = getattr(qg, fn)
+        W = torch.zeros(8 * qg.row_bytes(fmt, 256), dtype=torch.uint8, device=dev)
+        f(W, X, 4, 0, 256, y=y)   # n = 0: nothing written
+        f(W, X, 0, 8, 256, y=y)   # b = 0: nothing written
+        assert np.all(_host(y) == 7.0)
+        f(W, X, 4, 8, 0, y=y)     # k = 0: zeros
+        assert np.all(_host(y) == 0.0)
+        y.fill_(7.0)
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("name,b", [("q8_0_gemv", 8), ("q4_k_gemv", 8), ("q4_k_gemv", 3), ("q6_k_gemv", 4)])
+def test_gemv_batch_full_size(env, name, b):
+    """The workload shapes with b activation rows, on sampled output rows."""
+    qg, orc, torch, dev = env
+    p = synth.WORKLOADS[name]
+    fmt, n, k = p["fmt"], p["n"], p["k"]
+    w = synth.weights(fmt, n, k, p["seed"])
+    x = synth.normal(p["seed"], synth.T_X, (b, k))
+    X = qg.quantize_q8_1(_gpu(torch, dev, x))
+    y = _host(getattr(qg, GEMV_BATCH[fmt])(_gpu(torch, dev, w), X, b, n, k))
+    xq = orc.quantize_q8_1(x)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                     np.random.default_rng(2).integers(0, n, 1024)]))
+    for i in range(b):
+        assert rel_err(y[i][rows], orc.qgemv(fmt, w, xq[i], n, k, rows=rows)) <= REL_TOL, f"row {i}"
+
+
 @pytest.mark.big
 @pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv"])
 def test_gemv_full_size(env, name):
@@ -371,6 +476,9 @@ def test_graph_replay_matches_eager(env):
     Ws = {f: _gpu(torch, dev, synth.weights(f, n, k, seed=93)) for f in ("q8_0", "q4_k", "q6_k")}
     w_gu, w_dn, ids, rw, xm = _moe_case(94, E, F, H, T, K)
     WGU, WDN, IDS, RW, XM = (_gpu(torch, dev, v) for v in (w_gu, w_dn, ids, rw, xm))
+    xb = _gpu(torch, dev, synth.normal(95, 1, (5, k)))
+    xbq = torch.empty((5, k // 32 * 36), dtype=torch.uint8, device=dev)
+    ybs = {f: torch.empty((5, n), device=dev) for f in Ws}
     xq = torch.empty(k // 32 * 36, dtype=torch.uint8, device=dev)
     aq = torch.empty((m, k // 32 * 36), dtype=torch.uint8, device=dev)
     xmq = torch.empty((T, H // 32 * 36), dtype=torch.uint8, device=dev)
@@ -383,6 +491,9 @@ def test_graph_replay_matches_eager(env):
         qg.quantize_q8_1(x, xq)
         for f, W in Ws.items():
             getattr(qg, GEMV[f])(W, xq, n, k, y=ys[f])
+        qg.quantize_q8_1(xb, xbq)
+        for f, W in Ws.items():
+            getattr(qg, GEMV_BATCH[f])(W, xbq, 5, n, k, y=ybs[f])
         qg.quantize_q8_1(a, aq)
         qg.qgemm_q4_k_mmq(Ws["q4_k"], aq, m, n, k, c=c)
         qg.quantize_q8_1(XM, xmq)
@@ -390,7 +501,7 @@ def test_graph_replay_matches_eager(env):
 
     def snapshot():
         torch.cuda.synchronize()
-        return [t.clone() for t in (xq, *ys.values(), aq, c, xmq, out)]
+        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, xmq, out)]
 
     work()
     eager = snapshot()
@@ -404,7 +515,7 @@ def test_graph_replay_matches_eager(env):
             work()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (xq, *ys.values(), aq, c, xmq, out):
+        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, xmq, out):
             t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
