@@ -16,6 +16,10 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
 hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
                               hipStream_t stream);
 
+// Small-batch Q4_K GEMV on the int8 matrix cores (nb <= 8).
+hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
+                                       hipStream_t stream);
+
 hipError_t launch_qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,
                                  int64_t k, hipStream_t stream);
 

@@ -233,11 +233,12 @@ def test_gemv_batch_values_random_bytes(env, fmt):
         assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
 
 
-def test_gemv_batch_hand_superblock_exact(env):
+@pytest.mark.parametrize("b", [3, 5])  # Q4_K: the v_dot4 kernel up to 4 rows, the matrix-core one above
+def test_gemv_batch_hand_superblock_exact(env, b):
     """Rows with different power-of-two d_a and shifted codes: every
     intermediate is exact in fp32, so each y[i] equals its hand-computed dot."""
     qg, orc, torch, dev = env
-    b, k = 5, 256
+    k = 256
     xq = np.zeros((b, k // 32, 36), np.uint8)
     qa = np.zeros((b, k), np.int64)
     for i in range(b):
