@@ -52,7 +52,7 @@ BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8
 
 def _sources(workload):
     if "_gemv_b" in workload:
-        return ["qg_gemv_batch.hip", "qg_gemv_mfma.hip"] if workload.startswith("q4_k") else ["qg_gemv_batch.hip"]
+        return ["qg_gemv_batch.hip"] if workload.startswith("q8_0") else ["qg_gemv_batch.hip", "qg_gemv_mfma.hip"]
     return KERNEL_SOURCES[workload]
 
 

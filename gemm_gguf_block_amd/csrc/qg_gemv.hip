@@ -18,7 +18,6 @@
 //
 // With DUMP the same code writes the exact per-block int32 dots instead of y.
 #include <algorithm>
-#include <atomic>
 
 #include "qg_blocks.h"
 #include "qg_launch.h"
@@ -443,36 +442,16 @@ constexpr int kRowsQ6K = 4;
     default: QG_LAUNCH(KERNEL, 1, RV, __VA_ARGS__); break;      \
   }
 
-// Workgroups of `kernel` (256 threads, `lds` bytes of dynamic LDS) resident
-// on the current device at once.  Cached per device for the last LDS size
-// asked: (lds << 32 | count) in one word, so readers never see a torn pair.
-template <typename Kern>
-static int64_t resident_blocks(Kern kernel, size_t lds) {
-  constexpr int kMaxDev = 64;
-  static std::atomic<uint64_t> cached[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
-  const uint64_t c = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
-  if (c != 0 && (c >> 32) == (uint64_t)lds) return (int64_t)(c & 0xffffffffu);
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1) per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
-    cus = 1;
-  const int64_t v = (int64_t)per_cu * cus;
-  if (dev >= 0) cached[dev].store(((uint64_t)lds << 32) | (uint64_t)v, std::memory_order_relaxed);
-  return v;
-}
-
 // Persistent launch: at most the resident workgroups, each striding over the
 // row groups of 4 * (64 / L) * R rows; `xlds` bytes of dynamic LDS.
 #define QG_LAUNCH_PERSISTENT(KERNEL, LV, RV, ...)                                               \
   do {                                                                                          \
     const int64_t groups = (n + 4 * (64 / LV) * RV - 1) / (4 * (64 / LV) * RV);                 \
     if (dump) {                                                                                 \
-      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, true>, xlds));          \
+      const int64_t g = std::min(groups, resident_blocks<KERNEL<LV, RV, true>>(256, xlds));          \
       hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
     } else {                                                                                    \
-      const int64_t g = std::min(groups, resident_blocks(KERNEL<LV, RV, false>, xlds));         \
+      const int64_t g = std::min(groups, resident_blocks<KERNEL<LV, RV, false>>(256, xlds));         \
       hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
     }                                                                                           \
   } while (0)

@@ -22,7 +22,6 @@
 //   Q4_K  rec4[i * U + u]  = {d_a(2u), d_a(2u+1), d_a*sum q (2u), d_a*sum q (2u+1)}
 //   Q6_K  rec4[2(i * U + u)] = d_a of pieces 0..3, [+1] = sum of each piece's 16 qs
 #include <algorithm>
-#include <atomic>
 
 #include "qg_blocks.h"
 #include "qg_launch.h"
@@ -289,26 +288,6 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__r
   }
 }
 
-// Workgroups of `kernel` resident on the current device, cached per device
-// for the last LDS size asked (lds << 32 | count in one word).
-template <typename Kern>
-int64_t resident(Kern kernel, size_t lds) {
-  constexpr int kMaxDev = 64;
-  static std::atomic<uint64_t> cached[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
-  const uint64_t c = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
-  if (c != 0 && (c >> 32) == (uint64_t)lds) return (int64_t)(c & 0xffffffffu);
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
-    cus = 1;
-  const int64_t v = (int64_t)per_cu * cus;
-  if (dev >= 0) cached[dev].store(((uint64_t)lds << 32) | (uint64_t)v, std::memory_order_relaxed);
-  return v;
-}
-
 template <int FMT> constexpr int rows_per_lane() { return FMT == kFmtQ6K ? 2 : 1; }
 
 template <int FMT, int L, int B>
@@ -318,7 +297,7 @@ hipError_t launch_fmt_lb(const uint8_t *W, const uint8_t *X, float *y, int nb, i
   constexpr int kGroupRows = kWaves * (64 / L) * R;
   const size_t lds = batch_lds_bytes<FMT, B>(nblk);
   const int64_t groups = (n + kGroupRows - 1) / kGroupRows;
-  const int64_t g = std::min(groups, resident(gemv_batch_kernel<FMT, L, B, R>, lds));
+  const int64_t g = std::min(groups, resident_blocks<gemv_batch_kernel<FMT, L, B, R>>(kThreads, lds));
   hipLaunchKernelGGL((gemv_batch_kernel<FMT, L, B, R>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, nb,
                      (int)n, nblk);
   return hipGetLastError();
@@ -355,12 +334,14 @@ hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, 
   const uint8_t *X = static_cast<const uint8_t *>(xq);
   const int nblk = (int)(k / 32);
   if (fmt == 0) return launch_fmt<kFmtQ8_0>(W, X, y, (int)nb, n, nblk, stream);
+  // Measured on MI355X: v_dot4 is faster up to 4 rows; from 5 rows (where it
+  // runs its 8-row instance) the matrix-core kernels are.  8 rows, k = 4096:
+  // Q4_K 14336 rows 13.8 vs 16.0 us, Q6_K 128256 rows 108 vs 138 us.
   if (fmt == 1) {
-    // measured on MI355X (14336 x 4096): v_dot4 is faster up to 4 rows, the
-    // matrix-core kernel from 5 on (13.8 vs 16.0 us at 8 rows)
     if (nb > 4) return launch_qgemv_batch_mfma_q4k(w, xq, y, nb, n, k, stream);
     return launch_fmt<kFmtQ4K>(W, X, y, (int)nb, n, nblk, stream);
   }
+  if (nb > 4) return launch_qgemv_batch_mfma_q6k(w, xq, y, nb, n, k, stream);
   return launch_fmt<kFmtQ6K>(W, X, y, (int)nb, n, nblk, stream);
 }
 

@@ -1,23 +1,27 @@
-// qg_gemv_mfma.hip -- small-batch Q4_K GEMV on the int8 matrix cores.
+// qg_gemv_mfma.hip -- small-batch Q4_K and Q6_K GEMV on the int8 matrix cores.
 //
 // With b <= 8 activation rows the dot4 kernels spend VALU per (row, block,
-// activation row).  Here the b rows form the M side of
-// v_mfma_i32_32x32x32_i8 (rows b..31 are zero) and 32 weight rows the N side,
-// so one MFMA gives the exact int32 block dots of 32 weight rows against all b
+// activation row).  Here the activation rows form the M side of
+// v_mfma_i32_32x32x32_i8 (unused rows are zero) and 32 weight rows the N side,
+// so one MFMA gives the exact int32 block dots of 32 weight rows against all
 // activation rows, and the fp32 rescale costs the same few VALU per block
 // whatever b is.
 //
-// A workgroup of 8 waves owns a tile of 32 weight rows.  k is walked in
+// MFMA 32x32 output layout: register r of lane l holds row 8(r/4) + 4(l/32) +
+// r%4, column l%32.  The A operand of lane l is row l%32, k half l/32; the B
+// operand of lane l is column l%32, the same k half.
+//
+// Q4_K: a workgroup of 8 waves owns a tile of 32 weight rows.  k is walked in
 // chunks of 16 superblocks: the workgroup stages the chunk's activation blocks
 // in LDS, wave w takes superblocks w and w + 8 of the chunk (32 rows x 144
 // bytes each, loaded before the staging barrier), and runs their blocks on the
 // matrix core.  The 8 waves' partial tiles are summed through LDS at the end.
 // Two such workgroups fit on a CU, so 14336 rows (448 tiles) run in one pass.
-//
-// Output register r of a lane holds activation row 8(r/4) + 4(lane/32) + r%4,
-// so for b <= 8 only r = 0..3 carry rows (4(lane/32) + r) and are rescaled.
+// For b <= 8 only registers r = 0..3 carry rows (4(lane/32) + r).
 #include "qg_blocks.h"
 #include "qg_launch.h"
+
+#include <algorithm>
 
 namespace qg {
 
@@ -149,6 +153,187 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q4k(const uint8_t *_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Q6_K.  A scale covers 16 values, half a Q8_1 block, so a block's MFMA
+// carries each activation row twice: A row 2m + h holds activation row m in k
+// half h and zeros in the other half (those lanes read a zero unit in LDS).
+// Output registers 2j and 2j + 1 then hold the two sub-block dots of one
+// activation row.  They are combined with the sub-blocks' int8 scales in fp32:
+// each product is exact (a sub-block dot is at most 16 * 32 * 128 in
+// magnitude), so the pair's sum is rounded once, and not at all below 2^24.
+// (The MFMA results are read by compiler-generated code only: an inline-asm
+// reader gets none of the wait states an MFMA result needs.)
+//
+// B takes the codes as q - 32 in int8: the low nibble comes from ql and the
+// high nibble from a 4-entry byte table indexed by the two qh bits
+// (v_perm_b32), since (q - 32) mod 256 = ql + 16 * ((qh - 2) mod 16).
+//
+// A persistent workgroup of 8 waves takes one 32-row tile at a time; wave w
+// runs superblocks w, w + 8, ... of it (all of a 4096-wide row's superblocks
+// are in flight at once), the 8 partial tiles are summed through LDS, and the
+// next tile's first superblock is loaded before that reduction.  The
+// activation rows are staged in LDS once when k fits a chunk (7168 values),
+// else once per chunk and tile.
+namespace q6 {
+
+constexpr int kChunkBlk = 224;           // Q8_1 blocks per LDS chunk
+constexpr int kChunkSb = kChunkBlk / 8;  // superblocks per chunk
+
+// Per chunk block: 2 * BP units of 16 bytes (activation row m, k half h at
+// unit 2m + h) and a zero unit; after all units, 8 d_a per block, row m at
+// position pos(m) so that lane half lh reads rows {2lh, 2lh+1, 2lh+4, 2lh+5}
+// as one group at 4 * lh; then the waves' partial tiles, BP / 2 floats per
+// lane.
+__host__ __device__ constexpr int unit_stride(int bp) { return 2 * bp + 1; }
+__device__ __forceinline__ int pos(int m) { return (m & 1) | ((m & 2) << 1) | ((m & 4) >> 1); }
+__host__ __device__ constexpr size_t part_offset(int bp) { return (size_t)kChunkBlk * ((size_t)unit_stride(bp) * 16 + 32); }
+inline size_t lds_bytes(int bp) { return part_offset(bp) + (size_t)kWaves * 64 * (bp / 2) * 4; }
+
+// One superblock as lane half lh needs it: block j (k 32j..32j+31) takes its
+// half-lh codes from ql[2(j/4) + j%2] (nibble (j/2)%2) and qh[j/4] (bit pair
+// j%4); all 16 scales and d are read by both halves.
+struct Sb {
+  u32x4 ql[4];
+  u32x4 qh[2];
+  u32x4 sc;
+  uint32_t d;
+};
+
+__device__ __forceinline__ void load_sb(const uint8_t *p, int lh, Sb &s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s.ql[i] = ld16_a2(p + 64 * (i >> 1) + 32 * (i & 1) + 16 * lh);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) s.qh[h] = ld16_a2(p + 128 + 32 * h + 16 * lh);
+  s.sc = ld16_a2(p + 192);
+  s.d = ld2(p + 208);
+}
+
+// q - 32 of 4 codes: low nibbles of `lo`, bit pairs of `hi`.
+__device__ __forceinline__ int codes4(uint32_t lo, uint32_t hi) {
+  const uint32_t hb = hi & 0x03030303u;
+  // table bytes 0..3 = 0xE0, 0xF0, 0x00, 0x10; given as both sources so the
+  // selector 0..3 names a table byte either way round
+  const uint32_t top = __builtin_amdgcn_perm(0x1000F0E0u, 0x1000F0E0u, hb);
+  return (int)((lo & 0x0F0F0F0Fu) | top);
+}
+
+template <int BP>
+__global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *__restrict__ W,
+                                                                const uint8_t *__restrict__ XQ,
+                                                                float *__restrict__ Y, int nb, int n, int nsb) {
+  constexpr int S = unit_stride(BP);
+  constexpr int NJ = BP / 2;  // activation rows per lane
+  typedef float fNJ __attribute__((ext_vector_type(NJ)));
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  u32x4n *act = reinterpret_cast<u32x4n *>(lds);
+  float *da = reinterpret_cast<float *>(lds + (size_t)kChunkBlk * S * 16);
+  fNJ *part = reinterpret_cast<fNJ *>(lds + part_offset(BP));
+
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int nl = lane & 31, lh = lane >> 5;
+  // A row nl is activation row nl / 2 in k half nl % 2
+  const int aunit = ((nl & 1) == lh && (nl >> 1) < nb) ? nl : 2 * BP;
+  const int64_t rb = (int64_t)nsb * kQ6KBytes;
+  const int64_t xrb = (int64_t)nsb * 8 * kQ8_1Bytes;
+  const int ntiles = (n + 31) / 32;
+  const int nchunk = (nsb + kChunkSb - 1) / kChunkSb;
+  const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  auto wrow = [&](int tile) { return W + min((int64_t)tile * 32 + nl, (int64_t)n - 1) * rb; };
+
+  // zero units and the d_a of rows >= nb; never written by the staging
+  for (int t = tid; t < kChunkBlk; t += kThreads) {
+    act[t * S + 2 * BP] = u32x4n{0u, 0u, 0u, 0u};
+    for (int m = nb; m < 8; ++m) da[t * 8 + pos(m)] = 0.f;
+  }
+
+  auto step = [&](const Sb &w, int sbl, fNJ &acc) {
+    fNJ p = {};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = 8 * sbl + j;
+      const u32x4 lo = w.ql[2 * (j >> 2) + (j & 1)], hi = w.qh[j >> 2];
+      const uint32_t ls = 4u * (uint32_t)((j >> 1) & 1), hs = 2u * (uint32_t)(j & 3);
+      const v4i b = {codes4(lo.x >> ls, hi.x >> hs), codes4(lo.y >> ls, hi.y >> hs), codes4(lo.z >> ls, hi.z >> hs),
+                     codes4(lo.w >> ls, hi.w >> hs)};
+      const v4i a = __builtin_bit_cast(v4i, act[blk * S + aunit]);
+      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
+      const uint32_t scw = w.sc[j >> 1];
+      const float sc0 = (float)sbyte(scw, 16u * (uint32_t)(j & 1));
+      const float sc1 = (float)sbyte(scw, 16u * (uint32_t)(j & 1) + 8u);
+      const fNJ dv = *reinterpret_cast<const fNJ *>(da + blk * 8 + 4 * lh);
+#pragma unroll
+      for (int q = 0; q < NJ; ++q) p[q] = fmaf(dv[q], fmaf((float)D[2 * q + 1], sc1, (float)D[2 * q] * sc0), p[q]);
+      asm volatile("" : "+v"(p)::"memory");
+    }
+    acc += h2f(w.d) * p;
+  };
+
+  Sb cur, nxt;
+  int tile = (int)blockIdx.x;
+  if (tile < ntiles && wv < min(kChunkSb, nsb)) load_sb(wrow(tile) + (int64_t)wv * kQ6KBytes, lh, cur);
+  for (int rnd = 0; tile < ntiles; ++rnd, tile += (int)gridDim.x) {  // tile is uniform in the workgroup
+    const uint8_t *wr = wrow(tile);
+    fNJ acc = {};
+    for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
+      const int csb = min(kChunkSb, nsb - c0);
+      if (c0 > 0 && wv < csb) load_sb(wr + (int64_t)(c0 + wv) * kQ6KBytes, lh, cur);
+      if (nchunk > 1 || rnd == 0) {
+        if (rnd > 0 || c0 > 0) __syncthreads();  // the previous chunk is no longer read
+        for (int t = tid; t < nb * 8 * csb; t += kThreads) {
+          const int m = t / (8 * csb), blk = t - m * (8 * csb);
+          const uint8_t *ap = XQ + m * xrb + (int64_t)(8 * c0 + blk) * kQ8_1Bytes;
+          const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
+          const uint32_t v2 = ld4(ap + 32);
+          act[blk * S + 2 * m] = u32x4n{v0.y, v0.z, v0.w, v1.x};
+          act[blk * S + 2 * m + 1] = u32x4n{v1.y, v1.z, v1.w, v2};
+          da[blk * 8 + pos(m)] = h2f(v0.x);
+        }
+        __syncthreads();
+      }
+      // superblocks wv, wv + 8, ... of the chunk, the next one loaded ahead
+      for (int s = wv; s < csb; s += 2 * kWaves) {
+        if (s + kWaves < csb) load_sb(wr + (int64_t)(c0 + s + kWaves) * kQ6KBytes, lh, nxt);
+        step(cur, s, acc);
+        if (s + kWaves >= csb) break;
+        if (s + 2 * kWaves < csb) load_sb(wr + (int64_t)(c0 + s + 2 * kWaves) * kQ6KBytes, lh, cur);
+        step(nxt, s + kWaves, acc);
+      }
+    }
+    const int next = tile + (int)gridDim.x;
+    if (next < ntiles && wv < min(kChunkSb, nsb)) load_sb(wrow(next) + (int64_t)wv * kQ6KBytes, lh, cur);
+    // sum the waves' partial tiles: thread t < 32 * nb owns activation row
+    // m = t / 32, weight row nn = t % 32, held by lane nn + 32 * ((m / 2) % 2),
+    // element (m % 2) + 2 * (m / 4) of every wave
+    part[wv * 64 + lane] = acc;
+    __syncthreads();
+    if (tid < 32 * nb) {
+      const int m = tid >> 5, nn = tid & 31;
+      const int src = nn + 32 * ((m >> 1) & 1), q = (m & 1) + 2 * (m >> 2);
+      const int64_t r = (int64_t)tile * 32 + nn;
+      if (r < n) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += part[w * 64 + src][q];
+        Y[(int64_t)m * n + r] = sum;
+      }
+    }
+    __syncthreads();  // part is rewritten next round
+  }
+}
+
+template <int BP>
+hipError_t launch_bp(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k, hipStream_t stream) {
+  const size_t lds = lds_bytes(BP);
+  const int64_t groups = (n + 31) / 32;
+  const int64_t g = std::min(groups, resident_blocks<gemv_batch_mfma_q6k<BP>>(kThreads, lds));
+  hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP>), dim3((unsigned)g), dim3(kThreads), lds, stream,
+                     static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y, (int)nb, (int)n,
+                     (int)(k / 256));
+  return hipGetLastError();
+}
+
+}  // namespace q6
+
 }  // namespace
 
 hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
@@ -158,6 +343,12 @@ hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, 
                      static_cast<const uint8_t *>(w),
                      static_cast<const uint8_t *>(xq), y, (int)nb, (int)n, (int)(k / 256));
   return hipGetLastError();
+}
+
+hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
+                                       hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  return nb <= 4 ? q6::launch_bp<4>(w, xq, y, nb, n, k, stream) : q6::launch_bp<8>(w, xq, y, nb, n, k, stream);
 }
 
 }  // namespace qg

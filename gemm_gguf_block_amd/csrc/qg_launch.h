@@ -3,7 +3,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qg {
+
+// Workgroups of `Kernel` (`threads` per workgroup, `lds` bytes of dynamic LDS)
+// resident on the current device at once, for sizing persistent grids.  The
+// kernel is a template argument so that every kernel has a cache of its own
+// (kernels of one signature would otherwise share it); per device it holds the
+// last LDS size asked, as (lds << 32 | count) in one word so that readers never
+// see a torn pair.
+template <auto Kernel>
+int64_t resident_blocks(int threads, size_t lds) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<uint64_t> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+  const uint64_t c = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (c != 0 && (c >> 32) == (uint64_t)lds) return (int64_t)(c & 0xffffffffu);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
+    cus = 1;
+  const int64_t v = (int64_t)per_cu * cus;
+  if (dev >= 0) cached[dev].store(((uint64_t)lds << 32) | (uint64_t)v, std::memory_order_relaxed);
+  return v;
+}
 
 hipError_t launch_quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t k, hipStream_t stream);
 
@@ -16,8 +42,10 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
 hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
                               hipStream_t stream);
 
-// Small-batch Q4_K GEMV on the int8 matrix cores (nb <= 8).
+// Small-batch Q4_K / Q6_K GEMV on the int8 matrix cores (nb <= 8).
 hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
+                                       hipStream_t stream);
+hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
                                        hipStream_t stream);
 
 hipError_t launch_qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,

@@ -233,7 +233,7 @@ def test_gemv_batch_values_random_bytes(env, fmt):
         assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
 
 
-@pytest.mark.parametrize("b", [3, 5])  # Q4_K: the v_dot4 kernel up to 4 rows, the matrix-core one above
+@pytest.mark.parametrize("b", [3, 5])  # K-quants: the v_dot4 kernels up to 4 rows, the matrix-core ones above
 def test_gemv_batch_hand_superblock_exact(env, b):
     """Rows with different power-of-two d_a and shifted codes: every
     intermediate is exact in fp32, so each y[i] equals its hand-computed dot."""
@@ -288,7 +288,8 @@ def test_gemv_batch_empty_and_zero_k(env):
 
 
 @pytest.mark.big
-@pytest.mark.parametrize("name,b", [("q8_0_gemv", 8), ("q4_k_gemv", 8), ("q4_k_gemv", 3), ("q6_k_gemv", 4)])
+@pytest.mark.parametrize("name,b", [("q8_0_gemv", 8), ("q4_k_gemv", 8), ("q4_k_gemv", 3), ("q6_k_gemv", 4),
+                                    ("q6_k_gemv", 8)])
 def test_gemv_batch_full_size(env, name, b):
     """The workload shapes with b activation rows, on sampled output rows."""
     qg, orc, torch, dev = env
