@@ -4,7 +4,9 @@ A step is one pass of the hot path over one batch of synthetic input:
 quantize the activations to Q8_1 on the GPU, then run the product on the
 quantized weights.  Default workload: the Q4_K decode GEMV at a Llama-3-8B FFN
 shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
-q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each).
+q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); small-batch GEMVs
+<fmt>_gemv_b<B> (the GEMV workload's weights against B <= 8 activation rows),
+or batch for the standard set of them.
 
 Inputs are resident in HBM before timing starts.  The weights are replicated
 into enough copies (>= 512 MB in total) that consecutive steps read different
@@ -174,7 +176,9 @@ class GemvBatch(Gemv):
         self.xq = torch.empty((self.b, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
         self.y = torch.empty((self.b, self.n), dtype=torch.float32, device=dev)
         self.fn = getattr(qg, "qgemv_" + self.fmt + "_batch")
-        self.dominant = f"gemv_{self.fmt.replace('_', '')}_b{self.b}"
+        # the kernel the library dispatches to (matrix cores for K-quants above 4 rows)
+        self.dominant = (f"gemv_batch_mfma_{self.fmt.replace('_', '')}" if self.b > 4 and self.fmt != "q8_0"
+                         else "gemv_batch_kernel")
         wbytes = self.w_host.nbytes
         self.kernel_bytes = wbytes + self.b * (q81_bytes(self.k) + 4 * self.n)
         self.step_bytes = self.kernel_bytes + self.b * (4 * self.k + q81_bytes(self.k))
