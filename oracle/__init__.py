@@ -73,7 +73,11 @@ def _declare(L):
         "orc_blockdots_q6_k": [_P, _P, _P, _I, _I],
         "orc_qgemv_factored": [ctypes.c_int, _P, _P, _P, _I, _I],
         "orc_qgemm_q4_k": [_P, _P, _P, _I, _I, _I, _P, _I],
+        "orc_qgemm_q6_k": [_P, _P, _P, _I, _I, _I, _P, _I],
+        "orc_qgemm_q8_0": [_P, _P, _P, _I, _I, _I, _P, _I],
         "orc_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I],
+        "orc_blockdots_q6_k_mmq": [_P, _P, _P, _I, _I, _I],
+        "orc_blockdots_q8_0_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_moe_q4_k": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P],
     }.items():
         fn = getattr(L, name)
@@ -188,27 +192,38 @@ def qgemv_factored(fmt, w, xq, n, k):
 
 
 # ----------------------------------------------------------------------- mmq
-def qgemm_q4_k(w, aq, m, n, k, pairs=None):
-    """C[m][n] = sum_k a^[m,k] w^[n,k] in double.  `pairs` (array [P][2] of
-    (m, n)) selects entries; then a 1-D array of P values is returned."""
+def qgemm(fmt, w, aq, m, n, k, pairs=None):
+    """C[m][n] = sum_k a^[m,k] w^[n,k] in double, for fmt 'q4_k', 'q6_k' or
+    'q8_0' weights.  `pairs` (array [P][2] of (m, n)) selects entries; then a
+    1-D array of P values is returned."""
+    fn = getattr(lib(), "orc_qgemm_" + fmt)
     w = _c(w, np.uint8)
     aq = _c(aq, np.uint8)
     if pairs is None:
         c = np.empty((m, n), np.float64)
-        lib().orc_qgemm_q4_k(_ptr(w), _ptr(aq), _ptr(c), m, n, k, None, 0)
+        fn(_ptr(w), _ptr(aq), _ptr(c), m, n, k, None, 0)
         return c
     sel = _c(pairs, np.int64).reshape(-1, 2)
     c = np.empty(sel.shape[0], np.float64)
-    lib().orc_qgemm_q4_k(_ptr(w), _ptr(aq), _ptr(c), m, n, k, _ptr(sel), sel.shape[0])
+    fn(_ptr(w), _ptr(aq), _ptr(c), m, n, k, _ptr(sel), sel.shape[0])
     return c
 
 
-def blockdots_q4_k_mmq(w, aq, m, n, k):
+def qgemm_q4_k(w, aq, m, n, k, pairs=None):
+    return qgemm("q4_k", w, aq, m, n, k, pairs)
+
+
+def blockdots_mmq(fmt, w, aq, m, n, k):
+    """[m][n][k/32] block dots (Q6_K: [m][n][k/16] sub-block dots)."""
     w = _c(w, np.uint8)
     aq = _c(aq, np.uint8)
-    D = np.empty((m, n, k // 32), np.int32)
-    lib().orc_blockdots_q4_k_mmq(_ptr(w), _ptr(aq), _ptr(D), m, n, k)
+    D = np.empty((m, n, k // (16 if fmt == "q6_k" else 32)), np.int32)
+    getattr(lib(), f"orc_blockdots_{fmt}_mmq")(_ptr(w), _ptr(aq), _ptr(D), m, n, k)
     return D
+
+
+def blockdots_q4_k_mmq(w, aq, m, n, k):
+    return blockdots_mmq("q4_k", w, aq, m, n, k)
 
 
 # ----------------------------------------------------------------------- MoE

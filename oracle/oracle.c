@@ -427,22 +427,26 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
 /* ------------------------------------------------------------------------ */
 /* Prefill product (mmq), plain definition:                                   */
 /*   C[m][n] = sum_k a^[m,k] * w^[n,k]                                        */
-/* A is Q8_1 [M][K/32], B is Q4_K [N][K/256], C row-major [M][N].             */
+/* A is Q8_1 [M][K/32]; B is Q4_K or Q6_K [N][K/256] or Q8_0 [N][K/32];       */
+/* C row-major [M][N].  Both operands are dequantized exactly to double and   */
+/* dotted in k order.                                                         */
 /* `sel` picks (m, n) pairs: sel[2i], sel[2i+1]; NULL means every entry.      */
 /* ------------------------------------------------------------------------ */
-void orc_qgemm_q4_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
-                    const int64_t *sel, int64_t nsel)
+typedef void (*dequant_fn)(const uint8_t *, double *, int64_t, int64_t);
+
+static void qgemm_plain(dequant_fn deq, int64_t wrow, const uint8_t *w, const uint8_t *aq, double *c, int64_t m,
+                        int64_t n, int64_t k, const int64_t *sel, int64_t nsel)
 {
-    int64_t wrow = (k / QKK) * B_Q4_K, arow = (k / QK) * B_Q8_1;
+    int64_t arow = (k / QK) * B_Q8_1;
     if (sel) {
 #pragma omp parallel
         {
-            double *wd = (double *)malloc(sizeof(double) * (size_t)k);
-            double *ad = (double *)malloc(sizeof(double) * (size_t)k);
+            double *wd = (double *)malloc(sizeof(double) * (size_t)(k + 1));
+            double *ad = (double *)malloc(sizeof(double) * (size_t)(k + 1));
 #pragma omp for schedule(static)
             for (int64_t i = 0; i < nsel; ++i) {
                 int64_t mi = sel[2 * i], ni = sel[2 * i + 1];
-                orc_dequant_q4_k(w + ni * wrow, wd, 1, k);
+                deq(w + ni * wrow, wd, 1, k);
                 orc_dequant_q8_1(aq + mi * arow, ad, 1, k);
                 double acc = 0.0;
                 for (int64_t t = 0; t < k; ++t)
@@ -454,9 +458,9 @@ void orc_qgemm_q4_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, i
         }
         return;
     }
-    double *W = (double *)malloc(sizeof(double) * (size_t)(n * k));
-    double *A = (double *)malloc(sizeof(double) * (size_t)(m * k));
-    orc_dequant_q4_k(w, W, n, k);
+    double *W = (double *)malloc(sizeof(double) * (size_t)(n * k + 1));
+    double *A = (double *)malloc(sizeof(double) * (size_t)(m * k + 1));
+    deq(w, W, n, k);
     orc_dequant_q8_1(aq, A, m, k);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i)
@@ -470,7 +474,27 @@ void orc_qgemm_q4_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, i
     free(A);
 }
 
-/* mmq per-block dots: D[m][n][b] = sum_{i<32} q4[n, 32b+i] * qa[m, 32b+i]. */
+void orc_qgemm_q4_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    qgemm_plain(orc_dequant_q4_k, (k / QKK) * B_Q4_K, w, aq, c, m, n, k, sel, nsel);
+}
+
+void orc_qgemm_q6_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    qgemm_plain(orc_dequant_q6_k, (k / QKK) * B_Q6_K, w, aq, c, m, n, k, sel, nsel);
+}
+
+void orc_qgemm_q8_0(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    qgemm_plain(orc_dequant_q8_0, (k / QK) * B_Q8_0, w, aq, c, m, n, k, sel, nsel);
+}
+
+/* mmq per-block dots: for every activation row, the GEMV block dots of that  */
+/* row against all weight rows.  Q4_K and Q8_0: D[m][n][k/32]; Q6_K: the     */
+/* 16-value sub-block dots, D[m][n][k/16].                                    */
 void orc_blockdots_q4_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
 {
     int64_t nb = k / QK;
@@ -482,6 +506,20 @@ void orc_blockdots_q4_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int
     }
     free(S);
     free(row);
+}
+
+void orc_blockdots_q6_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
+{
+    int64_t nb = k / QK, per = k / 16;
+    for (int64_t i = 0; i < m; ++i)
+        orc_blockdots_q6_k(w, aq + i * nb * B_Q8_1, D + i * n * per, n, k);
+}
+
+void orc_blockdots_q8_0_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
+{
+    int64_t nb = k / QK;
+    for (int64_t i = 0; i < m; ++i)
+        orc_blockdots_q8_0(w, aq + i * nb * B_Q8_1, D + i * n * nb, n, k);
 }
 
 /* ------------------------------------------------------------------------ */

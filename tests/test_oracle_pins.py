@@ -315,30 +315,33 @@ def test_weight_quantizer_roundtrip_bound(orc, fmt):
 
 
 # ------------------------------------------------------------------ mmq oracle
-def test_mmq_rows_equal_gemv(orc):
-    m, n, k = 5, 33, 512
-    w = synth.weights("q4_k", n, k, seed=31)
+@pytest.mark.parametrize("fmt,k", [("q4_k", 512), ("q6_k", 512), ("q8_0", 512), ("q8_0", 96)])
+def test_mmq_rows_equal_gemv(orc, fmt, k):
+    m, n = 5, 33
+    w = synth.weights(fmt, n, k, seed=31)
     a = synth.normal(31, 1, (m, k))
     aq = orc.quantize_q8_1(a)
-    C = orc.qgemm_q4_k(w, aq, m, n, k)
+    C = orc.qgemm(fmt, w, aq, m, n, k)
     for i in range(m):
-        y = orc.qgemv("q4_k", w, aq[i], n, k)
+        y = orc.qgemv(fmt, w, aq[i], n, k)
         assert np.max(np.abs(C[i] - y)) <= 1e-12 * np.max(np.abs(y))
     pairs = np.array([[0, 0], [4, 32], [2, 17], [3, 5]])
-    sel = orc.qgemm_q4_k(w, aq, m, n, k, pairs=pairs)
+    sel = orc.qgemm(fmt, w, aq, m, n, k, pairs=pairs)
     assert np.array_equal(sel, C[pairs[:, 0], pairs[:, 1]])
     # mmq block dots are the GEMV block dots of each activation row
-    D = orc.blockdots_q4_k_mmq(w, aq, m, n, k)
+    D = orc.blockdots_mmq(fmt, w, aq, m, n, k)
     for i in range(m):
-        assert np.array_equal(D[i], orc.blockdots("q4_k", w, aq[i], n, k)[0])
+        Dg = orc.blockdots(fmt, w, aq[i], n, k)
+        assert np.array_equal(D[i], Dg[0] if fmt == "q4_k" else Dg)
 
 
-def test_mmq_against_numpy_matmul_of_dequantized(orc):
-    m, n, k = 7, 19, 256
-    w = synth.random_blocks("q4_k", n, k, seed=41, lo_exp=-10, hi_exp=0)
+@pytest.mark.parametrize("fmt,k", [("q4_k", 256), ("q6_k", 256), ("q8_0", 256), ("q8_0", 160)])
+def test_mmq_against_numpy_matmul_of_dequantized(orc, fmt, k):
+    m, n = 7, 19
+    w = synth.random_blocks(fmt, n, k, seed=41, lo_exp=-10, hi_exp=0)
     aq = synth.random_blocks("q8_1", m, k, seed=42, lo_exp=-10, hi_exp=0)
-    C = orc.qgemm_q4_k(w, aq, m, n, k)
-    ref = orc.dequant("q8_1", aq, m, k) @ orc.dequant("q4_k", w, n, k).T
+    C = orc.qgemm(fmt, w, aq, m, n, k)
+    ref = orc.dequant("q8_1", aq, m, k) @ orc.dequant(fmt, w, n, k).T
     assert np.max(np.abs(C - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
