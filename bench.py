@@ -4,7 +4,8 @@ A step is one pass of the hot path over one batch of synthetic input:
 quantize the activations to Q8_1 on the GPU, then run the product on the
 quantized weights.  Default workload: the Q4_K decode GEMV at a Llama-3-8B FFN
 shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
-q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); small-batch GEMVs
+q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); prefill products
+with the other weight types q6_k_mmq, q8_0_mmq; small-batch GEMVs
 <fmt>_gemv_b<B> (the GEMV workload's weights against B <= 8 activation rows),
 or batch for the standard set of them.
 
@@ -47,7 +48,8 @@ def _cpu_threads():
 
 KERNEL_SOURCES = {
     "q4_k_gemv": ["qg_gemv.hip"], "q8_0_gemv": ["qg_gemv.hip"], "q6_k_gemv": ["qg_gemv.hip"],
-    "q4_k_mmq": ["qg_mmq.hip"], "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
+    "q4_k_mmq": ["qg_mmq.hip"], "q6_k_mmq": ["qg_mmq.hip"], "q8_0_mmq": ["qg_mmq.hip"],
+    "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
 }
 BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8", "q6_k_gemv_b4", "q6_k_gemv_b8"]
 
@@ -209,13 +211,14 @@ class GemvBatch(Gemv):
 
 
 class Mmq(Workload):
-    def __init__(self, qg, torch, warm):
+    def __init__(self, qg, torch, name, warm):
         from gemm_gguf_block_amd import synth
-        p = synth.WORKLOADS["q4_k_mmq"]
-        self.name, self.m, self.n, self.k = "q4_k_mmq", p["m"], p["n"], p["k"]
+        p = synth.WORKLOADS[name]
+        self.name, self.fmt, self.m, self.n, self.k = name, p["fmt"], p["m"], p["n"], p["k"]
         self.qg, self.torch = qg, torch
+        self.fn = getattr(qg, f"qgemm_{self.fmt}_mmq")
         dev = torch.device("cuda:0")
-        w = synth.weights("q4_k", self.n, self.k, p["seed"])
+        w = synth.weights(self.fmt, self.n, self.k, p["seed"])
         self.w_host = w
         self.a_host = synth.normal(p["seed"], synth.T_X, (self.m, self.k))
         self.copies = 1 if warm else max(1, math.ceil(COLD_BYTES / w.nbytes))
@@ -224,7 +227,7 @@ class Mmq(Workload):
         self.a = torch.from_numpy(self.a_host).to(dev)
         self.aq = torch.empty((self.m, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
         self.c = torch.empty((self.m, self.n), dtype=torch.float32, device=dev)
-        self.dominant = "mmq_q4k"
+        self.dominant = f"mmq_kernel<{self.fmt}>"
         self.ops = 2.0 * self.m * self.n * self.k
         self.kernel_bytes = w.nbytes + self.m * q81_bytes(self.k) + 4 * self.m * self.n
         self.tokens_per_step = self.m
@@ -232,10 +235,10 @@ class Mmq(Workload):
 
     def step(self, i):
         self.qg.quantize_q8_1(self.a, self.aq)
-        self.qg.qgemm_q4_k_mmq(self.W[i % self.copies], self.aq, self.m, self.n, self.k, c=self.c)
+        self.fn(self.W[i % self.copies], self.aq, self.m, self.n, self.k, c=self.c)
 
     def dominant_call(self, i):
-        self.qg.qgemm_q4_k_mmq(self.W[i % self.copies], self.aq, self.m, self.n, self.k, c=self.c)
+        self.fn(self.W[i % self.copies], self.aq, self.m, self.n, self.k, c=self.c)
 
     def value(self, sec_per_step):
         return self.ops / sec_per_step / 1e12
@@ -251,7 +254,8 @@ class Mmq(Workload):
         g = np.random.default_rng(0)
         cnt = 1 << 18
         pairs = np.stack([g.integers(0, self.m, cnt), g.integers(0, self.n, cnt)], 1)
-        reps, t = _repeat(lambda: oracle.qgemm_q4_k(self.w_host, aq, self.m, self.n, self.k, pairs=pairs), budget_s)
+        reps, t = _repeat(lambda: oracle.qgemm(self.fmt, self.w_host, aq, self.m, self.n, self.k, pairs=pairs),
+                          budget_s)
         return dict(value=2.0 * reps * cnt * self.k / t / 1e12, unit="TOPS", cores=_cpu_threads(), kind="oracle",
                     sample=f"{cnt} random entries of C[{self.m}][{self.n}] (plain double dequant-and-dot) x {reps}, "
                            f"{t:.1f} s")
@@ -324,8 +328,8 @@ def make(name, qg, torch, warm):
         return GemvBatch(qg, torch, name, warm)
     if name.endswith("_gemv"):
         return Gemv(qg, torch, name, warm)
-    if name == "q4_k_mmq":
-        return Mmq(qg, torch, warm)
+    if name.endswith("_mmq"):
+        return Mmq(qg, torch, name, warm)
     if name == "moe_q4_k":
         return Moe(qg, torch, warm)
     raise SystemExit(f"unknown workload {name}")
@@ -450,6 +454,7 @@ def main():
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
+                         "q6_k_mmq, q8_0_mmq, "
                          "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")

@@ -33,14 +33,18 @@ SIGNATURES = {
     "qgemv_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_q6_k_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemm_q8_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemm_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "moe_qgemv_q4_k_workspace_size": [_I, _I, _I, _I, _I],
     "moe_qgemv_q4_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "qg_status_str": [ctypes.c_int],
     "qg_blockdots_q8_0": [_P, _P, _P, _I, _I, _P],
     "qg_blockdots_q4_k": [_P, _P, _P, _P, _I, _I, _P],
     "qg_blockdots_q6_k": [_P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q8_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
 }
 
 
@@ -170,15 +174,28 @@ def qgemv_q6_k_batch(w, xq, b, n, k, y=None, stream=None):
     return _gemv_batch("q6_k", w, xq, b, n, k, y, stream)
 
 
-def qgemm_q4_k_mmq(w, aq, m, n, k, c=None, stream=None):
+def _mmq(fmt, w, aq, m, n, k, c, stream):
     import torch
     if c is None:
         c = _empty((m, n), torch.float32, w)
-    pw = _need(w, torch.uint8, n * row_bytes("q4_k", k), "w")
+    pw = _need(w, torch.uint8, n * row_bytes(fmt, k), "w")
     pa = _need(aq, torch.uint8, m * row_bytes("q8_1", k), "aq")
     pc = _need(c, torch.float32, m * n * 4, "c")
-    _check("qgemm_q4_k_mmq", lib().qgemm_q4_k_mmq(pw, pa, pc, m, n, k, _stream(stream)))
+    name = f"qgemm_{fmt}_mmq"
+    _check(name, getattr(lib(), name)(pw, pa, pc, m, n, k, _stream(stream)))
     return c
+
+
+def qgemm_q4_k_mmq(w, aq, m, n, k, c=None, stream=None):
+    return _mmq("q4_k", w, aq, m, n, k, c, stream)
+
+
+def qgemm_q6_k_mmq(w, aq, m, n, k, c=None, stream=None):
+    return _mmq("q6_k", w, aq, m, n, k, c, stream)
+
+
+def qgemm_q8_0_mmq(w, aq, m, n, k, c=None, stream=None):
+    return _mmq("q8_0", w, aq, m, n, k, c, stream)
 
 
 def moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd) -> int:
@@ -253,10 +270,24 @@ def blockdots_q6_k(w, xq, n, k, stream=None):
     return D
 
 
-def blockdots_q4_k_mmq(w, aq, m, n, k, stream=None):
+def _blockdots_mmq(fmt, w, aq, m, n, k, stream):
     import torch
-    D = _empty((m, n, k // 32), torch.int32, w)
-    _check("qg_blockdots_q4_k_mmq", lib().qg_blockdots_q4_k_mmq(
-        _need(w, torch.uint8, n * row_bytes("q4_k", k), "w"), _need(aq, torch.uint8, m * row_bytes("q8_1", k), "aq"),
+    D = _empty((m, n, k // (16 if fmt == "q6_k" else 32)), torch.int32, w)
+    name = f"qg_blockdots_{fmt}_mmq"
+    _check(name, getattr(lib(), name)(
+        _need(w, torch.uint8, n * row_bytes(fmt, k), "w"), _need(aq, torch.uint8, m * row_bytes("q8_1", k), "aq"),
         _need(D, torch.int32, D.numel() * 4, "D"), m, n, k, _stream(stream)))
     return D
+
+
+def blockdots_q4_k_mmq(w, aq, m, n, k, stream=None):
+    return _blockdots_mmq("q4_k", w, aq, m, n, k, stream)
+
+
+def blockdots_q6_k_mmq(w, aq, m, n, k, stream=None):
+    """[m][n][k/16]: the exact dot of every 16-value sub-block."""
+    return _blockdots_mmq("q6_k", w, aq, m, n, k, stream)
+
+
+def blockdots_q8_0_mmq(w, aq, m, n, k, stream=None):
+    return _blockdots_mmq("q8_0", w, aq, m, n, k, stream)

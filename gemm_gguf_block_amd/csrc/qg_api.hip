@@ -81,9 +81,10 @@ qg_status run_gemv_batch(int fmt, const void *w, const void *xq, float *y, int64
   return launched(qg::launch_qgemv_batch(fmt, w, xq, y, nb, n, k, stream));
 }
 
-qg_status check_mmq(const void *w, const void *aq, const void *out, int64_t m, int64_t n, int64_t k) {
+qg_status check_mmq(int fmt, const void *w, const void *aq, const void *out, int64_t m, int64_t n, int64_t k) {
   if (!w || !aq || !out) return QG_ERR_NULL;
-  if (m < 0 || n < 0 || k < 0 || m > kMaxRows || n > kMaxRows || k > kMaxK || k % 256 != 0) return QG_ERR_SHAPE;
+  if (m < 0 || n < 0 || k < 0 || m > kMaxRows || n > kMaxRows || k > kMaxK) return QG_ERR_SHAPE;
+  if (k % (fmt == 0 ? 32 : 256) != 0) return QG_ERR_SHAPE;
   if (((m + 63) / 64) * ((n + 63) / 64) > kMaxRows) return QG_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(aq, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
   return QG_OK;
@@ -146,14 +147,31 @@ QG_EXPORT qg_status qgemv_q6_k_batch(const void *w, const void *xq, float *y, in
   return run_gemv_batch(2, w, xq, y, b, n, k, stream);
 }
 
-QG_EXPORT qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
-                                   hipStream_t stream) {
-  qg_status st = check_mmq(w, aq, c, m, n, k);
+static qg_status run_mmq(int fmt, const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n, int64_t k,
+                  hipStream_t stream) {
+  qg_status st = check_mmq(fmt, w, aq, c ? static_cast<const void *>(c) : D, m, n, k);
   if (st != QG_OK) return st;
+  // the dump holds m * n dots per block (Q6_K: per 16 values)
+  if (D && m > 0 && n > 0 && k > 0 && m * n > (int64_t(1) << 28) / (k / (fmt == 2 ? 16 : 32))) return QG_ERR_SHAPE;
   if (m == 0 || n == 0) return QG_OK;
   st = check_device();
   if (st != QG_OK) return st;
-  return launched(qg::launch_qgemm_q4_k_mmq(w, aq, c, nullptr, m, n, k, stream));
+  return launched(qg::launch_qgemm_mmq(fmt, w, aq, c, D, m, n, k, stream));
+}
+
+QG_EXPORT qg_status qgemm_q8_0_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return run_mmq(0, w, aq, c, nullptr, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return run_mmq(1, w, aq, c, nullptr, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemm_q6_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return run_mmq(2, w, aq, c, nullptr, m, n, k, stream);
 }
 
 QG_EXPORT size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
@@ -220,13 +238,17 @@ QG_EXPORT qg_status qg_blockdots_q6_k(const void *w, const void *xq, int32_t *D,
   return st != QG_OK ? st : run_gemv(2, w, xq, nullptr, D, nullptr, n, k, stream);
 }
 
+QG_EXPORT qg_status qg_blockdots_q8_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_mmq(0, w, aq, nullptr, D, m, n, k, stream);
+}
+
 QG_EXPORT qg_status qg_blockdots_q4_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                           hipStream_t stream) {
-  qg_status st = check_mmq(w, aq, D, m, n, k);
-  if (st != QG_OK) return st;
-  if (m > 0 && n > 0 && k > 0 && m * n > (int64_t(1) << 28) / (k / 32)) return QG_ERR_SHAPE;
-  if (m == 0 || n == 0) return QG_OK;
-  st = check_device();
-  if (st != QG_OK) return st;
-  return launched(qg::launch_qgemm_q4_k_mmq(w, aq, nullptr, D, m, n, k, stream));
+  return run_mmq(1, w, aq, nullptr, D, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q6_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_mmq(2, w, aq, nullptr, D, m, n, k, stream);
 }

@@ -34,6 +34,16 @@ __device__ __forceinline__ void q4k_scales(uint32_t hy, uint32_t hz, uint32_t hw
   m1 = (int)((mw >> (sh + 8)) & 0xFFu);
 }
 
+// Q6_K codes as int8 q - 32, four at a time: low nibbles of `lo` (ql) and the
+// low bit pairs of `hi` (qh).  The high nibble comes from a 4-entry byte table
+// indexed by the qh bits (v_perm_b32), since (q - 32) mod 256 = ql + 16 * ((qh -
+// 2) mod 16); the table is given as both sources so that the selector 0..3
+// names a table byte either way round.
+__device__ __forceinline__ int q6k_codes4(uint32_t lo, uint32_t hi) {
+  const uint32_t top = __builtin_amdgcn_perm(0x1000F0E0u, 0x1000F0E0u, hi & 0x03030303u);
+  return (int)((lo & 0x0F0F0F0Fu) | top);
+}
+
 // Lanes sharing one row: the largest power of two <= 64 dividing the row's
 // unit count, so every lane of a row does the same number of units.
 inline int lanes_per_row(int64_t units) {

@@ -164,9 +164,7 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q4k(const uint8_t *_
 // (The MFMA results are read by compiler-generated code only: an inline-asm
 // reader gets none of the wait states an MFMA result needs.)
 //
-// B takes the codes as q - 32 in int8: the low nibble comes from ql and the
-// high nibble from a 4-entry byte table indexed by the two qh bits
-// (v_perm_b32), since (q - 32) mod 256 = ql + 16 * ((qh - 2) mod 16).
+// B takes the codes as q - 32 in int8 (q6k_codes4).
 //
 // A persistent workgroup of 8 waves takes one 32-row tile at a time; wave w
 // runs superblocks w, w + 8, ... of it (all of a 4096-wide row's superblocks
@@ -208,15 +206,6 @@ __device__ __forceinline__ void load_sb(const uint8_t *p, int lh, Sb &s) {
   s.d = ld2(p + 208);
 }
 
-// q - 32 of 4 codes: low nibbles of `lo`, bit pairs of `hi`.
-__device__ __forceinline__ int codes4(uint32_t lo, uint32_t hi) {
-  const uint32_t hb = hi & 0x03030303u;
-  // table bytes 0..3 = 0xE0, 0xF0, 0x00, 0x10; given as both sources so the
-  // selector 0..3 names a table byte either way round
-  const uint32_t top = __builtin_amdgcn_perm(0x1000F0E0u, 0x1000F0E0u, hb);
-  return (int)((lo & 0x0F0F0F0Fu) | top);
-}
-
 template <int BP>
 __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *__restrict__ W,
                                                                 const uint8_t *__restrict__ XQ,
@@ -253,8 +242,8 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
       const int blk = 8 * sbl + j;
       const u32x4 lo = w.ql[2 * (j >> 2) + (j & 1)], hi = w.qh[j >> 2];
       const uint32_t ls = 4u * (uint32_t)((j >> 1) & 1), hs = 2u * (uint32_t)(j & 3);
-      const v4i b = {codes4(lo.x >> ls, hi.x >> hs), codes4(lo.y >> ls, hi.y >> hs), codes4(lo.z >> ls, hi.z >> hs),
-                     codes4(lo.w >> ls, hi.w >> hs)};
+      const v4i b = {q6k_codes4(lo.x >> ls, hi.x >> hs), q6k_codes4(lo.y >> ls, hi.y >> hs),
+                     q6k_codes4(lo.z >> ls, hi.z >> hs), q6k_codes4(lo.w >> ls, hi.w >> hs)};
       const v4i a = __builtin_bit_cast(v4i, act[blk * S + aunit]);
       const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
       const uint32_t scw = w.sc[j >> 1];

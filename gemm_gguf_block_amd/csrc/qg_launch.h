@@ -48,8 +48,10 @@ hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, 
 hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
                                        hipStream_t stream);
 
-hipError_t launch_qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,
-                                 int64_t k, hipStream_t stream);
+// Prefill product on the int8 matrix cores; fmt as for launch_qgemv.  D
+// non-null selects the per-block (Q6_K: per 16-value sub-block) dot dump.
+hipError_t launch_qgemm_mmq(int fmt, const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,
+                            int64_t k, hipStream_t stream);
 
 struct MoeArgs {
   const void *w_gu, *w_down, *xq;

@@ -1,25 +1,28 @@
-// qg_mmq.hip -- prefill product C[m][n] = sum_k a^[m,k] w^[n,k] with Q4_K
-// weights and Q8_1 activations on gfx950 int8 matrix cores.
+// qg_mmq.hip -- prefill product C[m][n] = sum_k a^[m,k] w^[n,k] with Q4_K,
+// Q6_K or Q8_0 weights and Q8_1 activations on gfx950 int8 matrix cores.
 //
 // The pages run this step as "in-shader dequant and dp4a mmq" (infr page,
 // "models") and as cooperative-matrix matmul (infr page, "Vulkan-first, Metal
-// too").  Here a workgroup of 8 waves owns a 64 (tokens) x 128 (weight rows)
-// output tile; each wave owns 32x32.  Per 256-wide superblock of k the
-// workgroup stages in LDS:
-//   A  Q8_1 qs as int8, plus per (row, block) d_a and d_a*sum(qa)
-//   B  Q4_K nibbles widened to int8, plus per (weight row, sub-block) d*sc_j
-//      and -dmin*m_j
-// double-buffered: the global loads of superblock s+1 are in flight while the
-// MFMAs of superblock s run.  Each 32-wide sub-block j is exactly one
-// v_mfma_i32_32x32x32_i8 -> the exact int32 dots D of that block for the wave's
-// 32x32 tile.  Its fp32 rescale is acc += F * D with F[m][n] = d_a[m] * (d*sc_j)[n],
-// a rank-1 outer product that the matrix core forms as well: d_a (fp16) is
-// exactly the sum of two bf16 parts and d*sc_j is two bf16 parts to 2^-17, so
-// one v_mfma_f32_32x32x8_bf16 over those parts gives F in the MFMA output
-// layout, leaving one convert and one fma per output on the VALU.  The min term
+// too"); the blazr README ("Model Formats > GGUF") names Q4_K, Q6_K and Q8_0 as
+// the integer-dot types.  Here a workgroup owns a 64 (tokens) x 128 (weight
+// rows) output tile; each 32x32 of it belongs to a pair of waves.  Per 256-wide
+// step of k (one K-quant superblock, eight Q8_0 blocks) the workgroup stages in
+// LDS:
+//   A  Q8_1 qs as int8, plus per (row, block) d_a (and d_a*sum(qa) for Q4_K)
+//   B  the weight codes as int8 (Q4_K nibbles, Q6_K q - 32, Q8_0 qs), plus per
+//      (weight row, scale group) the group's factor (d*sc_j, d*sc_j, d) and for
+//      Q4_K -dmin*m_j
+// double-buffered: the global loads of step s+2 are in flight while the MFMAs
+// of step s run.  Each 32-wide block of k is one v_mfma_i32_32x32x32_i8 -> the
+// exact int32 dots D of that block for the wave's 32x32 tile; Q6_K's 16-wide
+// sub-blocks are two v_mfma_i32_32x32x16_i8.  A dot's fp32 rescale is
+// acc += F * D with F[m][n] = d_a[m] * f[n], a rank-1 outer product that the
+// matrix core forms as well: d_a (fp16) is exactly the sum of two bf16 parts
+// and f is two bf16 parts to 2^-17 (exactly, for Q8_0's fp16 d), so one
+// v_mfma_f32_32x32x8_bf16 over those parts gives F in the MFMA output layout,
+// leaving one convert and one fma per output on the VALU.  Q4_K's min term
 // -sum_j (d_a*sum qa)_j (dmin*m_j) is a rank-8-per-superblock product of two
-// small fp32 matrices and runs on the matrix core too (v_mfma_f32_32x32x2_f32
-// over pairs of sub-blocks) into a second accumulator.
+// small matrices and runs on the matrix core too, into the same accumulator.
 #include "qg_blocks.h"
 #include "qg_launch.h"
 
@@ -30,20 +33,34 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));  // naturally aligned: one 16-byte LDS read
 
 constexpr int kBM = 64, kBN = 128;
 constexpr int kRow = 272;  // LDS bytes per staged row: 256 + 16 (spreads rows over banks)
 
-// Per-block factor arrays are [block][row] so that the MFMA operand reads of a
-// wave are contiguous; one spare entry per block row spreads the transposed
-// staging writes over the LDS banks.
+// Formats, numbered as the GEMV entry points number them.
+constexpr int kMQ8_0 = 0, kMQ4K = 1, kMQ6K = 2;
+
+template <int FMT>
+struct MmqFmt {
+  static constexpr int kGroups = FMT == kMQ6K ? 16 : 8;  // scale groups per 256-wide step
+  static constexpr bool kMin = FMT == kMQ4K;
+  static constexpr int kRegs = FMT == kMQ8_0 ? 5 : (FMT == kMQ6K ? 4 : 3);  // u32x4 staging registers
+};
+
+// Per-group factor arrays are [group][row] so that the MFMA operand reads of a
+// wave are contiguous; one spare entry per group row spreads the transposed
+// staging writes over the LDS banks.  For Q6_K each 32-byte block of A and B
+// is stored as bytes [0..7, 16..23, 8..15, 24..31]: lane half h then reads its
+// 8-byte slice of both 16-wide sub-blocks as one 16-byte group.
+template <int FMT>
 struct MmqStage {
   uint8_t a[kBM * kRow];
   uint8_t b[kBN * kRow];
-  uint32_t fa[8][kBM + 1][2];   // bf16 (ah, ah, al, al) of d_a = ah + al, per (block j, activation row)
-  uint32_t fb[8][kBN + 1][2];   // bf16 (dh, dl, dh, dl) of d*sc_j = dh + dl, per (sub-block j, weight row)
-  uint32_t fs[8][kBM + 1][2];   // bf16 (sh, sh, sl, sl) of d_a * sum(qa) = sh + sl
-  uint32_t fm[8][kBN + 1][2];   // bf16 (mh, ml, mh, ml) of -2 dmin m_j = mh + ml
+  uint32_t fa[8][kBM + 1][2];  // bf16 (ah, ah, al, al) of d_a = ah + al, per (block j, activation row)
+  uint32_t fb[MmqFmt<FMT>::kGroups][kBN + 1][2];  // bf16 (fh, fl, fh, fl) of the group factor f = fh + fl
+  uint32_t fs[MmqFmt<FMT>::kMin ? 8 : 1][kBM + 1][2];  // bf16 (sh, sh, sl, sl) of d_a * sum(qa)
+  uint32_t fm[MmqFmt<FMT>::kMin ? 8 : 1][kBN + 1][2];  // bf16 (mh, ml, mh, ml) of -2 dmin m_j
 };
 
 __device__ __forceinline__ uint32_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -55,102 +72,184 @@ __device__ __forceinline__ void bf16_split(float x, uint32_t &hi, uint32_t &lo) 
   lo = bf16_bits(x - (float)h);
 }
 
-// Global -> registers for one superblock.  Activation staging thread t
-// (0..511) holds block t%8 of tile row t/8: x0 = bytes 0-15, x1 = 16-31,
-// x2.x = 32-35.  Weight staging thread t holds tile row t/4, qs byte group t%4:
-// x0 = header (d, dmin, scales), x1, x2 = its 32 qs bytes.  Rows past the end
-// of A or B load the last row instead; they only feed outputs that are never
-// stored.
-struct MmqRegs {
-  u32x4 x0, x1, x2;
-};
-
-__device__ __forceinline__ void load_act(MmqRegs &g, const uint8_t *__restrict__ AQ, int M, int nsb, int m0, int sb,
-                                         int t) {
-  const int gm = min(m0 + (t >> 3), M - 1);
-  const uint8_t *ap = AQ + ((int64_t)gm * nsb * 8 + sb * 8 + (t & 7)) * kQ8_1Bytes;
-  g.x0 = ld16(ap);
-  g.x1 = ld16(ap + 16);
-  g.x2.x = ld4(ap + 32);
+__device__ __forceinline__ void put_factor(uint32_t (&f)[2], float x) {
+  uint32_t hi, lo;
+  bf16_split(x, hi, lo);
+  f[0] = f[1] = hi | (lo << 16);
 }
 
-__device__ __forceinline__ void load_wgt(MmqRegs &g, const uint8_t *__restrict__ W, int N, int nsb, int n0, int sb,
-                                         int t) {
+// Global -> registers for one 256-wide step.  A staging thread and a weight
+// staging thread use the same registers (a wave stages one or the other).
+// Activation thread t (0..511) holds block t%8 of tile row t/8: x[0] = bytes
+// 0-15, x[1] = 16-31, x[2].x = 32-35.  Rows past the end of A or B load the last
+// row instead; they only feed outputs that are never stored.  Blocks past k
+// (Q8_0 only) load as zeros.
+template <int FMT>
+struct MmqRegs {
+  u32x4 x[MmqFmt<FMT>::kRegs];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_act(MmqRegs<FMT> &g, const uint8_t *__restrict__ AQ, int M, int nblk, int m0,
+                                         int s, int t) {
+  const int gm = min(m0 + (t >> 3), M - 1);
+  const int blk = 8 * s + (t & 7);
+  if (FMT == kMQ8_0 && blk >= nblk) {
+    g.x[0] = g.x[1] = u32x4{0u, 0u, 0u, 0u};
+    g.x[2].x = 0u;
+    return;
+  }
+  const uint8_t *ap = AQ + ((int64_t)gm * nblk + blk) * kQ8_1Bytes;
+  g.x[0] = ld16(ap);
+  g.x[1] = ld16(ap + 16);
+  g.x[2].x = ld4(ap + 32);
+}
+
+// Weight thread t: tile row t/4 and part c = t%4 of its 256-wide step.
+//   Q4_K: x[0] = header (d, dmin, scales), x[1], x[2] = qs bytes 32c..32c+31
+//   Q8_0: blocks 2c, 2c+1: x[0..1] and x[2..3] their qs, x[4].x/.y their d
+//   Q6_K: 128-half h = c/2, positions l = 16(c%2)..+15 of all four 32-groups:
+//         x[0] = ql[64h + l] (groups 0, 2), x[1] = ql[64h + 32 + l] (groups
+//         1, 3), x[2] = qh[32h + l], x[3].x/.y = scales[8h..8h+7], x[3].z = d
+template <int FMT>
+__device__ __forceinline__ void load_wgt(MmqRegs<FMT> &g, const uint8_t *__restrict__ W, int N, int nblk, int n0,
+                                         int s, int t) {
   const int gn = min(n0 + (t >> 2), N - 1);
-  const uint8_t *bp = W + ((int64_t)gn * nsb + sb) * kQ4KBytes;
-  g.x0 = ld16(bp);
-  g.x1 = ld16(bp + 16 + 32 * (t & 3));
-  g.x2 = ld16(bp + 32 + 32 * (t & 3));
+  const int c = t & 3;
+  if constexpr (FMT == kMQ4K) {
+    const uint8_t *bp = W + ((int64_t)gn * (nblk / 8) + s) * kQ4KBytes;
+    g.x[0] = ld16(bp);
+    g.x[1] = ld16(bp + 16 + 32 * c);
+    g.x[2] = ld16(bp + 32 + 32 * c);
+  } else if constexpr (FMT == kMQ6K) {
+    const uint8_t *bp = W + ((int64_t)gn * (nblk / 8) + s) * kQ6KBytes;
+    const int h = c >> 1, l = 16 * (c & 1);
+    g.x[0] = ld16_a2(bp + 64 * h + l);
+    g.x[1] = ld16_a2(bp + 64 * h + 32 + l);
+    g.x[2] = ld16_a2(bp + 128 + 32 * h + l);
+    const u32x2 sc = ld8_a2(bp + 192 + 8 * h);
+    g.x[3].x = sc.x;
+    g.x[3].y = sc.y;
+    g.x[3].z = ld2(bp + 208);
+  } else {
+    const int b0 = 8 * s + 2 * c;
+    const uint8_t *bp = W + ((int64_t)gn * nblk + b0) * kQ8_0Bytes;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    g.x[0] = g.x[1] = g.x[2] = g.x[3] = z;
+    g.x[4].x = g.x[4].y = 0u;
+    if (b0 < nblk) {
+      g.x[4].x = ld2(bp);
+      g.x[0] = ld16_a2(bp + 2);
+      g.x[1] = ld16_a2(bp + 18);
+    }
+    if (b0 + 1 < nblk) {
+      g.x[4].y = ld2(bp + kQ8_0Bytes);
+      g.x[2] = ld16_a2(bp + kQ8_0Bytes + 2);
+      g.x[3] = ld16_a2(bp + kQ8_0Bytes + 18);
+    }
+  }
 }
 
 // activation block: qs -> int8 row, factors
-__device__ __forceinline__ void store_act(const MmqRegs &g, MmqStage &s, int t) {
+template <int FMT>
+__device__ __forceinline__ void store_act(const MmqRegs<FMT> &g, MmqStage<FMT> &s, int t) {
   const int ar = t >> 3, ab = t & 7;
-  const uint32_t q[8] = {g.x0.y, g.x0.z, g.x0.w, g.x1.x, g.x1.y, g.x1.z, g.x1.w, g.x2.x};
-  int S = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) S = bsum4(q[i], S);
-  uint32_t *dst = reinterpret_cast<uint32_t *>(s.a + ar * kRow + 32 * ab);
-  *reinterpret_cast<u32x4 *>(dst) = u32x4{q[0], q[1], q[2], q[3]};
-  *reinterpret_cast<u32x4 *>(dst + 4) = u32x4{q[4], q[5], q[6], q[7]};
-  const float da = h2f(g.x0.x);
+  const uint32_t q[8] = {g.x[0].y, g.x[0].z, g.x[0].w, g.x[1].x, g.x[1].y, g.x[1].z, g.x[1].w, g.x[2].x};
+  u32x4 *dst = reinterpret_cast<u32x4 *>(s.a + ar * kRow + 32 * ab);
+  if constexpr (FMT == kMQ6K) {
+    dst[0] = u32x4{q[0], q[1], q[4], q[5]};
+    dst[1] = u32x4{q[2], q[3], q[6], q[7]};
+  } else {
+    dst[0] = u32x4{q[0], q[1], q[2], q[3]};
+    dst[1] = u32x4{q[4], q[5], q[6], q[7]};
+  }
+  const float da = h2f(g.x[0].x);
   uint32_t hi, lo;
   bf16_split(da, hi, lo);
   s.fa[ab][ar][0] = hi | (hi << 16);
   s.fa[ab][ar][1] = lo | (lo << 16);
-  bf16_split(da * (float)S, hi, lo);
-  s.fs[ab][ar][0] = hi | (hi << 16);
-  s.fs[ab][ar][1] = lo | (lo << 16);
+  if constexpr (MmqFmt<FMT>::kMin) {
+    int S = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S = bsum4(q[i], S);
+    bf16_split(da * (float)S, hi, lo);
+    s.fs[ab][ar][0] = hi | (hi << 16);
+    s.fs[ab][ar][1] = lo | (lo << 16);
+  }
 }
 
-// weight group: nibbles -> int8 (sub-block 2g low, 2g+1 high), factors
-__device__ __forceinline__ void store_wgt(const MmqRegs &g, MmqStage &s, int t) {
-  const int br = t >> 2, bg = t & 3;
-  const uint32_t Q[8] = {g.x1.x, g.x1.y, g.x1.z, g.x1.w, g.x2.x, g.x2.y, g.x2.z, g.x2.w};
-  uint32_t *dst = reinterpret_cast<uint32_t *>(s.b + br * kRow + 64 * bg);
-  *reinterpret_cast<u32x4 *>(dst) =
-      u32x4{Q[0] & 0x0F0F0F0Fu, Q[1] & 0x0F0F0F0Fu, Q[2] & 0x0F0F0F0Fu, Q[3] & 0x0F0F0F0Fu};
-  *reinterpret_cast<u32x4 *>(dst + 4) =
-      u32x4{Q[4] & 0x0F0F0F0Fu, Q[5] & 0x0F0F0F0Fu, Q[6] & 0x0F0F0F0Fu, Q[7] & 0x0F0F0F0Fu};
-  *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{(Q[0] >> 4) & 0x0F0F0F0Fu, (Q[1] >> 4) & 0x0F0F0F0Fu,
-                                              (Q[2] >> 4) & 0x0F0F0F0Fu, (Q[3] >> 4) & 0x0F0F0F0Fu};
-  *reinterpret_cast<u32x4 *>(dst + 12) = u32x4{(Q[4] >> 4) & 0x0F0F0F0Fu, (Q[5] >> 4) & 0x0F0F0F0Fu,
-                                               (Q[6] >> 4) & 0x0F0F0F0Fu, (Q[7] >> 4) & 0x0F0F0F0Fu};
-  int sc0, sc1, mn0, mn1;
-  q4k_scales(g.x0.y, g.x0.z, g.x0.w, bg, sc0, sc1, mn0, mn1);
-  const float d = h2f(g.x0.x), dmin = h2f(g.x0.x >> 16);
-  uint32_t hi, lo;
-  bf16_split(d * (float)sc0, hi, lo);
-  s.fb[2 * bg][br][0] = s.fb[2 * bg][br][1] = hi | (lo << 16);
-  bf16_split(d * (float)sc1, hi, lo);
-  s.fb[2 * bg + 1][br][0] = s.fb[2 * bg + 1][br][1] = hi | (lo << 16);
-  // doubled like the factor product 2F (exact); see the kernel's accumulator
-  bf16_split(-2.f * (dmin * (float)mn0), hi, lo);
-  s.fm[2 * bg][br][0] = s.fm[2 * bg][br][1] = hi | (lo << 16);
-  bf16_split(-2.f * (dmin * (float)mn1), hi, lo);
-  s.fm[2 * bg + 1][br][0] = s.fm[2 * bg + 1][br][1] = hi | (lo << 16);
+// weight part: codes -> int8 row, factors
+template <int FMT>
+__device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &s, int t) {
+  const int br = t >> 2, c = t & 3;
+  if constexpr (FMT == kMQ4K) {
+    // sub-block 2c in the low nibbles, 2c+1 in the high ones
+    const uint32_t Q[8] = {g.x[1].x, g.x[1].y, g.x[1].z, g.x[1].w, g.x[2].x, g.x[2].y, g.x[2].z, g.x[2].w};
+    u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
+    dst[0] = u32x4{Q[0] & 0x0F0F0F0Fu, Q[1] & 0x0F0F0F0Fu, Q[2] & 0x0F0F0F0Fu, Q[3] & 0x0F0F0F0Fu};
+    dst[1] = u32x4{Q[4] & 0x0F0F0F0Fu, Q[5] & 0x0F0F0F0Fu, Q[6] & 0x0F0F0F0Fu, Q[7] & 0x0F0F0F0Fu};
+    dst[2] = u32x4{(Q[0] >> 4) & 0x0F0F0F0Fu, (Q[1] >> 4) & 0x0F0F0F0Fu, (Q[2] >> 4) & 0x0F0F0F0Fu,
+                   (Q[3] >> 4) & 0x0F0F0F0Fu};
+    dst[3] = u32x4{(Q[4] >> 4) & 0x0F0F0F0Fu, (Q[5] >> 4) & 0x0F0F0F0Fu, (Q[6] >> 4) & 0x0F0F0F0Fu,
+                   (Q[7] >> 4) & 0x0F0F0F0Fu};
+    int sc0, sc1, mn0, mn1;
+    q4k_scales(g.x[0].y, g.x[0].z, g.x[0].w, c, sc0, sc1, mn0, mn1);
+    const float d = h2f(g.x[0].x), dmin = h2f(g.x[0].x >> 16);
+    put_factor(s.fb[2 * c][br], d * (float)sc0);
+    put_factor(s.fb[2 * c + 1][br], d * (float)sc1);
+    // doubled like the factor product 2F (exact); see the kernel's accumulator
+    put_factor(s.fm[2 * c][br], -2.f * (dmin * (float)mn0));
+    put_factor(s.fm[2 * c + 1][br], -2.f * (dmin * (float)mn1));
+  } else if constexpr (FMT == kMQ6K) {
+    // group gq (0..3) of half h is block j = 4h + gq; this thread's 16 values
+    // are its sub-block 2j + (c & 1), stored at bytes 8(c&1) and 16 + 8(c&1)
+    // of the block's permuted 32
+    const int h = c >> 1, hl = c & 1;
+    const float d = h2f(g.x[3].z);
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const u32x4 lo = g.x[gq & 1];
+      const uint32_t ls = 4u * (uint32_t)(gq >> 1), hs = 2u * (uint32_t)gq;
+      const int j = 4 * h + gq;
+      uint8_t *dst = s.b + br * kRow + 32 * j + 8 * hl;
+      *reinterpret_cast<u32x2 *>(dst) =
+          u32x2{(uint32_t)q6k_codes4(lo.x >> ls, g.x[2].x >> hs), (uint32_t)q6k_codes4(lo.y >> ls, g.x[2].y >> hs)};
+      *reinterpret_cast<u32x2 *>(dst + 16) =
+          u32x2{(uint32_t)q6k_codes4(lo.z >> ls, g.x[2].z >> hs), (uint32_t)q6k_codes4(lo.w >> ls, g.x[2].w >> hs)};
+      // scale of sub-block 8h + 2gq + hl: byte 2gq + hl of scales[8h..8h+7]
+      const uint32_t scw = gq < 2 ? g.x[3].x : g.x[3].y;
+      put_factor(s.fb[2 * j + hl][br], d * (float)sbyte(scw, 8u * (uint32_t)((2 * gq + hl) & 3)));
+    }
+  } else {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
+    dst[0] = g.x[0];
+    dst[1] = g.x[1];
+    dst[2] = g.x[2];
+    dst[3] = g.x[3];
+    put_factor(s.fb[2 * c][br], h2f(g.x[4].x));
+    put_factor(s.fb[2 * c + 1][br], h2f(g.x[4].y));
+  }
 }
 
-// Two waves share each 32x32 output tile and split every superblock's eight
-// blocks between them; the workgroup has 16 waves.  Waves 0-7 stage
-// activations and waves 8-15 weights, and the two partial tiles are summed
-// through LDS at the end.
-constexpr bool kPipe = false;  // issue block j+1's MFMAs before block j's rescale
-
-template <bool DUMP>
-__global__ __launch_bounds__(1024) void mmq_q4k_kernel(const uint8_t *__restrict__ W,
-                                                           const uint8_t *__restrict__ AQ, float *__restrict__ C,
-                                                           int32_t *__restrict__ Dd, int M, int N, int nsb) {
-  constexpr int kJ = 4;  // blocks per superblock per wave
-  __shared__ MmqStage stage[2];
+// Two waves share each 32x32 output tile and split every step's eight blocks
+// between them; the workgroup has 16 waves.  Waves 0-7 stage activations and
+// waves 8-15 weights, and the two partial tiles are summed through LDS at the
+// end.  With DUMP the exact dots are written instead of C: [m][n][k/32] per
+// block, or [m][n][k/16] per Q6_K sub-block.
+template <int FMT, bool DUMP>
+__global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ AQ,
+                                                   float *__restrict__ C, int32_t *__restrict__ Dd, int M, int N,
+                                                   int nblk) {
+  constexpr int kJ = 4;  // blocks per step per wave
+  __shared__ MmqStage<FMT> stage[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int kh = wv >> 3;                         // which part of each superblock
+  const int kh = wv >> 3;                         // which half of each step
   const int wm = (wv >> 2) & 1, wn = wv & 3;      // 2 x 4 tiles of 32x32
   const int tiles_n = (N + kBN - 1) / kBN;
   const int m0 = (int)(blockIdx.x / tiles_n) * kBM, n0 = (int)(blockIdx.x % tiles_n) * kBN;
   const int lr = lane & 31, lh = lane >> 5;
-  const int nbrow = nsb * 8;
+  const int nsteps = (nblk + 7) / 8;
   const int st = tid & 511;
   const bool act = tid < 512;  // this wave stages activations, else weights
 
@@ -166,86 +265,113 @@ __global__ __launch_bounds__(1024) void mmq_q4k_kernel(const uint8_t *__restrict
     fzero[r] = 0.f;
   }
 
-  // Superblock s is staged from registers R[s & 1]: its global loads are
-  // issued two superblocks ahead, so two compute phases cover their latency.
-  MmqRegs R0, R1;
-  auto load = [&](MmqRegs &g, int s) {
+  // Step s is staged from registers R[s & 1]: its global loads are issued two
+  // steps ahead, so two compute phases cover their latency.
+  MmqRegs<FMT> R0, R1;
+  auto load = [&](MmqRegs<FMT> &g, int s) {
     if (act)
-      load_act(g, AQ, M, nsb, m0, s, st);
+      load_act<FMT>(g, AQ, M, nblk, m0, s, st);
     else
-      load_wgt(g, W, N, nsb, n0, s, st);
+      load_wgt<FMT>(g, W, N, nblk, n0, s, st);
   };
-  auto store = [&](const MmqRegs &g, MmqStage &dst) {
+  auto store = [&](const MmqRegs<FMT> &g, MmqStage<FMT> &dst) {
     if (act)
-      store_act(g, dst, st);
+      store_act<FMT>(g, dst, st);
     else
-      store_wgt(g, dst, st);
+      store_wgt<FMT>(g, dst, st);
   };
-  auto compute = [&](MmqStage &cur, int sb) {
+  // output register r holds tile row 8(r/4) + 4*lh + r%4, column lr
+  auto dump = [&](const v16i &D, int idx, int per_row) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4), gn = n0 + wn * 32 + lr;
+      if (gm < M && gn < N) Dd[((int64_t)gm * N + gn) * per_row + idx] = D[r];
+    }
+  };
+  auto factor = [&](const uint32_t *pa, const uint32_t *pb) {
+    const v4s fav = __builtin_bit_cast(v4s, u32x2{pa[0], pa[1]});
+    const v4s fbv = __builtin_bit_cast(v4s, u32x2{pb[0], pb[1]});
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fav, fbv, fzero, 0, 0, 0);
+  };
+  auto compute = [&](MmqStage<FMT> &cur, int s) {
     const int j0 = kh * kJ;
     const uint8_t *arow = cur.a + (wm * 32 + lr) * kRow + 16 * lh + 32 * j0;
     const uint8_t *brow = cur.b + (wn * 32 + lr) * kRow + 16 * lh + 32 * j0;
-    const uint32_t *fa = cur.fa[j0][wm * 32 + lr];
-    const uint32_t *fb = cur.fb[j0][wn * 32 + lr];
-    if (!DUMP) {
-      // min term of this wave's four blocks, -sum_j (d_a S)_j (dmin m_j): a
-      // rank-4 product, split hi + lo on both sides into K = 16 bf16 terms
-      // (lanes 0-31 carry blocks j0, j0+1, lanes 32-63 blocks j0+2, j0+3),
-      // accumulated straight into acc on the matrix core
-      const uint32_t *ps = cur.fs[j0 + 2 * lh][wm * 32 + lr];
-      const uint32_t *pm = cur.fm[j0 + 2 * lh][wn * 32 + lr];
-      constexpr int sA = (kBM + 1) * 2, sB = (kBN + 1) * 2;
-      const v8bf sv = __builtin_bit_cast(v8bf, u32x4{ps[0], ps[1], ps[sA], ps[sA + 1]});
-      const v8bf mv = __builtin_bit_cast(v8bf, u32x4{pm[0], pm[1], pm[sB], pm[sB + 1]});
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sv, mv, acc, 0, 0, 0);
+    if constexpr (MmqFmt<FMT>::kMin) {
+      if (!DUMP) {
+        // min term of this wave's four blocks, -sum_j (d_a S)_j (dmin m_j): a
+        // rank-4 product, split hi + lo on both sides into K = 16 bf16 terms
+        // (lanes 0-31 carry blocks j0, j0+1, lanes 32-63 blocks j0+2, j0+3),
+        // accumulated straight into acc on the matrix core
+        const uint32_t *ps = cur.fs[j0 + 2 * lh][wm * 32 + lr];
+        const uint32_t *pm = cur.fm[j0 + 2 * lh][wn * 32 + lr];
+        constexpr int sA = (kBM + 1) * 2, sB = (kBN + 1) * 2;
+        const v8bf sv = __builtin_bit_cast(v8bf, u32x4{ps[0], ps[1], ps[sA], ps[sA + 1]});
+        const v8bf mv = __builtin_bit_cast(v8bf, u32x4{pm[0], pm[1], pm[sB], pm[sB + 1]});
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sv, mv, acc, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < kJ; ++jj) {
-      // D = exact int32 dots of block j0+jj; F2 = 2F for its rescale: lanes
-      // 32-63 (k = 4..7) of the bf16 MFMA repeat the four parts of lanes 0-31,
-      // so it returns exactly twice the outer product
-      const v4i av = *reinterpret_cast<const v4i *>(arow + 32 * jj);
-      const v4i bv = *reinterpret_cast<const v4i *>(brow + 32 * jj);
-      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
-      v16f F2 = fzero;
-      if (!DUMP) {
-        const uint32_t *pa = fa + jj * (kBM + 1) * 2, *pb = fb + jj * (kBN + 1) * 2;
-        const v4s fav = __builtin_bit_cast(v4s, u32x2{pa[0], pa[1]});
-        const v4s fbv = __builtin_bit_cast(v4s, u32x2{pb[0], pb[1]});
-        F2 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fav, fbv, fzero, 0, 0, 0);
-      }
+      const int j = j0 + jj;
+      if (FMT == kMQ8_0 && 8 * s + j >= nblk) break;  // ragged last step (wave-uniform)
+      const uint32_t *pa = cur.fa[j][wm * 32 + lr];
+      const u32x4n av = *reinterpret_cast<const u32x4n *>(arow + 32 * jj);
+      const u32x4n bv = *reinterpret_cast<const u32x4n *>(brow + 32 * jj);
+      if constexpr (FMT == kMQ6K) {
+        // sub-blocks 2j and 2j+1: the lane's 8-byte slices are (x, y) and (z, w)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // output register r holds tile row 8(r/4) + 4*lh + r%4, column lr
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t alo = hh ? av.z : av.x, ahi = hh ? av.w : av.y;
+          const uint32_t blo = hh ? bv.z : bv.x, bhi = hh ? bv.w : bv.y;
+          const v16i D = __builtin_amdgcn_mfma_i32_32x32x16_i8((long)(((uint64_t)ahi << 32) | alo),
+                                                                (long)(((uint64_t)bhi << 32) | blo), zero, 0, 0, 0);
+          if (DUMP) {
+            dump(D, 16 * s + 2 * j + hh, 2 * nblk);
+          } else {
+            const v16f F2 = factor(pa, cur.fb[2 * j + hh][wn * 32 + lr]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += F2[r] * (float)D[r];
+          }
+          asm volatile("" : "+v"(acc)::"memory");  // one sub-block's D and F live at a time
+        }
+      } else {
+        // D = exact int32 dots of block j; F2 = 2F for its rescale: lanes
+        // 32-63 (k = 4..7) of the bf16 MFMA repeat the four parts of lanes
+        // 0-31, so it returns exactly twice the outer product
+        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, av),
+                                                              __builtin_bit_cast(v4i, bv), zero, 0, 0, 0);
         if (DUMP) {
-          const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4), gn = n0 + wn * 32 + lr;
-          if (gm < M && gn < N) Dd[((int64_t)gm * N + gn) * nbrow + sb * 8 + j0 + jj] = D[r];
+          dump(D, 8 * s + j, nblk);
         } else {
-          acc[r] += F2[r] * (float)D[r];
+          const v16f F2 = factor(pa, cur.fb[j][wn * 32 + lr]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += F2[r] * (float)D[r];
         }
       }
       // Fence: the MFMA builtins carry no memory dependence, so without it
-      // every block's products would be hoisted to the top of the
-      // superblock, with all their results live at once.
+      // every block's products would be hoisted to the top of the step, with
+      // all their results live at once.
       asm volatile("" : "+v"(acc)::"memory");
     }
   };
-  // One step: superblock s+2 loads into `mine` (free: it held s, staged one
-  // step earlier), s computes from `cur`, and s+1 (loaded one step earlier,
-  // in `next`) is staged into `other`, which nobody reads during this step.
-  auto step = [&](int s, MmqRegs &mine, const MmqRegs &next, MmqStage &cur, MmqStage &other) {
-    if (s + 2 < nsb) load(mine, s + 2);
+  // One step: step s+2 loads into `mine` (free: it held s, staged one step
+  // earlier), s computes from `cur`, and s+1 (loaded one step earlier, in
+  // `next`) is staged into `other`, which nobody reads during this step.
+  auto step = [&](int s, MmqRegs<FMT> &mine, const MmqRegs<FMT> &next, MmqStage<FMT> &cur,
+                  MmqStage<FMT> &other) {
+    if (s + 2 < nsteps) load(mine, s + 2);
     compute(cur, s);
-    if (s + 1 < nsb) store(next, other);
+    if (s + 1 < nsteps) store(next, other);
     __syncthreads();
   };
-  if (nsb > 0) load(R0, 0);
-  if (nsb > 1) load(R1, 1);
-  if (nsb > 0) store(R0, stage[0]);
+  if (nsteps > 0) load(R0, 0);
+  if (nsteps > 1) load(R1, 1);
+  if (nsteps > 0) store(R0, stage[0]);
   __syncthreads();
-  for (int sb = 0; sb < nsb; sb += 2) {
-    step(sb, R0, R1, stage[0], stage[1]);
-    if (sb + 1 < nsb) step(sb + 1, R1, R0, stage[1], stage[0]);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, R0, R1, stage[0], stage[1]);
+    if (s + 1 < nsteps) step(s + 1, R1, R0, stage[1], stage[0]);
   }
 
   if (!DUMP) {
@@ -274,18 +400,26 @@ __global__ __launch_bounds__(1024) void mmq_q4k_kernel(const uint8_t *__restrict
   }
 }
 
-hipError_t launch_qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n, int64_t k,
-                                 hipStream_t stream) {
+template <int FMT>
+static hipError_t launch_fmt(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n, int64_t k,
+                             hipStream_t stream) {
   const dim3 grid((unsigned)(((n + kBN - 1) / kBN) * ((m + kBM - 1) / kBM)));
   const uint8_t *W = static_cast<const uint8_t *>(w);
   const uint8_t *A = static_cast<const uint8_t *>(aq);
   if (D)
-    hipLaunchKernelGGL((mmq_q4k_kernel<true>), grid, dim3(1024), 0, stream, W, A, c, D, (int)m,
-                       (int)n, (int)(k / 256));
+    hipLaunchKernelGGL((mmq_kernel<FMT, true>), grid, dim3(1024), 0, stream, W, A, c, D, (int)m, (int)n,
+                       (int)(k / 32));
   else
-    hipLaunchKernelGGL((mmq_q4k_kernel<false>), grid, dim3(1024), 0, stream, W, A, c, D, (int)m,
-                       (int)n, (int)(k / 256));
+    hipLaunchKernelGGL((mmq_kernel<FMT, false>), grid, dim3(1024), 0, stream, W, A, c, D, (int)m, (int)n,
+                       (int)(k / 32));
   return hipGetLastError();
+}
+
+hipError_t launch_qgemm_mmq(int fmt, const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,
+                            int64_t k, hipStream_t stream) {
+  if (fmt == kMQ4K) return launch_fmt<kMQ4K>(w, aq, c, D, m, n, k, stream);
+  if (fmt == kMQ6K) return launch_fmt<kMQ6K>(w, aq, c, D, m, n, k, stream);
+  return launch_fmt<kMQ8_0>(w, aq, c, D, m, n, k, stream);
 }
 
 }  // namespace qg

@@ -41,6 +41,11 @@ WORKLOADS = {
     "q6_k_gemv": dict(fmt="q6_k", n=128256, k=4096, seed=1002),
     "q4_k_mmq": dict(fmt="q4_k", m=512, n=4096, k=4096, seed=1003),
     "moe_q4_k": dict(fmt="q4_k", n_expert=128, n_ff=768, n_embd=2048, n_tok=16, top_k=8, seed=1004),
+    # prefill with the other two integer-dot types: a Q6_K ffn_down of the
+    # Llama-3-8B shape (Q4_K_M files keep part of ffn_down in Q6_K) and a Q8_0
+    # 4096 x 4096 projection, both at 512 tokens
+    "q6_k_mmq": dict(fmt="q6_k", m=512, n=4096, k=14336, seed=1005),
+    "q8_0_mmq": dict(fmt="q8_0", m=512, n=4096, k=4096, seed=1006),
 }
 
 
@@ -270,8 +275,8 @@ def workload(name: str, **override):
     if name.endswith("_gemv"):
         return dict(p, w=weights(p["fmt"], p["n"], p["k"], seed),
                     x=normal(seed, T_X, (p["k"],)))
-    if name == "q4_k_mmq":
-        return dict(p, w=weights("q4_k", p["n"], p["k"], seed),
+    if name.endswith("_mmq"):
+        return dict(p, w=weights(p["fmt"], p["n"], p["k"], seed),
                     a=normal(seed, T_X, (p["m"], p["k"])))
     if name == "moe_q4_k":
         E, F, H = p["n_expert"], p["n_ff"], p["n_embd"]

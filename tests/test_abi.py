@@ -30,6 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemm_q4_k_mmq",
+                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq",
                  "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
         assert want in names
@@ -125,6 +126,26 @@ def test_mmq_validation(lib):
     assert f(A16, A16b, c, 4, 0, 256, None) == OK
     # the dot dump refuses outputs it would not be asked to hold
     assert lib.qg_blockdots_q4_k_mmq(A16, A16b, c, 1 << 14, 1 << 14, 4096, None) == SHAPE
+
+
+@pytest.mark.parametrize("fmt,kmult", [("q6_k", 256), ("q8_0", 32)])
+def test_mmq_validation_other_formats(lib, fmt, kmult):
+    c = P((1 << 20) + 8192)
+    f = getattr(lib, f"qgemm_{fmt}_mmq")
+    assert f(None, A16b, c, 4, 4, kmult, None) == NULL
+    assert f(A16, A16b, c, 4, 4, kmult // 2, None) == SHAPE
+    assert f(A16, A16b, c, 4, 4, kmult + kmult // 2, None) == SHAPE
+    assert f(A16, A16b, c, 4, -1, kmult, None) == SHAPE
+    assert f(MIS, A16b, c, 4, 4, kmult, None) == ALIGN
+    assert f(A16, A16b, P((1 << 20) + 2), 4, 4, kmult, None) == ALIGN
+    assert f(A16, A16b, c, 0, 4, kmult, None) == OK
+    assert f(A16, A16b, c, 4, 0, kmult, None) == OK
+    d = getattr(lib, f"qg_blockdots_{fmt}_mmq")
+    assert d(A16, A16b, None, 4, 4, kmult, None) == NULL
+    # dump limit m * n * (dots per row) <= 2^28; Q6_K has one dot per 16 values
+    per = 16 if fmt == "q6_k" else 32
+    assert d(A16, A16b, c, 1 << 10, 1 << 10, 256 * per, None) != SHAPE  # at the limit (then: no device here)
+    assert d(A16, A16b, c, 1 << 10, 1 << 10, 512 * per, None) == SHAPE
 
 
 def test_moe_validation(lib):

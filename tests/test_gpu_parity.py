@@ -391,6 +391,102 @@ def test_mmq_full_size(env):
     assert np.array_equal(_host(D), orc.blockdots_q4_k_mmq(w[:96], aq[:80], 80, 96, k))
 
 
+# ------------------------------------------- mmq with the other weight types
+MMQ_SHAPES = [(1, 1, 256), (32, 32, 256), (70, 100, 512), (130, 65, 768), (3, 200, 1024), (64, 128, 2048)]
+# Q8_0 rows need k % 32 only: a ragged last 256-wide step
+MMQ_Q80_RAGGED = [(5, 7, 32), (33, 70, 96), (64, 128, 288), (65, 129, 4128)]
+
+
+@pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES] +
+                         [("q8_0",) + s for s in MMQ_SHAPES + MMQ_Q80_RAGGED])
+def test_mmq_block_dots_exact_other_formats(env, fmt, m, n, k):
+    """Random bytes: the matrix-core dots equal the oracle's block dots
+    (per 16 values for Q6_K)."""
+    qg, orc, torch, dev = env
+    w = synth.random_blocks(fmt, n, k, seed=m + n + 7)
+    aq = synth.random_blocks("q8_1", m, k, seed=m * n + k + 7)
+    D = getattr(qg, f"blockdots_{fmt}_mmq")(_gpu(torch, dev, w), _gpu(torch, dev, aq), m, n, k)
+    assert np.array_equal(_host(D), orc.blockdots_mmq(fmt, w, aq, m, n, k))
+
+
+@pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES + [(1, 64, 4096), (257, 70, 1024)]] +
+                         [("q8_0",) + s for s in MMQ_SHAPES + MMQ_Q80_RAGGED + [(257, 70, 1024)]])
+def test_mmq_values_other_formats(env, fmt, m, n, k):
+    qg, orc, torch, dev = env
+    w = synth.weights(fmt, n, k, seed=m + 2 * n + k)
+    a = synth.normal(m + n, 1, (m, k))
+    AQ = qg.quantize_q8_1(_gpu(torch, dev, a))
+    C = _host(getattr(qg, f"qgemm_{fmt}_mmq")(_gpu(torch, dev, w), AQ, m, n, k))
+    aq = orc.quantize_q8_1(a)
+    assert np.array_equal(_host(AQ), aq)
+    assert rel_err(C, orc.qgemm(fmt, w, aq, m, n, k)) <= REL_TOL
+
+
+@pytest.mark.parametrize("fmt", ["q6_k", "q8_0"])
+def test_mmq_values_random_bytes_other_formats(env, fmt):
+    qg, orc, torch, dev = env
+    m, n, k = 70, 130, 512
+    w = synth.random_blocks(fmt, n, k, seed=191, lo_exp=-14, hi_exp=2)
+    aq = synth.random_blocks("q8_1", m, k, seed=192, lo_exp=-14, hi_exp=2)
+    C = _host(getattr(qg, f"qgemm_{fmt}_mmq")(_gpu(torch, dev, w), _gpu(torch, dev, aq), m, n, k))
+    assert rel_err(C, orc.qgemm(fmt, w, aq, m, n, k)) <= REL_TOL
+
+
+def test_mmq_hand_blocks_exact_other_formats(env):
+    """Hand-built Q6_K superblock and Q8_0 blocks against d_a = 1/8: every
+    intermediate is exact in fp32, so C equals the hand-computed dot."""
+    qg, orc, torch, dev = env
+    xq, qa = _hand_activation(256)
+    A = _gpu(torch, dev, np.tile(xq, (40, 1)))
+    fx = read_golden("q6_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["scales"][0].split()]
+    exact = sum(Fraction(1, 256) * sc[i // 16] * (q[i] - 32) * Fraction(1, 8) * qa[i] for i in range(256))
+    C = _host(qg.qgemm_q6_k_mmq(_gpu(torch, dev, np.tile(blk, (70, 1))), A, 40, 70, 256))
+    assert all(Fraction(float(v)) == exact for v in C.ravel())
+    blk = np.frombuffer(bytes.fromhex(read_golden("q8_0_block.txt")["bytes"][0]), np.uint8)
+    exact = sum(Fraction((i % 32) - 16, 4) * Fraction(1, 8) * qa[i] for i in range(256))
+    C = _host(qg.qgemm_q8_0_mmq(_gpu(torch, dev, np.tile(blk, (70, 8))), A, 40, 70, 256))
+    assert all(Fraction(float(v)) == exact for v in C.ravel())
+
+
+def test_mmq_empty_other_formats(env):
+    qg, orc, torch, dev = env
+    A = torch.zeros(4 * 288, dtype=torch.uint8, device=dev)
+    for fmt, k in (("q6_k", 256), ("q8_0", 32)):
+        W = torch.zeros(4 * qg.row_bytes(fmt, 256), dtype=torch.uint8, device=dev)
+        c = torch.full((4, 4), 7.0, device=dev)
+        f = getattr(qg, f"qgemm_{fmt}_mmq")
+        f(W, A, 0, 4, k, c=c)   # m = 0: nothing written
+        f(W, A, 4, 0, k, c=c)   # n = 0: nothing written
+        assert np.all(_host(c) == 7.0)
+        f(W, A, 4, 4, 0, c=c)   # k = 0: zeros
+        assert np.all(_host(c) == 0.0)
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("name", ["q6_k_mmq", "q8_0_mmq"])
+def test_mmq_full_size_other_formats(env, name):
+    qg, orc, torch, dev = env
+    p = synth.WORKLOADS[name]
+    fmt, m, n, k = p["fmt"], p["m"], p["n"], p["k"]
+    w = synth.weights(fmt, n, k, p["seed"])
+    a = synth.normal(p["seed"], synth.T_X, (m, k))
+    AQ = qg.quantize_q8_1(_gpu(torch, dev, a))
+    C = _host(getattr(qg, f"qgemm_{fmt}_mmq")(_gpu(torch, dev, w), AQ, m, n, k))
+    aq = orc.quantize_q8_1(a)
+    assert np.array_equal(_host(AQ), aq)
+    g = np.random.default_rng(4)
+    pairs = np.concatenate([np.stack([g.integers(0, m, 4096), g.integers(0, n, 4096)], 1),
+                            np.stack([np.zeros(n, int), np.arange(n)], 1),          # a full row
+                            np.stack([np.arange(m), np.full(m, n - 1)], 1)])        # a full column
+    r = orc.qgemm(fmt, w, aq, m, n, k, pairs=pairs)
+    assert rel_err(C[pairs[:, 0], pairs[:, 1]], r) <= REL_TOL
+    D = getattr(qg, f"blockdots_{fmt}_mmq")(_gpu(torch, dev, w[:96]), AQ[:80].contiguous(), 80, 96, k)
+    assert np.array_equal(_host(D), orc.blockdots_mmq(fmt, w[:96], aq[:80], 80, 96, k))
+
+
 # ------------------------------------------------------------------------ MoE
 def _moe_case(seed, E, F, H, T, K):
     w_gu = synth.weights("q4_k", E * 2 * F, H, seed, synth.T_W).reshape(E, -1)
@@ -486,6 +582,8 @@ def test_graph_replay_matches_eager(env):
     xmq = torch.empty((T, H // 32 * 36), dtype=torch.uint8, device=dev)
     ys = {f: torch.empty(n, device=dev) for f in Ws}
     c = torch.empty((m, n), device=dev)
+    c6 = torch.empty((m, n), device=dev)
+    c8 = torch.empty((m, n), device=dev)
     out = torch.empty((T, H), device=dev)
     ws = torch.empty(qg.moe_qgemv_q4_k_workspace_size(T, K, E, F, H), dtype=torch.uint8, device=dev)
 
@@ -498,12 +596,14 @@ def test_graph_replay_matches_eager(env):
             getattr(qg, GEMV_BATCH[f])(W, xbq, 5, n, k, y=ybs[f])
         qg.quantize_q8_1(a, aq)
         qg.qgemm_q4_k_mmq(Ws["q4_k"], aq, m, n, k, c=c)
+        qg.qgemm_q6_k_mmq(Ws["q6_k"], aq, m, n, k, c=c6)
+        qg.qgemm_q8_0_mmq(Ws["q8_0"], aq, m, n, k, c=c8)
         qg.quantize_q8_1(XM, xmq)
         qg.moe_qgemv_q4_k(WGU, WDN, xmq, IDS, RW, T, K, E, F, H, out=out, workspace=ws)
 
     def snapshot():
         torch.cuda.synchronize()
-        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, xmq, out)]
+        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out)]
 
     work()
     eager = snapshot()
@@ -517,7 +617,7 @@ def test_graph_replay_matches_eager(env):
             work()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, xmq, out):
+        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out):
             t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
