@@ -59,6 +59,7 @@ def _declare(L):
         "orc_f16_to_f32_n": [_P, _P, _I],
         "orc_f32_to_f16_n": [_P, _P, _I],
         "orc_quantize_q8_1": [_P, _P, _I, _I],
+        "orc_rms_scale": [_P, _P, _I, _I, ctypes.c_double],
         "orc_unpack_q4_k": [_P, _P, _P, _P, _P, _P],
         "orc_unpack_q6_k": [_P, _P, _P, _P],
         "orc_dequant_q8_0": [_P, _P, _I, _I],
@@ -118,6 +119,17 @@ def quantize_q8_1(x):
     out = np.empty((rows, (k // 32) * Q8_1_BYTES), np.uint8)
     lib().orc_quantize_q8_1(_ptr(x), _ptr(out), rows, k)
     return out
+
+
+def rms_scale(x, eps):
+    """r = 1/sqrt(mean(x^2) + eps) per row of f32 x ([rows][k] or [k]), in double."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, k = x.shape
+    r = np.empty(rows, np.float64)
+    lib().orc_rms_scale(_ptr(x), _ptr(r), rows, k, float(eps))
+    return r
 
 
 # -------------------------------------------------------------------- decode

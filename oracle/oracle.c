@@ -94,6 +94,21 @@ static void wr16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)(v & 0xff); p[1] = (u
 static double h2d(const uint8_t *p) { return (double)orc_f16_to_f32(rd16(p)); }
 
 /* ------------------------------------------------------------------------ */
+/* RMS scale of an activation row (the RMSNorm that precedes a projection in  */
+/* the model families the infr page runs): r = 1 / sqrt(sum(x^2)/k + eps),    */
+/* in double, from the f32 values.  The normalized row is x * r * gamma.      */
+/* ------------------------------------------------------------------------ */
+void orc_rms_scale(const float *x, double *r, int64_t rows, int64_t k, double eps)
+{
+    for (int64_t i = 0; i < rows; ++i) {
+        double ss = 0.0;
+        for (int64_t t = 0; t < k; ++t)
+            ss += (double)x[i * k + t] * (double)x[i * k + t];
+        r[i] = 1.0 / sqrt(ss / (double)k + eps);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Activation quantization to Q8_1 (on the path).                             */
 /* Per 32-element block: amax; d = amax/127 (fp32, correctly rounded);        */
 /* q = round-half-away(x/d) from the fp32 d, clamped to +-127; s = d*sum(q)   */

@@ -67,6 +67,25 @@ def test_quantize_q8_1_hand_vectors(orc):
     assert orc.quantize_q8_1(x).tobytes() == b"".join(c[1] for c in cases)
 
 
+def test_rms_scale_closed_forms(orc):
+    """r = 1/sqrt(sum(x^2)/k + eps): hand values, with and without eps."""
+    x = np.array([[1, 2, 2, 4], [0.5, 0.5, 0.5, 0.5], [0, 0, 0, 0]], np.float32)
+    assert np.array_equal(orc.rms_scale(x, 0.0)[:2], [0.4, 2.0])      # mean 6.25 -> 1/2.5; mean 0.25 -> 2
+    r = orc.rms_scale(x, 0.75)
+    assert abs(r[0] - 1 / np.sqrt(7.0)) <= 1e-16                       # 6.25 + 0.75
+    assert abs(r[1] - 1.0) <= 1e-16                                    # 0.25 + 0.75
+    assert abs(orc.rms_scale(x[2], 1e-6)[0] - 1000.0) <= 1e-9          # zero row: 1/sqrt(eps)
+
+
+def test_rms_scale_normalizes_and_scales(orc):
+    x = synth.normal(61, 0, (3, 4096))
+    r = orc.rms_scale(x, 0.0)
+    xd = x.astype(np.float64)
+    assert np.allclose(np.mean((xd * r[:, None]) ** 2, axis=1), 1.0, rtol=1e-13, atol=0)
+    # r(a x) = r(x) / |a| (a = -4, a power of two, keeps the f32 values exact)
+    assert np.allclose(orc.rms_scale(np.float32(-4) * x, 0.0), r / 4, rtol=1e-14, atol=0)
+
+
 def test_quantize_q8_1_roundtrip_bound(orc):
     g = np.random.default_rng(11)
     x = np.concatenate([g.standard_normal((64, 256)), g.standard_normal((64, 256)) * 1e-6,
