@@ -5,7 +5,8 @@ quantize the activations to Q8_1 on the GPU, then run the product on the
 quantized weights.  Default workload: the Q4_K decode GEMV at a Llama-3-8B FFN
 shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
 q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); prefill products
-with the other weight types q6_k_mmq, q8_0_mmq; small-batch GEMVs
+with the other weight types q6_k_mmq, q8_0_mmq; the RMSNorm + quantize
+prologue rmsnorm_q8_1; small-batch GEMVs
 <fmt>_gemv_b<B> (the GEMV workload's weights against B <= 8 activation rows),
 or batch for the standard set of them.
 
@@ -49,6 +50,7 @@ def _cpu_threads():
 KERNEL_SOURCES = {
     "q4_k_gemv": ["qg_gemv.hip"], "q8_0_gemv": ["qg_gemv.hip"], "q6_k_gemv": ["qg_gemv.hip"],
     "q4_k_mmq": ["qg_mmq.hip"], "q6_k_mmq": ["qg_mmq.hip"], "q8_0_mmq": ["qg_mmq.hip"],
+    "rmsnorm_q8_1": ["qg_quant.hip", "qg_quant.h"],
     "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
 }
 BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8", "q6_k_gemv_b4", "q6_k_gemv_b8"]
@@ -210,6 +212,66 @@ class GemvBatch(Gemv):
                            f"dequant-and-dot per row) x {reps}, {t:.1f} s")
 
 
+class RmsnormQ81(Workload):
+    """`rmsnorm_q8_1`: x (f32 [rows][k]) -> Q8_1((x * r) * gamma) per row in one
+    launch.  The same work as two launches (torch's rms_norm writing f32, then
+    quantize_q8_1) is timed alongside as `alt_call`."""
+
+    def __init__(self, qg, torch, warm):
+        from gemm_gguf_block_amd import synth
+        p = synth.WORKLOADS["rmsnorm_q8_1"]
+        self.name, self.rows, self.k, self.eps = "rmsnorm_q8_1", p["rows"], p["k"], p["eps"]
+        self.qg, self.torch = qg, torch
+        dev = torch.device("cuda:0")
+        self.x_host = synth.normal(p["seed"], synth.T_X, (self.rows, self.k))
+        self.g_host = (1.0 + 0.25 * synth.normal(p["seed"], synth.T_W, (self.k,))).astype("float32")
+        self.copies = 1 if warm else max(1, math.ceil(COLD_BYTES / self.x_host.nbytes))
+        X0 = torch.from_numpy(self.x_host).to(dev)
+        self.X = [X0] + [X0.clone() for _ in range(self.copies - 1)]
+        self.gamma = torch.from_numpy(self.g_host).to(dev)
+        self.xq = torch.empty((self.rows, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
+        self.dominant = "rmsnorm_quantize_q8_1_kernel"
+        self.kernel_bytes = self.x_host.nbytes + 4 * self.k + self.rows * q81_bytes(self.k)
+        self.step_bytes = self.kernel_bytes
+        self.tokens_per_step = self.rows
+        self.unit, self.bound = "GB/s", "hbm"
+
+    def step(self, i):
+        self.qg.rmsnorm_quantize_q8_1(self.X[i % self.copies], self.gamma, self.eps, xq=self.xq)
+
+    def dominant_call(self, i):
+        self.step(i)
+
+    def alt_call(self, i):
+        F = self.torch.nn.functional
+        y = F.rms_norm(self.X[i % self.copies], (self.k,), self.gamma, self.eps)
+        self.qg.quantize_q8_1(y, self.xq)
+
+    alt_what = "torch rms_norm (f32 out), then quantize_q8_1"
+
+    def value(self, sec_per_step):
+        return self.step_bytes / sec_per_step / 1e9
+
+    def kernel_rate(self, sec):
+        return self.kernel_bytes / sec / 1e9
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+
+        import oracle
+        rows = min(self.rows, 64)
+        x = self.x_host[:rows]
+
+        def once():
+            r = oracle.rms_scale(x, self.eps).astype(np.float32)
+            oracle.quantize_q8_1((x * r[:, None]) * self.g_host[None, :])
+        reps, t = _repeat(once, budget_s)
+        nb = reps * rows * (4 * self.k + q81_bytes(self.k))
+        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
+                    sample=f"rows 0..{rows - 1} of {self.rows} (double RMS scale, f32 products, quantize) x {reps}, "
+                           f"{t:.1f} s")
+
+
 class Mmq(Workload):
     def __init__(self, qg, torch, name, warm):
         from gemm_gguf_block_amd import synth
@@ -330,6 +392,8 @@ def make(name, qg, torch, warm):
         return Gemv(qg, torch, name, warm)
     if name.endswith("_mmq"):
         return Mmq(qg, torch, name, warm)
+    if name == "rmsnorm_q8_1":
+        return RmsnormQ81(qg, torch, warm)
     if name == "moe_q4_k":
         return Moe(qg, torch, warm)
     raise SystemExit(f"unknown workload {name}")
@@ -432,12 +496,15 @@ def bench_one(name, args, qg, torch):
     if wl.unit == "GB/s":
         rec["pct_of_hbm_peak"] = round(100.0 * value / HBM_PEAK_GBS, 2)
     cfg = rec["config"]
-    for key in ("fmt", "b", "m", "n", "k", "E", "F", "H", "T", "K"):
+    for key in ("fmt", "b", "m", "n", "k", "rows", "E", "F", "H", "T", "K"):
         if hasattr(wl, key):
             cfg[key] = getattr(wl, key)
     cfg["weight_copies"] = wl.copies
     if name == "moe_q4_k":
         cfg["distinct_experts"] = wl.distinct
+    if hasattr(wl, "alt_call"):
+        ms_alt = _time(wl.alt_call, args.warmup, args.steps, args.warmup, torch, not args.no_graph, args.spinup)
+        rec["comparison"] = {"what": wl.alt_what, "ms_per_step": round(ms_alt, 6)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
     print(f"[bench] {name}: setup {setup_s:.1f} s, step {ms_step * 1e3:.2f} us, "
@@ -454,7 +521,7 @@ def main():
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
-                         "q6_k_mmq, q8_0_mmq, "
+                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, "
                          "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")

@@ -30,6 +30,7 @@ SIGNATURES = {
     "qgemv_q8_0": [_P, _P, _P, _I, _I, _P],
     "qgemv_q4_k": [_P, _P, _P, _I, _I, _P],
     "qgemv_q6_k": [_P, _P, _P, _I, _I, _P],
+    "rmsnorm_quantize_q8_1": [_P, _P, ctypes.c_float, _P, _P, _I, _I, _P],
     "qgemv_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_q6_k_batch": [_P, _P, _P, _I, _I, _I, _P],
@@ -172,6 +173,23 @@ def qgemv_q4_k_batch(w, xq, b, n, k, y=None, stream=None):
 
 def qgemv_q6_k_batch(w, xq, b, n, k, y=None, stream=None):
     return _gemv_batch("q6_k", w, xq, b, n, k, y, stream)
+
+
+def rmsnorm_quantize_q8_1(x, gamma, eps, xq=None, r=None, stream=None):
+    """x: f32 [rows][k] (or [k]) -> Q8_1 bytes of (x * r) * gamma per row, with
+    r = 1/sqrt(mean(x^2) + eps).  Returns (xq, r) when r (f32 [rows]) is given,
+    else xq."""
+    import torch
+    rows, k = (1, x.shape[0]) if x.dim() == 1 else (x.shape[0], x.shape[1])
+    if xq is None:
+        xq = _empty((rows, row_bytes("q8_1", k)), torch.uint8, x)
+    px = _need(x, torch.float32, rows * k * 4, "x")
+    pg = _need(gamma, torch.float32, k * 4, "gamma")
+    pq = _need(xq, torch.uint8, rows * row_bytes("q8_1", k), "xq")
+    pr = None if r is None else _need(r, torch.float32, rows * 4, "r")
+    _check("rmsnorm_quantize_q8_1", lib().rmsnorm_quantize_q8_1(px, pg, float(eps), pq, pr, rows, k,
+                                                                 _stream(stream)))
+    return xq if r is None else (xq, r)
 
 
 def _mmq(fmt, w, aq, m, n, k, c, stream):

@@ -117,6 +117,19 @@ QG_EXPORT qg_status quantize_q8_1(const float *x, void *xq, int64_t rows, int64_
   return launched(qg::launch_quantize_q8_1(x, xq, rows, k, stream));
 }
 
+QG_EXPORT qg_status rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *xq, float *r_out,
+                                          int64_t rows, int64_t k, hipStream_t stream) {
+  if (!x || !gamma || !xq) return QG_ERR_NULL;
+  if (rows < 0 || k < 0 || k % 32 != 0 || k > kMaxK || rows > kMaxRows) return QG_ERR_SHAPE;
+  if (!(eps >= 0.f) || !__builtin_isfinite(eps)) return QG_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(xq, 16) || (r_out && !aligned(r_out, 4)))
+    return QG_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QG_OK;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_rmsnorm_quantize_q8_1(x, gamma, eps, xq, r_out, rows, k, stream));
+}
+
 QG_EXPORT qg_status qgemv_q8_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
   qg_status st = check_gemv(0, w, xq, y, n, k);
   return st != QG_OK ? st : run_gemv(0, w, xq, y, nullptr, nullptr, n, k, stream);

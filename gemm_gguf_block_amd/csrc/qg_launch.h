@@ -38,6 +38,11 @@ hipError_t launch_quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t 
 hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_t *D, int32_t *S, int64_t n,
                         int64_t k, hipStream_t stream);
 
+// f32 rows -> Q8_1 of x * r * gamma, r = 1 / sqrt(mean(x^2) + eps) per row
+// (r_out nullable).
+hipError_t launch_rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *xq, float *r_out,
+                                        int64_t rows, int64_t k, hipStream_t stream);
+
 // Small-batch GEMV: nb (1..8) Q8_1 rows [nb][k/32] against the weights; y is [nb][n].
 hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
                               hipStream_t stream);

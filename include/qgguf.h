@@ -110,6 +110,19 @@ qg_status qgemv_q6_k_batch(const void *w, const void *xq, float *y, int64_t b, i
                            hipStream_t stream);
 
 /*
+ * rmsnorm_quantize_q8_1 -- the activation prologue of a projection in the
+ * model families the infr page runs ("models": Llama, Qwen, Gemma): per row,
+ *   r = 1 / sqrt(sum(x^2) / k + eps)     (fp32; the sum in a fixed order)
+ *   xq = Q8_1((x * r) * gamma)           (fp32 products, then quantize_q8_1's rule)
+ *   x     : f32 [rows][k];  gamma : f32 [k];  both 16-byte aligned
+ *   xq    : Q8_1 [rows][k/32], written;  r_out : f32 [rows] or NULL
+ *   k     : multiple of 32, <= 2^24;  eps >= 0 and finite
+ * rows = 0 or k = 0 writes nothing.
+ */
+qg_status rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *xq, float *r_out,
+                                int64_t rows, int64_t k, hipStream_t stream);
+
+/*
  * qgemm_q4_k_mmq -- prefill product on int8 matrix cores.
  * c[i][r] = sum_j a^[i][j] * w^[r][j]: each 32-wide slice of k is one int8
  * 32x32x32 MFMA tile of exact per-block dots, rescaled in fp32 by d*sc_j*d_a

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemm_q4_k_mmq",
-                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq",
+                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "rmsnorm_quantize_q8_1",
                  "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
         assert want in names
@@ -193,3 +193,20 @@ def test_no_device_status_without_a_gpu():
                        env=dict(os.environ, HIP_VISIBLE_DEVICES=os.environ.get("HIP_VISIBLE_DEVICES", "")))
     assert r.returncode == 0, r.stderr
     assert int(r.stdout.strip().splitlines()[-1]) == NO_DEVICE
+
+
+def test_rmsnorm_quantize_validation(lib):
+    f = lib.rmsnorm_quantize_q8_1
+    f.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_int64, ctypes.c_int64, P]
+    xq = P((1 << 20) + 8192)
+    assert f(None, A16b, 1e-5, xq, None, 2, 64, None) == NULL
+    assert f(A16, None, 1e-5, xq, None, 2, 64, None) == NULL
+    assert f(A16, A16b, 1e-5, None, None, 2, 64, None) == NULL
+    assert f(A16, A16b, 1e-5, xq, None, 2, 48, None) == SHAPE
+    assert f(A16, A16b, 1e-5, xq, None, -1, 64, None) == SHAPE
+    assert f(A16, A16b, -1.0, xq, None, 2, 64, None) == SHAPE
+    assert f(A16, A16b, float("nan"), xq, None, 2, 64, None) == SHAPE
+    assert f(MIS, A16b, 1e-5, xq, None, 2, 64, None) == ALIGN
+    assert f(A16, A16b, 1e-5, xq, P((1 << 20) + 2), 2, 64, None) == ALIGN
+    assert f(A16, A16b, 1e-5, xq, None, 0, 64, None) == OK
+    assert f(A16, A16b, 1e-5, xq, None, 2, 0, None) == OK

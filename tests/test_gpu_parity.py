@@ -391,6 +391,44 @@ def test_mmq_full_size(env):
     assert np.array_equal(_host(D), orc.blockdots_q4_k_mmq(w[:96], aq[:80], 80, 96, k))
 
 
+# ------------------------------------------------- activation prologue fusion
+def _gamma(k, seed):
+    return (1.0 + 0.25 * synth.normal(seed, 5, (k,))).astype(np.float32)
+
+
+def _check_rmsnorm_stagewise(orc, x, gamma, eps, xq_gpu, r_gpu):
+    """r within 1e-6 of the double oracle; the bytes exactly the oracle's
+    quantization of (x * r) * gamma formed in fp32 from the GPU's own r."""
+    r_ref = orc.rms_scale(x, eps)
+    assert np.max(np.abs(r_gpu.astype(np.float64) - r_ref) / r_ref) <= 1e-6
+    v = (x * r_gpu[:, None].astype(np.float32)) * gamma[None, :]
+    assert v.dtype == np.float32
+    assert np.array_equal(xq_gpu, orc.quantize_q8_1(v))
+
+
+@pytest.mark.parametrize("rows,k,std", [(1, 32, 1.0), (3, 4096, 1.0), (2, 14336, 1e-3), (5, 768, 30.0),
+                                        (2, 33536, 1.0)])
+def test_rmsnorm_quantize_stagewise(env, rows, k, std):
+    qg, orc, torch, dev = env
+    x = synth.normal(rows + k, 4, (rows, k), std=std)
+    gamma = _gamma(k, k)
+    r = torch.empty(rows, device=dev)
+    XQ, r = qg.rmsnorm_quantize_q8_1(_gpu(torch, dev, x), _gpu(torch, dev, gamma), 1e-5, r=r)
+    _check_rmsnorm_stagewise(orc, x, gamma, 1e-5, _host(XQ), _host(r))
+
+
+def test_rmsnorm_quantize_zero_row(env):
+    """An all-zero row gives r = 1/sqrt(eps) and all-zero blocks."""
+    qg, orc, torch, dev = env
+    x = np.zeros((2, 256), np.float32)
+    x[1] = synth.normal(3, 4, (256,))
+    gamma = _gamma(256, 9)
+    r = torch.empty(2, device=dev)
+    XQ, r = qg.rmsnorm_quantize_q8_1(_gpu(torch, dev, x), _gpu(torch, dev, gamma), 1e-4, r=r)
+    _check_rmsnorm_stagewise(orc, x, gamma, 1e-4, _host(XQ), _host(r))
+    assert np.all(_host(XQ)[0] == 0)
+
+
 # ------------------------------------------- mmq with the other weight types
 MMQ_SHAPES = [(1, 1, 256), (32, 32, 256), (70, 100, 512), (130, 65, 768), (3, 200, 1024), (64, 128, 2048)]
 # Q8_0 rows need k % 32 only: a ragged last 256-wide step
@@ -586,8 +624,12 @@ def test_graph_replay_matches_eager(env):
     c8 = torch.empty((m, n), device=dev)
     out = torch.empty((T, H), device=dev)
     ws = torch.empty(qg.moe_qgemv_q4_k_workspace_size(T, K, E, F, H), dtype=torch.uint8, device=dev)
+    gam = _gpu(torch, dev, _gamma(k, 96))
+    xnq = torch.empty((5, k // 32 * 36), dtype=torch.uint8, device=dev)
+    rr = torch.empty(5, device=dev)
 
     def work():
+        qg.rmsnorm_quantize_q8_1(xb, gam, 1e-5, xq=xnq, r=rr)
         qg.quantize_q8_1(x, xq)
         for f, W in Ws.items():
             getattr(qg, GEMV[f])(W, xq, n, k, y=ys[f])
@@ -603,7 +645,7 @@ def test_graph_replay_matches_eager(env):
 
     def snapshot():
         torch.cuda.synchronize()
-        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out)]
+        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr)]
 
     work()
     eager = snapshot()
@@ -617,7 +659,7 @@ def test_graph_replay_matches_eager(env):
             work()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out):
+        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr):
             t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
