@@ -16,6 +16,7 @@ types -- blazr README, "Model Formats > GGUF" -- but give no layout):
   scale = (hi-lo)/15, min = -lo; d = max(scale)/63, dmin = max(min)/63;
   6-bit sc = round(scale/d), m = round(min/dmin); q = round((w + dmin*m)/(d*sc))
   clamped to [0, 15], using the fp16-rounded d and dmin.
+* Q5_K: as Q4_K with 32 levels: scale = (hi-lo)/31, q clamped to [0, 31].
 * Q6_K: per 16-value sub-block, scale = amax/31; d = max(scale)/127;
   int8 sc = round(scale/d); q = round(w/(d*sc)) + 32 clamped to [0, 63].
 
@@ -27,9 +28,9 @@ from __future__ import annotations
 
 import numpy as np
 
-Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES = 34, 36, 144, 210
-BLOCK_BYTES = {"q8_0": Q8_0_BYTES, "q8_1": Q8_1_BYTES, "q4_k": Q4_K_BYTES, "q6_k": Q6_K_BYTES}
-BLOCK_ELEMS = {"q8_0": 32, "q8_1": 32, "q4_k": 256, "q6_k": 256}
+Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES, Q5_K_BYTES = 34, 36, 144, 210, 176
+BLOCK_BYTES = {"q8_0": Q8_0_BYTES, "q8_1": Q8_1_BYTES, "q4_k": Q4_K_BYTES, "q6_k": Q6_K_BYTES, "q5_k": Q5_K_BYTES}
+BLOCK_ELEMS = {"q8_0": 32, "q8_1": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256}
 
 # tensor ids within a workload seed
 T_W, T_X, T_ROUTE, T_WDOWN = 0, 1, 2, 3
@@ -158,6 +159,47 @@ def quantize_weights_q4_k(W: np.ndarray) -> np.ndarray:
     return _rows_in_chunks(W, conv, row_bytes("q4_k", k))
 
 
+def pack_q5_k(d16: np.ndarray, dmin16: np.ndarray, sc: np.ndarray, m: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q5_K fields into 176-byte superblocks: Q4_K's 16-byte header, then
+    qh[32] (bit j of qh[l] = fifth bit of element 32j + l), then the low
+    nibbles packed as Q4_K's qs.  q: 5-bit codes [B][256] in element order."""
+    q = q.astype(np.int32)
+    p4 = pack_q4_k(d16, dmin16, sc, m, q & 15)
+    B = q.shape[0]
+    hb = ((q >> 4) & 1).reshape(B, 8, 32).astype(np.uint8)  # [sub-block j][l]
+    qh = np.zeros((B, 32), np.uint8)
+    for j in range(8):
+        qh |= hb[:, j, :] << j
+    blk = np.empty((B, Q5_K_BYTES), np.uint8)
+    blk[:, 0:16] = p4[:, 0:16]
+    blk[:, 16:48] = qh
+    blk[:, 48:] = p4[:, 16:]
+    return blk
+
+
+def quantize_weights_q5_k(W: np.ndarray) -> np.ndarray:
+    n, k = W.shape
+    assert k % 256 == 0
+
+    def conv(X):
+        X = X.reshape(-1, 8, 32)
+        lo = np.minimum(X.min(axis=2), 0)
+        hi = X.max(axis=2)
+        scale = (hi - lo) / np.float32(31)
+        minv = -lo
+        d = scale.max(axis=1) / np.float32(63)
+        dmin = minv.max(axis=1) / np.float32(63)
+        sc = np.clip(_round_away(_div(scale, d[:, None])), 0, 63)
+        m = np.clip(_round_away(_div(minv, dmin[:, None])), 0, 63)
+        eff = _f16_val(d)[:, None] * sc
+        mm = _f16_val(dmin)[:, None] * m
+        q = np.clip(_round_away(_div(X + mm[:, :, None], eff[:, :, None])), 0, 31)
+        return pack_q5_k(d.astype(np.float16).view(np.uint16), dmin.astype(np.float16).view(np.uint16),
+                         sc.astype(np.int32), m.astype(np.int32), q.reshape(-1, 256).astype(np.int32))
+
+    return _rows_in_chunks(W, conv, row_bytes("q5_k", k))
+
+
 def pack_q6_k(d16: np.ndarray, sc: np.ndarray, q: np.ndarray) -> np.ndarray:
     """Pack Q6_K fields into 210-byte superblocks.
 
@@ -196,7 +238,8 @@ def quantize_weights_q6_k(W: np.ndarray) -> np.ndarray:
     return _rows_in_chunks(W, conv, row_bytes("q6_k", k))
 
 
-QUANTIZE_WEIGHTS = {"q8_0": quantize_weights_q8_0, "q4_k": quantize_weights_q4_k, "q6_k": quantize_weights_q6_k}
+QUANTIZE_WEIGHTS = {"q8_0": quantize_weights_q8_0, "q4_k": quantize_weights_q4_k, "q6_k": quantize_weights_q6_k,
+                    "q5_k": quantize_weights_q5_k}
 
 
 def weights(fmt: str, n: int, k: int, seed: int, tensor: int = T_W, std: float = 0.02,
@@ -246,7 +289,7 @@ def random_blocks(fmt: str, rows: int, k: int, seed: int, tensor: int = T_W,
     g = rng(seed, tensor)
     nb = k // BLOCK_ELEMS[fmt]
     blk = g.integers(0, 256, (rows * nb, BLOCK_BYTES[fmt]), dtype=np.uint8)
-    offs = {"q8_0": [0], "q8_1": [0, 2], "q4_k": [0, 2], "q6_k": [208]}[fmt]
+    offs = {"q8_0": [0], "q8_1": [0, 2], "q4_k": [0, 2], "q6_k": [208], "q5_k": [0, 2]}[fmt]
     for o in offs:
         bits = random_f16_bits(g, rows * nb, lo_exp, hi_exp)
         blk[:, o:o + 2] = bits.view(np.uint8).reshape(-1, 2)

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES = 34, 36, 144, 210
+Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES, Q5_K_BYTES = 34, 36, 144, 210, 176
 
 
 def build() -> str:
@@ -61,16 +61,20 @@ def _declare(L):
         "orc_quantize_q8_1": [_P, _P, _I, _I],
         "orc_rms_scale": [_P, _P, _I, _I, ctypes.c_double],
         "orc_unpack_q4_k": [_P, _P, _P, _P, _P, _P],
+        "orc_unpack_q5_k": [_P, _P, _P, _P, _P, _P],
         "orc_unpack_q6_k": [_P, _P, _P, _P],
         "orc_dequant_q8_0": [_P, _P, _I, _I],
         "orc_dequant_q8_1": [_P, _P, _I, _I],
         "orc_dequant_q4_k": [_P, _P, _I, _I],
+        "orc_dequant_q5_k": [_P, _P, _I, _I],
         "orc_dequant_q6_k": [_P, _P, _I, _I],
         "orc_qgemv_q8_0": [_P, _P, _P, _I, _I, _P, _I],
         "orc_qgemv_q4_k": [_P, _P, _P, _I, _I, _P, _I],
+        "orc_qgemv_q5_k": [_P, _P, _P, _I, _I, _P, _I],
         "orc_qgemv_q6_k": [_P, _P, _P, _I, _I, _P, _I],
         "orc_blockdots_q8_0": [_P, _P, _P, _I, _I],
         "orc_blockdots_q4_k": [_P, _P, _P, _P, _I, _I],
+        "orc_blockdots_q5_k": [_P, _P, _P, _P, _I, _I],
         "orc_blockdots_q6_k": [_P, _P, _P, _I, _I],
         "orc_qgemv_factored": [ctypes.c_int, _P, _P, _P, _I, _I],
         "orc_qgemm_q4_k": [_P, _P, _P, _I, _I, _I, _P, _I],
@@ -144,6 +148,18 @@ def unpack_q4_k(block):
     return float(d[0]), float(dmin[0]), sc, m, q
 
 
+def unpack_q5_k(block):
+    """(d, dmin, sc[8], m[8], q[256]) of one Q5_K superblock, q in 0..31."""
+    block = _c(block, np.uint8)
+    d = np.zeros(1, np.float32)
+    dmin = np.zeros(1, np.float32)
+    sc = np.zeros(8, np.int32)
+    m = np.zeros(8, np.int32)
+    q = np.zeros(256, np.int32)
+    lib().orc_unpack_q5_k(_ptr(block), _ptr(d), _ptr(dmin), _ptr(sc), _ptr(m), _ptr(q))
+    return float(d[0]), float(dmin[0]), sc, m, q
+
+
 def unpack_q6_k(block):
     block = _c(block, np.uint8)
     d = np.zeros(1, np.float32)
@@ -154,7 +170,7 @@ def unpack_q6_k(block):
 
 
 def dequant(fmt, w, rows, k):
-    """Dequantize `rows` rows of format fmt ('q8_0','q8_1','q4_k','q6_k') to f64."""
+    """Dequantize `rows` rows of format fmt ('q8_0','q8_1','q4_k','q5_k','q6_k') to f64."""
     w = _c(w, np.uint8)
     out = np.empty((rows, k), np.float64)
     getattr(lib(), "orc_dequant_" + fmt)(_ptr(w), _ptr(out), rows, k)
@@ -175,7 +191,7 @@ def qgemv(fmt, w, xq, n, k, rows=None):
 
 
 def blockdots(fmt, w, xq, n, k):
-    """Per-block int32 dots.  q8_0: D[n][k/32]; q4_k: (D[n][k/32], S[k/32]);
+    """Per-block int32 dots.  q8_0: D[n][k/32]; q4_k, q5_k: (D[n][k/32], S[k/32]);
     q6_k: D[n][k/16]."""
     w = _c(w, np.uint8)
     xq = _c(xq, np.uint8)
@@ -183,10 +199,10 @@ def blockdots(fmt, w, xq, n, k):
         D = np.empty((n, k // 32), np.int32)
         lib().orc_blockdots_q8_0(_ptr(w), _ptr(xq), _ptr(D), n, k)
         return D
-    if fmt == "q4_k":
+    if fmt in ("q4_k", "q5_k"):
         D = np.empty((n, k // 32), np.int32)
         S = np.empty(k // 32, np.int32)
-        lib().orc_blockdots_q4_k(_ptr(w), _ptr(xq), _ptr(D), _ptr(S), n, k)
+        getattr(lib(), "orc_blockdots_" + fmt)(_ptr(w), _ptr(xq), _ptr(D), _ptr(S), n, k)
         return D, S
     if fmt == "q6_k":
         D = np.empty((n, k // 16), np.int32)
@@ -199,7 +215,7 @@ def qgemv_factored(fmt, w, xq, n, k):
     w = _c(w, np.uint8)
     xq = _c(xq, np.uint8)
     y = np.empty(n, np.float64)
-    lib().orc_qgemv_factored({"q8_0": 0, "q4_k": 1, "q6_k": 2}[fmt], _ptr(w), _ptr(xq), _ptr(y), n, k)
+    lib().orc_qgemv_factored({"q8_0": 0, "q4_k": 1, "q6_k": 2, "q5_k": 3}[fmt], _ptr(w), _ptr(xq), _ptr(y), n, k)
     return y
 
 

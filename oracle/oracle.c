@@ -6,14 +6,17 @@
  *
  * What the pages fix and what they leave open:
  *   - blazr README, "Model Formats > GGUF": the types with dedicated GPU dot
- *     kernels are Q4_K, Q6_K and Q8_0; the pages give no byte layout.
+ *     kernels are Q4_K, Q6_K and Q8_0, the other GGUF types run on a generic
+ *     path; the pages give no byte layout.  Q5_K is one of those others.
  *   - infr page, "Vulkan-first, Metal too": GPU output is checked against a
  *     CPU reference backend -- the role this file plays.
  *   - Block layouts and dequant formulas are GGUF's published ones (the pages
  *     are silent): Q8_0 = fp16 d + 32 int8; Q8_1 = fp16 d + fp16 s + 32 int8;
  *     Q4_K = fp16 d, fp16 dmin, 12 bytes of packed 6-bit scales/mins, 128
  *     bytes of nibbles (w = d*sc*q - dmin*m); Q6_K = 128 bytes low nibbles,
- *     64 bytes high 2-bit pairs, 16 int8 scales, fp16 d (w = d*sc*(q-32)).
+ *     64 bytes high 2-bit pairs, 16 int8 scales, fp16 d (w = d*sc*(q-32));
+ *     Q5_K = Q4_K's header, 32 bytes of fifth bits, 128 bytes of nibbles
+ *     (w = d*sc*q - dmin*m with q in 0..31).
  *
  * Everything is computed in double from the stored fields.  The dequantizers
  * and the integer block-dot routines decode the fields independently of each
@@ -30,6 +33,7 @@
 #define B_Q8_1 36
 #define B_Q4_K 144
 #define B_Q6_K 210
+#define B_Q5_K 176
 
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format definition.       */
@@ -187,6 +191,29 @@ void orc_unpack_q4_k(const uint8_t *blk, float *d, float *dmin, int32_t *sc, int
     }
 }
 
+/* Decode one Q5_K superblock: fp16 d, fp16 dmin, the 12 scale bytes packed as
+ * Q4_K's, qh[32], qs[128].  Element i (sub-block j = i/32) takes its low four
+ * bits from qs by Q4_K's rule and its fifth bit from bit j of qh[i % 32]:
+ * q[i] in 0..31. */
+void orc_unpack_q5_k(const uint8_t *blk, float *d, float *dmin, int32_t *sc, int32_t *m, int32_t *q)
+{
+    *d = orc_f16_to_f32(rd16(blk));
+    *dmin = orc_f16_to_f32(rd16(blk + 2));
+    for (int j = 0; j < 8; ++j) {
+        int a, b;
+        q4k_scale_min(blk + 4, j, &a, &b);
+        sc[j] = a;
+        m[j] = b;
+    }
+    const uint8_t *qh = blk + 16, *qs = blk + 48;
+    for (int i = 0; i < QKK; ++i) {
+        int g = i / 64, r = i % 64, j = i / 32;
+        uint8_t byte = qs[32 * g + (r % 32)];
+        int nib = (r < 32) ? (byte & 0x0f) : (byte >> 4);
+        q[i] = nib | (((qh[i % 32] >> j) & 1) << 4);
+    }
+}
+
 /* Decode one Q6_K superblock.  q[i] is element i's 6-bit code (0..63). */
 void orc_unpack_q6_k(const uint8_t *blk, float *d, int32_t *sc, int32_t *q)
 {
@@ -244,6 +271,22 @@ void orc_dequant_q4_k(const uint8_t *w, double *out, int64_t rows, int64_t k)
             float d, dmin;
             int32_t sc[8], m[8], q[QKK];
             orc_unpack_q4_k(blk, &d, &dmin, sc, m, q);
+            for (int i = 0; i < QKK; ++i) {
+                int j = i / 32;
+                out[r * k + s * QKK + i] = (double)d * sc[j] * q[i] - (double)dmin * m[j];
+            }
+        }
+}
+
+void orc_dequant_q5_k(const uint8_t *w, double *out, int64_t rows, int64_t k)
+{
+    int64_t ns = k / QKK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t s = 0; s < ns; ++s) {
+            const uint8_t *blk = w + (r * ns + s) * B_Q5_K;
+            float d, dmin;
+            int32_t sc[8], m[8], q[QKK];
+            orc_unpack_q5_k(blk, &d, &dmin, sc, m, q);
             for (int i = 0; i < QKK; ++i) {
                 int j = i / 32;
                 out[r * k + s * QKK + i] = (double)d * sc[j] * q[i] - (double)dmin * m[j];
@@ -309,6 +352,12 @@ void orc_qgemv_q4_k(const uint8_t *w, const uint8_t *xq, double *y, int64_t n, i
     gemv_plain(orc_dequant_q4_k, (k / QKK) * B_Q4_K, w, xq, y, n, k, sel, nsel);
 }
 
+void orc_qgemv_q5_k(const uint8_t *w, const uint8_t *xq, double *y, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    gemv_plain(orc_dequant_q5_k, (k / QKK) * B_Q5_K, w, xq, y, n, k, sel, nsel);
+}
+
 void orc_qgemv_q6_k(const uint8_t *w, const uint8_t *xq, double *y, int64_t n, int64_t k,
                     const int64_t *sel, int64_t nsel)
 {
@@ -367,6 +416,36 @@ void orc_blockdots_q4_k(const uint8_t *w, const uint8_t *xq, int32_t *D, int32_t
         }
 }
 
+/* Q5_K: as Q4_K with the 5-bit code: D[n][8s+j] = sum_{i<32} q[i] * qa[i],
+ * q = nibble | (bit j of qh[i]) << 4; S[b] = sum of qa over activation block b. */
+void orc_blockdots_q5_k(const uint8_t *w, const uint8_t *xq, int32_t *D, int32_t *S, int64_t n, int64_t k)
+{
+    int64_t ns = k / QKK, nb = k / QK;
+    for (int64_t b = 0; b < nb; ++b) {
+        const int8_t *qa = (const int8_t *)(xq + b * B_Q8_1 + 4);
+        int32_t acc = 0;
+        for (int i = 0; i < QK; ++i)
+            acc += qa[i];
+        S[b] = acc;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t s = 0; s < ns; ++s) {
+            const uint8_t *blk = w + (r * ns + s) * B_Q5_K;
+            const uint8_t *qh = blk + 16, *qs = blk + 48;
+            for (int j = 0; j < 8; ++j) {
+                const int8_t *qa = (const int8_t *)(xq + (s * 8 + j) * B_Q8_1 + 4);
+                int32_t acc = 0;
+                for (int i = 0; i < QK; ++i) {
+                    uint8_t byte = qs[32 * (j / 2) + i];
+                    int q = ((j % 2 == 0) ? (byte & 15) : (byte >> 4)) | (((qh[i] >> j) & 1) << 4);
+                    acc += q * qa[i];
+                }
+                D[r * nb + s * 8 + j] = acc;
+            }
+        }
+}
+
 /* Q6_K: D[n][16s+j] = sum_{i<16} (q[i]-32) * qa over 16-element sub-block j of
  * superblock s; its activation is half (j%2) of Q8_1 block 8s + j/2. */
 void orc_blockdots_q6_k(const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t n, int64_t k)
@@ -394,8 +473,8 @@ void orc_blockdots_q6_k(const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t
 }
 
 /* GEMV from the integer dots, factored per block:
- *   Q8_0: sum_b dw*da*D;   Q4_K: sum_{s,j} da*(d*sc_j*D - dmin*m_j*S);
- *   Q6_K: sum_{s,j} d*sc_j*da*D.
+ *   Q8_0: sum_b dw*da*D;   Q4_K, Q5_K: sum_{s,j} da*(d*sc_j*D - dmin*m_j*S);
+ *   Q6_K: sum_{s,j} d*sc_j*da*D.   fmt: 0 Q8_0, 1 Q4_K, 2 Q6_K, 3 Q5_K.
  * Exactly equal (up to double rounding) to the plain definition. */
 void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y, int64_t n, int64_t k)
 {
@@ -406,6 +485,8 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
         orc_blockdots_q8_0(w, xq, D, n, k);
     else if (fmt == 1)
         orc_blockdots_q4_k(w, xq, D, S, n, k);
+    else if (fmt == 3)
+        orc_blockdots_q5_k(w, xq, D, S, n, k);
     else
         orc_blockdots_q6_k(w, xq, D, n, k);
     for (int64_t r = 0; r < n; ++r) {
@@ -413,9 +494,9 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
         if (fmt == 0) {
             for (int64_t b = 0; b < nb; ++b)
                 acc += h2d(w + (r * nb + b) * B_Q8_0) * h2d(xq + b * B_Q8_1) * D[r * nb + b];
-        } else if (fmt == 1) {
+        } else if (fmt == 1 || fmt == 3) {
             for (int64_t s = 0; s < ns; ++s) {
-                const uint8_t *blk = w + (r * ns + s) * B_Q4_K;
+                const uint8_t *blk = w + (r * ns + s) * (fmt == 1 ? B_Q4_K : B_Q5_K);
                 double d = h2d(blk), dmin = h2d(blk + 2);
                 for (int j = 0; j < 8; ++j) {
                     int sc, m;

@@ -131,6 +131,19 @@ def test_q4_k_hand_block_fields_and_values(orc):
     assert [Fraction(v) for v in w] == want
 
 
+def test_q5_k_hand_block_fields_and_values(orc):
+    fx, blk = _fixture_block("q5_k_superblock.txt")
+    assert blk.size == 176
+    d, dmin, sc, m, q = orc.unpack_q5_k(blk)
+    assert d == 2.0 ** -4 and dmin == 2.0 ** -5
+    assert np.array_equal(sc, _ints(fx["sc"][0])) and np.array_equal(m, _ints(fx["m"][0]))
+    assert np.array_equal(q, _ints(fx["q"][0]))
+    w = orc.dequant("q5_k", blk, 1, 256)[0]
+    qq, scc, mm = _ints(fx["q"][0]), _ints(fx["sc"][0]), _ints(fx["m"][0])
+    want = [Fraction(1, 16) * scc[i // 32] * qq[i] - Fraction(1, 32) * mm[i // 32] for i in range(256)]
+    assert [Fraction(v) for v in w] == want
+
+
 def test_q6_k_hand_block_fields_and_values(orc):
     fx, blk = _fixture_block("q6_k_superblock.txt")
     assert blk.size == 210
@@ -171,6 +184,24 @@ def test_q4_k_pack_unpack_bijection(orc):
         assert np.array_equal(s2, sc[i]) and np.array_equal(m2, mn[i]) and np.array_equal(q2, qq[i])
 
 
+def test_q5_k_pack_unpack_bijection(orc):
+    g = np.random.default_rng(5)
+    raw = g.integers(0, 256, (200, 176), dtype=np.uint8)
+    for blk in raw:
+        d, dmin, sc, m, q = orc.unpack_q5_k(blk)
+        re = synth.pack_q5_k(blk[0:2].copy().view(np.uint16), blk[2:4].copy().view(np.uint16),
+                             sc[None], m[None], q[None])[0]
+        assert np.array_equal(re, blk)
+    sc = g.integers(0, 64, (50, 8))
+    mn = g.integers(0, 64, (50, 8))
+    qq = g.integers(0, 32, (50, 256))
+    blks = synth.pack_q5_k(np.full(50, 0x3C00, np.uint16), np.full(50, 0x3800, np.uint16), sc, mn, qq)
+    for i in range(50):
+        d, dmin, s2, m2, q2 = orc.unpack_q5_k(blks[i])
+        assert (d, dmin) == (1.0, 0.5)
+        assert np.array_equal(s2, sc[i]) and np.array_equal(m2, mn[i]) and np.array_equal(q2, qq[i])
+
+
 def test_q6_k_pack_unpack_bijection(orc):
     g = np.random.default_rng(4)
     raw = g.integers(0, 256, (200, 210), dtype=np.uint8)
@@ -186,7 +217,7 @@ def _select_rows(n, k):
     return np.array([(r * 37) % k for r in range(n)])
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 def test_selection_matrix_gives_activation_entries(orc, fmt):
     """Weights that dequantize to one-hot rows must return exactly the selected
     dequantized activation entries: catches transposed operands, wrong block or
@@ -208,6 +239,16 @@ def test_selection_matrix_gives_activation_entries(orc, fmt):
             q[r * ns + c // 256, c % 256] = 1
         w = synth.pack_q4_k(np.full(n * ns, 0x3C00, np.uint16), np.zeros(n * ns, np.uint16), sc, mm, q)
         w = w.reshape(n, -1)
+    elif fmt == "q5_k":
+        # d = 1/16 and code 16: the selected weight is exactly 1 and needs the fifth bit
+        ns = k // 256
+        sc = np.ones((n * ns, 8), np.int64)
+        mm = np.zeros((n * ns, 8), np.int64)
+        q = np.zeros((n * ns, 256), np.int64)
+        for r, c in enumerate(cols):
+            q[r * ns + c // 256, c % 256] = 16
+        w = synth.pack_q5_k(np.full(n * ns, 0x2C00, np.uint16), np.zeros(n * ns, np.uint16), sc, mm, q)
+        w = w.reshape(n, -1)
     else:
         ns = k // 256
         sc = np.ones((n * ns, 16), np.int64)
@@ -224,7 +265,7 @@ def test_selection_matrix_gives_activation_entries(orc, fmt):
 
 
 # ---------------------------------------------- integer dots vs float dequant
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 def test_integer_block_dots_agree_with_dequant_dot(orc, fmt):
     """The factored sum over exact int32 block dots equals the plain double
     dequant-and-dot on fully random block bytes (finite fp16 fields)."""
@@ -237,7 +278,7 @@ def test_integer_block_dots_agree_with_dequant_dot(orc, fmt):
         assert np.max(np.abs(plain - fact)) <= 1e-12 * scale
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 def test_block_dots_brute_force_from_decoded_codes(orc, fmt):
     """Block dots from the oracle's blockdots routine vs numpy dots of the codes
     the (separately written) field decoder returns, on random bytes."""
@@ -250,10 +291,10 @@ def test_block_dots_brute_force_from_decoded_codes(orc, fmt):
         codes = w.reshape(n, -1, 34)[:, :, 2:].view(np.int8).astype(np.int64).reshape(n, k)
         want = (codes * qa[None]).reshape(n, -1, 32).sum(axis=2)
         assert np.array_equal(D, want)
-    elif fmt == "q4_k":
-        D, S = orc.blockdots("q4_k", w, xq, n, k)
-        codes = np.stack([np.concatenate([orc.unpack_q4_k(b)[4] for b in row.reshape(-1, 144)])
-                          for row in w])
+    elif fmt in ("q4_k", "q5_k"):
+        D, S = orc.blockdots(fmt, w, xq, n, k)
+        unpack, nbytes = (orc.unpack_q4_k, 144) if fmt == "q4_k" else (orc.unpack_q5_k, 176)
+        codes = np.stack([np.concatenate([unpack(b)[4] for b in row.reshape(-1, nbytes)]) for row in w])
         want = (codes * qa[None]).reshape(n, -1, 32).sum(axis=2)
         assert np.array_equal(D, want)
         assert np.array_equal(S, qa.reshape(-1, 32).sum(axis=1))
@@ -285,6 +326,13 @@ def test_hand_superblock_dot_exact(orc):
                 for i in range(256))
     assert Fraction(orc.qgemv("q4_k", blk[None], xq, 1, 256)[0]) == exact
     assert Fraction(orc.qgemv_factored("q4_k", blk[None], xq, 1, 256)[0]) == exact
+    # Q5_K
+    fx, blk = _fixture_block("q5_k_superblock.txt")
+    q, sc, m = _ints(fx["q"][0]), _ints(fx["sc"][0]), _ints(fx["m"][0])
+    exact = sum((Fraction(1, 16) * sc[i // 32] * q[i] - Fraction(1, 32) * m[i // 32]) * Fraction(1, 8) * qa[i]
+                for i in range(256))
+    assert Fraction(orc.qgemv("q5_k", blk[None], xq, 1, 256)[0]) == exact
+    assert Fraction(orc.qgemv_factored("q5_k", blk[None], xq, 1, 256)[0]) == exact
     # Q6_K
     fx, blk = _fixture_block("q6_k_superblock.txt")
     q, sc = _ints(fx["q"][0]), _ints(fx["scales"][0])
@@ -299,7 +347,7 @@ def test_hand_superblock_dot_exact(orc):
 
 
 # --------------------------------------------------- weight quantizers (data)
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 def test_weight_quantizer_roundtrip_bound(orc, fmt):
     g = np.random.default_rng(21)
     W = (g.standard_normal((64, 512)) * 0.02).astype(np.float32)
@@ -312,10 +360,11 @@ def test_weight_quantizer_roundtrip_bound(orc, fmt):
         d32 = np.abs(W.reshape(-1, 32)).max(axis=1).astype(np.float64) / 127
         bound = d32 / 2 * (1 + 1e-5) + 127 * np.abs(d32 - d16)
         assert np.all(err.reshape(-1, 32).max(axis=1) <= bound)
-    elif fmt == "q4_k":
+    elif fmt in ("q4_k", "q5_k"):
         effs = []
-        for b in wq.reshape(-1, 144):
-            d, dmin, sc, m, q = orc.unpack_q4_k(b)
+        unpack, nbytes = (orc.unpack_q4_k, 144) if fmt == "q4_k" else (orc.unpack_q5_k, 176)
+        for b in wq.reshape(-1, nbytes):
+            d, dmin, sc, m, q = unpack(b)
             effs.append(np.repeat(d * sc.astype(np.float64), 32))
         eff = np.concatenate(effs).reshape(64, 512)
         frac_bad = np.mean(err > eff / 2 * (1 + 1e-5) + 1e-9)
