@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgguf.so")
 
 Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES = 34, 36, 144, 210
-_BLOCK = {"q8_0": (32, Q8_0_BYTES), "q8_1": (32, Q8_1_BYTES), "q4_k": (256, Q4_K_BYTES), "q6_k": (256, Q6_K_BYTES)}
+_BLOCK = {"q8_0": (32, Q8_0_BYTES), "q8_1": (32, Q8_1_BYTES), "q4_k": (256, Q4_K_BYTES), "q6_k": (256, Q6_K_BYTES),
+          "q5_k": (256, 176)}
 
 STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_ALIGN", 4: "QG_ERR_WORKSPACE",
           5: "QG_ERR_NO_DEVICE", 6: "QG_ERR_ARCH", 7: "QG_ERR_LAUNCH"}
@@ -30,6 +31,7 @@ SIGNATURES = {
     "qgemv_q8_0": [_P, _P, _P, _I, _I, _P],
     "qgemv_q4_k": [_P, _P, _P, _I, _I, _P],
     "qgemv_q6_k": [_P, _P, _P, _I, _I, _P],
+    "qgemv_q5_k": [_P, _P, _P, _I, _I, _P],
     "rmsnorm_quantize_q8_1": [_P, _P, ctypes.c_float, _P, _P, _I, _I, _P],
     "qgemv_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
@@ -42,6 +44,7 @@ SIGNATURES = {
     "qg_status_str": [ctypes.c_int],
     "qg_blockdots_q8_0": [_P, _P, _P, _I, _I, _P],
     "qg_blockdots_q4_k": [_P, _P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q5_k": [_P, _P, _P, _P, _I, _I, _P],
     "qg_blockdots_q6_k": [_P, _P, _P, _I, _I, _P],
     "qg_blockdots_q8_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
@@ -148,6 +151,10 @@ def qgemv_q4_k(w, xq, n, k, y=None, stream=None):
 
 def qgemv_q6_k(w, xq, n, k, y=None, stream=None):
     return _gemv("q6_k", w, xq, n, k, y, stream)
+
+
+def qgemv_q5_k(w, xq, n, k, y=None, stream=None):
+    return _gemv("q5_k", w, xq, n, k, y, stream)
 
 
 def _gemv_batch(fmt, w, xq, b, n, k, y, stream):
@@ -268,15 +275,24 @@ def blockdots_q8_0(w, xq, n, k, stream=None):
     return D
 
 
-def blockdots_q4_k(w, xq, n, k, stream=None):
+def _blockdots_kmin(fmt, w, xq, n, k, stream):
     import torch
     D = _empty((n, k // 32), torch.int32, w)
     S = _empty((k // 32,), torch.int32, w)
-    _check("qg_blockdots_q4_k", lib().qg_blockdots_q4_k(
-        _need(w, torch.uint8, n * row_bytes("q4_k", k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
+    name = f"qg_blockdots_{fmt}"
+    _check(name, getattr(lib(), name)(
+        _need(w, torch.uint8, n * row_bytes(fmt, k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
         _need(D, torch.int32, D.numel() * 4, "D"), _need(S, torch.int32, S.numel() * 4, "S"), n, k,
         _stream(stream)))
     return D, S
+
+
+def blockdots_q4_k(w, xq, n, k, stream=None):
+    return _blockdots_kmin("q4_k", w, xq, n, k, stream)
+
+
+def blockdots_q5_k(w, xq, n, k, stream=None):
+    return _blockdots_kmin("q5_k", w, xq, n, k, stream)
 
 
 def blockdots_q6_k(w, xq, n, k, stream=None):

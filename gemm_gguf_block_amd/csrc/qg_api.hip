@@ -43,7 +43,7 @@ qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_LAUNC
 constexpr int64_t kMaxK = int64_t(1) << 24;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
-// fmt 0 = Q8_0 (k % 32), 1 = Q4_K, 2 = Q6_K (k % 256)
+// fmt 0 = Q8_0 (k % 32), 1 = Q4_K, 2 = Q6_K, 3 = Q5_K (k % 256)
 qg_status check_gemv(int fmt, const void *w, const void *xq, const void *out, int64_t n, int64_t k) {
   if (!w || !xq || !out) return QG_ERR_NULL;
   if (n < 0 || k < 0 || n > kMaxRows || k > kMaxK) return QG_ERR_SHAPE;
@@ -145,6 +145,11 @@ QG_EXPORT qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t 
   return st != QG_OK ? st : run_gemv(2, w, xq, y, nullptr, nullptr, n, k, stream);
 }
 
+QG_EXPORT qg_status qgemv_q5_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv(3, w, xq, y, n, k);
+  return st != QG_OK ? st : run_gemv(3, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
 QG_EXPORT qg_status qgemv_q8_0_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
                                      hipStream_t stream) {
   return run_gemv_batch(0, w, xq, y, b, n, k, stream);
@@ -243,6 +248,14 @@ QG_EXPORT qg_status qg_blockdots_q4_k(const void *w, const void *xq, int32_t *D,
   if (!aligned(S, 4)) return QG_ERR_ALIGN;
   qg_status st = check_gemv(1, w, xq, D, n, k);
   return st != QG_OK ? st : run_gemv(1, w, xq, nullptr, D, S, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q5_k(const void *w, const void *xq, int32_t *D, int32_t *S, int64_t n, int64_t k,
+                                      hipStream_t stream) {
+  if (!S) return QG_ERR_NULL;
+  if (!aligned(S, 4)) return QG_ERR_ALIGN;
+  qg_status st = check_gemv(3, w, xq, D, n, k);
+  return st != QG_OK ? st : run_gemv(3, w, xq, nullptr, D, S, n, k, stream);
 }
 
 QG_EXPORT qg_status qg_blockdots_q6_k(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k,

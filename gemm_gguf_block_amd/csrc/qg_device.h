@@ -6,6 +6,7 @@
 //   Q8_1 36 B = fp16 d | fp16 s | int8 qs[32]     (qs is dword-aligned in a block)
 //   Q4_K 144 B = fp16 d | fp16 dmin | scales[12] | qs[128]   (9 x 16 B, aligned)
 //   Q6_K 210 B = ql[128] | qh[64] | int8 scales[16] | fp16 d
+//   Q5_K 176 B = fp16 d | fp16 dmin | scales[12] | qh[32] | qs[128]  (11 x 16 B, aligned)
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,6 +17,7 @@ constexpr int kQ8_0Bytes = 34;
 constexpr int kQ8_1Bytes = 36;
 constexpr int kQ4KBytes = 144;
 constexpr int kQ6KBytes = 210;
+constexpr int kQ5KBytes = 176;
 
 // 16 bytes at a 4-byte aligned address: global_load_dwordx4 needs only dword
 // alignment, and this type tells the compiler exactly that.

@@ -90,18 +90,24 @@ __device__ __forceinline__ void stage_x(XView x, const uint8_t *__restrict__ XQ,
   }
 }
 
-// ---------------------------------------------------------------- Q4_K
-template <int L, int R, bool DUMP>
-__global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
-                                                       float *__restrict__ Y, int32_t *__restrict__ Dd,
-                                                       int32_t *__restrict__ Sd, int n, int nsb) {
+// ------------------------------------------------------------- Q4_K, Q5_K
+// The K-quants with a min term share this kernel.  Q5_K (FMT 3) is Q4_K's
+// block with qh[32] between the header and qs: element 32j + l of a
+// superblock takes bit j of qh[l] as its fifth code bit.
+template <int L, int R, bool DUMP, int FMT>
+__device__ __forceinline__ void gemv_kmin(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
+                                          float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                          int32_t *__restrict__ Sd, int n, int nsb) {
+  constexpr bool Q5 = FMT == 3;
+  constexpr int kBlockBytes = Q5 ? kQ5KBytes : kQ4KBytes;
+  constexpr int kQsOff = Q5 ? 48 : 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
   constexpr int kChunkSb = kXBlocks / 8;
   constexpr int kGroupRows = 4 * G * R;  // rows per workgroup per group
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t rb = (int64_t)nsb * kQ4KBytes;
+  const int64_t rb = (int64_t)nsb * kBlockBytes;
   const int64_t ngroups = ((int64_t)n + kGroupRows - 1) / kGroupRows;
   int staged = -1;  // first superblock of the chunk in xs
   // persistent over row groups, like the Q6_K kernel
@@ -123,16 +129,21 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
         const int sbl = u >> 2, g = u & 3;
         const int sb = c0 + sbl;
         // weights of this unit for the R rows, all loads issued before any use
-        u32x4 hdr[R], qa[R], qb[R];
+        u32x4 hdr[R], qa[R], qb[R], ha[Q5 ? R : 1], hb[Q5 ? R : 1];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (row0 + r < n) {
-            const uint8_t *bp = wrow + r * rb + sb * kQ4KBytes;
+            const uint8_t *bp = wrow + r * rb + sb * kBlockBytes;
             hdr[r] = ld16(bp);
-            qa[r] = ld16(bp + 16 + 32 * g);
-            qb[r] = ld16(bp + 32 + 32 * g);
+            qa[r] = ld16(bp + kQsOff + 32 * g);
+            qb[r] = ld16(bp + kQsOff + 16 + 32 * g);
+            if constexpr (Q5) {
+              ha[r] = ld16(bp + 16);  // qh[0..15]
+              hb[r] = ld16(bp + 32);  // qh[16..31]
+            }
           } else {
             hdr[r] = qa[r] = qb[r] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (Q5) ha[r] = hb[r] = hdr[r];
           }
         }
         if (staged != c0) {
@@ -155,10 +166,22 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
         for (int r = 0; r < R; ++r) {
           const uint32_t Q[8] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w, qb[r].x, qb[r].y, qb[r].z, qb[r].w};
           int D0 = 0, D1 = 0;
+          if constexpr (Q5) {
+            // fifth bits of sub-blocks 2g and 2g+1: bits 2g, 2g+1 of qh[l]
+            const uint32_t H[8] = {ha[r].x, ha[r].y, ha[r].z, ha[r].w, hb[r].x, hb[r].y, hb[r].z, hb[r].w};
+            const uint32_t s0 = 2u * (uint32_t)g;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            D0 = dot4(Q[i] & 0x0F0F0F0Fu, A0[i], D0);
-            D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A1[i], D1);
+            for (int i = 0; i < 8; ++i) {
+              const uint32_t h0 = ((H[i] >> s0) & 0x01010101u) << 4, h1 = ((H[i] >> (s0 + 1)) & 0x01010101u) << 4;
+              D0 = dot4((Q[i] & 0x0F0F0F0Fu) | h0, A0[i], D0);
+              D1 = dot4(((Q[i] >> 4) & 0x0F0F0F0Fu) | h1, A1[i], D1);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              D0 = dot4(Q[i] & 0x0F0F0F0Fu, A0[i], D0);
+              D1 = dot4((Q[i] >> 4) & 0x0F0F0F0Fu, A1[i], D1);
+            }
           }
           if (DUMP) {
             if (row0 + r < n) {
@@ -188,6 +211,20 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict
       }
     }
   }
+}
+
+template <int L, int R, bool DUMP>
+__global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
+                                                       float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                                       int32_t *__restrict__ Sd, int n, int nsb) {
+  gemv_kmin<L, R, DUMP, 1>(W, XQ, Y, Dd, Sd, n, nsb);
+}
+
+template <int L, int R, bool DUMP>
+__global__ __launch_bounds__(256) void gemv_q5k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
+                                                       float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                                       int32_t *__restrict__ Sd, int n, int nsb) {
+  gemv_kmin<L, R, DUMP, 3>(W, XQ, Y, Dd, Sd, n, nsb);
 }
 
 // ---------------------------------------------------------------- Q6_K
@@ -493,6 +530,11 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
     QG_GEMV_SWITCH_PERSISTENT(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
+  } else if (fmt == 3) {
+    const int nsb = (int)(k / 256);
+    const int L = lanes_per_row((int64_t)nsb * 4);
+    const size_t xlds = x_chunk_bytes(k / 32);
+    QG_GEMV_SWITCH_PERSISTENT(gemv_q5k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);

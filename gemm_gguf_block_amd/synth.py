@@ -40,6 +40,8 @@ WORKLOADS = {
     "q8_0_gemv": dict(fmt="q8_0", n=4096, k=4096, seed=1000),
     "q4_k_gemv": dict(fmt="q4_k", n=14336, k=4096, seed=1001),
     "q6_k_gemv": dict(fmt="q6_k", n=128256, k=4096, seed=1002),
+    # the Llama-3-8B FFN shape in Q5_K (Q5_K_M files)
+    "q5_k_gemv": dict(fmt="q5_k", n=14336, k=4096, seed=1008),
     "q4_k_mmq": dict(fmt="q4_k", m=512, n=4096, k=4096, seed=1003),
     "moe_q4_k": dict(fmt="q4_k", n_expert=128, n_ff=768, n_embd=2048, n_tok=16, top_k=8, seed=1004),
     # prefill with the other two integer-dot types: a Q6_K ffn_down of the

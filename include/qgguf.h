@@ -90,6 +90,17 @@ qg_status qgemv_q4_k(const void *w, const void *xq, float *y, int64_t n, int64_t
 qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
 
 /*
+ * qgemv_q5_k -- the same decode GEMV for Q5_K weights, one of the GGUF types
+ * the blazr README ("Model Formats > GGUF") runs beyond the three with
+ * dedicated dot kernels.  Block (176 bytes): fp16 d, fp16 dmin, 12 bytes of
+ * six-bit scales/mins packed as Q4_K's, qh[32], qs[128]; element 32j + l of a
+ * superblock has the 4-bit code Q4_K's qs rule gives plus bit j of qh[l] as
+ * its fifth bit, w = d*sc_j*q - dmin*m_j.  Same arguments, limits and errors
+ * as qgemv_q4_k (w: Q5_K [n][k/256]).
+ */
+qg_status qgemv_q5_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
+
+/*
  * qgemv_q8_0_batch / qgemv_q4_k_batch / qgemv_q6_k_batch -- small-batch GEMV,
  * b activation rows against one read of the weights (the decode step of b
  * concurrent sequences: infr page, "Concurrent slots, many models").
@@ -190,6 +201,7 @@ qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *
  *   qg_blockdots_q8_0 : D int32 [n][k/32],  D[r][b] = sum_i qw*qa over block b
  *   qg_blockdots_q4_k : D int32 [n][k/32] (4-bit codes times qa per 32 values),
  *                       S int32 [k/32] = sum of qa per activation block
+ *   qg_blockdots_q5_k : as qg_blockdots_q4_k, with the 5-bit Q5_K codes
  *   qg_blockdots_q6_k : D int32 [n][k/16],  sum over 16 values of (q-32)*qa
  *   qg_blockdots_q4_k_mmq : D int32 [m][n][k/32] from the int8 MFMA tiles of
  *                       qgemm_q4_k_mmq; m*n*(k/32) <= 2^28
@@ -200,6 +212,8 @@ qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *
  */
 qg_status qg_blockdots_q8_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
 qg_status qg_blockdots_q4_k(const void *w, const void *xq, int32_t *D, int32_t *S, int64_t n, int64_t k,
+                            hipStream_t stream);
+qg_status qg_blockdots_q5_k(const void *w, const void *xq, int32_t *D, int32_t *S, int64_t n, int64_t k,
                             hipStream_t stream);
 qg_status qg_blockdots_q6_k(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
 qg_status qg_blockdots_q4_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemm_q4_k_mmq",
+    for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q5_k", "qgemm_q4_k_mmq",
                  "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "rmsnorm_quantize_q8_1",
                  "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
@@ -76,7 +76,8 @@ def test_quantize_validation(lib):
     assert lib.quantize_q8_1(A16, A16b, 5, 0, None) == OK
 
 
-@pytest.mark.parametrize("name,kmult", [("qgemv_q8_0", 32), ("qgemv_q4_k", 256), ("qgemv_q6_k", 256)])
+@pytest.mark.parametrize("name,kmult", [("qgemv_q8_0", 32), ("qgemv_q4_k", 256), ("qgemv_q6_k", 256),
+                                        ("qgemv_q5_k", 256)])
 def test_gemv_validation(lib, name, kmult):
     f = getattr(lib, name)
     y = P((1 << 20) + 8192)

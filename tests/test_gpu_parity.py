@@ -11,7 +11,7 @@ from gemm_gguf_block_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-GEMV = {"q8_0": "qgemv_q8_0", "q4_k": "qgemv_q4_k", "q6_k": "qgemv_q6_k"}
+GEMV = {"q8_0": "qgemv_q8_0", "q4_k": "qgemv_q4_k", "q6_k": "qgemv_q6_k", "q5_k": "qgemv_q5_k"}
 
 
 @pytest.fixture(scope="module")
@@ -85,7 +85,7 @@ def test_quantize_q8_1_bytes_exact(env, rows, k, scale):
 SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (257, 2048), (64, 4096), (33, 14336), (7, 17152), (5, 33536)]
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 @pytest.mark.parametrize("n,k", SHAPES)
 @pytest.mark.parametrize("data", ["random_bytes", "weights"])
 def test_gemv_block_dots_exact(env, fmt, n, k, data):
@@ -97,9 +97,9 @@ def test_gemv_block_dots_exact(env, fmt, n, k, data):
         w = synth.weights(fmt, n, k, seed=n + 3 * k)
         xq = orc.quantize_q8_1(synth.normal(n + k, 1, (1, k)))
     W, X = _gpu(torch, dev, w), _gpu(torch, dev, xq)
-    if fmt == "q4_k":
-        D, S = qg.blockdots_q4_k(W, X, n, k)
-        Dr, Sr = orc.blockdots("q4_k", w, xq, n, k)
+    if fmt in ("q4_k", "q5_k"):
+        D, S = getattr(qg, "blockdots_" + fmt)(W, X, n, k)
+        Dr, Sr = orc.blockdots(fmt, w, xq, n, k)
         assert np.array_equal(_host(S), Sr)
     else:
         D = getattr(qg, "blockdots_" + fmt)(W, X, n, k)
@@ -118,7 +118,7 @@ def test_q8_0_block_dots_odd_block_count(env):
 
 
 # ---------------------------------------------------------------- GEMV values
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 @pytest.mark.parametrize("n,k", SHAPES + [(1, 4096), (511, 1024), (1000, 4096)])
 def test_gemv_values(env, fmt, n, k):
     qg, orc, torch, dev = env
@@ -131,7 +131,7 @@ def test_gemv_values(env, fmt, n, k):
     assert rel_err(_host(y), orc.qgemv(fmt, w, xq, n, k)) <= REL_TOL
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
 def test_gemv_values_random_bytes(env, fmt):
     qg, orc, torch, dev = env
     n, k = 300, 1024
@@ -174,6 +174,15 @@ def test_gemv_hand_superblock_exact(env):
                 for i in range(256))
     y = _host(qg.qgemv_q4_k(_gpu(torch, dev, np.tile(blk, (5, 1))), X, 5, 256))
     assert all(Fraction(float(v)) == exact for v in y)
+    fx = read_golden("q5_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["sc"][0].split()]
+    m = [int(t) for t in fx["m"][0].split()]
+    exact = sum((Fraction(1, 16) * sc[i // 32] * q[i] - Fraction(1, 32) * m[i // 32]) * Fraction(1, 8) * qa[i]
+                for i in range(256))
+    y = _host(qg.qgemv_q5_k(_gpu(torch, dev, np.tile(blk, (6, 1))), X, 6, 256))
+    assert all(Fraction(float(v)) == exact for v in y)
     fx = read_golden("q6_k_superblock.txt")
     blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
     q = [int(t) for t in fx["q"][0].split()]
@@ -191,7 +200,7 @@ def test_gemv_empty_and_zero_k(env):
     qg, orc, torch, dev = env
     X = torch.zeros(288, dtype=torch.uint8, device=dev)
     y = torch.full((8,), 7.0, device=dev)
-    for fn in (qg.qgemv_q8_0, qg.qgemv_q4_k, qg.qgemv_q6_k):
+    for fn in (qg.qgemv_q8_0, qg.qgemv_q4_k, qg.qgemv_q6_k, qg.qgemv_q5_k):
         fn(torch.zeros(16, dtype=torch.uint8, device=dev), X, 0, 256, y=y)   # n = 0: nothing written
         assert np.all(_host(y) == 7.0)
         fn(torch.zeros(16, dtype=torch.uint8, device=dev), X, 8, 0, y=y)     # k = 0: zeros
@@ -200,7 +209,7 @@ def test_gemv_empty_and_zero_k(env):
 
 
 # ------------------------------------------------------------ small-batch GEMV
-GEMV_BATCH = {f: g + "_batch" for f, g in GEMV.items()}
+GEMV_BATCH = {f: GEMV[f] + "_batch" for f in ("q8_0", "q4_k", "q6_k")}
 # k = 17152 and 33536 span several activation chunks for every batch template
 BATCH_SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (64, 4096), (33, 14336), (7, 17152), (5, 33536)]
 
@@ -307,7 +316,7 @@ def test_gemv_batch_full_size(env, name, b):
 
 
 @pytest.mark.big
-@pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv"])
+@pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv", "q5_k_gemv"])
 def test_gemv_full_size(env, name):
     """The full workload sizes in the launch configuration the bench times."""
     qg, orc, torch, dev = env
@@ -325,9 +334,9 @@ def test_gemv_full_size(env, name):
     # the floor of the metric is the RMS over the sampled rows
     assert rel_err(y[rows], r) <= REL_TOL
     D = getattr(qg, "blockdots_" + fmt)(_gpu(torch, dev, w[rows[:256]]), X, 256, k)
-    D = D[0] if fmt == "q4_k" else D
+    D = D[0] if fmt in ("q4_k", "q5_k") else D
     Dr = orc.blockdots(fmt, w[rows[:256]], xq, 256, k)
-    Dr = Dr[0] if fmt == "q4_k" else Dr
+    Dr = Dr[0] if fmt in ("q4_k", "q5_k") else Dr
     assert np.array_equal(_host(D), Dr)
 
 
