@@ -79,9 +79,11 @@ def _declare(L):
         "orc_qgemv_factored": [ctypes.c_int, _P, _P, _P, _I, _I],
         "orc_qgemm_q4_k": [_P, _P, _P, _I, _I, _I, _P, _I],
         "orc_qgemm_q6_k": [_P, _P, _P, _I, _I, _I, _P, _I],
+        "orc_qgemm_q5_k": [_P, _P, _P, _I, _I, _I, _P, _I],
         "orc_qgemm_q8_0": [_P, _P, _P, _I, _I, _I, _P, _I],
         "orc_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_blockdots_q6_k_mmq": [_P, _P, _P, _I, _I, _I],
+        "orc_blockdots_q5_k_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_blockdots_q8_0_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_moe_q4_k": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P],
     }.items():
@@ -221,8 +223,8 @@ def qgemv_factored(fmt, w, xq, n, k):
 
 # ----------------------------------------------------------------------- mmq
 def qgemm(fmt, w, aq, m, n, k, pairs=None):
-    """C[m][n] = sum_k a^[m,k] w^[n,k] in double, for fmt 'q4_k', 'q6_k' or
-    'q8_0' weights.  `pairs` (array [P][2] of (m, n)) selects entries; then a
+    """C[m][n] = sum_k a^[m,k] w^[n,k] in double, for fmt 'q4_k', 'q5_k', 'q6_k'
+    or 'q8_0' weights.  `pairs` (array [P][2] of (m, n)) selects entries; then a
     1-D array of P values is returned."""
     fn = getattr(lib(), "orc_qgemm_" + fmt)
     w = _c(w, np.uint8)

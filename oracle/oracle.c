@@ -523,7 +523,7 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
 /* ------------------------------------------------------------------------ */
 /* Prefill product (mmq), plain definition:                                   */
 /*   C[m][n] = sum_k a^[m,k] * w^[n,k]                                        */
-/* A is Q8_1 [M][K/32]; B is Q4_K or Q6_K [N][K/256] or Q8_0 [N][K/32];       */
+/* A is Q8_1 [M][K/32]; B is Q4_K, Q5_K or Q6_K [N][K/256] or Q8_0 [N][K/32]; */
 /* C row-major [M][N].  Both operands are dequantized exactly to double and   */
 /* dotted in k order.                                                         */
 /* `sel` picks (m, n) pairs: sel[2i], sel[2i+1]; NULL means every entry.      */
@@ -576,6 +576,12 @@ void orc_qgemm_q4_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, i
     qgemm_plain(orc_dequant_q4_k, (k / QKK) * B_Q4_K, w, aq, c, m, n, k, sel, nsel);
 }
 
+void orc_qgemm_q5_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    qgemm_plain(orc_dequant_q5_k, (k / QKK) * B_Q5_K, w, aq, c, m, n, k, sel, nsel);
+}
+
 void orc_qgemm_q6_k(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
                     const int64_t *sel, int64_t nsel)
 {
@@ -589,7 +595,7 @@ void orc_qgemm_q8_0(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, i
 }
 
 /* mmq per-block dots: for every activation row, the GEMV block dots of that  */
-/* row against all weight rows.  Q4_K and Q8_0: D[m][n][k/32]; Q6_K: the     */
+/* row against all weight rows.  Q4_K, Q5_K, Q8_0: D[m][n][k/32]; Q6_K: the  */
 /* 16-value sub-block dots, D[m][n][k/16].                                    */
 void orc_blockdots_q4_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
 {
@@ -602,6 +608,15 @@ void orc_blockdots_q4_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int
     }
     free(S);
     free(row);
+}
+
+void orc_blockdots_q5_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
+{
+    int64_t nb = k / QK;
+    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nb + 1));
+    for (int64_t i = 0; i < m; ++i)
+        orc_blockdots_q5_k(w, aq + i * nb * B_Q8_1, D + i * n * nb, S, n, k);
+    free(S);
 }
 
 void orc_blockdots_q6_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)

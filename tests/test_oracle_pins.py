@@ -383,7 +383,7 @@ def test_weight_quantizer_roundtrip_bound(orc, fmt):
 
 
 # ------------------------------------------------------------------ mmq oracle
-@pytest.mark.parametrize("fmt,k", [("q4_k", 512), ("q6_k", 512), ("q8_0", 512), ("q8_0", 96)])
+@pytest.mark.parametrize("fmt,k", [("q4_k", 512), ("q5_k", 512), ("q6_k", 512), ("q8_0", 512), ("q8_0", 96)])
 def test_mmq_rows_equal_gemv(orc, fmt, k):
     m, n = 5, 33
     w = synth.weights(fmt, n, k, seed=31)
@@ -400,10 +400,10 @@ def test_mmq_rows_equal_gemv(orc, fmt, k):
     D = orc.blockdots_mmq(fmt, w, aq, m, n, k)
     for i in range(m):
         Dg = orc.blockdots(fmt, w, aq[i], n, k)
-        assert np.array_equal(D[i], Dg[0] if fmt == "q4_k" else Dg)
+        assert np.array_equal(D[i], Dg[0] if fmt in ("q4_k", "q5_k") else Dg)
 
 
-@pytest.mark.parametrize("fmt,k", [("q4_k", 256), ("q6_k", 256), ("q8_0", 256), ("q8_0", 160)])
+@pytest.mark.parametrize("fmt,k", [("q4_k", 256), ("q5_k", 256), ("q6_k", 256), ("q8_0", 256), ("q8_0", 160)])
 def test_mmq_against_numpy_matmul_of_dequantized(orc, fmt, k):
     m, n = 7, 19
     w = synth.random_blocks(fmt, n, k, seed=41, lo_exp=-10, hi_exp=0)
