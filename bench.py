@@ -5,8 +5,8 @@ quantize the activations to Q8_1 on the GPU, then run the product on the
 quantized weights.  Default workload: the Q4_K decode GEMV at a Llama-3-8B FFN
 shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
 q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); prefill products
-with the other weight types q6_k_mmq, q8_0_mmq; the Q5_K GEMV q5_k_gemv
-(14336 x 4096); the RMSNorm + quantize
+with the other weight types q6_k_mmq, q8_0_mmq, q5_k_mmq; the Q5_K GEMV
+q5_k_gemv (14336 x 4096); the RMSNorm + quantize
 prologue rmsnorm_q8_1; small-batch GEMVs
 <fmt>_gemv_b<B> (the GEMV workload's weights against B <= 8 activation rows),
 or batch for the standard set of them.
@@ -51,7 +51,7 @@ def _cpu_threads():
 KERNEL_SOURCES = {
     "q4_k_gemv": ["qg_gemv.hip"], "q8_0_gemv": ["qg_gemv.hip"], "q6_k_gemv": ["qg_gemv.hip"],
     "q5_k_gemv": ["qg_gemv.hip"],
-    "q4_k_mmq": ["qg_mmq.hip"], "q6_k_mmq": ["qg_mmq.hip"], "q8_0_mmq": ["qg_mmq.hip"],
+    "q4_k_mmq": ["qg_mmq.hip"], "q6_k_mmq": ["qg_mmq.hip"], "q8_0_mmq": ["qg_mmq.hip"], "q5_k_mmq": ["qg_mmq.hip"],
     "rmsnorm_q8_1": ["qg_quant.hip", "qg_quant.h"],
     "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
 }
@@ -523,7 +523,7 @@ def main():
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
-                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, "
+                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, q5_k_mmq, "
                          "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")

@@ -39,6 +39,7 @@ SIGNATURES = {
     "qgemm_q8_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemm_q5_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "moe_qgemv_q4_k_workspace_size": [_I, _I, _I, _I, _I],
     "moe_qgemv_q4_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "qg_status_str": [ctypes.c_int],
@@ -49,6 +50,7 @@ SIGNATURES = {
     "qg_blockdots_q8_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q5_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
 }
 
 
@@ -223,6 +225,10 @@ def qgemm_q8_0_mmq(w, aq, m, n, k, c=None, stream=None):
     return _mmq("q8_0", w, aq, m, n, k, c, stream)
 
 
+def qgemm_q5_k_mmq(w, aq, m, n, k, c=None, stream=None):
+    return _mmq("q5_k", w, aq, m, n, k, c, stream)
+
+
 def moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd) -> int:
     return int(lib().moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd))
 
@@ -325,3 +331,7 @@ def blockdots_q6_k_mmq(w, aq, m, n, k, stream=None):
 
 def blockdots_q8_0_mmq(w, aq, m, n, k, stream=None):
     return _blockdots_mmq("q8_0", w, aq, m, n, k, stream)
+
+
+def blockdots_q5_k_mmq(w, aq, m, n, k, stream=None):
+    return _blockdots_mmq("q5_k", w, aq, m, n, k, stream)

@@ -187,6 +187,11 @@ QG_EXPORT qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int6
   return run_mmq(1, w, aq, c, nullptr, m, n, k, stream);
 }
 
+QG_EXPORT qg_status qgemm_q5_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return run_mmq(3, w, aq, c, nullptr, m, n, k, stream);
+}
+
 QG_EXPORT qg_status qgemm_q6_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
                                    hipStream_t stream) {
   return run_mmq(2, w, aq, c, nullptr, m, n, k, stream);
@@ -272,6 +277,11 @@ QG_EXPORT qg_status qg_blockdots_q8_0_mmq(const void *w, const void *aq, int32_t
 QG_EXPORT qg_status qg_blockdots_q4_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                           hipStream_t stream) {
   return run_mmq(1, w, aq, nullptr, D, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q5_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_mmq(3, w, aq, nullptr, D, m, n, k, stream);
 }
 
 QG_EXPORT qg_status qg_blockdots_q6_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,

@@ -1,5 +1,5 @@
 // qg_mmq.hip -- prefill product C[m][n] = sum_k a^[m,k] w^[n,k] with Q4_K,
-// Q6_K or Q8_0 weights and Q8_1 activations on gfx950 int8 matrix cores.
+// Q5_K, Q6_K or Q8_0 weights and Q8_1 activations on gfx950 int8 matrix cores.
 //
 // The pages run this step as "in-shader dequant and dp4a mmq" (infr page,
 // "models") and as cooperative-matrix matmul (infr page, "Vulkan-first, Metal
@@ -39,13 +39,13 @@ constexpr int kBM = 64, kBN = 128;
 constexpr int kRow = 272;  // LDS bytes per staged row: 256 + 16 (spreads rows over banks)
 
 // Formats, numbered as the GEMV entry points number them.
-constexpr int kMQ8_0 = 0, kMQ4K = 1, kMQ6K = 2;
+constexpr int kMQ8_0 = 0, kMQ4K = 1, kMQ6K = 2, kMQ5K = 3;
 
 template <int FMT>
 struct MmqFmt {
   static constexpr int kGroups = FMT == kMQ6K ? 16 : 8;  // scale groups per 256-wide step
-  static constexpr bool kMin = FMT == kMQ4K;
-  static constexpr int kRegs = FMT == kMQ8_0 ? 5 : (FMT == kMQ6K ? 4 : 3);  // u32x4 staging registers
+  static constexpr bool kMin = FMT == kMQ4K || FMT == kMQ5K;
+  static constexpr int kRegs = (FMT == kMQ8_0 || FMT == kMQ5K) ? 5 : (FMT == kMQ6K ? 4 : 3);  // u32x4 staging
 };
 
 // Per-group factor arrays are [group][row] so that the MFMA operand reads of a
@@ -107,6 +107,7 @@ __device__ __forceinline__ void load_act(MmqRegs<FMT> &g, const uint8_t *__restr
 
 // Weight thread t: tile row t/4 and part c = t%4 of its 256-wide step.
 //   Q4_K: x[0] = header (d, dmin, scales), x[1], x[2] = qs bytes 32c..32c+31
+//   Q5_K: as Q4_K (qs at byte 48), plus x[3], x[4] = qh[0..31]
 //   Q8_0: blocks 2c, 2c+1: x[0..1] and x[2..3] their qs, x[4].x/.y their d
 //   Q6_K: 128-half h = c/2, positions l = 16(c%2)..+15 of all four 32-groups:
 //         x[0] = ql[64h + l] (groups 0, 2), x[1] = ql[64h + 32 + l] (groups
@@ -116,11 +117,16 @@ __device__ __forceinline__ void load_wgt(MmqRegs<FMT> &g, const uint8_t *__restr
                                          int s, int t) {
   const int gn = min(n0 + (t >> 2), N - 1);
   const int c = t & 3;
-  if constexpr (FMT == kMQ4K) {
-    const uint8_t *bp = W + ((int64_t)gn * (nblk / 8) + s) * kQ4KBytes;
+  if constexpr (FMT == kMQ4K || FMT == kMQ5K) {
+    constexpr int kB = FMT == kMQ5K ? kQ5KBytes : kQ4KBytes, kQs = FMT == kMQ5K ? 48 : 16;
+    const uint8_t *bp = W + ((int64_t)gn * (nblk / 8) + s) * kB;
     g.x[0] = ld16(bp);
-    g.x[1] = ld16(bp + 16 + 32 * c);
-    g.x[2] = ld16(bp + 32 + 32 * c);
+    g.x[1] = ld16(bp + kQs + 32 * c);
+    g.x[2] = ld16(bp + kQs + 16 + 32 * c);
+    if constexpr (FMT == kMQ5K) {
+      g.x[3] = ld16(bp + 16);
+      g.x[4] = ld16(bp + 32);
+    }
   } else if constexpr (FMT == kMQ6K) {
     const uint8_t *bp = W + ((int64_t)gn * (nblk / 8) + s) * kQ6KBytes;
     const int h = c >> 1, l = 16 * (c & 1);
@@ -182,16 +188,30 @@ __device__ __forceinline__ void store_act(const MmqRegs<FMT> &g, MmqStage<FMT> &
 template <int FMT>
 __device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &s, int t) {
   const int br = t >> 2, c = t & 3;
-  if constexpr (FMT == kMQ4K) {
-    // sub-block 2c in the low nibbles, 2c+1 in the high ones
+  if constexpr (FMT == kMQ4K || FMT == kMQ5K) {
+    // sub-block 2c in the low nibbles, 2c+1 in the high ones (Q5_K: plus bits
+    // 2c and 2c+1 of qh[l] as the fifth code bit)
     const uint32_t Q[8] = {g.x[1].x, g.x[1].y, g.x[1].z, g.x[1].w, g.x[2].x, g.x[2].y, g.x[2].z, g.x[2].w};
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = Q[i] & 0x0F0F0F0Fu;
+      hi[i] = (Q[i] >> 4) & 0x0F0F0F0Fu;
+    }
+    if constexpr (FMT == kMQ5K) {
+      const uint32_t H[8] = {g.x[3].x, g.x[3].y, g.x[3].z, g.x[3].w, g.x[4].x, g.x[4].y, g.x[4].z, g.x[4].w};
+      const uint32_t s0 = 2u * (uint32_t)c;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] |= ((H[i] >> s0) & 0x01010101u) << 4;
+        hi[i] |= ((H[i] >> (s0 + 1)) & 0x01010101u) << 4;
+      }
+    }
     u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
-    dst[0] = u32x4{Q[0] & 0x0F0F0F0Fu, Q[1] & 0x0F0F0F0Fu, Q[2] & 0x0F0F0F0Fu, Q[3] & 0x0F0F0F0Fu};
-    dst[1] = u32x4{Q[4] & 0x0F0F0F0Fu, Q[5] & 0x0F0F0F0Fu, Q[6] & 0x0F0F0F0Fu, Q[7] & 0x0F0F0F0Fu};
-    dst[2] = u32x4{(Q[0] >> 4) & 0x0F0F0F0Fu, (Q[1] >> 4) & 0x0F0F0F0Fu, (Q[2] >> 4) & 0x0F0F0F0Fu,
-                   (Q[3] >> 4) & 0x0F0F0F0Fu};
-    dst[3] = u32x4{(Q[4] >> 4) & 0x0F0F0F0Fu, (Q[5] >> 4) & 0x0F0F0F0Fu, (Q[6] >> 4) & 0x0F0F0F0Fu,
-                   (Q[7] >> 4) & 0x0F0F0F0Fu};
+    dst[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    dst[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+    dst[2] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    dst[3] = u32x4{hi[4], hi[5], hi[6], hi[7]};
     int sc0, sc1, mn0, mn1;
     q4k_scales(g.x[0].y, g.x[0].z, g.x[0].w, c, sc0, sc1, mn0, mn1);
     const float d = h2f(g.x[0].x), dmin = h2f(g.x[0].x >> 16);
@@ -419,6 +439,7 @@ hipError_t launch_qgemm_mmq(int fmt, const void *w, const void *aq, float *c, in
                             int64_t k, hipStream_t stream) {
   if (fmt == kMQ4K) return launch_fmt<kMQ4K>(w, aq, c, D, m, n, k, stream);
   if (fmt == kMQ6K) return launch_fmt<kMQ6K>(w, aq, c, D, m, n, k, stream);
+  if (fmt == kMQ5K) return launch_fmt<kMQ5K>(w, aq, c, D, m, n, k, stream);
   return launch_fmt<kMQ8_0>(w, aq, c, D, m, n, k, stream);
 }
 

@@ -49,6 +49,7 @@ WORKLOADS = {
     # 4096 x 4096 projection, both at 512 tokens
     "q6_k_mmq": dict(fmt="q6_k", m=512, n=4096, k=14336, seed=1005),
     "q8_0_mmq": dict(fmt="q8_0", m=512, n=4096, k=4096, seed=1006),
+    "q5_k_mmq": dict(fmt="q5_k", m=512, n=4096, k=4096, seed=1009),
     # the activation prologue of a 512-token prefill at hidden size 4096
     "rmsnorm_q8_1": dict(rows=512, k=4096, eps=1e-5, seed=1007),
 }

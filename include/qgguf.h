@@ -147,20 +147,24 @@ qg_status qgemm_q4_k_mmq(const void *w, const void *aq, float *c, int64_t m, int
                          hipStream_t stream);
 
 /*
- * qgemm_q6_k_mmq / qgemm_q8_0_mmq -- the same prefill product for the other two
- * integer-dot weight types the blazr README ("Model Formats > GGUF") names.
+ * qgemm_q6_k_mmq / qgemm_q8_0_mmq / qgemm_q5_k_mmq -- the same prefill product
+ * for the other two integer-dot weight types the blazr README ("Model Formats
+ * > GGUF") names, and for Q5_K (see qgemv_q5_k for its block).
  *   Q6_K: each 16-wide sub-block is one int8 32x32x16 MFMA tile of exact dots
  *         of (q - 32) and qa, rescaled in fp32 by d*scales_j*d_a.
  *   Q8_0: each 32-wide block is one int8 32x32x32 MFMA tile of exact dots,
  *         rescaled in fp32 by d_w*d_a.
- *   w   : Q6_K [n][k/256] or Q8_0 [n][k/32]
+ *   Q5_K: as Q4_K with the 5-bit codes.
+ *   w   : Q6_K or Q5_K [n][k/256], or Q8_0 [n][k/32]
  *   aq  : Q8_1 [m][k/32];  c : f32 [m][n] row-major, written
- *   k   : multiple of 256 (Q6_K) or 32 (Q8_0), <= 2^24;  m, n <= 2^31 - 1
+ *   k   : multiple of 256 (Q6_K, Q5_K) or 32 (Q8_0), <= 2^24;  m, n <= 2^31 - 1
  * Same errors and conventions as qgemm_q4_k_mmq.
  */
 qg_status qgemm_q6_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
                          hipStream_t stream);
 qg_status qgemm_q8_0_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream);
+qg_status qgemm_q5_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
                          hipStream_t stream);
 
 /*
@@ -205,7 +209,8 @@ qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *
  *   qg_blockdots_q6_k : D int32 [n][k/16],  sum over 16 values of (q-32)*qa
  *   qg_blockdots_q4_k_mmq : D int32 [m][n][k/32] from the int8 MFMA tiles of
  *                       qgemm_q4_k_mmq; m*n*(k/32) <= 2^28
- *   qg_blockdots_q8_0_mmq : the same for qgemm_q8_0_mmq
+ *   qg_blockdots_q8_0_mmq, qg_blockdots_q5_k_mmq : the same for
+ *                       qgemm_q8_0_mmq and qgemm_q5_k_mmq
  *   qg_blockdots_q6_k_mmq : D int32 [m][n][k/16] per 16-value sub-block, from
  *                       qgemm_q6_k_mmq; m*n*(k/16) <= 2^28
  * Same validation rules and limits as the corresponding products.
@@ -221,6 +226,8 @@ qg_status qg_blockdots_q4_k_mmq(const void *w, const void *aq, int32_t *D, int64
 qg_status qg_blockdots_q8_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                 hipStream_t stream);
 qg_status qg_blockdots_q6_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                hipStream_t stream);
+qg_status qg_blockdots_q5_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                 hipStream_t stream);
 
 #ifdef __cplusplus

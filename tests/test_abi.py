@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q5_k", "qgemm_q4_k_mmq",
-                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "rmsnorm_quantize_q8_1",
+                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "qgemm_q5_k_mmq", "rmsnorm_quantize_q8_1",
                  "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
         assert want in names
@@ -129,7 +129,7 @@ def test_mmq_validation(lib):
     assert lib.qg_blockdots_q4_k_mmq(A16, A16b, c, 1 << 14, 1 << 14, 4096, None) == SHAPE
 
 
-@pytest.mark.parametrize("fmt,kmult", [("q6_k", 256), ("q8_0", 32)])
+@pytest.mark.parametrize("fmt,kmult", [("q6_k", 256), ("q8_0", 32), ("q5_k", 256)])
 def test_mmq_validation_other_formats(lib, fmt, kmult):
     c = P((1 << 20) + 8192)
     f = getattr(lib, f"qgemm_{fmt}_mmq")

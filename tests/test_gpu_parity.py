@@ -444,7 +444,7 @@ MMQ_SHAPES = [(1, 1, 256), (32, 32, 256), (70, 100, 512), (130, 65, 768), (3, 20
 MMQ_Q80_RAGGED = [(5, 7, 32), (33, 70, 96), (64, 128, 288), (65, 129, 4128)]
 
 
-@pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES] +
+@pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES] + [("q5_k",) + s for s in MMQ_SHAPES] +
                          [("q8_0",) + s for s in MMQ_SHAPES + MMQ_Q80_RAGGED])
 def test_mmq_block_dots_exact_other_formats(env, fmt, m, n, k):
     """Random bytes: the matrix-core dots equal the oracle's block dots
@@ -457,6 +457,7 @@ def test_mmq_block_dots_exact_other_formats(env, fmt, m, n, k):
 
 
 @pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES + [(1, 64, 4096), (257, 70, 1024)]] +
+                         [("q5_k",) + s for s in MMQ_SHAPES + [(257, 70, 1024)]] +
                          [("q8_0",) + s for s in MMQ_SHAPES + MMQ_Q80_RAGGED + [(257, 70, 1024)]])
 def test_mmq_values_other_formats(env, fmt, m, n, k):
     qg, orc, torch, dev = env
@@ -469,7 +470,7 @@ def test_mmq_values_other_formats(env, fmt, m, n, k):
     assert rel_err(C, orc.qgemm(fmt, w, aq, m, n, k)) <= REL_TOL
 
 
-@pytest.mark.parametrize("fmt", ["q6_k", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q6_k", "q8_0", "q5_k"])
 def test_mmq_values_random_bytes_other_formats(env, fmt):
     qg, orc, torch, dev = env
     m, n, k = 70, 130, 512
@@ -496,12 +497,21 @@ def test_mmq_hand_blocks_exact_other_formats(env):
     exact = sum(Fraction((i % 32) - 16, 4) * Fraction(1, 8) * qa[i] for i in range(256))
     C = _host(qg.qgemm_q8_0_mmq(_gpu(torch, dev, np.tile(blk, (70, 8))), A, 40, 70, 256))
     assert all(Fraction(float(v)) == exact for v in C.ravel())
+    fx = read_golden("q5_k_superblock.txt")
+    blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+    q = [int(t) for t in fx["q"][0].split()]
+    sc = [int(t) for t in fx["sc"][0].split()]
+    m = [int(t) for t in fx["m"][0].split()]
+    exact = sum((Fraction(1, 16) * sc[i // 32] * q[i] - Fraction(1, 32) * m[i // 32]) * Fraction(1, 8) * qa[i]
+                for i in range(256))
+    C = _host(qg.qgemm_q5_k_mmq(_gpu(torch, dev, np.tile(blk, (70, 1))), A, 40, 70, 256))
+    assert all(Fraction(float(v)) == exact for v in C.ravel())
 
 
 def test_mmq_empty_other_formats(env):
     qg, orc, torch, dev = env
     A = torch.zeros(4 * 288, dtype=torch.uint8, device=dev)
-    for fmt, k in (("q6_k", 256), ("q8_0", 32)):
+    for fmt, k in (("q6_k", 256), ("q8_0", 32), ("q5_k", 256)):
         W = torch.zeros(4 * qg.row_bytes(fmt, 256), dtype=torch.uint8, device=dev)
         c = torch.full((4, 4), 7.0, device=dev)
         f = getattr(qg, f"qgemm_{fmt}_mmq")
@@ -513,7 +523,7 @@ def test_mmq_empty_other_formats(env):
 
 
 @pytest.mark.big
-@pytest.mark.parametrize("name", ["q6_k_mmq", "q8_0_mmq"])
+@pytest.mark.parametrize("name", ["q6_k_mmq", "q8_0_mmq", "q5_k_mmq"])
 def test_mmq_full_size_other_formats(env, name):
     qg, orc, torch, dev = env
     p = synth.WORKLOADS[name]
