@@ -150,11 +150,20 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
 constexpr int kMaxIdWords = 4;      // up to 256 (token, slot) pairs
 constexpr int kMaxExpertWords = 4;  // up to 256 experts
 
-template <int L, int R>
+//
+// With STAGE (the gate/up call when the token rows fit in LDS) the workgroup
+// first stages every activation row, unit-major: piece c of unit u of row t at
+// slot t*5U + c*U + u (16 bytes: half c%2 of block 2u + c/2), and the record
+// {d_a(2u), d_a(2u+1), sum qa(2u), sum qa(2u+1)} at slot t*5U + 4U + u.  The
+// pair loop then reads its activation from LDS instead of L2.
+template <int L, int R, bool STAGE>
 __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
     const uint8_t *__restrict__ W, const uint8_t *__restrict__ act, const int32_t *__restrict__ ids,
     const float *__restrict__ weights, float *__restrict__ out, int rows, int nsb, int npairs, int top_k,
-    int act_per_token, int64_t expert_bytes, int64_t act_row_bytes, int tiles, int n_expert) {
+    int act_per_token, int64_t expert_bytes, int64_t act_row_bytes, int tiles, int n_expert, int n_act) {
+  typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  u32x4n *xs = reinterpret_cast<u32x4n *>(lds);
   constexpr int G = 64 / L;
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
@@ -192,6 +201,27 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
 
   const int u = li;  // this lane's unit (L >= U here, so at most one)
   const int sb = u >> 2, g = u & 3;
+  if constexpr (STAGE) {
+    for (int t = threadIdx.x; t < n_act * U; t += 256) {
+      const int row = t / U, uu = t - row * U;
+      uint32_t A[18];
+      load_q8_1_pair(act + (int64_t)row * act_row_bytes + (int64_t)(2 * uu) * kQ8_1Bytes, A);
+      int S0 = 0, S1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        S0 = bsum4(A[1 + i], S0);
+        S1 = bsum4(A[10 + i], S1);
+      }
+      u32x4n *base = xs + row * 5 * U;
+      base[uu] = u32x4n{A[1], A[2], A[3], A[4]};
+      base[U + uu] = u32x4n{A[5], A[6], A[7], A[8]};
+      base[2 * U + uu] = u32x4n{A[10], A[11], A[12], A[13]};
+      base[3 * U + uu] = u32x4n{A[14], A[15], A[16], A[17]};
+      base[4 * U + uu] = u32x4n{__builtin_bit_cast(uint32_t, h2f(A[0])), __builtin_bit_cast(uint32_t, h2f(A[9])),
+                                (uint32_t)S0, (uint32_t)S1};
+    }
+    __syncthreads();
+  }
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     // expert = the (item / tiles)-th touched expert
     int k = item / tiles, e = -1;
@@ -232,14 +262,30 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
         if (u < U) {
           uint32_t A[18];
-          load_q8_1_pair(xr + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes, A);
           int S0 = 0, S1 = 0;
+          float da0, da1;
+          if constexpr (STAGE) {
+            const u32x4n *base = xs + (p / top_k) * 5 * U;
+            const u32x4n x0 = base[u], x1 = base[U + u], x2 = base[2 * U + u], x3 = base[3 * U + u];
+            const u32x4n rec = base[4 * U + u];
+            A[1] = x0.x; A[2] = x0.y; A[3] = x0.z; A[4] = x0.w;
+            A[5] = x1.x; A[6] = x1.y; A[7] = x1.z; A[8] = x1.w;
+            A[10] = x2.x; A[11] = x2.y; A[12] = x2.z; A[13] = x2.w;
+            A[14] = x3.x; A[15] = x3.y; A[16] = x3.z; A[17] = x3.w;
+            da0 = as_f32(rec.x);
+            da1 = as_f32(rec.y);
+            S0 = (int)rec.z;
+            S1 = (int)rec.w;
+          } else {
+            load_q8_1_pair(xr + (int64_t)(8 * sb + 2 * g) * kQ8_1Bytes, A);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            S0 = bsum4(A[1 + i], S0);
-            S1 = bsum4(A[10 + i], S1);
+            for (int i = 0; i < 8; ++i) {
+              S0 = bsum4(A[1 + i], S0);
+              S1 = bsum4(A[10 + i], S1);
+            }
+            da0 = h2f(A[0]);
+            da1 = h2f(A[9]);
           }
-          const float da0 = h2f(A[0]), da1 = h2f(A[9]);
           const float dS0 = da0 * (float)S0, dS1 = da1 * (float)S1;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
@@ -333,6 +379,10 @@ constexpr int kMoePersistentBlocks = 1024;
 // Lanes per row: the smallest power of two >= the row's unit count, capped at
 // 64 (lanes past the last unit idle); each lane then keeps ceil(U/L) units'
 // weights for R rows in VGPRs (up to two units; longer rows reload per pair).
+// LDS for staging all activation rows of a gate/up call: 5 x 16 bytes per unit
+// of each row.  Up to this much, four workgroups still fit on a CU.
+constexpr size_t kMoeStageBytes = 40 * 1024;
+
 template <int L, int R>
 static void launch_expert_gemv_persistent(const uint8_t *W, const uint8_t *act, const int32_t *ids,
                                           const float *weights, float *out, int rows, int nsb, int npairs,
@@ -342,8 +392,16 @@ static void launch_expert_gemv_persistent(const uint8_t *W, const uint8_t *act, 
   const int tiles = (rows + rows_per_block - 1) / rows_per_block;
   const int64_t max_items = (int64_t)tiles * n_expert;
   const dim3 grid((unsigned)(max_items < kMoePersistentBlocks ? max_items : kMoePersistentBlocks));
-  hipLaunchKernelGGL((moe_expert_gemv_persistent<L, R>), grid, dim3(256), 0, stream, W, act, ids, weights, out,
-                     rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles, n_expert);
+  const int n_act = act_per_token ? (npairs + top_k - 1) / top_k : npairs;
+  const size_t stage = (size_t)n_act * nsb * 4 * 80;
+  if (act_per_token && stage <= kMoeStageBytes)
+    hipLaunchKernelGGL((moe_expert_gemv_persistent<L, R, true>), grid, dim3(256), stage, stream, W, act, ids,
+                       weights, out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles,
+                       n_expert, n_act);
+  else
+    hipLaunchKernelGGL((moe_expert_gemv_persistent<L, R, false>), grid, dim3(256), 0, stream, W, act, ids, weights,
+                       out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles, n_expert,
+                       n_act);
 }
 
 static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights, float *out,
