@@ -86,6 +86,8 @@ def _declare(L):
         "orc_blockdots_q5_k_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_blockdots_q8_0_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_moe_q4_k": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P],
+        "orc_router_logits": [_P, _P, _P, _I, _I, _I],
+        "orc_route_topk": [_P, _P, _P, _I, _I, _I],
     }.items():
         fn = getattr(L, name)
         fn.restype = None
@@ -254,6 +256,29 @@ def blockdots_mmq(fmt, w, aq, m, n, k):
 
 def blockdots_q4_k_mmq(w, aq, m, n, k):
     return blockdots_mmq("q4_k", w, aq, m, n, k)
+
+
+# -------------------------------------------------------------------- router
+def router_logits(wr, x):
+    """logits[t][e] = Wr[e] . x[t] in double; wr f32 [E][H], x f32 [T][H]."""
+    wr = _c(wr, np.float32)
+    x = _c(x, np.float32)
+    E, H = wr.shape
+    T = x.shape[0]
+    out = np.empty((T, E), np.float64)
+    lib().orc_router_logits(_ptr(wr), _ptr(x), _ptr(out), T, E, H)
+    return out
+
+
+def route_topk(logits, k):
+    """(ids int32 [T][k], weights f64 [T][k]) from f32 logits [T][E]: the k
+    largest, larger first, ties to the lower expert; softmax over those k."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    lib().orc_route_topk(_ptr(logits), _ptr(ids), _ptr(w), T, E, k)
+    return ids, w
 
 
 # ----------------------------------------------------------------------- MoE

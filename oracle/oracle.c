@@ -634,6 +634,51 @@ void orc_blockdots_q8_0_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* MoE router (the step that makes the routing table the expert FFN takes):  */
+/*   logits[t][e] = sum_h Wr[e][h] * x[t][h]       (double, from f32 inputs)   */
+/* and, from a given table of logits (f32), per token:                       */
+/*   ids[t][0..K-1]: the K experts with the largest logits, larger first,     */
+/*                   equal logits in increasing expert order                  */
+/*   weights[t][i] = exp(l_i - l_0) / sum_j exp(l_j - l_0) over those K       */
+/*                   (double)                                                 */
+/* The selection takes the logits it is given, so it can be applied to the   */
+/* GPU's own f32 logits and compared exactly.                                 */
+/* ------------------------------------------------------------------------ */
+void orc_router_logits(const float *wr, const float *x, double *logits, int64_t T, int64_t E, int64_t H)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h)
+                acc += (double)wr[e * H + h] * (double)x[t * H + h];
+            logits[t * E + e] = acc;
+        }
+}
+
+void orc_route_topk(const float *logits, int32_t *ids, double *weights, int64_t T, int64_t E, int64_t K)
+{
+    unsigned char *taken = (unsigned char *)malloc((size_t)(E > 0 ? E : 1));
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        memset(taken, 0, (size_t)(E > 0 ? E : 1));
+        for (int64_t i = 0; i < K; ++i) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best]))   /* strict: the lower index keeps a tie */
+                    best = e;
+            taken[best] = 1;
+            ids[t * K + i] = (int32_t)best;
+        }
+        double sum = 0.0;
+        for (int64_t i = 0; i < K; ++i)
+            sum += exp((double)l[ids[t * K + i]] - (double)l[ids[t * K]]);
+        for (int64_t i = 0; i < K; ++i)
+            weights[t * K + i] = exp((double)l[ids[t * K + i]] - (double)l[ids[t * K]]) / sum;
+    }
+    free(taken);
+}
+
+/* ------------------------------------------------------------------------ */
 /* MoE expert FFN (Q4_K experts), per token t and routed slot e = ids[t][i]:  */
 /*   g = Wgu[e][0:F] . x^_t,  u = Wgu[e][F:2F] . x^_t        (double)          */
 /*   h = silu(g) * u, silu(g) = g / (1 + exp(-g)), rounded once to f32         */

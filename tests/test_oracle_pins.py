@@ -413,6 +413,50 @@ def test_mmq_against_numpy_matmul_of_dequantized(orc, fmt, k):
     assert np.max(np.abs(C - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+# --------------------------------------------------------------- router oracle
+def test_route_topk_hand_example(orc):
+    """Ties go to the lower expert; weights are the softmax of the selected."""
+    logits = np.array([[0.5, 2.0, -1.0, 2.0, 1.5]], np.float32)
+    ids, w = orc.route_topk(logits, 3)
+    assert ids.tolist() == [[1, 3, 4]]
+    e = np.exp(-0.5)
+    assert np.allclose(w[0], [1 / (2 + e), 1 / (2 + e), e / (2 + e)], rtol=1e-15, atol=0)
+    ids1, w1 = orc.route_topk(logits, 1)
+    assert ids1.tolist() == [[1]] and w1[0, 0] == 1.0
+
+
+def test_route_topk_against_lexsort(orc):
+    g = np.random.default_rng(71)
+    T, E = 40, 128
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    logits[:, 7] = logits[:, 90]                          # exact ties across the cut
+    logits[3, :] = 0.25                                   # an all-equal row
+    for k in (1, 2, 8, E):
+        ids, w = orc.route_topk(logits, k)
+        for t in range(T):
+            want = np.lexsort((np.arange(E), -logits[t].astype(np.float64)))[:k]
+            assert ids[t].tolist() == want.tolist()
+            sel = logits[t][ids[t]].astype(np.float64)
+            ref = np.exp(sel - sel[0]) / np.exp(sel - sel[0]).sum()
+            assert np.allclose(w[t], ref, rtol=1e-14, atol=0)
+            assert abs(w[t].sum() - 1.0) <= 1e-14 and np.all(np.diff(w[t]) <= 0)
+    assert orc.route_topk(logits[3:4], 4)[0].tolist() == [[0, 1, 2, 3]]
+
+
+def test_router_logits_against_matmul(orc):
+    g = np.random.default_rng(72)
+    wr = (0.02 * g.standard_normal((64, 512))).astype(np.float32)
+    x = g.standard_normal((5, 512)).astype(np.float32)
+    got = orc.router_logits(wr, x)
+    ref = x.astype(np.float64) @ wr.astype(np.float64).T
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # a one-hot router row picks out an activation entry exactly
+    wr1 = np.zeros((3, 512), np.float32)
+    wr1[0, 5] = wr1[1, 511] = 1.0
+    wr1[2, 0] = -2.0
+    assert np.array_equal(orc.router_logits(wr1, x), np.stack([x[:, 5], x[:, 511], -2.0 * x[:, 0]], 1))
+
+
 # ------------------------------------------------------------------ MoE oracle
 def _small_moe(seed=51, E=6, F=256, H=512, T=4, K=3):
     w_gu = synth.weights("q4_k", E * 2 * F, H, seed, 0).reshape(E, -1)
