@@ -41,6 +41,7 @@ SIGNATURES = {
     "qgemm_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q5_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "moe_qgemv_q4_k_workspace_size": [_I, _I, _I, _I, _I],
+    "moe_router_topk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "moe_qgemv_q4_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "qg_status_str": [ctypes.c_int],
     "qg_blockdots_q8_0": [_P, _P, _P, _I, _I, _P],
@@ -227,6 +228,24 @@ def qgemm_q8_0_mmq(w, aq, m, n, k, c=None, stream=None):
 
 def qgemm_q5_k_mmq(w, aq, m, n, k, c=None, stream=None):
     return _mmq("q5_k", w, aq, m, n, k, c, stream)
+
+
+def moe_router_topk(w_router, x, top_k, ids=None, weights=None, logits=None, stream=None):
+    """(ids int32 [T][top_k], weights f32 [T][top_k]) for x f32 [T][H] and the
+    router f32 [E][H]; `logits` (f32 [T][E]) receives the logits when given."""
+    import torch
+    E, H = w_router.shape
+    T = x.shape[0]
+    if ids is None:
+        ids = _empty((T, top_k), torch.int32, x)
+    if weights is None:
+        weights = _empty((T, top_k), torch.float32, x)
+    pl = None if logits is None else _need(logits, torch.float32, T * E * 4, "logits")
+    _check("moe_router_topk", lib().moe_router_topk(
+        _need(w_router, torch.float32, E * H * 4, "w_router"), _need(x, torch.float32, T * H * 4, "x"),
+        _need(ids, torch.int32, T * top_k * 4, "ids"), _need(weights, torch.float32, T * top_k * 4, "weights"),
+        pl, T, E, H, top_k, _stream(stream)))
+    return ids, weights
 
 
 def moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd) -> int:

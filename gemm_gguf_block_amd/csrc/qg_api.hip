@@ -197,6 +197,22 @@ QG_EXPORT qg_status qgemm_q6_k_mmq(const void *w, const void *aq, float *c, int6
   return run_mmq(2, w, aq, c, nullptr, m, n, k, stream);
 }
 
+QG_EXPORT qg_status moe_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights,
+                                    float *logits, int64_t n_tok, int64_t n_expert, int64_t n_embd, int64_t top_k,
+                                    hipStream_t stream) {
+  if (!w_router || (n_tok > 0 && (!x || !ids || !weights))) return QG_ERR_NULL;  // per-token buffers may be null when empty
+  if (n_tok < 0 || n_tok > kMaxRows || n_expert < 1 || n_expert > 256 || top_k < 1 || top_k > 64 ||
+      top_k > n_expert || n_embd < 4 || n_embd % 4 != 0 || n_embd > 8192)
+    return QG_ERR_SHAPE;
+  if (!aligned(w_router, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4) ||
+      (logits && !aligned(logits, 4)))
+    return QG_ERR_ALIGN;
+  if (n_tok == 0) return QG_OK;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_router_topk(w_router, x, ids, weights, logits, n_tok, n_expert, n_embd, top_k, stream));
+}
+
 QG_EXPORT size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
                                                int64_t n_embd) {
   (void)n_expert;

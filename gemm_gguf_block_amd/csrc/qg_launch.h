@@ -58,6 +58,10 @@ hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, 
 hipError_t launch_qgemm_mmq(int fmt, const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n,
                             int64_t k, hipStream_t stream);
 
+// MoE router: logits, top-k, softmax per token (validated arguments).
+hipError_t launch_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights, float *logits,
+                              int64_t n_tok, int64_t n_expert, int64_t n_embd, int64_t top_k, hipStream_t stream);
+
 struct MoeArgs {
   const void *w_gu, *w_down, *xq;
   const int32_t *ids;

@@ -194,6 +194,26 @@ qg_status qgemm_q5_k_mmq(const void *w, const void *aq, float *c, int64_t m, int
  */
 size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
                                      int64_t n_embd);
+
+/*
+ * moe_router_topk -- the router that makes the routing table moe_qgemv_q4_k
+ * takes, in one launch.  Per token t:
+ *   logits[t][e] = sum_h w_router[e][h] * x[t][h]           (fp32)
+ *   ids[t][0..top_k-1]: the top_k experts by logit, larger first, equal
+ *                       logits in increasing expert order
+ *   weights[t][i] = exp(l_i - l_0) / sum_j exp(l_j - l_0) over the selected
+ * (the softmax of the selected logits, as the MoE models the infr page runs
+ * use; "models").  The router matrix is f32, as in their Q4_K_M files.
+ *   w_router : f32 [n_expert][n_embd];  x : f32 [n_tok][n_embd] (16-byte aligned)
+ *   ids      : int32 [n_tok][top_k], weights : f32 [n_tok][top_k], written
+ *   logits   : f32 [n_tok][n_expert] or NULL (written when given)
+ *   n_expert in [1, 256];  top_k in [1, min(64, n_expert)];
+ *   n_embd a multiple of 4 in [4, 8192];  n_tok = 0 does nothing (x, ids and
+ *   weights may then be NULL)
+ * NaN logits are not defined.
+ */
+qg_status moe_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights, float *logits,
+                          int64_t n_tok, int64_t n_expert, int64_t n_embd, int64_t top_k, hipStream_t stream);
 qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
                          const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
                          int64_t n_ff, int64_t n_embd, void *workspace, size_t workspace_bytes,

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q5_k", "qgemm_q4_k_mmq",
-                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "qgemm_q5_k_mmq", "rmsnorm_quantize_q8_1",
+                 "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "qgemm_q5_k_mmq", "rmsnorm_quantize_q8_1", "moe_router_topk",
                  "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
         assert want in names
@@ -211,3 +211,18 @@ def test_rmsnorm_quantize_validation(lib):
     assert f(A16, A16b, 1e-5, xq, P((1 << 20) + 2), 2, 64, None) == ALIGN
     assert f(A16, A16b, 1e-5, xq, None, 0, 64, None) == OK
     assert f(A16, A16b, 1e-5, xq, None, 2, 0, None) == OK
+
+
+def test_router_validation(lib):
+    f = lib.moe_router_topk
+    o = P((1 << 20) + 8192)
+    assert f(None, A16b, o, o, None, 2, 128, 2048, 8, None) == NULL
+    assert f(A16, A16b, None, o, None, 2, 128, 2048, 8, None) == NULL
+    assert f(A16, A16b, o, o, None, 2, 300, 2048, 8, None) == SHAPE      # more than 256 experts
+    assert f(A16, A16b, o, o, None, 2, 128, 2048, 65, None) == SHAPE     # top_k above 64
+    assert f(A16, A16b, o, o, None, 2, 4, 2048, 5, None) == SHAPE        # top_k above n_expert
+    assert f(A16, A16b, o, o, None, 2, 128, 2050, 8, None) == SHAPE      # n_embd not a multiple of 4
+    assert f(A16, A16b, o, o, None, 2, 128, 16384, 8, None) == SHAPE     # n_embd above 8192
+    assert f(MIS, A16b, o, o, None, 2, 128, 2048, 8, None) == ALIGN
+    assert f(A16, A16b, P((1 << 20) + 2), o, None, 2, 128, 2048, 8, None) == ALIGN
+    assert f(A16, A16b, o, o, None, 0, 128, 2048, 8, None) == OK

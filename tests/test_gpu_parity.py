@@ -544,6 +544,72 @@ def test_mmq_full_size_other_formats(env, name):
     assert np.array_equal(_host(D), orc.blockdots_mmq(fmt, w[:96], aq[:80], 80, 96, k))
 
 
+# --------------------------------------------------------------------- router
+def _router_case(seed, T, E, H):
+    g = np.random.default_rng(seed)
+    wr = (0.02 * g.standard_normal((E, H))).astype(np.float32)
+    x = g.standard_normal((T, H)).astype(np.float32)
+    return wr, x
+
+
+def _check_router_stagewise(orc, wr, x, k, ids, w, logits):
+    """logits within 1e-5 of the double oracle; ids exactly and weights within
+    1e-6 of the oracle's selection from the GPU's own f32 logits."""
+    ref = orc.router_logits(wr, x)
+    assert rel_err(logits, ref) <= 1e-5
+    ids_ref, w_ref = orc.route_topk(logits, k)
+    assert np.array_equal(ids, ids_ref)
+    assert np.max(np.abs(w.astype(np.float64) - w_ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,H,k", [(1, 8, 4, 1), (16, 128, 2048, 8), (33, 64, 256, 2), (5, 256, 8192, 64),
+                                     (7, 40, 1024, 40), (3, 128, 2048, 1)])
+def test_router_topk_stagewise(env, T, E, H, k):
+    qg, orc, torch, dev = env
+    wr, x = _router_case(T * E + H, T, E, H)
+    logits = torch.empty((T, E), device=dev)
+    ids, w = qg.moe_router_topk(_gpu(torch, dev, wr), _gpu(torch, dev, x), k, logits=logits)
+    _check_router_stagewise(orc, wr, x, k, _host(ids), _host(w), _host(logits))
+
+
+def test_router_topk_exact_ties(env):
+    """Duplicated router rows give bit-equal logits: the lower expert wins."""
+    qg, orc, torch, dev = env
+    T, E, H, k = 9, 96, 512, 6
+    wr, x = _router_case(5, T, E, H)
+    wr[50] = wr[3]
+    wr[77] = wr[3]
+    wr[60] = wr[10]
+    x[2] = 0.0                                             # an all-zero row: every logit equal
+    logits = torch.empty((T, E), device=dev)
+    ids, w = qg.moe_router_topk(_gpu(torch, dev, wr), _gpu(torch, dev, x), k, logits=logits)
+    L, I = _host(logits), _host(ids)
+    assert np.array_equal(L[:, 50], L[:, 3]) and np.array_equal(L[:, 77], L[:, 3])
+    assert I[2].tolist() == list(range(k))
+    _check_router_stagewise(orc, wr, x, k, I, _host(w), L)
+
+
+def test_router_feeds_moe(env):
+    """The router's table drives the expert FFN as is: the stage-wise MoE
+    check passes on the ids and weights the router wrote."""
+    qg, orc, torch, dev = env
+    E, F, H, T, K = 6, 256, 512, 5, 2
+    w_gu, w_dn, _, _, x = _moe_case(97, E, F, H, T, K)
+    wr, _ = _router_case(98, 1, E, H)
+    ids, rw = qg.moe_router_topk(_gpu(torch, dev, wr), _gpu(torch, dev, x), K)
+    ids, rw = _host(ids), _host(rw)
+    assert ids.dtype == np.int32 and rw.dtype == np.float32
+    _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
+
+
+def test_router_empty(env):
+    qg, orc, torch, dev = env
+    wr, _ = _router_case(1, 1, 8, 16)
+    x = torch.zeros((0, 16), device=dev)
+    ids, w = qg.moe_router_topk(_gpu(torch, dev, wr), x, 2)
+    assert ids.shape == (0, 2) and w.shape == (0, 2)
+
+
 # ------------------------------------------------------------------------ MoE
 def _moe_case(seed, E, F, H, T, K):
     w_gu = synth.weights("q4_k", E * 2 * F, H, seed, synth.T_W).reshape(E, -1)
@@ -646,9 +712,15 @@ def test_graph_replay_matches_eager(env):
     gam = _gpu(torch, dev, _gamma(k, 96))
     xnq = torch.empty((5, k // 32 * 36), dtype=torch.uint8, device=dev)
     rr = torch.empty(5, device=dev)
+    wr_h, xr_h = _router_case(99, 16, 128, 2048)
+    WR, XR = _gpu(torch, dev, wr_h), _gpu(torch, dev, xr_h)
+    rids = torch.empty((16, 8), dtype=torch.int32, device=dev)
+    rws = torch.empty((16, 8), device=dev)
+    rlg = torch.empty((16, 128), device=dev)
 
     def work():
         qg.rmsnorm_quantize_q8_1(xb, gam, 1e-5, xq=xnq, r=rr)
+        qg.moe_router_topk(WR, XR, 8, ids=rids, weights=rws, logits=rlg)
         qg.quantize_q8_1(x, xq)
         for f, W in Ws.items():
             getattr(qg, GEMV[f])(W, xq, n, k, y=ys[f])
@@ -664,7 +736,8 @@ def test_graph_replay_matches_eager(env):
 
     def snapshot():
         torch.cuda.synchronize()
-        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr)]
+        return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr,
+                                    rids, rws, rlg)]
 
     work()
     eager = snapshot()
@@ -678,7 +751,7 @@ def test_graph_replay_matches_eager(env):
             work()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr):
+        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr, rids, rws, rlg):
             t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
