@@ -7,7 +7,7 @@ shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
 q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); prefill products
 with the other weight types q6_k_mmq, q8_0_mmq, q5_k_mmq; the Q5_K GEMV
 q5_k_gemv (14336 x 4096); the RMSNorm + quantize
-prologue rmsnorm_q8_1; small-batch GEMVs
+prologue rmsnorm_q8_1; the MoE router router_topk; small-batch GEMVs
 <fmt>_gemv_b<B> (the GEMV workload's weights against B <= 8 activation rows),
 or batch for the standard set of them.
 
@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "q4_k_mmq": ["qg_mmq.hip"], "q6_k_mmq": ["qg_mmq.hip"], "q8_0_mmq": ["qg_mmq.hip"], "q5_k_mmq": ["qg_mmq.hip"],
     "rmsnorm_q8_1": ["qg_quant.hip", "qg_quant.h"],
     "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
+    "router_topk": ["qg_router.hip"],
 }
 BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8", "q6_k_gemv_b4", "q6_k_gemv_b8"]
 
@@ -387,6 +388,56 @@ class Moe(Workload):
                     sample=f"all {T} tokens ({self.distinct} distinct experts) x {reps}, {t:.1f} s")
 
 
+class Router(Workload):
+    """`router_topk`: logits of an f32 router, then top-k and softmax."""
+
+    def __init__(self, qg, torch, warm):
+        from gemm_gguf_block_amd import synth
+        inp = synth.workload("router_topk")
+        self.inp, self.name = inp, "router_topk"
+        self.E, self.H, self.T, self.K = inp["n_expert"], inp["n_embd"], inp["n_tok"], inp["top_k"]
+        self.qg, self.torch = qg, torch
+        dev = torch.device("cuda:0")
+        wr = inp["w_router"]
+        self.copies = 1 if warm else max(1, math.ceil(COLD_BYTES / wr.nbytes))
+        W0 = torch.from_numpy(wr).to(dev)
+        self.W = [W0] + [W0.clone() for _ in range(self.copies - 1)]
+        self.x = torch.from_numpy(inp["x"]).to(dev)
+        self.ids = torch.empty((self.T, self.K), dtype=torch.int32, device=dev)
+        self.rw = torch.empty((self.T, self.K), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((self.T, self.E), dtype=torch.float32, device=dev)
+        self.dominant = "router (2 kernels)"
+        # router and tokens read, logits written and read back, ids and weights written
+        self.kernel_bytes = wr.nbytes + inp["x"].nbytes + 8 * self.T * self.E + 8 * self.T * self.K
+        self.step_bytes = self.kernel_bytes
+        self.tokens_per_step = self.T
+        self.unit, self.bound = "GB/s", "hbm"
+
+    def step(self, i):
+        self.qg.moe_router_topk(self.W[i % self.copies], self.x, self.K, ids=self.ids, weights=self.rw,
+                                logits=self.logits)
+
+    def dominant_call(self, i):
+        self.step(i)
+
+    def value(self, sec_per_step):
+        return self.step_bytes / sec_per_step / 1e9
+
+    def kernel_rate(self, sec):
+        return self.kernel_bytes / sec / 1e9
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        inp = self.inp
+
+        def once():
+            oracle.route_topk(oracle.router_logits(inp["w_router"], inp["x"]).astype("float32"), self.K)
+        reps, t = _repeat(once, budget_s)
+        nb = reps * self.kernel_bytes
+        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
+                    sample=f"all {self.T} tokens (double logits, top-k, softmax) x {reps}, {t:.1f} s")
+
+
 def make(name, qg, torch, warm):
     if "_gemv_b" in name:
         return GemvBatch(qg, torch, name, warm)
@@ -398,6 +449,8 @@ def make(name, qg, torch, warm):
         return RmsnormQ81(qg, torch, warm)
     if name == "moe_q4_k":
         return Moe(qg, torch, warm)
+    if name == "router_topk":
+        return Router(qg, torch, warm)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -523,7 +576,7 @@ def main():
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
-                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, q5_k_mmq, "
+                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, q5_k_mmq, router_topk, "
                          "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")

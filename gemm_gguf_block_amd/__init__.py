@@ -232,7 +232,8 @@ def qgemm_q5_k_mmq(w, aq, m, n, k, c=None, stream=None):
 
 def moe_router_topk(w_router, x, top_k, ids=None, weights=None, logits=None, stream=None):
     """(ids int32 [T][top_k], weights f32 [T][top_k]) for x f32 [T][H] and the
-    router f32 [E][H]; `logits` (f32 [T][E]) receives the logits when given."""
+    router f32 [E][H]; the logits (f32 [T][E]) are written to `logits`, which is
+    allocated when not given."""
     import torch
     E, H = w_router.shape
     T = x.shape[0]
@@ -240,7 +241,9 @@ def moe_router_topk(w_router, x, top_k, ids=None, weights=None, logits=None, str
         ids = _empty((T, top_k), torch.int32, x)
     if weights is None:
         weights = _empty((T, top_k), torch.float32, x)
-    pl = None if logits is None else _need(logits, torch.float32, T * E * 4, "logits")
+    if logits is None:
+        logits = _empty((T, E), torch.float32, x)
+    pl = _need(logits, torch.float32, T * E * 4, "logits")
     _check("moe_router_topk", lib().moe_router_topk(
         _need(w_router, torch.float32, E * H * 4, "w_router"), _need(x, torch.float32, T * H * 4, "x"),
         _need(ids, torch.int32, T * top_k * 4, "ids"), _need(weights, torch.float32, T * top_k * 4, "weights"),

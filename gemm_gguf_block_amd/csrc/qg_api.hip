@@ -200,12 +200,12 @@ QG_EXPORT qg_status qgemm_q6_k_mmq(const void *w, const void *aq, float *c, int6
 QG_EXPORT qg_status moe_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights,
                                     float *logits, int64_t n_tok, int64_t n_expert, int64_t n_embd, int64_t top_k,
                                     hipStream_t stream) {
-  if (!w_router || (n_tok > 0 && (!x || !ids || !weights))) return QG_ERR_NULL;  // per-token buffers may be null when empty
+  if (!w_router || (n_tok > 0 && (!x || !ids || !weights || !logits))) return QG_ERR_NULL;  // may be null when empty
   if (n_tok < 0 || n_tok > kMaxRows || n_expert < 1 || n_expert > 256 || top_k < 1 || top_k > 64 ||
-      top_k > n_expert || n_embd < 4 || n_embd % 4 != 0 || n_embd > 8192)
+      top_k > n_expert || n_embd < 4 || n_embd % 4 != 0 || n_embd > 65536)
     return QG_ERR_SHAPE;
   if (!aligned(w_router, 16) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4) ||
-      (logits && !aligned(logits, 4)))
+      !aligned(logits, 4))
     return QG_ERR_ALIGN;
   if (n_tok == 0) return QG_OK;
   qg_status st = check_device();

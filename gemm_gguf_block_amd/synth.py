@@ -52,6 +52,9 @@ WORKLOADS = {
     "q5_k_mmq": dict(fmt="q5_k", m=512, n=4096, k=4096, seed=1009),
     # the activation prologue of a 512-token prefill at hidden size 4096
     "rmsnorm_q8_1": dict(rows=512, k=4096, eps=1e-5, seed=1007),
+    # the router in front of the MoE FFN above: f32 [128][2048] router, 16
+    # tokens, 8 experts each
+    "router_topk": dict(n_expert=128, n_embd=2048, n_tok=16, top_k=8, seed=1010),
 }
 
 
@@ -333,4 +336,7 @@ def workload(name: str, **override):
         ids, rw = routing(seed, p["n_tok"], E, p["top_k"])
         return dict(p, w_gu=w_gu.reshape(E, -1), w_down=w_dn.reshape(E, -1),
                     x=normal(seed, T_X, (p["n_tok"], H)), ids=ids, weights=rw)
+    if name == "router_topk":
+        E, H, T = p["n_expert"], p["n_embd"], p["n_tok"]
+        return dict(p, w_router=normal(seed, T_W, (E, H), std=0.02), x=normal(seed, T_X, (T, H)))
     raise KeyError(name)

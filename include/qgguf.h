@@ -197,7 +197,8 @@ size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_exp
 
 /*
  * moe_router_topk -- the router that makes the routing table moe_qgemv_q4_k
- * takes, in one launch.  Per token t:
+ * takes: two launches on `stream` (the logits, then the selection).  Per
+ * token t:
  *   logits[t][e] = sum_h w_router[e][h] * x[t][h]           (fp32)
  *   ids[t][0..top_k-1]: the top_k experts by logit, larger first, equal
  *                       logits in increasing expert order
@@ -206,10 +207,11 @@ size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int64_t n_exp
  * use; "models").  The router matrix is f32, as in their Q4_K_M files.
  *   w_router : f32 [n_expert][n_embd];  x : f32 [n_tok][n_embd] (16-byte aligned)
  *   ids      : int32 [n_tok][top_k], weights : f32 [n_tok][top_k], written
- *   logits   : f32 [n_tok][n_expert] or NULL (written when given)
+ *   logits   : f32 [n_tok][n_expert], written (the selection reads them back);
+ *              each logit is summed in an order that depends on n_embd alone
  *   n_expert in [1, 256];  top_k in [1, min(64, n_expert)];
- *   n_embd a multiple of 4 in [4, 8192];  n_tok = 0 does nothing (x, ids and
- *   weights may then be NULL)
+ *   n_embd a multiple of 4 in [4, 65536];  n_tok = 0 does nothing (x, ids,
+ *   weights and logits may then be NULL)
  * NaN logits are not defined.
  */
 qg_status moe_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights, float *logits,

@@ -216,13 +216,15 @@ def test_rmsnorm_quantize_validation(lib):
 def test_router_validation(lib):
     f = lib.moe_router_topk
     o = P((1 << 20) + 8192)
-    assert f(None, A16b, o, o, None, 2, 128, 2048, 8, None) == NULL
-    assert f(A16, A16b, None, o, None, 2, 128, 2048, 8, None) == NULL
-    assert f(A16, A16b, o, o, None, 2, 300, 2048, 8, None) == SHAPE      # more than 256 experts
-    assert f(A16, A16b, o, o, None, 2, 128, 2048, 65, None) == SHAPE     # top_k above 64
-    assert f(A16, A16b, o, o, None, 2, 4, 2048, 5, None) == SHAPE        # top_k above n_expert
-    assert f(A16, A16b, o, o, None, 2, 128, 2050, 8, None) == SHAPE      # n_embd not a multiple of 4
-    assert f(A16, A16b, o, o, None, 2, 128, 16384, 8, None) == SHAPE     # n_embd above 8192
-    assert f(MIS, A16b, o, o, None, 2, 128, 2048, 8, None) == ALIGN
-    assert f(A16, A16b, P((1 << 20) + 2), o, None, 2, 128, 2048, 8, None) == ALIGN
-    assert f(A16, A16b, o, o, None, 0, 128, 2048, 8, None) == OK
+    assert f(None, A16b, o, o, o, 2, 128, 2048, 8, None) == NULL
+    assert f(A16, A16b, None, o, o, 2, 128, 2048, 8, None) == NULL
+    assert f(A16, A16b, o, o, None, 2, 128, 2048, 8, None) == NULL       # logits are required
+    assert f(A16, A16b, o, o, o, 2, 300, 2048, 8, None) == SHAPE         # more than 256 experts
+    assert f(A16, A16b, o, o, o, 2, 128, 2048, 65, None) == SHAPE        # top_k above 64
+    assert f(A16, A16b, o, o, o, 2, 4, 2048, 5, None) == SHAPE           # top_k above n_expert
+    assert f(A16, A16b, o, o, o, 2, 128, 2050, 8, None) == SHAPE         # n_embd not a multiple of 4
+    assert f(A16, A16b, o, o, o, 2, 128, 1 << 17, 8, None) == SHAPE      # n_embd above 65536
+    assert f(MIS, A16b, o, o, o, 2, 128, 2048, 8, None) == ALIGN
+    assert f(A16, A16b, P((1 << 20) + 2), o, o, 2, 128, 2048, 8, None) == ALIGN
+    assert f(A16, A16b, o, o, P((1 << 20) + 2), 2, 128, 2048, 8, None) == ALIGN
+    assert f(A16, None, None, None, None, 0, 128, 2048, 8, None) == OK    # nothing to do

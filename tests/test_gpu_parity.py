@@ -563,7 +563,8 @@ def _check_router_stagewise(orc, wr, x, k, ids, w, logits):
 
 
 @pytest.mark.parametrize("T,E,H,k", [(1, 8, 4, 1), (16, 128, 2048, 8), (33, 64, 256, 2), (5, 256, 8192, 64),
-                                     (7, 40, 1024, 40), (3, 128, 2048, 1)])
+                                     (7, 40, 1024, 40), (3, 128, 2048, 1), (9, 7, 512, 3), (2, 16, 16384, 4),
+                                     (130, 128, 2048, 8)])
 def test_router_topk_stagewise(env, T, E, H, k):
     qg, orc, torch, dev = env
     wr, x = _router_case(T * E + H, T, E, H)
