@@ -19,6 +19,10 @@ types -- blazr README, "Model Formats > GGUF" -- but give no layout):
 * Q5_K: as Q4_K with 32 levels: scale = (hi-lo)/31, q clamped to [0, 31].
 * Q6_K: per 16-value sub-block, scale = amax/31; d = max(scale)/127;
   int8 sc = round(scale/d); q = round(w/(d*sc)) + 32 clamped to [0, 63].
+* Q4_0 / Q5_0: per 32 values, v = the value of largest magnitude (sign kept),
+  d = v/-8 (Q4_0) or v/-16 (Q5_0), so that v takes the lowest code;
+  q = round(w/d) + 8 (+ 16) clamped to [0, 15] ([0, 31]), from the
+  fp16-rounded d.
 
 "round" is half away from zero.  Shapes and distributions of the five
 workloads (``WORKLOADS``) follow the workload descriptions: weights N(0, 0.02),
@@ -29,8 +33,10 @@ from __future__ import annotations
 import numpy as np
 
 Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES, Q5_K_BYTES = 34, 36, 144, 210, 176
-BLOCK_BYTES = {"q8_0": Q8_0_BYTES, "q8_1": Q8_1_BYTES, "q4_k": Q4_K_BYTES, "q6_k": Q6_K_BYTES, "q5_k": Q5_K_BYTES}
-BLOCK_ELEMS = {"q8_0": 32, "q8_1": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256}
+Q4_0_BYTES, Q5_0_BYTES = 18, 22
+BLOCK_BYTES = {"q8_0": Q8_0_BYTES, "q8_1": Q8_1_BYTES, "q4_k": Q4_K_BYTES, "q6_k": Q6_K_BYTES, "q5_k": Q5_K_BYTES,
+               "q4_0": Q4_0_BYTES, "q5_0": Q5_0_BYTES}
+BLOCK_ELEMS = {"q8_0": 32, "q8_1": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256, "q4_0": 32, "q5_0": 32}
 
 # tensor ids within a workload seed
 T_W, T_X, T_ROUTE, T_WDOWN = 0, 1, 2, 3
@@ -50,6 +56,12 @@ WORKLOADS = {
     "q6_k_mmq": dict(fmt="q6_k", m=512, n=4096, k=14336, seed=1005),
     "q8_0_mmq": dict(fmt="q8_0", m=512, n=4096, k=4096, seed=1006),
     "q5_k_mmq": dict(fmt="q5_k", m=512, n=4096, k=4096, seed=1009),
+    # the 32-value types of Q4_0 / Q5_0 files at the Llama-3-8B FFN shape, and
+    # their prefill at 512 tokens
+    "q4_0_gemv": dict(fmt="q4_0", n=14336, k=4096, seed=1011),
+    "q5_0_gemv": dict(fmt="q5_0", n=14336, k=4096, seed=1012),
+    "q4_0_mmq": dict(fmt="q4_0", m=512, n=4096, k=4096, seed=1013),
+    "q5_0_mmq": dict(fmt="q5_0", m=512, n=4096, k=4096, seed=1014),
     # the activation prologue of a 512-token prefill at hidden size 4096
     "rmsnorm_q8_1": dict(rows=512, k=4096, eps=1e-5, seed=1007),
     # the router in front of the MoE FFN above: f32 [128][2048] router, 16
@@ -244,8 +256,58 @@ def quantize_weights_q6_k(W: np.ndarray) -> np.ndarray:
     return _rows_in_chunks(W, conv, row_bytes("q6_k", k))
 
 
+def pack_q4_0(d16: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q4_0 fields into 18-byte blocks: d16 [nb] fp16 bits, q [nb][32]
+    codes 0..15; byte 2 + j holds q[j] (low nibble) and q[j + 16] (high)."""
+    q = np.asarray(q, dtype=np.int64)
+    nb = q.shape[0]
+    blk = np.zeros((nb, Q4_0_BYTES), np.uint8)
+    blk[:, 0:2] = np.asarray(d16, np.uint16).reshape(nb).view(np.uint8).reshape(nb, 2)
+    blk[:, 2:18] = ((q[:, :16] & 15) | ((q[:, 16:] & 15) << 4)).astype(np.uint8)
+    return blk
+
+
+def pack_q5_0(d16: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q5_0 fields into 22-byte blocks: d16 [nb] fp16 bits, q [nb][32]
+    codes 0..31; bytes 2..5 hold the fifth bits (bit i of that little-endian
+    word for q[i]), bytes 6..21 the low nibbles as in Q4_0."""
+    q = np.asarray(q, dtype=np.int64)
+    nb = q.shape[0]
+    blk = np.zeros((nb, Q5_0_BYTES), np.uint8)
+    blk[:, 0:2] = np.asarray(d16, np.uint16).reshape(nb).view(np.uint8).reshape(nb, 2)
+    qh = (((q >> 4) & 1) << np.arange(32, dtype=np.int64)[None, :]).sum(axis=1).astype(np.uint32)
+    blk[:, 2:6] = qh.astype("<u4").view(np.uint8).reshape(nb, 4)
+    blk[:, 6:22] = ((q[:, :16] & 15) | ((q[:, 16:] & 15) << 4)).astype(np.uint8)
+    return blk
+
+
+def _quantize_weights_legacy(W: np.ndarray, bits: int) -> np.ndarray:
+    n, k = W.shape
+    assert k % 32 == 0
+    half = 1 << (bits - 1)
+    fmt = "q4_0" if bits == 4 else "q5_0"
+
+    def conv(X):
+        X = X.reshape(-1, 32)
+        v = X[np.arange(X.shape[0]), np.abs(X).argmax(axis=1)]
+        d = _f16_val(v / np.float32(-half))
+        q = np.clip(_round_away(_div(X, d[:, None])) + half, 0, 2 * half - 1)
+        pack = pack_q4_0 if bits == 4 else pack_q5_0
+        return pack(d.astype(np.float16).view(np.uint16), q.astype(np.int64))
+
+    return _rows_in_chunks(W, conv, row_bytes(fmt, k))
+
+
+def quantize_weights_q4_0(W: np.ndarray) -> np.ndarray:
+    return _quantize_weights_legacy(W, 4)
+
+
+def quantize_weights_q5_0(W: np.ndarray) -> np.ndarray:
+    return _quantize_weights_legacy(W, 5)
+
+
 QUANTIZE_WEIGHTS = {"q8_0": quantize_weights_q8_0, "q4_k": quantize_weights_q4_k, "q6_k": quantize_weights_q6_k,
-                    "q5_k": quantize_weights_q5_k}
+                    "q5_k": quantize_weights_q5_k, "q4_0": quantize_weights_q4_0, "q5_0": quantize_weights_q5_0}
 
 
 def weights(fmt: str, n: int, k: int, seed: int, tensor: int = T_W, std: float = 0.02,
@@ -295,7 +357,8 @@ def random_blocks(fmt: str, rows: int, k: int, seed: int, tensor: int = T_W,
     g = rng(seed, tensor)
     nb = k // BLOCK_ELEMS[fmt]
     blk = g.integers(0, 256, (rows * nb, BLOCK_BYTES[fmt]), dtype=np.uint8)
-    offs = {"q8_0": [0], "q8_1": [0, 2], "q4_k": [0, 2], "q6_k": [208], "q5_k": [0, 2]}[fmt]
+    offs = {"q8_0": [0], "q8_1": [0, 2], "q4_k": [0, 2], "q6_k": [208], "q5_k": [0, 2], "q4_0": [0],
+            "q5_0": [0]}[fmt]
     for o in offs:
         bits = random_f16_bits(g, rows * nb, lo_exp, hi_exp)
         blk[:, o:o + 2] = bits.view(np.uint8).reshape(-1, 2)

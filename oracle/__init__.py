@@ -21,6 +21,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES, Q5_K_BYTES = 34, 36, 144, 210, 176
+Q4_0_BYTES, Q5_0_BYTES = 18, 22
+FMT_CODE = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "q5_k": 3, "q4_0": 4, "q5_0": 5}
 
 
 def build() -> str:
@@ -63,6 +65,18 @@ def _declare(L):
         "orc_unpack_q4_k": [_P, _P, _P, _P, _P, _P],
         "orc_unpack_q5_k": [_P, _P, _P, _P, _P, _P],
         "orc_unpack_q6_k": [_P, _P, _P, _P],
+        "orc_unpack_q4_0": [_P, _P, _P],
+        "orc_unpack_q5_0": [_P, _P, _P],
+        "orc_dequant_q4_0": [_P, _P, _I, _I],
+        "orc_dequant_q5_0": [_P, _P, _I, _I],
+        "orc_qgemv_q4_0": [_P, _P, _P, _I, _I, _P, _I],
+        "orc_qgemv_q5_0": [_P, _P, _P, _I, _I, _P, _I],
+        "orc_blockdots_q4_0": [_P, _P, _P, _I, _I],
+        "orc_blockdots_q5_0": [_P, _P, _P, _I, _I],
+        "orc_qgemm_q4_0": [_P, _P, _P, _I, _I, _I, _P, _I],
+        "orc_qgemm_q5_0": [_P, _P, _P, _I, _I, _I, _P, _I],
+        "orc_blockdots_q4_0_mmq": [_P, _P, _P, _I, _I, _I],
+        "orc_blockdots_q5_0_mmq": [_P, _P, _P, _I, _I, _I],
         "orc_dequant_q8_0": [_P, _P, _I, _I],
         "orc_dequant_q8_1": [_P, _P, _I, _I],
         "orc_dequant_q4_k": [_P, _P, _I, _I],
@@ -173,8 +187,18 @@ def unpack_q6_k(block):
     return float(d[0]), sc, q
 
 
+def unpack_legacy(fmt, block):
+    """(d, q[32]) of one Q4_0 (q in 0..15) or Q5_0 (q in 0..31) block."""
+    block = _c(block, np.uint8)
+    d = np.zeros(1, np.float32)
+    q = np.zeros(32, np.int32)
+    getattr(lib(), "orc_unpack_" + fmt)(_ptr(block), _ptr(d), _ptr(q))
+    return float(d[0]), q
+
+
 def dequant(fmt, w, rows, k):
-    """Dequantize `rows` rows of format fmt ('q8_0','q8_1','q4_k','q5_k','q6_k') to f64."""
+    """Dequantize `rows` rows of format fmt ('q8_0','q8_1','q4_k','q5_k','q6_k',
+    'q4_0','q5_0') to f64."""
     w = _c(w, np.uint8)
     out = np.empty((rows, k), np.float64)
     getattr(lib(), "orc_dequant_" + fmt)(_ptr(w), _ptr(out), rows, k)
@@ -195,13 +219,13 @@ def qgemv(fmt, w, xq, n, k, rows=None):
 
 
 def blockdots(fmt, w, xq, n, k):
-    """Per-block int32 dots.  q8_0: D[n][k/32]; q4_k, q5_k: (D[n][k/32], S[k/32]);
-    q6_k: D[n][k/16]."""
+    """Per-block int32 dots.  q8_0, q4_0, q5_0: D[n][k/32]; q4_k, q5_k:
+    (D[n][k/32], S[k/32]); q6_k: D[n][k/16]."""
     w = _c(w, np.uint8)
     xq = _c(xq, np.uint8)
-    if fmt == "q8_0":
+    if fmt in ("q8_0", "q4_0", "q5_0"):
         D = np.empty((n, k // 32), np.int32)
-        lib().orc_blockdots_q8_0(_ptr(w), _ptr(xq), _ptr(D), n, k)
+        getattr(lib(), "orc_blockdots_" + fmt)(_ptr(w), _ptr(xq), _ptr(D), n, k)
         return D
     if fmt in ("q4_k", "q5_k"):
         D = np.empty((n, k // 32), np.int32)
@@ -219,14 +243,14 @@ def qgemv_factored(fmt, w, xq, n, k):
     w = _c(w, np.uint8)
     xq = _c(xq, np.uint8)
     y = np.empty(n, np.float64)
-    lib().orc_qgemv_factored({"q8_0": 0, "q4_k": 1, "q6_k": 2, "q5_k": 3}[fmt], _ptr(w), _ptr(xq), _ptr(y), n, k)
+    lib().orc_qgemv_factored(FMT_CODE[fmt], _ptr(w), _ptr(xq), _ptr(y), n, k)
     return y
 
 
 # ----------------------------------------------------------------------- mmq
 def qgemm(fmt, w, aq, m, n, k, pairs=None):
-    """C[m][n] = sum_k a^[m,k] w^[n,k] in double, for fmt 'q4_k', 'q5_k', 'q6_k'
-    or 'q8_0' weights.  `pairs` (array [P][2] of (m, n)) selects entries; then a
+    """C[m][n] = sum_k a^[m,k] w^[n,k] in double, for fmt 'q4_k', 'q5_k', 'q6_k',
+    'q8_0', 'q4_0' or 'q5_0' weights.  `pairs` (array [P][2] of (m, n)) selects entries; then a
     1-D array of P values is returned."""
     fn = getattr(lib(), "orc_qgemm_" + fmt)
     w = _c(w, np.uint8)

@@ -16,7 +16,9 @@
  *     bytes of nibbles (w = d*sc*q - dmin*m); Q6_K = 128 bytes low nibbles,
  *     64 bytes high 2-bit pairs, 16 int8 scales, fp16 d (w = d*sc*(q-32));
  *     Q5_K = Q4_K's header, 32 bytes of fifth bits, 128 bytes of nibbles
- *     (w = d*sc*q - dmin*m with q in 0..31).
+ *     (w = d*sc*q - dmin*m with q in 0..31); the 32-value types Q4_0 = fp16 d
+ *     + 16 bytes of nibbles (w = d*(q - 8)) and Q5_0 = fp16 d + 32 fifth bits
+ *     + 16 bytes of nibbles (w = d*(q - 16)), two more of those others.
  *
  * Everything is computed in double from the stored fields.  The dequantizers
  * and the integer block-dot routines decode the fields independently of each
@@ -34,6 +36,8 @@
 #define B_Q4_K 144
 #define B_Q6_K 210
 #define B_Q5_K 176
+#define B_Q4_0 18
+#define B_Q5_0 22
 
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format definition.       */
@@ -214,6 +218,30 @@ void orc_unpack_q5_k(const uint8_t *blk, float *d, float *dmin, int32_t *sc, int
     }
 }
 
+/* Decode one Q4_0 block: element i < 16 is the low nibble of qs[i] (bytes
+ * 2..17), element 16 + i the high nibble; q in 0..15, w = d*(q - 8). */
+void orc_unpack_q4_0(const uint8_t *blk, float *d, int32_t *q)
+{
+    *d = orc_f16_to_f32(rd16(blk));
+    const uint8_t *qs = blk + 2;
+    for (int i = 0; i < QK; ++i)
+        q[i] = (i < 16) ? (qs[i] & 0x0f) : (qs[i - 16] >> 4);
+}
+
+/* Decode one Q5_0 block: fp16 d, then qh (bytes 2..5): bit i of that
+ * little-endian 32-bit field is element i's fifth bit; the low four bits are
+ * placed as in Q4_0 (qs at bytes 6..21).  q in 0..31, w = d*(q - 16). */
+void orc_unpack_q5_0(const uint8_t *blk, float *d, int32_t *q)
+{
+    *d = orc_f16_to_f32(rd16(blk));
+    const uint8_t *qh = blk + 2, *qs = blk + 6;
+    for (int i = 0; i < QK; ++i) {
+        int nib = (i < 16) ? (qs[i] & 0x0f) : (qs[i - 16] >> 4);
+        int hb = (qh[i / 8] >> (i % 8)) & 1;
+        q[i] = nib | (hb << 4);
+    }
+}
+
 /* Decode one Q6_K superblock.  q[i] is element i's 6-bit code (0..63). */
 void orc_unpack_q6_k(const uint8_t *blk, float *d, int32_t *sc, int32_t *q)
 {
@@ -294,6 +322,32 @@ void orc_dequant_q5_k(const uint8_t *w, double *out, int64_t rows, int64_t k)
         }
 }
 
+void orc_dequant_q4_0(const uint8_t *w, double *out, int64_t rows, int64_t k)
+{
+    int64_t nb = k / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float d;
+            int32_t q[QK];
+            orc_unpack_q4_0(w + (r * nb + b) * B_Q4_0, &d, q);
+            for (int i = 0; i < QK; ++i)
+                out[r * k + b * QK + i] = (double)d * (q[i] - 8);
+        }
+}
+
+void orc_dequant_q5_0(const uint8_t *w, double *out, int64_t rows, int64_t k)
+{
+    int64_t nb = k / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float d;
+            int32_t q[QK];
+            orc_unpack_q5_0(w + (r * nb + b) * B_Q5_0, &d, q);
+            for (int i = 0; i < QK; ++i)
+                out[r * k + b * QK + i] = (double)d * (q[i] - 16);
+        }
+}
+
 void orc_dequant_q6_k(const uint8_t *w, double *out, int64_t rows, int64_t k)
 {
     int64_t ns = k / QKK;
@@ -364,6 +418,18 @@ void orc_qgemv_q6_k(const uint8_t *w, const uint8_t *xq, double *y, int64_t n, i
     gemv_plain(orc_dequant_q6_k, (k / QKK) * B_Q6_K, w, xq, y, n, k, sel, nsel);
 }
 
+void orc_qgemv_q4_0(const uint8_t *w, const uint8_t *xq, double *y, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    gemv_plain(orc_dequant_q4_0, (k / QK) * B_Q4_0, w, xq, y, n, k, sel, nsel);
+}
+
+void orc_qgemv_q5_0(const uint8_t *w, const uint8_t *xq, double *y, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    gemv_plain(orc_dequant_q5_0, (k / QK) * B_Q5_0, w, xq, y, n, k, sel, nsel);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Per-block integer dots (the quantities the GPU must reproduce exactly).    */
 /* Decoding here is written directly against the byte layout, separately     */
@@ -384,6 +450,45 @@ void orc_blockdots_q8_0(const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t
                 acc += (int32_t)qw[i] * qa[i];
             D[r * nb + b] = acc;
         }
+}
+
+/* Q4_0 and Q5_0: D[n][b] = sum_{i<32} (q[i] - off) * qa[i], off = 8 or 16.
+ * Byte j of qs carries elements j (low nibble) and j + 16 (high nibble); for
+ * Q5_0 the fifth bits are read as one little-endian 32-bit word. */
+static void blockdots_legacy(int five, const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t n, int64_t k)
+{
+    int64_t nb = k / QK;
+    int bytes = five ? B_Q5_0 : B_Q4_0, off = five ? 16 : 8;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = w + (r * nb + b) * bytes;
+            uint32_t qh = 0;
+            if (five)
+                qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+            const uint8_t *qs = blk + (five ? 6 : 2);
+            const int8_t *qa = (const int8_t *)(xq + b * B_Q8_1 + 4);
+            int32_t acc = 0;
+            for (int j = 0; j < 16; ++j) {
+                int lo = qs[j] & 0x0f, hi = qs[j] >> 4;
+                if (five) {
+                    lo |= (int)((qh >> j) & 1u) << 4;
+                    hi |= (int)((qh >> (j + 16)) & 1u) << 4;
+                }
+                acc += (lo - off) * qa[j] + (hi - off) * qa[j + 16];
+            }
+            D[r * nb + b] = acc;
+        }
+}
+
+void orc_blockdots_q4_0(const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t n, int64_t k)
+{
+    blockdots_legacy(0, w, xq, D, n, k);
+}
+
+void orc_blockdots_q5_0(const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t n, int64_t k)
+{
+    blockdots_legacy(1, w, xq, D, n, k);
 }
 
 /* Q4_K: D[n][8s+j] = sum_{i<32} q[i] * qa[i] over sub-block j of superblock s
@@ -474,7 +579,8 @@ void orc_blockdots_q6_k(const uint8_t *w, const uint8_t *xq, int32_t *D, int64_t
 
 /* GEMV from the integer dots, factored per block:
  *   Q8_0: sum_b dw*da*D;   Q4_K, Q5_K: sum_{s,j} da*(d*sc_j*D - dmin*m_j*S);
- *   Q6_K: sum_{s,j} d*sc_j*da*D.   fmt: 0 Q8_0, 1 Q4_K, 2 Q6_K, 3 Q5_K.
+ *   Q6_K: sum_{s,j} d*sc_j*da*D;   Q4_0, Q5_0: sum_b dw*da*D.
+ *   fmt: 0 Q8_0, 1 Q4_K, 2 Q6_K, 3 Q5_K, 4 Q4_0, 5 Q5_0.
  * Exactly equal (up to double rounding) to the plain definition. */
 void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y, int64_t n, int64_t k)
 {
@@ -483,6 +589,10 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
     int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nb + 1));
     if (fmt == 0)
         orc_blockdots_q8_0(w, xq, D, n, k);
+    else if (fmt == 4)
+        orc_blockdots_q4_0(w, xq, D, n, k);
+    else if (fmt == 5)
+        orc_blockdots_q5_0(w, xq, D, n, k);
     else if (fmt == 1)
         orc_blockdots_q4_k(w, xq, D, S, n, k);
     else if (fmt == 3)
@@ -491,9 +601,10 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
         orc_blockdots_q6_k(w, xq, D, n, k);
     for (int64_t r = 0; r < n; ++r) {
         double acc = 0.0;
-        if (fmt == 0) {
+        if (fmt == 0 || fmt == 4 || fmt == 5) {
+            int bytes = fmt == 0 ? B_Q8_0 : (fmt == 4 ? B_Q4_0 : B_Q5_0);
             for (int64_t b = 0; b < nb; ++b)
-                acc += h2d(w + (r * nb + b) * B_Q8_0) * h2d(xq + b * B_Q8_1) * D[r * nb + b];
+                acc += h2d(w + (r * nb + b) * bytes) * h2d(xq + b * B_Q8_1) * D[r * nb + b];
         } else if (fmt == 1 || fmt == 3) {
             for (int64_t s = 0; s < ns; ++s) {
                 const uint8_t *blk = w + (r * ns + s) * (fmt == 1 ? B_Q4_K : B_Q5_K);
@@ -523,7 +634,8 @@ void orc_qgemv_factored(int fmt, const uint8_t *w, const uint8_t *xq, double *y,
 /* ------------------------------------------------------------------------ */
 /* Prefill product (mmq), plain definition:                                   */
 /*   C[m][n] = sum_k a^[m,k] * w^[n,k]                                        */
-/* A is Q8_1 [M][K/32]; B is Q4_K, Q5_K or Q6_K [N][K/256] or Q8_0 [N][K/32]; */
+/* A is Q8_1 [M][K/32]; B is Q4_K, Q5_K or Q6_K [N][K/256] or Q8_0, Q4_0 or   */
+/* Q5_0 [N][K/32];                                                            */
 /* C row-major [M][N].  Both operands are dequantized exactly to double and   */
 /* dotted in k order.                                                         */
 /* `sel` picks (m, n) pairs: sel[2i], sel[2i+1]; NULL means every entry.      */
@@ -594,8 +706,21 @@ void orc_qgemm_q8_0(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, i
     qgemm_plain(orc_dequant_q8_0, (k / QK) * B_Q8_0, w, aq, c, m, n, k, sel, nsel);
 }
 
+void orc_qgemm_q4_0(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    qgemm_plain(orc_dequant_q4_0, (k / QK) * B_Q4_0, w, aq, c, m, n, k, sel, nsel);
+}
+
+void orc_qgemm_q5_0(const uint8_t *w, const uint8_t *aq, double *c, int64_t m, int64_t n, int64_t k,
+                    const int64_t *sel, int64_t nsel)
+{
+    qgemm_plain(orc_dequant_q5_0, (k / QK) * B_Q5_0, w, aq, c, m, n, k, sel, nsel);
+}
+
 /* mmq per-block dots: for every activation row, the GEMV block dots of that  */
-/* row against all weight rows.  Q4_K, Q5_K, Q8_0: D[m][n][k/32]; Q6_K: the  */
+/* row against all weight rows.  Q4_K, Q5_K and the 32-value types:          */
+/* D[m][n][k/32]; Q6_K: the                                                   */
 /* 16-value sub-block dots, D[m][n][k/16].                                    */
 void orc_blockdots_q4_k_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
 {
@@ -631,6 +756,20 @@ void orc_blockdots_q8_0_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int
     int64_t nb = k / QK;
     for (int64_t i = 0; i < m; ++i)
         orc_blockdots_q8_0(w, aq + i * nb * B_Q8_1, D + i * n * nb, n, k);
+}
+
+void orc_blockdots_q4_0_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
+{
+    int64_t nb = k / QK;
+    for (int64_t i = 0; i < m; ++i)
+        orc_blockdots_q4_0(w, aq + i * nb * B_Q8_1, D + i * n * nb, n, k);
+}
+
+void orc_blockdots_q5_0_mmq(const uint8_t *w, const uint8_t *aq, int32_t *D, int64_t m, int64_t n, int64_t k)
+{
+    int64_t nb = k / QK;
+    for (int64_t i = 0; i < m; ++i)
+        orc_blockdots_q5_0(w, aq + i * nb * B_Q8_1, D + i * n * nb, n, k);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -157,6 +157,17 @@ def test_q6_k_hand_block_fields_and_values(orc):
     assert [Fraction(v) for v in w] == want
 
 
+@pytest.mark.parametrize("fmt,d,off", [("q4_0", -2.0 ** -3, 8), ("q5_0", 2.0 ** -5, 16)])
+def test_legacy_hand_block_fields_and_values(orc, fmt, d, off):
+    fx, blk = _fixture_block(f"{fmt}_block.txt")
+    assert blk.size == (18 if fmt == "q4_0" else 22)
+    dd, q = orc.unpack_legacy(fmt, blk)
+    assert dd == d
+    assert np.array_equal(q, _ints(fx["q"][0]))
+    w = orc.dequant(fmt, blk, 1, 32)[0]
+    assert [Fraction(v) for v in w] == [Fraction(d) * (int(c) - off) for c in _ints(fx["q"][0])]
+
+
 def test_q8_0_hand_block_values(orc):
     fx, blk = _fixture_block("q8_0_block.txt")
     w = orc.dequant("q8_0", blk, 1, 32)[0]
@@ -202,6 +213,17 @@ def test_q5_k_pack_unpack_bijection(orc):
         assert np.array_equal(s2, sc[i]) and np.array_equal(m2, mn[i]) and np.array_equal(q2, qq[i])
 
 
+@pytest.mark.parametrize("fmt", ["q4_0", "q5_0"])
+def test_legacy_pack_unpack_bijection(orc, fmt):
+    """Every byte of a Q4_0 / Q5_0 block is a field: decoding random bytes and
+    packing the fields again must give the same bytes."""
+    nbytes, pack = (18, synth.pack_q4_0) if fmt == "q4_0" else (22, synth.pack_q5_0)
+    raw = np.random.default_rng(6).integers(0, 256, (300, nbytes), dtype=np.uint8)
+    qs = np.stack([orc.unpack_legacy(fmt, b)[1] for b in raw])
+    re = pack(raw[:, 0:2].copy().view(np.uint16).ravel(), qs)
+    assert np.array_equal(re, raw)
+
+
 def test_q6_k_pack_unpack_bijection(orc):
     g = np.random.default_rng(4)
     raw = g.integers(0, 256, (200, 210), dtype=np.uint8)
@@ -217,7 +239,7 @@ def _select_rows(n, k):
     return np.array([(r * 37) % k for r in range(n)])
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k", "q4_0", "q5_0"])
 def test_selection_matrix_gives_activation_entries(orc, fmt):
     """Weights that dequantize to one-hot rows must return exactly the selected
     dequantized activation entries: catches transposed operands, wrong block or
@@ -249,6 +271,15 @@ def test_selection_matrix_gives_activation_entries(orc, fmt):
             q[r * ns + c // 256, c % 256] = 16
         w = synth.pack_q5_k(np.full(n * ns, 0x2C00, np.uint16), np.zeros(n * ns, np.uint16), sc, mm, q)
         w = w.reshape(n, -1)
+    elif fmt in ("q4_0", "q5_0"):
+        # a negative d and code 0 give the selected weight exactly 1; the others
+        # sit at the zero code (8, or 16 whose fifth bit is set)
+        off = 8 if fmt == "q4_0" else 16
+        q = np.full((n * (k // 32), 32), off, np.int64)
+        for r, c in enumerate(cols):
+            q[r * (k // 32) + c // 32, c % 32] = 0
+        d16 = np.full(n * (k // 32), np.float16(-1.0 / off).view(np.uint16), np.uint16)
+        w = (synth.pack_q4_0 if fmt == "q4_0" else synth.pack_q5_0)(d16, q).reshape(n, -1)
     else:
         ns = k // 256
         sc = np.ones((n * ns, 16), np.int64)
@@ -265,7 +296,7 @@ def test_selection_matrix_gives_activation_entries(orc, fmt):
 
 
 # ---------------------------------------------- integer dots vs float dequant
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k", "q4_0", "q5_0"])
 def test_integer_block_dots_agree_with_dequant_dot(orc, fmt):
     """The factored sum over exact int32 block dots equals the plain double
     dequant-and-dot on fully random block bytes (finite fp16 fields)."""
@@ -278,7 +309,7 @@ def test_integer_block_dots_agree_with_dequant_dot(orc, fmt):
         assert np.max(np.abs(plain - fact)) <= 1e-12 * scale
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k", "q4_0", "q5_0"])
 def test_block_dots_brute_force_from_decoded_codes(orc, fmt):
     """Block dots from the oracle's blockdots routine vs numpy dots of the codes
     the (separately written) field decoder returns, on random bytes."""
@@ -298,6 +329,13 @@ def test_block_dots_brute_force_from_decoded_codes(orc, fmt):
         want = (codes * qa[None]).reshape(n, -1, 32).sum(axis=2)
         assert np.array_equal(D, want)
         assert np.array_equal(S, qa.reshape(-1, 32).sum(axis=1))
+    elif fmt in ("q4_0", "q5_0"):
+        D = orc.blockdots(fmt, w, xq, n, k)
+        nbytes, off = (18, 8) if fmt == "q4_0" else (22, 16)
+        codes = np.stack([np.concatenate([orc.unpack_legacy(fmt, b)[1] for b in row.reshape(-1, nbytes)])
+                          for row in w])
+        want = ((codes - off) * qa[None]).reshape(n, -1, 32).sum(axis=2)
+        assert np.array_equal(D, want)
     else:
         D = orc.blockdots("q6_k", w, xq, n, k)
         codes = np.stack([np.concatenate([orc.unpack_q6_k(b)[2] for b in row.reshape(-1, 210)])
@@ -344,10 +382,18 @@ def test_hand_superblock_dot_exact(orc):
     row = np.tile(blk, 8)[None]
     exact = sum(Fraction(((i % 32) - 16), 4) * Fraction(1, 8) * qa[i] for i in range(256))
     assert Fraction(orc.qgemv("q8_0", row, xq, 1, 256)[0]) == exact
+    # Q4_0 and Q5_0: eight copies of each hand block
+    for fmt, d, off in (("q4_0", Fraction(-1, 8), 8), ("q5_0", Fraction(1, 32), 16)):
+        fx, blk = _fixture_block(f"{fmt}_block.txt")
+        q = _ints(fx["q"][0])
+        row = np.tile(blk, 8)[None]
+        exact = sum(d * (int(q[i % 32]) - off) * Fraction(1, 8) * qa[i] for i in range(256))
+        assert Fraction(orc.qgemv(fmt, row, xq, 1, 256)[0]) == exact
+        assert Fraction(orc.qgemv_factored(fmt, row, xq, 1, 256)[0]) == exact
 
 
 # --------------------------------------------------- weight quantizers (data)
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k", "q4_0", "q5_0"])
 def test_weight_quantizer_roundtrip_bound(orc, fmt):
     g = np.random.default_rng(21)
     W = (g.standard_normal((64, 512)) * 0.02).astype(np.float32)
@@ -370,6 +416,16 @@ def test_weight_quantizer_roundtrip_bound(orc, fmt):
         frac_bad = np.mean(err > eff / 2 * (1 + 1e-5) + 1e-9)
         assert frac_bad < 0.01
         assert np.sqrt(np.mean(err ** 2)) < 0.6 * np.sqrt(np.mean(eff ** 2))
+    elif fmt in ("q4_0", "q5_0"):
+        # within half a step except where the top code clamps: the opposite
+        # extreme is at most off steps of the fp16-rounded d (relative error
+        # <= 2^-11) above the zero code, so it misses by at most one step plus
+        # off * 2^-11 of a step
+        nbytes, off = (18, 8) if fmt == "q4_0" else (22, 16)
+        d16 = np.abs(wq.reshape(-1, nbytes)[:, 0:2].copy().view(np.float16).astype(np.float64).ravel())
+        eb = err.reshape(-1, 32)
+        assert np.all(eb.max(axis=1) <= d16 * (1 + off * 2.0 ** -10))
+        assert np.mean(eb > (d16 / 2 * (1 + 1e-5))[:, None]) < 0.01
     else:
         effs = []
         for b in wq.reshape(-1, 210):
@@ -383,7 +439,8 @@ def test_weight_quantizer_roundtrip_bound(orc, fmt):
 
 
 # ------------------------------------------------------------------ mmq oracle
-@pytest.mark.parametrize("fmt,k", [("q4_k", 512), ("q5_k", 512), ("q6_k", 512), ("q8_0", 512), ("q8_0", 96)])
+@pytest.mark.parametrize("fmt,k", [("q4_k", 512), ("q5_k", 512), ("q6_k", 512), ("q8_0", 512), ("q8_0", 96),
+                                   ("q4_0", 512), ("q5_0", 96)])
 def test_mmq_rows_equal_gemv(orc, fmt, k):
     m, n = 5, 33
     w = synth.weights(fmt, n, k, seed=31)
@@ -403,7 +460,8 @@ def test_mmq_rows_equal_gemv(orc, fmt, k):
         assert np.array_equal(D[i], Dg[0] if fmt in ("q4_k", "q5_k") else Dg)
 
 
-@pytest.mark.parametrize("fmt,k", [("q4_k", 256), ("q5_k", 256), ("q6_k", 256), ("q8_0", 256), ("q8_0", 160)])
+@pytest.mark.parametrize("fmt,k", [("q4_k", 256), ("q5_k", 256), ("q6_k", 256), ("q8_0", 256), ("q8_0", 160),
+                                   ("q4_0", 160), ("q5_0", 256)])
 def test_mmq_against_numpy_matmul_of_dequantized(orc, fmt, k):
     m, n = 7, 19
     w = synth.random_blocks(fmt, n, k, seed=41, lo_exp=-10, hi_exp=0)
