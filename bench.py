@@ -6,7 +6,8 @@ quantized weights.  Default workload: the Q4_K decode GEMV at a Llama-3-8B FFN
 shape (n = 14336, k = 4096).  Other workloads: --workload q8_0_gemv,
 q6_k_gemv, q4_k_mmq, moe_q4_k, or all (one JSON line each); prefill products
 with the other weight types q6_k_mmq, q8_0_mmq, q5_k_mmq; the Q5_K GEMV
-q5_k_gemv (14336 x 4096); the RMSNorm + quantize
+q5_k_gemv (14336 x 4096); the 32-value types q4_0_gemv, q5_0_gemv (14336 x
+4096), q4_0_mmq, q5_0_mmq; the RMSNorm + quantize
 prologue rmsnorm_q8_1; the MoE router router_topk; small-batch GEMVs
 <fmt>_gemv_b<B> (the GEMV workload's weights against B <= 8 activation rows),
 or batch for the standard set of them.
@@ -50,12 +51,15 @@ def _cpu_threads():
 
 KERNEL_SOURCES = {
     "q4_k_gemv": ["qg_gemv.hip"], "q8_0_gemv": ["qg_gemv.hip"], "q6_k_gemv": ["qg_gemv.hip"],
-    "q5_k_gemv": ["qg_gemv.hip"],
+    "q5_k_gemv": ["qg_gemv.hip"], "q4_0_gemv": ["qg_gemv.hip"], "q5_0_gemv": ["qg_gemv.hip"],
+    "q4_0_mmq": ["qg_mmq.hip"], "q5_0_mmq": ["qg_mmq.hip"],
     "q4_k_mmq": ["qg_mmq.hip"], "q6_k_mmq": ["qg_mmq.hip"], "q8_0_mmq": ["qg_mmq.hip"], "q5_k_mmq": ["qg_mmq.hip"],
     "rmsnorm_q8_1": ["qg_quant.hip", "qg_quant.h"],
     "moe_q4_k": ["qg_moe.hip", "qg_quant.h"],
     "router_topk": ["qg_router.hip"],
 }
+GEMV_KERNEL = {"q8_0": "gemv_q8_0_pair_kernel", "q4_k": "gemv_q4k_kernel", "q6_k": "gemv_q6k_kernel",
+               "q5_k": "gemv_q5k_kernel", "q4_0": "gemv_q4_0_kernel", "q5_0": "gemv_q5_0_kernel"}
 BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8", "q6_k_gemv_b4", "q6_k_gemv_b8"]
 
 
@@ -136,7 +140,7 @@ class Gemv(Workload):
         self.xq = torch.empty(q81_bytes(self.k), dtype=torch.uint8, device=dev)
         self.y = torch.empty(self.n, dtype=torch.float32, device=dev)
         self.fn = getattr(qg, "qgemv_" + self.fmt)
-        self.dominant = "gemv_" + self.fmt.replace("_", "")
+        self.dominant = GEMV_KERNEL[self.fmt]
         # algorithmic bytes: every weight byte once, the activation, the output
         self.kernel_bytes = wbytes + q81_bytes(self.k) + 4 * self.n
         self.step_bytes = self.kernel_bytes + 4 * self.k + q81_bytes(self.k)  # + quantize's f32 read / Q8_1 write
@@ -576,7 +580,8 @@ def main():
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
                     help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
-                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, q5_k_mmq, router_topk, "
+                         "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, q5_k_mmq, router_topk, q4_0_gemv, q5_0_gemv, "
+                         "q4_0_mmq, q5_0_mmq, "
                          "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")

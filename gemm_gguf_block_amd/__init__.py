@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libqgguf.so")
 
 Q8_0_BYTES, Q8_1_BYTES, Q4_K_BYTES, Q6_K_BYTES = 34, 36, 144, 210
 _BLOCK = {"q8_0": (32, Q8_0_BYTES), "q8_1": (32, Q8_1_BYTES), "q4_k": (256, Q4_K_BYTES), "q6_k": (256, Q6_K_BYTES),
-          "q5_k": (256, 176)}
+          "q5_k": (256, 176), "q4_0": (32, 18), "q5_0": (32, 22)}
 
 STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_ALIGN", 4: "QG_ERR_WORKSPACE",
           5: "QG_ERR_NO_DEVICE", 6: "QG_ERR_ARCH", 7: "QG_ERR_LAUNCH"}
@@ -32,6 +32,8 @@ SIGNATURES = {
     "qgemv_q4_k": [_P, _P, _P, _I, _I, _P],
     "qgemv_q6_k": [_P, _P, _P, _I, _I, _P],
     "qgemv_q5_k": [_P, _P, _P, _I, _I, _P],
+    "qgemv_q4_0": [_P, _P, _P, _I, _I, _P],
+    "qgemv_q5_0": [_P, _P, _P, _I, _I, _P],
     "rmsnorm_quantize_q8_1": [_P, _P, ctypes.c_float, _P, _P, _I, _I, _P],
     "qgemv_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qgemv_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
@@ -40,6 +42,8 @@ SIGNATURES = {
     "qgemm_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qgemm_q5_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemm_q4_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qgemm_q5_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "moe_qgemv_q4_k_workspace_size": [_I, _I, _I, _I, _I],
     "moe_router_topk": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "moe_qgemv_q4_k": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
@@ -52,6 +56,10 @@ SIGNATURES = {
     "qg_blockdots_q4_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q6_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q5_k_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q4_0": [_P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q5_0": [_P, _P, _P, _I, _I, _P],
+    "qg_blockdots_q4_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q5_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
 }
 
 
@@ -160,6 +168,14 @@ def qgemv_q5_k(w, xq, n, k, y=None, stream=None):
     return _gemv("q5_k", w, xq, n, k, y, stream)
 
 
+def qgemv_q4_0(w, xq, n, k, y=None, stream=None):
+    return _gemv("q4_0", w, xq, n, k, y, stream)
+
+
+def qgemv_q5_0(w, xq, n, k, y=None, stream=None):
+    return _gemv("q5_0", w, xq, n, k, y, stream)
+
+
 def _gemv_batch(fmt, w, xq, b, n, k, y, stream):
     import torch
     if y is None:
@@ -230,6 +246,14 @@ def qgemm_q5_k_mmq(w, aq, m, n, k, c=None, stream=None):
     return _mmq("q5_k", w, aq, m, n, k, c, stream)
 
 
+def qgemm_q4_0_mmq(w, aq, m, n, k, c=None, stream=None):
+    return _mmq("q4_0", w, aq, m, n, k, c, stream)
+
+
+def qgemm_q5_0_mmq(w, aq, m, n, k, c=None, stream=None):
+    return _mmq("q5_0", w, aq, m, n, k, c, stream)
+
+
 def moe_router_topk(w_router, x, top_k, ids=None, weights=None, logits=None, stream=None):
     """(ids int32 [T][top_k], weights f32 [T][top_k]) for x f32 [T][H] and the
     router f32 [E][H]; the logits (f32 [T][E]) are written to `logits`, which is
@@ -294,13 +318,26 @@ def moe_workspace_regions(workspace, n_tok, top_k, n_ff, n_embd):
 
 
 # ------------------------------------------------------- per-block dots (tests)
-def blockdots_q8_0(w, xq, n, k, stream=None):
+def _blockdots_32(fmt, w, xq, n, k, stream):
     import torch
     D = _empty((n, k // 32), torch.int32, w)
-    _check("qg_blockdots_q8_0", lib().qg_blockdots_q8_0(
-        _need(w, torch.uint8, n * row_bytes("q8_0", k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
+    name = f"qg_blockdots_{fmt}"
+    _check(name, getattr(lib(), name)(
+        _need(w, torch.uint8, n * row_bytes(fmt, k), "w"), _need(xq, torch.uint8, row_bytes("q8_1", k), "xq"),
         _need(D, torch.int32, D.numel() * 4, "D"), n, k, _stream(stream)))
     return D
+
+
+def blockdots_q8_0(w, xq, n, k, stream=None):
+    return _blockdots_32("q8_0", w, xq, n, k, stream)
+
+
+def blockdots_q4_0(w, xq, n, k, stream=None):
+    return _blockdots_32("q4_0", w, xq, n, k, stream)
+
+
+def blockdots_q5_0(w, xq, n, k, stream=None):
+    return _blockdots_32("q5_0", w, xq, n, k, stream)
 
 
 def _blockdots_kmin(fmt, w, xq, n, k, stream):
@@ -353,6 +390,14 @@ def blockdots_q6_k_mmq(w, aq, m, n, k, stream=None):
 
 def blockdots_q8_0_mmq(w, aq, m, n, k, stream=None):
     return _blockdots_mmq("q8_0", w, aq, m, n, k, stream)
+
+
+def blockdots_q4_0_mmq(w, aq, m, n, k, stream=None):
+    return _blockdots_mmq("q4_0", w, aq, m, n, k, stream)
+
+
+def blockdots_q5_0_mmq(w, aq, m, n, k, stream=None):
+    return _blockdots_mmq("q5_0", w, aq, m, n, k, stream)
 
 
 def blockdots_q5_k_mmq(w, aq, m, n, k, stream=None):

@@ -43,11 +43,12 @@ qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_LAUNC
 constexpr int64_t kMaxK = int64_t(1) << 24;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
-// fmt 0 = Q8_0 (k % 32), 1 = Q4_K, 2 = Q6_K, 3 = Q5_K (k % 256)
+// fmt 0 = Q8_0 (k % 32), 1 = Q4_K, 2 = Q6_K, 3 = Q5_K (k % 256), 4 = Q4_0,
+// 5 = Q5_0 (k % 64: the kernel takes block pairs)
 qg_status check_gemv(int fmt, const void *w, const void *xq, const void *out, int64_t n, int64_t k) {
   if (!w || !xq || !out) return QG_ERR_NULL;
   if (n < 0 || k < 0 || n > kMaxRows || k > kMaxK) return QG_ERR_SHAPE;
-  if (k % (fmt == 0 ? 32 : 256) != 0) return QG_ERR_SHAPE;
+  if (k % (fmt == 0 ? 32 : (fmt >= 4 ? 64 : 256)) != 0) return QG_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
   return QG_OK;
 }
@@ -84,7 +85,7 @@ qg_status run_gemv_batch(int fmt, const void *w, const void *xq, float *y, int64
 qg_status check_mmq(int fmt, const void *w, const void *aq, const void *out, int64_t m, int64_t n, int64_t k) {
   if (!w || !aq || !out) return QG_ERR_NULL;
   if (m < 0 || n < 0 || k < 0 || m > kMaxRows || n > kMaxRows || k > kMaxK) return QG_ERR_SHAPE;
-  if (k % (fmt == 0 ? 32 : 256) != 0) return QG_ERR_SHAPE;
+  if (k % ((fmt == 0 || fmt >= 4) ? 32 : 256) != 0) return QG_ERR_SHAPE;  // 32-value block types: k % 32
   if (((m + 63) / 64) * ((n + 63) / 64) > kMaxRows) return QG_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(aq, 16) || !aligned(out, 4)) return QG_ERR_ALIGN;
   return QG_OK;
@@ -150,6 +151,16 @@ QG_EXPORT qg_status qgemv_q5_k(const void *w, const void *xq, float *y, int64_t 
   return st != QG_OK ? st : run_gemv(3, w, xq, y, nullptr, nullptr, n, k, stream);
 }
 
+QG_EXPORT qg_status qgemv_q4_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv(4, w, xq, y, n, k);
+  return st != QG_OK ? st : run_gemv(4, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemv_q5_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv(5, w, xq, y, n, k);
+  return st != QG_OK ? st : run_gemv(5, w, xq, y, nullptr, nullptr, n, k, stream);
+}
+
 QG_EXPORT qg_status qgemv_q8_0_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
                                      hipStream_t stream) {
   return run_gemv_batch(0, w, xq, y, b, n, k, stream);
@@ -195,6 +206,16 @@ QG_EXPORT qg_status qgemm_q5_k_mmq(const void *w, const void *aq, float *c, int6
 QG_EXPORT qg_status qgemm_q6_k_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
                                    hipStream_t stream) {
   return run_mmq(2, w, aq, c, nullptr, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemm_q4_0_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return run_mmq(4, w, aq, c, nullptr, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qgemm_q5_0_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                                   hipStream_t stream) {
+  return run_mmq(5, w, aq, c, nullptr, m, n, k, stream);
 }
 
 QG_EXPORT qg_status moe_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights,
@@ -283,6 +304,28 @@ QG_EXPORT qg_status qg_blockdots_q6_k(const void *w, const void *xq, int32_t *D,
                                       hipStream_t stream) {
   qg_status st = check_gemv(2, w, xq, D, n, k);
   return st != QG_OK ? st : run_gemv(2, w, xq, nullptr, D, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q4_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k,
+                                      hipStream_t stream) {
+  qg_status st = check_gemv(4, w, xq, D, n, k);
+  return st != QG_OK ? st : run_gemv(4, w, xq, nullptr, D, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q5_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k,
+                                      hipStream_t stream) {
+  qg_status st = check_gemv(5, w, xq, D, n, k);
+  return st != QG_OK ? st : run_gemv(5, w, xq, nullptr, D, nullptr, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q4_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_mmq(4, w, aq, nullptr, D, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q5_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_mmq(5, w, aq, nullptr, D, m, n, k, stream);
 }
 
 QG_EXPORT qg_status qg_blockdots_q8_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,

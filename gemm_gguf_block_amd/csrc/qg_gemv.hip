@@ -1,6 +1,7 @@
 // qg_gemv.hip -- batch-1 decode GEMV over Q8_0 / Q4_K / Q6_K weight blocks
 // against one Q8_1 activation row (the dp4a-style dot kernels the blazr README
-// lists for these three types, "Model Formats > GGUF", re-designed for gfx950).
+// lists for these three types, "Model Formats > GGUF", re-designed for gfx950),
+// and over Q5_K, Q4_0 and Q5_0, GGUF types that README runs on its generic path.
 //
 // Work decomposition (all three formats): a row is cut into units of 64
 // weights; L lanes (a power of two, <= 64) share a row and walk its units with
@@ -15,6 +16,8 @@
 //        qh[32h+16l..]: 16-value sub-blocks 8h+2g+l for g = 0..3.
 //   Q8_0 unit: a pair of blocks (68 bytes, dword aligned when the row has an
 //        even block count), else one block read with byte realignment.
+//   Q4_0 / Q5_0 unit: a pair of blocks (36 / 44 bytes, dword aligned; rows
+//        with an even block count only).
 //
 // With DUMP the same code writes the exact per-block int32 dots instead of y.
 #include <algorithm>
@@ -453,6 +456,136 @@ __global__ __launch_bounds__(256) void gemv_q8_0_single_kernel(const uint8_t *__
   }
 }
 
+// ---------------------------------------------------------------- Q4_0, Q5_0
+// Bits b0..b3 of h moved to bit 0 of bytes 0..3 (the four shifted copies of h
+// set disjoint bits, so the product carries nothing).
+__device__ __forceinline__ uint32_t spread4(uint32_t h) { return (h * 0x00204081u) & 0x01010101u; }
+
+// Rows with an even block count; unit = a block pair at a dword-aligned offset:
+//   Q4_0 (36 bytes): d0 | qs0[16] | d1 | qs1[16]
+//   Q5_0 (44 bytes): d0 | qh0[4] | qs0[16] | d1 | qh1[4] | qs1[16]
+// Byte j of qs holds codes j (low nibble) and 16 + j (high nibble); Q5_0's
+// fifth bits are bit i of the little-endian qh word.  The lane dots the stored
+// codes (0..15 / 0..31, non-negative bytes) with v_dot4 and subtracts
+// off * sum(qa): sum (q - off) qa exactly, off = 8 / 16.  sum(qa) is taken
+// once per unit and reused for the R rows.
+template <int FMT, int L, int R, bool DUMP>
+__device__ __forceinline__ void gemv_legacy_pair(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
+                                                 float *__restrict__ Y, int32_t *__restrict__ Dd, int n, int npair) {
+  constexpr bool kQ5 = FMT == 5;
+  constexpr int kPair = kQ5 ? 44 : 36;   // bytes per block pair
+  constexpr int kDw = kPair / 4;         // dwords per pair
+  constexpr int kOff = kQ5 ? 16 : 8;
+  constexpr int G = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (L - 1);
+  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+  const int64_t rb = (int64_t)npair * kPair;
+  const uint8_t *wrow = W + row0 * rb;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  if (row0 < n) {
+    for (int u = li; u < npair; u += L) {
+      uint32_t Wd[R][kDw];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r < n) {
+          const uint8_t *bp = wrow + r * rb + (int64_t)u * kPair;
+          const u32x4 w0 = ld16(bp), w1 = ld16(bp + 16);
+          Wd[r][0] = w0.x; Wd[r][1] = w0.y; Wd[r][2] = w0.z; Wd[r][3] = w0.w;
+          Wd[r][4] = w1.x; Wd[r][5] = w1.y; Wd[r][6] = w1.z; Wd[r][7] = w1.w;
+#pragma unroll
+          for (int i = 8; i < kDw; ++i) Wd[r][i] = ld4(bp + 4 * i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kDw; ++i) Wd[r][i] = 0u;
+        }
+      }
+      uint32_t A[18];
+      load_q8_1_pair(XQ + (int64_t)(2 * u) * kQ8_1Bytes, A);
+      const float da0 = h2f(A[0]), da1 = h2f(A[9]);
+      int sa0 = 0, sa1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sa0 = bsum4(A[1 + i], sa0);
+        sa1 = bsum4(A[10 + i], sa1);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // the two blocks' qs dwords, qh words and d halves
+        uint32_t Q0[4], Q1[4], h0 = 0u, h1 = 0u, d0, d1;
+        if constexpr (kQ5) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Q0[i] = align_bytes(Wd[r][i + 2], Wd[r][i + 1], 2);  // bytes 6..21
+            Q1[i] = Wd[r][7 + i];                                // bytes 28..43
+          }
+          h0 = align_bytes(Wd[r][1], Wd[r][0], 2);  // bytes 2..5
+          h1 = Wd[r][6];                             // bytes 24..27
+          d0 = Wd[r][0];
+          d1 = Wd[r][5] >> 16;                       // bytes 22..23
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Q0[i] = align_bytes(Wd[r][i + 1], Wd[r][i], 2);  // bytes 2..17
+            Q1[i] = Wd[r][5 + i];                            // bytes 20..35
+          }
+          d0 = Wd[r][0];
+          d1 = Wd[r][4] >> 16;                               // bytes 18..19
+        }
+        int D0 = 0, D1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t l0 = Q0[i] & 0x0F0F0F0Fu, u0 = (Q0[i] >> 4) & 0x0F0F0F0Fu;
+          uint32_t l1 = Q1[i] & 0x0F0F0F0Fu, u1 = (Q1[i] >> 4) & 0x0F0F0F0Fu;
+          if constexpr (kQ5) {
+            l0 |= spread4((h0 >> (4 * i)) & 0xFu) << 4;
+            u0 |= spread4((h0 >> (16 + 4 * i)) & 0xFu) << 4;
+            l1 |= spread4((h1 >> (4 * i)) & 0xFu) << 4;
+            u1 |= spread4((h1 >> (16 + 4 * i)) & 0xFu) << 4;
+          }
+          D0 = dot4(l0, A[1 + i], D0);   // codes 4i..4i+3
+          D0 = dot4(u0, A[5 + i], D0);   // codes 16+4i..
+          D1 = dot4(l1, A[10 + i], D1);
+          D1 = dot4(u1, A[14 + i], D1);
+        }
+        D0 -= kOff * sa0;
+        D1 -= kOff * sa1;
+        if (DUMP) {
+          if (row0 + r < n) {
+            Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * u] = D0;
+            Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * u + 1] = D1;
+          }
+        } else {
+          acc[r] += h2f(d0) * da0 * (float)D0 + h2f(d1) * da1 * (float)D1;
+        }
+      }
+    }
+  }
+  if (!DUMP) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = group_sum_last<L>(acc[r]);
+      if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
+    }
+  }
+}
+
+template <int L, int R, bool DUMP>
+__global__ __launch_bounds__(256) void gemv_q4_0_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
+                                                        float *__restrict__ Y, int32_t *__restrict__ Dd, int n,
+                                                        int npair) {
+  gemv_legacy_pair<4, L, R, DUMP>(W, XQ, Y, Dd, n, npair);
+}
+
+template <int L, int R, bool DUMP>
+__global__ __launch_bounds__(256) void gemv_q5_0_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
+                                                        float *__restrict__ Y, int32_t *__restrict__ Dd, int n,
+                                                        int npair) {
+  gemv_legacy_pair<5, L, R, DUMP>(W, XQ, Y, Dd, n, npair);
+}
+
 // ---------------------------------------------------------------- dispatch
 // Rows per lane group (R): each lane reuses its activation slice across R
 // rows and keeps R rows' worth of weight loads in flight.
@@ -530,6 +663,15 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
     QG_GEMV_SWITCH_PERSISTENT(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
+  } else if (fmt == 4 || fmt == 5) {
+    const int npair = (int)(k / 64);
+    const int L = lanes_per_row(npair);
+    const dim3 grid = gemv_grid(n, L, kRowsQ8_0);
+    if (fmt == 4) {
+      QG_GEMV_SWITCH(gemv_q4_0_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
+    } else {
+      QG_GEMV_SWITCH(gemv_q5_0_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
+    }
   } else if (fmt == 3) {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);

@@ -33,8 +33,8 @@ int64_t resident_blocks(int threads, size_t lds) {
 
 hipError_t launch_quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t k, hipStream_t stream);
 
-// fmt: 0 = Q8_0, 1 = Q4_K, 2 = Q6_K, 3 = Q5_K.  D/S non-null selects the per-block dot
-// dump instead of y.
+// fmt: 0 = Q8_0, 1 = Q4_K, 2 = Q6_K, 3 = Q5_K, 4 = Q4_0, 5 = Q5_0.  D/S
+// non-null selects the per-block dot dump instead of y.
 hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_t *D, int32_t *S, int64_t n,
                         int64_t k, hipStream_t stream);
 

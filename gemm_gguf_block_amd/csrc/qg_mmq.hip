@@ -1,5 +1,6 @@
 // qg_mmq.hip -- prefill product C[m][n] = sum_k a^[m,k] w^[n,k] with Q4_K,
-// Q5_K, Q6_K or Q8_0 weights and Q8_1 activations on gfx950 int8 matrix cores.
+// Q5_K, Q6_K, Q8_0, Q4_0 or Q5_0 weights and Q8_1 activations on gfx950 int8
+// matrix cores.
 //
 // The pages run this step as "in-shader dequant and dp4a mmq" (infr page,
 // "models") and as cooperative-matrix matmul (infr page, "Vulkan-first, Metal
@@ -9,9 +10,9 @@
 // step of k (one K-quant superblock, eight Q8_0 blocks) the workgroup stages in
 // LDS:
 //   A  Q8_1 qs as int8, plus per (row, block) d_a (and d_a*sum(qa) for Q4_K)
-//   B  the weight codes as int8 (Q4_K nibbles, Q6_K q - 32, Q8_0 qs), plus per
-//      (weight row, scale group) the group's factor (d*sc_j, d*sc_j, d) and for
-//      Q4_K -dmin*m_j
+//   B  the weight codes as int8 (Q4_K nibbles, Q6_K q - 32, Q8_0 qs, Q4_0
+//      q - 8, Q5_0 q - 16), plus per (weight row, scale group) the group's
+//      factor (d*sc_j, d*sc_j, d) and for Q4_K -dmin*m_j
 // double-buffered: the global loads of step s+2 are in flight while the MFMAs
 // of step s run.  Each 32-wide block of k is one v_mfma_i32_32x32x32_i8 -> the
 // exact int32 dots D of that block for the wave's 32x32 tile; Q6_K's 16-wide
@@ -39,12 +40,14 @@ constexpr int kBM = 64, kBN = 128;
 constexpr int kRow = 272;  // LDS bytes per staged row: 256 + 16 (spreads rows over banks)
 
 // Formats, numbered as the GEMV entry points number them.
-constexpr int kMQ8_0 = 0, kMQ4K = 1, kMQ6K = 2, kMQ5K = 3;
+constexpr int kMQ8_0 = 0, kMQ4K = 1, kMQ6K = 2, kMQ5K = 3, kMQ4_0 = 4, kMQ5_0 = 5;
 
 template <int FMT>
 struct MmqFmt {
   static constexpr int kGroups = FMT == kMQ6K ? 16 : 8;  // scale groups per 256-wide step
   static constexpr bool kMin = FMT == kMQ4K || FMT == kMQ5K;
+  // 32-value blocks: k need only be a multiple of 32 (the last step is ragged)
+  static constexpr bool kBlk32 = FMT == kMQ8_0 || FMT == kMQ4_0 || FMT == kMQ5_0;
   static constexpr int kRegs = (FMT == kMQ8_0 || FMT == kMQ5K) ? 5 : (FMT == kMQ6K ? 4 : 3);  // u32x4 staging
 };
 
@@ -83,7 +86,7 @@ __device__ __forceinline__ void put_factor(uint32_t (&f)[2], float x) {
 // Activation thread t (0..511) holds block t%8 of tile row t/8: x[0] = bytes
 // 0-15, x[1] = 16-31, x[2].x = 32-35.  Rows past the end of A or B load the last
 // row instead; they only feed outputs that are never stored.  Blocks past k
-// (Q8_0 only) load as zeros.
+// (32-value block formats only) load as zeros.
 template <int FMT>
 struct MmqRegs {
   u32x4 x[MmqFmt<FMT>::kRegs];
@@ -94,7 +97,7 @@ __device__ __forceinline__ void load_act(MmqRegs<FMT> &g, const uint8_t *__restr
                                          int s, int t) {
   const int gm = min(m0 + (t >> 3), M - 1);
   const int blk = 8 * s + (t & 7);
-  if (FMT == kMQ8_0 && blk >= nblk) {
+  if (MmqFmt<FMT>::kBlk32 && blk >= nblk) {
     g.x[0] = g.x[1] = u32x4{0u, 0u, 0u, 0u};
     g.x[2].x = 0u;
     return;
@@ -109,6 +112,8 @@ __device__ __forceinline__ void load_act(MmqRegs<FMT> &g, const uint8_t *__restr
 //   Q4_K: x[0] = header (d, dmin, scales), x[1], x[2] = qs bytes 32c..32c+31
 //   Q5_K: as Q4_K (qs at byte 48), plus x[3], x[4] = qh[0..31]
 //   Q8_0: blocks 2c, 2c+1: x[0..1] and x[2..3] their qs, x[4].x/.y their d
+//   Q4_0: blocks 2c, 2c+1: x[0], x[1] their qs, x[2].x/.y their d
+//   Q5_0: as Q4_0, plus x[2].z/.w their qh words
 //   Q6_K: 128-half h = c/2, positions l = 16(c%2)..+15 of all four 32-groups:
 //         x[0] = ql[64h + l] (groups 0, 2), x[1] = ql[64h + 32 + l] (groups
 //         1, 3), x[2] = qh[32h + l], x[3].x/.y = scales[8h..8h+7], x[3].z = d
@@ -137,6 +142,22 @@ __device__ __forceinline__ void load_wgt(MmqRegs<FMT> &g, const uint8_t *__restr
     g.x[3].x = sc.x;
     g.x[3].y = sc.y;
     g.x[3].z = ld2(bp + 208);
+  } else if constexpr (FMT == kMQ4_0 || FMT == kMQ5_0) {
+    constexpr int kB = FMT == kMQ4_0 ? 18 : 22, kQs = FMT == kMQ4_0 ? 2 : 6;
+    const int b0 = 8 * s + 2 * c;
+    const uint8_t *bp = W + ((int64_t)gn * nblk + b0) * kB;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    g.x[0] = g.x[1] = g.x[2] = z;
+    if (b0 < nblk) {
+      g.x[2].x = ld2(bp);
+      g.x[0] = ld16_a2(bp + kQs);
+      if constexpr (FMT == kMQ5_0) g.x[2].z = ld2(bp + 2) | (ld2(bp + 4) << 16);
+    }
+    if (b0 + 1 < nblk) {
+      g.x[2].y = ld2(bp + kB);
+      g.x[1] = ld16_a2(bp + kB + kQs);
+      if constexpr (FMT == kMQ5_0) g.x[2].w = ld2(bp + kB + 2) | (ld2(bp + kB + 4) << 16);
+    }
   } else {
     const int b0 = 8 * s + 2 * c;
     const uint8_t *bp = W + ((int64_t)gn * nblk + b0) * kQ8_0Bytes;
@@ -240,6 +261,36 @@ __device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &
       const uint32_t scw = gq < 2 ? g.x[3].x : g.x[3].y;
       put_factor(s.fb[2 * j + hl][br], d * (float)sbyte(scw, 8u * (uint32_t)((2 * gq + hl) & 3)));
     }
+  } else if constexpr (FMT == kMQ4_0 || FMT == kMQ5_0) {
+    // codes j (low nibble of qs byte j) and 16 + j (high nibble), minus the
+    // zero code, as int8: a byte b <= 31 plus 0x80 - off stays below 0x100,
+    // and flipping bit 7 then leaves b - off in two's complement
+    constexpr uint32_t kBias = FMT == kMQ4_0 ? 0x78787878u : 0x70707070u;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 q = g.x[h];
+      const uint32_t Q[4] = {q.x, q.y, q.z, q.w};
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = Q[i] & 0x0F0F0F0Fu;
+        hi[i] = (Q[i] >> 4) & 0x0F0F0F0Fu;
+        if constexpr (FMT == kMQ5_0) {
+          // bit i of the qh word is the fifth bit of code i: bits 4i..4i+3
+          // land on bit 4 of the four bytes
+          const uint32_t qh = h ? g.x[2].w : g.x[2].z;
+          lo[i] |= (((qh >> (4 * i)) & 0xFu) * 0x00204081u & 0x01010101u) << 4;
+          hi[i] |= (((qh >> (16 + 4 * i)) & 0xFu) * 0x00204081u & 0x01010101u) << 4;
+        }
+        lo[i] = (lo[i] + kBias) ^ 0x80808080u;
+        hi[i] = (hi[i] + kBias) ^ 0x80808080u;
+      }
+      dst[2 * h] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      dst[2 * h + 1] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    }
+    put_factor(s.fb[2 * c][br], h2f(g.x[2].x));
+    put_factor(s.fb[2 * c + 1][br], h2f(g.x[2].y));
   } else {
     u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
     dst[0] = g.x[0];
@@ -334,7 +385,7 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
 #pragma unroll
     for (int jj = 0; jj < kJ; ++jj) {
       const int j = j0 + jj;
-      if (FMT == kMQ8_0 && 8 * s + j >= nblk) break;  // ragged last step (wave-uniform)
+      if (MmqFmt<FMT>::kBlk32 && 8 * s + j >= nblk) break;  // ragged last step (wave-uniform)
       const uint32_t *pa = cur.fa[j][wm * 32 + lr];
       const u32x4n av = *reinterpret_cast<const u32x4n *>(arow + 32 * jj);
       const u32x4n bv = *reinterpret_cast<const u32x4n *>(brow + 32 * jj);
@@ -440,6 +491,8 @@ hipError_t launch_qgemm_mmq(int fmt, const void *w, const void *aq, float *c, in
   if (fmt == kMQ4K) return launch_fmt<kMQ4K>(w, aq, c, D, m, n, k, stream);
   if (fmt == kMQ6K) return launch_fmt<kMQ6K>(w, aq, c, D, m, n, k, stream);
   if (fmt == kMQ5K) return launch_fmt<kMQ5K>(w, aq, c, D, m, n, k, stream);
+  if (fmt == kMQ4_0) return launch_fmt<kMQ4_0>(w, aq, c, D, m, n, k, stream);
+  if (fmt == kMQ5_0) return launch_fmt<kMQ5_0>(w, aq, c, D, m, n, k, stream);
   return launch_fmt<kMQ8_0>(w, aq, c, D, m, n, k, stream);
 }
 

@@ -101,6 +101,22 @@ qg_status qgemv_q6_k(const void *w, const void *xq, float *y, int64_t n, int64_t
 qg_status qgemv_q5_k(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
 
 /*
+ * qgemv_q4_0 / qgemv_q5_0 -- the same decode GEMV for the 32-value GGUF types
+ * Q4_0 and Q5_0, two more of the types the blazr README ("Model Formats >
+ * GGUF") runs beyond the three with dedicated dot kernels.
+ *   Q4_0 block (18 bytes): fp16 d, qs[16]; byte j of qs holds the 4-bit codes
+ *        of elements j (low nibble) and 16 + j (high nibble); w = d*(q - 8).
+ *   Q5_0 block (22 bytes): fp16 d, qh (4 bytes), qs[16] as Q4_0; bit i of the
+ *        little-endian 32-bit qh is element i's fifth bit; w = d*(q - 16).
+ * The per-block dot is the exact integer sum of (q - 8)*qa (q - 16 for Q5_0),
+ * scaled in fp32 by d*d_a.  Same arguments and errors as qgemv_q8_0
+ * (w: [n][k/32] blocks, 16-byte aligned), except that k must be a multiple of
+ * 64 (the kernel reads block pairs).
+ */
+qg_status qgemv_q4_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
+qg_status qgemv_q5_0(const void *w, const void *xq, float *y, int64_t n, int64_t k, hipStream_t stream);
+
+/*
  * qgemv_q8_0_batch / qgemv_q4_k_batch / qgemv_q6_k_batch -- small-batch GEMV,
  * b activation rows against one read of the weights (the decode step of b
  * concurrent sequences: infr page, "Concurrent slots, many models").
@@ -168,6 +184,18 @@ qg_status qgemm_q5_k_mmq(const void *w, const void *aq, float *c, int64_t m, int
                          hipStream_t stream);
 
 /*
+ * qgemm_q4_0_mmq / qgemm_q5_0_mmq -- the prefill product for Q4_0 and Q5_0
+ * weights (blocks as in qgemv_q4_0 / qgemv_q5_0): each 32-wide block is one
+ * int8 32x32x32 MFMA tile of exact dots of (q - 8) (or q - 16) and qa,
+ * rescaled in fp32 by d_w*d_a.  Arguments, errors and conventions as
+ * qgemm_q8_0_mmq (w: [n][k/32]; k a multiple of 32, <= 2^24).
+ */
+qg_status qgemm_q4_0_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream);
+qg_status qgemm_q5_0_mmq(const void *w, const void *aq, float *c, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream);
+
+/*
  * MoE expert FFN with Q4_K experts (the expert_gateup + down calls of an MoE
  * layer).  For token t and each routed slot i with expert e = ids[t][i]:
  *   g = Wgu[e][0:n_ff] . x^_t, u = Wgu[e][n_ff:2n_ff] . x^_t       (fp32)
@@ -229,10 +257,13 @@ qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *
  *                       S int32 [k/32] = sum of qa per activation block
  *   qg_blockdots_q5_k : as qg_blockdots_q4_k, with the 5-bit Q5_K codes
  *   qg_blockdots_q6_k : D int32 [n][k/16],  sum over 16 values of (q-32)*qa
+ *   qg_blockdots_q4_0, qg_blockdots_q5_0 : D int32 [n][k/32], sum over the
+ *                       block of (q-8)*qa or (q-16)*qa
  *   qg_blockdots_q4_k_mmq : D int32 [m][n][k/32] from the int8 MFMA tiles of
  *                       qgemm_q4_k_mmq; m*n*(k/32) <= 2^28
- *   qg_blockdots_q8_0_mmq, qg_blockdots_q5_k_mmq : the same for
- *                       qgemm_q8_0_mmq and qgemm_q5_k_mmq
+ *   qg_blockdots_q8_0_mmq, qg_blockdots_q5_k_mmq, qg_blockdots_q4_0_mmq,
+ *   qg_blockdots_q5_0_mmq : the same for qgemm_q8_0_mmq, qgemm_q5_k_mmq,
+ *                       qgemm_q4_0_mmq and qgemm_q5_0_mmq
  *   qg_blockdots_q6_k_mmq : D int32 [m][n][k/16] per 16-value sub-block, from
  *                       qgemm_q6_k_mmq; m*n*(k/16) <= 2^28
  * Same validation rules and limits as the corresponding products.
@@ -250,6 +281,12 @@ qg_status qg_blockdots_q8_0_mmq(const void *w, const void *aq, int32_t *D, int64
 qg_status qg_blockdots_q6_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                 hipStream_t stream);
 qg_status qg_blockdots_q5_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                hipStream_t stream);
+qg_status qg_blockdots_q4_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
+qg_status qg_blockdots_q5_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
+qg_status qg_blockdots_q4_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
+                                hipStream_t stream);
+qg_status qg_blockdots_q5_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                 hipStream_t stream);
 
 #ifdef __cplusplus

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["quantize_q8_1", "qgemv_q8_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q5_k", "qgemm_q4_k_mmq",
                  "qgemm_q6_k_mmq", "qgemm_q8_0_mmq", "qgemm_q5_k_mmq", "rmsnorm_quantize_q8_1", "moe_router_topk",
-                 "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch",
+                 "qgemv_q8_0_batch", "qgemv_q4_k_batch", "qgemv_q6_k_batch", "qgemv_q4_0", "qgemv_q5_0",
+                 "qgemm_q4_0_mmq", "qgemm_q5_0_mmq",
                  "moe_qgemv_q4_k", "moe_qgemv_q4_k_workspace_size", "qg_status_str"]:
         assert want in names
 
@@ -77,7 +78,7 @@ def test_quantize_validation(lib):
 
 
 @pytest.mark.parametrize("name,kmult", [("qgemv_q8_0", 32), ("qgemv_q4_k", 256), ("qgemv_q6_k", 256),
-                                        ("qgemv_q5_k", 256)])
+                                        ("qgemv_q5_k", 256), ("qgemv_q4_0", 64), ("qgemv_q5_0", 64)])
 def test_gemv_validation(lib, name, kmult):
     f = getattr(lib, name)
     y = P((1 << 20) + 8192)
@@ -93,6 +94,8 @@ def test_gemv_validation(lib, name, kmult):
     assert f(A16, MIS, y, 4, kmult, None) == ALIGN
     assert f(A16, A16b, P((1 << 20) + 2), 4, kmult, None) == ALIGN
     assert f(A16, A16b, y, 0, kmult, None) == OK
+    if kmult == 64:
+        assert f(A16, A16b, y, 4, 96, None) == SHAPE   # an odd block count: the kernel reads block pairs
 
 
 @pytest.mark.parametrize("name,kmult", [("qgemv_q8_0_batch", 32), ("qgemv_q4_k_batch", 256),
@@ -129,7 +132,7 @@ def test_mmq_validation(lib):
     assert lib.qg_blockdots_q4_k_mmq(A16, A16b, c, 1 << 14, 1 << 14, 4096, None) == SHAPE
 
 
-@pytest.mark.parametrize("fmt,kmult", [("q6_k", 256), ("q8_0", 32), ("q5_k", 256)])
+@pytest.mark.parametrize("fmt,kmult", [("q6_k", 256), ("q8_0", 32), ("q5_k", 256), ("q4_0", 32), ("q5_0", 32)])
 def test_mmq_validation_other_formats(lib, fmt, kmult):
     c = P((1 << 20) + 8192)
     f = getattr(lib, f"qgemm_{fmt}_mmq")

@@ -11,7 +11,9 @@ from gemm_gguf_block_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-GEMV = {"q8_0": "qgemv_q8_0", "q4_k": "qgemv_q4_k", "q6_k": "qgemv_q6_k", "q5_k": "qgemv_q5_k"}
+GEMV = {"q8_0": "qgemv_q8_0", "q4_k": "qgemv_q4_k", "q6_k": "qgemv_q6_k", "q5_k": "qgemv_q5_k", "q4_0": "qgemv_q4_0",
+        "q5_0": "qgemv_q5_0"}
+ALL_GEMV = list(GEMV)
 
 
 @pytest.fixture(scope="module")
@@ -85,7 +87,7 @@ def test_quantize_q8_1_bytes_exact(env, rows, k, scale):
 SHAPES = [(1, 256), (3, 512), (65, 256), (130, 768), (257, 2048), (64, 4096), (33, 14336), (7, 17152), (5, 33536)]
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ALL_GEMV)
 @pytest.mark.parametrize("n,k", SHAPES)
 @pytest.mark.parametrize("data", ["random_bytes", "weights"])
 def test_gemv_block_dots_exact(env, fmt, n, k, data):
@@ -118,7 +120,7 @@ def test_q8_0_block_dots_odd_block_count(env):
 
 
 # ---------------------------------------------------------------- GEMV values
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ALL_GEMV)
 @pytest.mark.parametrize("n,k", SHAPES + [(1, 4096), (511, 1024), (1000, 4096)])
 def test_gemv_values(env, fmt, n, k):
     qg, orc, torch, dev = env
@@ -131,7 +133,7 @@ def test_gemv_values(env, fmt, n, k):
     assert rel_err(_host(y), orc.qgemv(fmt, w, xq, n, k)) <= REL_TOL
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k", "q5_k"])
+@pytest.mark.parametrize("fmt", ALL_GEMV)
 def test_gemv_values_random_bytes(env, fmt):
     qg, orc, torch, dev = env
     n, k = 300, 1024
@@ -194,13 +196,20 @@ def test_gemv_hand_superblock_exact(env):
     exact = sum(Fraction((i % 32) - 16, 4) * Fraction(1, 8) * qa[i] for i in range(256))
     y = _host(qg.qgemv_q8_0(_gpu(torch, dev, np.tile(blk, (2, 8))), X, 2, 256))
     assert all(Fraction(float(v)) == exact for v in y)
+    for fmt, d, off in (("q4_0", Fraction(-1, 8), 8), ("q5_0", Fraction(1, 32), 16)):
+        fx = read_golden(f"{fmt}_block.txt")
+        blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+        q = [int(t) for t in fx["q"][0].split()]
+        exact = sum(d * (q[i % 32] - off) * Fraction(1, 8) * qa[i] for i in range(256))
+        y = _host(getattr(qg, GEMV[fmt])(_gpu(torch, dev, np.tile(blk, (7, 8))), X, 7, 256))
+        assert all(Fraction(float(v)) == exact for v in y), fmt
 
 
 def test_gemv_empty_and_zero_k(env):
     qg, orc, torch, dev = env
     X = torch.zeros(288, dtype=torch.uint8, device=dev)
     y = torch.full((8,), 7.0, device=dev)
-    for fn in (qg.qgemv_q8_0, qg.qgemv_q4_k, qg.qgemv_q6_k, qg.qgemv_q5_k):
+    for fn in (qg.qgemv_q8_0, qg.qgemv_q4_k, qg.qgemv_q6_k, qg.qgemv_q5_k, qg.qgemv_q4_0, qg.qgemv_q5_0):
         fn(torch.zeros(16, dtype=torch.uint8, device=dev), X, 0, 256, y=y)   # n = 0: nothing written
         assert np.all(_host(y) == 7.0)
         fn(torch.zeros(16, dtype=torch.uint8, device=dev), X, 8, 0, y=y)     # k = 0: zeros
@@ -316,7 +325,7 @@ def test_gemv_batch_full_size(env, name, b):
 
 
 @pytest.mark.big
-@pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv", "q5_k_gemv"])
+@pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv", "q5_k_gemv", "q4_0_gemv", "q5_0_gemv"])
 def test_gemv_full_size(env, name):
     """The full workload sizes in the launch configuration the bench times."""
     qg, orc, torch, dev = env
@@ -445,7 +454,7 @@ MMQ_Q80_RAGGED = [(5, 7, 32), (33, 70, 96), (64, 128, 288), (65, 129, 4128)]
 
 
 @pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES] + [("q5_k",) + s for s in MMQ_SHAPES] +
-                         [("q8_0",) + s for s in MMQ_SHAPES + MMQ_Q80_RAGGED])
+                         [(f,) + s for f in ("q8_0", "q4_0", "q5_0") for s in MMQ_SHAPES + MMQ_Q80_RAGGED])
 def test_mmq_block_dots_exact_other_formats(env, fmt, m, n, k):
     """Random bytes: the matrix-core dots equal the oracle's block dots
     (per 16 values for Q6_K)."""
@@ -458,7 +467,8 @@ def test_mmq_block_dots_exact_other_formats(env, fmt, m, n, k):
 
 @pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES + [(1, 64, 4096), (257, 70, 1024)]] +
                          [("q5_k",) + s for s in MMQ_SHAPES + [(257, 70, 1024)]] +
-                         [("q8_0",) + s for s in MMQ_SHAPES + MMQ_Q80_RAGGED + [(257, 70, 1024)]])
+                         [(f,) + s for f in ("q8_0", "q4_0", "q5_0")
+                          for s in MMQ_SHAPES + MMQ_Q80_RAGGED + [(257, 70, 1024)]])
 def test_mmq_values_other_formats(env, fmt, m, n, k):
     qg, orc, torch, dev = env
     w = synth.weights(fmt, n, k, seed=m + 2 * n + k)
@@ -470,7 +480,7 @@ def test_mmq_values_other_formats(env, fmt, m, n, k):
     assert rel_err(C, orc.qgemm(fmt, w, aq, m, n, k)) <= REL_TOL
 
 
-@pytest.mark.parametrize("fmt", ["q6_k", "q8_0", "q5_k"])
+@pytest.mark.parametrize("fmt", ["q6_k", "q8_0", "q5_k", "q4_0", "q5_0"])
 def test_mmq_values_random_bytes_other_formats(env, fmt):
     qg, orc, torch, dev = env
     m, n, k = 70, 130, 512
@@ -506,12 +516,19 @@ def test_mmq_hand_blocks_exact_other_formats(env):
                 for i in range(256))
     C = _host(qg.qgemm_q5_k_mmq(_gpu(torch, dev, np.tile(blk, (70, 1))), A, 40, 70, 256))
     assert all(Fraction(float(v)) == exact for v in C.ravel())
+    for fmt, d, off in (("q4_0", Fraction(-1, 8), 8), ("q5_0", Fraction(1, 32), 16)):
+        fx = read_golden(f"{fmt}_block.txt")
+        blk = np.frombuffer(bytes.fromhex(fx["bytes"][0]), np.uint8)
+        q = [int(t) for t in fx["q"][0].split()]
+        exact = sum(d * (q[i % 32] - off) * Fraction(1, 8) * qa[i] for i in range(256))
+        C = _host(getattr(qg, f"qgemm_{fmt}_mmq")(_gpu(torch, dev, np.tile(blk, (70, 8))), A, 40, 70, 256))
+        assert all(Fraction(float(v)) == exact for v in C.ravel()), fmt
 
 
 def test_mmq_empty_other_formats(env):
     qg, orc, torch, dev = env
     A = torch.zeros(4 * 288, dtype=torch.uint8, device=dev)
-    for fmt, k in (("q6_k", 256), ("q8_0", 32), ("q5_k", 256)):
+    for fmt, k in (("q6_k", 256), ("q8_0", 32), ("q5_k", 256), ("q4_0", 32), ("q5_0", 32)):
         W = torch.zeros(4 * qg.row_bytes(fmt, 256), dtype=torch.uint8, device=dev)
         c = torch.full((4, 4), 7.0, device=dev)
         f = getattr(qg, f"qgemm_{fmt}_mmq")
@@ -523,7 +540,7 @@ def test_mmq_empty_other_formats(env):
 
 
 @pytest.mark.big
-@pytest.mark.parametrize("name", ["q6_k_mmq", "q8_0_mmq", "q5_k_mmq"])
+@pytest.mark.parametrize("name", ["q6_k_mmq", "q8_0_mmq", "q5_k_mmq", "q4_0_mmq", "q5_0_mmq"])
 def test_mmq_full_size_other_formats(env, name):
     qg, orc, torch, dev = env
     p = synth.WORKLOADS[name]
@@ -718,6 +735,9 @@ def test_graph_replay_matches_eager(env):
     rids = torch.empty((16, 8), dtype=torch.int32, device=dev)
     rws = torch.empty((16, 8), device=dev)
     rlg = torch.empty((16, 128), device=dev)
+    Wl = {f: _gpu(torch, dev, synth.weights(f, n, k, seed=97)) for f in ("q4_0", "q5_0")}
+    yl = {f: torch.empty(n, device=dev) for f in Wl}
+    cl = {f: torch.empty((m, n), device=dev) for f in Wl}
 
     def work():
         qg.rmsnorm_quantize_q8_1(xb, gam, 1e-5, xq=xnq, r=rr)
@@ -732,13 +752,16 @@ def test_graph_replay_matches_eager(env):
         qg.qgemm_q4_k_mmq(Ws["q4_k"], aq, m, n, k, c=c)
         qg.qgemm_q6_k_mmq(Ws["q6_k"], aq, m, n, k, c=c6)
         qg.qgemm_q8_0_mmq(Ws["q8_0"], aq, m, n, k, c=c8)
+        for f, W in Wl.items():
+            getattr(qg, GEMV[f])(W, xq, n, k, y=yl[f])
+            getattr(qg, f"qgemm_{f}_mmq")(W, aq, m, n, k, c=cl[f])
         qg.quantize_q8_1(XM, xmq)
         qg.moe_qgemv_q4_k(WGU, WDN, xmq, IDS, RW, T, K, E, F, H, out=out, workspace=ws)
 
     def snapshot():
         torch.cuda.synchronize()
         return [t.clone() for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr,
-                                    rids, rws, rlg)]
+                                    rids, rws, rlg, *yl.values(), *cl.values())]
 
     work()
     eager = snapshot()
@@ -752,7 +775,8 @@ def test_graph_replay_matches_eager(env):
             work()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr, rids, rws, rlg):
+        for t in (xq, *ys.values(), xbq, *ybs.values(), aq, c, c6, c8, xmq, out, xnq, rr, rids, rws, rlg,
+                  *yl.values(), *cl.values()):
             t.zero_()                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
