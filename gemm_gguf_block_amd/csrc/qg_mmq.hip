@@ -114,14 +114,44 @@ __device__ __forceinline__ void load_act(MmqRegs<FMT> &g, const uint8_t *__restr
 //   Q8_0: blocks 2c, 2c+1: x[0..1] and x[2..3] their qs, x[4].x/.y their d
 //   Q4_0: blocks 2c, 2c+1: x[0], x[1] their qs, x[2].x/.y their d
 //   Q5_0: as Q4_0, plus x[2].z/.w their qh words
+// With `al` (32-value block types, an even block count per row) the block
+// pair starts on a dword boundary and is loaded as it is stored, in aligned
+// dwords: x[0], x[1], ... hold bytes 0-15, 16-31, ... of the pair; the
+// fields are realigned when the pair is staged.
 //   Q6_K: 128-half h = c/2, positions l = 16(c%2)..+15 of all four 32-groups:
 //         x[0] = ql[64h + l] (groups 0, 2), x[1] = ql[64h + 32 + l] (groups
 //         1, 3), x[2] = qh[32h + l], x[3].x/.y = scales[8h..8h+7], x[3].z = d
 template <int FMT>
 __device__ __forceinline__ void load_wgt(MmqRegs<FMT> &g, const uint8_t *__restrict__ W, int N, int nblk, int n0,
-                                         int s, int t) {
+                                         int s, int t, bool al) {
   const int gn = min(n0 + (t >> 2), N - 1);
   const int c = t & 3;
+  if constexpr (MmqFmt<FMT>::kBlk32) {
+    if (al) {
+      constexpr int kPair = FMT == kMQ8_0 ? 2 * kQ8_0Bytes : (FMT == kMQ4_0 ? 36 : 44);
+      const int b0 = 8 * s + 2 * c;
+      const uint8_t *bp = W + ((int64_t)gn * nblk + b0) * (kPair / 2);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < MmqFmt<FMT>::kRegs; ++i) g.x[i] = z;
+      if (b0 < nblk) {  // then b0 + 1 < nblk as well: nblk is even
+        g.x[0] = ld16(bp);
+        g.x[1] = ld16(bp + 16);
+        if constexpr (FMT == kMQ8_0) {
+          g.x[2] = ld16(bp + 32);
+          g.x[3] = ld16(bp + 48);
+          g.x[4].x = ld4(bp + 64);
+        } else if constexpr (FMT == kMQ4_0) {
+          g.x[2].x = ld4(bp + 32);
+        } else {
+          g.x[2].x = ld4(bp + 32);
+          g.x[2].y = ld4(bp + 36);
+          g.x[2].z = ld4(bp + 40);
+        }
+      }
+      return;
+    }
+  }
   if constexpr (FMT == kMQ4K || FMT == kMQ5K) {
     constexpr int kB = FMT == kMQ5K ? kQ5KBytes : kQ4KBytes, kQs = FMT == kMQ5K ? 48 : 16;
     const uint8_t *bp = W + ((int64_t)gn * (nblk / 8) + s) * kB;
@@ -207,7 +237,7 @@ __device__ __forceinline__ void store_act(const MmqRegs<FMT> &g, MmqStage<FMT> &
 
 // weight part: codes -> int8 row, factors
 template <int FMT>
-__device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &s, int t) {
+__device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &s, int t, bool al) {
   const int br = t >> 2, c = t & 3;
   if constexpr (FMT == kMQ4K || FMT == kMQ5K) {
     // sub-block 2c in the low nibbles, 2c+1 in the high ones (Q5_K: plus bits
@@ -262,6 +292,45 @@ __device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &
       put_factor(s.fb[2 * j + hl][br], d * (float)sbyte(scw, 8u * (uint32_t)((2 * gq + hl) & 3)));
     }
   } else if constexpr (FMT == kMQ4_0 || FMT == kMQ5_0) {
+    // the two blocks' qs dwords, qh words and d, from either load layout
+    uint32_t Qb[2][4], qh[2] = {0u, 0u}, dd[2];
+    if (al) {
+      const uint32_t w[12] = {g.x[0].x, g.x[0].y, g.x[0].z, g.x[0].w, g.x[1].x, g.x[1].y,
+                              g.x[1].z, g.x[1].w, g.x[2].x, g.x[2].y, g.x[2].z, g.x[2].w};
+      if constexpr (FMT == kMQ4_0) {  // d0 | qs0[16] | d1 | qs1[16]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Qb[0][i] = align_bytes(w[i + 1], w[i], 2);
+          Qb[1][i] = w[5 + i];
+        }
+        dd[0] = w[0];
+        dd[1] = w[4] >> 16;
+      } else {  // d0 | qh0 | qs0[16] | d1 | qh1 | qs1[16]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Qb[0][i] = align_bytes(w[i + 2], w[i + 1], 2);
+          Qb[1][i] = w[7 + i];
+        }
+        qh[0] = align_bytes(w[1], w[0], 2);
+        qh[1] = w[6];
+        dd[0] = w[0];
+        dd[1] = w[5] >> 16;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        Qb[h][0] = g.x[h].x;
+        Qb[h][1] = g.x[h].y;
+        Qb[h][2] = g.x[h].z;
+        Qb[h][3] = g.x[h].w;
+      }
+      dd[0] = g.x[2].x;
+      dd[1] = g.x[2].y;
+      if constexpr (FMT == kMQ5_0) {
+        qh[0] = g.x[2].z;
+        qh[1] = g.x[2].w;
+      }
+    }
     // codes j (low nibble of qs byte j) and 16 + j (high nibble), minus the
     // zero code, as int8: a byte b <= 31 plus 0x80 - off stays below 0x100,
     // and flipping bit 7 then leaves b - off in two's complement
@@ -269,19 +338,17 @@ __device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &
     u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4 q = g.x[h];
-      const uint32_t Q[4] = {q.x, q.y, q.z, q.w};
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lo[i] = Q[i] & 0x0F0F0F0Fu;
-        hi[i] = (Q[i] >> 4) & 0x0F0F0F0Fu;
+        lo[i] = Qb[h][i] & 0x0F0F0F0Fu;
+        hi[i] = (Qb[h][i] >> 4) & 0x0F0F0F0Fu;
         if constexpr (FMT == kMQ5_0) {
           // bit i of the qh word is the fifth bit of code i: bits 4i..4i+3
-          // land on bit 4 of the four bytes
-          const uint32_t qh = h ? g.x[2].w : g.x[2].z;
-          lo[i] |= (((qh >> (4 * i)) & 0xFu) * 0x00204081u & 0x01010101u) << 4;
-          hi[i] |= (((qh >> (16 + 4 * i)) & 0xFu) * 0x00204081u & 0x01010101u) << 4;
+          // land on bit 4 of the four bytes (the four shifted copies of the
+          // group set disjoint bits)
+          lo[i] |= ((qh[h] >> (4 * i)) & 0xFu) * 0x02040810u & 0x10101010u;
+          hi[i] |= ((qh[h] >> (16 + 4 * i)) & 0xFu) * 0x02040810u & 0x10101010u;
         }
         lo[i] = (lo[i] + kBias) ^ 0x80808080u;
         hi[i] = (hi[i] + kBias) ^ 0x80808080u;
@@ -289,16 +356,31 @@ __device__ __forceinline__ void store_wgt(const MmqRegs<FMT> &g, MmqStage<FMT> &
       dst[2 * h] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       dst[2 * h + 1] = u32x4{hi[0], hi[1], hi[2], hi[3]};
     }
-    put_factor(s.fb[2 * c][br], h2f(g.x[2].x));
-    put_factor(s.fb[2 * c + 1][br], h2f(g.x[2].y));
+    put_factor(s.fb[2 * c][br], h2f(dd[0]));
+    put_factor(s.fb[2 * c + 1][br], h2f(dd[1]));
   } else {
     u32x4 *dst = reinterpret_cast<u32x4 *>(s.b + br * kRow + 64 * c);
-    dst[0] = g.x[0];
-    dst[1] = g.x[1];
-    dst[2] = g.x[2];
-    dst[3] = g.x[3];
-    put_factor(s.fb[2 * c][br], h2f(g.x[4].x));
-    put_factor(s.fb[2 * c + 1][br], h2f(g.x[4].y));
+    if (al) {  // d0 | qs0[32] | d1 | qs1[32]: 17 dwords in x[0..3], x[4].x
+      const uint32_t w[17] = {g.x[0].x, g.x[0].y, g.x[0].z, g.x[0].w, g.x[1].x, g.x[1].y, g.x[1].z,
+                              g.x[1].w, g.x[2].x, g.x[2].y, g.x[2].z, g.x[2].w, g.x[3].x, g.x[3].y,
+                              g.x[3].z, g.x[3].w, g.x[4].x};
+      uint32_t q0[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q0[i] = align_bytes(w[i + 1], w[i], 2);
+      dst[0] = u32x4{q0[0], q0[1], q0[2], q0[3]};
+      dst[1] = u32x4{q0[4], q0[5], q0[6], q0[7]};
+      dst[2] = u32x4{w[9], w[10], w[11], w[12]};
+      dst[3] = u32x4{w[13], w[14], w[15], w[16]};
+      put_factor(s.fb[2 * c][br], h2f(w[0]));
+      put_factor(s.fb[2 * c + 1][br], h2f(w[8] >> 16));
+    } else {
+      dst[0] = g.x[0];
+      dst[1] = g.x[1];
+      dst[2] = g.x[2];
+      dst[3] = g.x[3];
+      put_factor(s.fb[2 * c][br], h2f(g.x[4].x));
+      put_factor(s.fb[2 * c + 1][br], h2f(g.x[4].y));
+    }
   }
 }
 
@@ -323,6 +405,9 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
   const int nsteps = (nblk + 7) / 8;
   const int st = tid & 511;
   const bool act = tid < 512;  // this wave stages activations, else weights
+  // 32-value block types with an even block count per row: block pairs are
+  // dword aligned and load as aligned dwords
+  const bool al = MmqFmt<FMT>::kBlk32 && (nblk & 1) == 0;
 
   // acc = 2 * (sum of F*D over blocks + min term); halved at the end
   v16f acc;
@@ -343,13 +428,13 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
     if (act)
       load_act<FMT>(g, AQ, M, nblk, m0, s, st);
     else
-      load_wgt<FMT>(g, W, N, nblk, n0, s, st);
+      load_wgt<FMT>(g, W, N, nblk, n0, s, st, al);
   };
   auto store = [&](const MmqRegs<FMT> &g, MmqStage<FMT> &dst) {
     if (act)
       store_act<FMT>(g, dst, st);
     else
-      store_wgt<FMT>(g, dst, st);
+      store_wgt<FMT>(g, dst, st, al);
   };
   // output register r holds tile row 8(r/4) + 4*lh + r%4, column lr
   auto dump = [&](const v16i &D, int idx, int per_row) {

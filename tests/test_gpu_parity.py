@@ -449,8 +449,9 @@ def test_rmsnorm_quantize_zero_row(env):
 
 # ------------------------------------------- mmq with the other weight types
 MMQ_SHAPES = [(1, 1, 256), (32, 32, 256), (70, 100, 512), (130, 65, 768), (3, 200, 1024), (64, 128, 2048)]
-# Q8_0 rows need k % 32 only: a ragged last 256-wide step
-MMQ_Q80_RAGGED = [(5, 7, 32), (33, 70, 96), (64, 128, 288), (65, 129, 4128)]
+# Q8_0 rows need k % 32 only: a ragged last 256-wide step, with an odd block
+# count (rows at 2-byte offsets) or an even one (dword-aligned block pairs)
+MMQ_Q80_RAGGED = [(5, 7, 32), (33, 70, 96), (64, 128, 288), (65, 129, 4128), (33, 70, 320), (17, 40, 64)]
 
 
 @pytest.mark.parametrize("fmt,m,n,k", [("q6_k",) + s for s in MMQ_SHAPES] + [("q5_k",) + s for s in MMQ_SHAPES] +
