@@ -193,6 +193,9 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
   for (int x = 0; x < kMaxExpertWords; ++x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) touched[x] |= __shfl_xor(touched[x], off, 64);
+    // the same in every lane now: keep it in scalar registers
+    touched[x] = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(touched[x] >> 32)) << 32) |
+                 (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)touched[x]);
   }
   int active = 0;
 #pragma unroll
