@@ -151,13 +151,20 @@ constexpr int kMaxIdWords = 4;      // up to 256 (token, slot) pairs
 constexpr int kMaxExpertWords = 4;  // up to 256 experts
 
 //
+// Item bookkeeping stays off the scalar unit's critical path: the expert of an
+// item comes from per-lane ranks of the touched experts (one compare and ballot
+// per bitmap word), the item's (expert, tile) pair advances by the grid size
+// without dividing, and the token row of a pair is read from a VGPR with
+// v_readlane.  Bit scans and divisions per item and per pair had cost each wave
+// about as many scalar as vector instructions.
+//
 // With STAGE (the gate/up call when the token rows fit in LDS) the workgroup
 // first stages every activation row, unit-major: piece c of unit u of row t at
 // slot t*5U + c*U + u (16 bytes: half c%2 of block 2u + c/2), and the record
 // {d_a(2u), d_a(2u+1), sum qa(2u), sum qa(2u+1)} at slot t*5U + 4U + u.  The
 // pair loop then reads its activation from LDS instead of L2.
-template <int L, int R, bool STAGE>
-__global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
+template <int L, int R, bool STAGE, int NT, int WPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void moe_expert_gemv_persistent(
     const uint8_t *__restrict__ W, const uint8_t *__restrict__ act, const int32_t *__restrict__ ids,
     const float *__restrict__ weights, float *__restrict__ out, int rows, int nsb, int npairs, int top_k,
     int act_per_token, int64_t expert_bytes, int64_t act_row_bytes, int tiles, int n_expert, int n_act) {
@@ -197,15 +204,28 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
     touched[x] = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(touched[x] >> 32)) << 32) |
                  (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)touched[x]);
   }
+  // rank[x] = position of expert 64x + lane among the touched experts, or -1
+  // if it is untouched; the expert at position k is then the one lane whose
+  // rank equals k (one compare and ballot per word)
+  int rank[kMaxExpertWords];
   int active = 0;
 #pragma unroll
-  for (int x = 0; x < kMaxExpertWords; ++x) active += __builtin_popcountll(touched[x]);
+  for (int x = 0; x < kMaxExpertWords; ++x) {
+    const uint64_t t = touched[x];
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(t >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)t, 0u));
+    rank[x] = ((t >> lane) & 1) ? active + below : -1;
+    active += __builtin_popcountll(t);
+  }
   const int items = active * tiles;
+  // token row of pair 64w + lane (the activation row of the staged form)
+  int tok[kMaxIdWords];
+#pragma unroll
+  for (int w = 0; w < kMaxIdWords; ++w) tok[w] = STAGE ? (64 * w + lane) / top_k : 0;
 
   const int u = li;  // this lane's unit (L >= U here, so at most one)
   const int sb = u >> 2, g = u & 3;
   if constexpr (STAGE) {
-    for (int t = threadIdx.x; t < n_act * U; t += 256) {
+    for (int t = threadIdx.x; t < n_act * U; t += NT) {
       const int row = t / U, uu = t - row * U;
       uint32_t A[18];
       load_q8_1_pair(act + (int64_t)row * act_row_bytes + (int64_t)(2 * uu) * kQ8_1Bytes, A);
@@ -225,21 +245,23 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
     }
     __syncthreads();
   }
+  // item = k * tiles + t, advanced by the grid size without dividing
+  const int kstep = (int)gridDim.x / tiles, tstep = (int)gridDim.x - kstep * tiles;
+  int ik = (int)blockIdx.x / tiles, it = (int)blockIdx.x - ik * tiles;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    // expert = the (item / tiles)-th touched expert
-    int k = item / tiles, e = -1;
+    int e = -1;
 #pragma unroll
     for (int x = 0; x < kMaxExpertWords; ++x) {
-      const int c = __builtin_popcountll(touched[x]);
-      if (e < 0 && k < c) {
-        uint64_t m = touched[x];
-        for (int t = 0; t < k; ++t) m &= m - 1;
-        e = 64 * x + __builtin_ctzll(m);
-      } else if (e < 0) {
-        k -= c;
-      }
+      const uint64_t m = __ballot(rank[x] == ik);
+      if (m) e = 64 * x + __builtin_ctzll(m);
     }
-    const int row0 = (((item % tiles) * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+    const int row0 = ((it * (NT / 64) + (threadIdx.x >> 6)) * G + lane / L) * R;
+    ik += kstep;
+    it += tstep;
+    if (it >= tiles) {
+      it -= tiles;
+      ++ik;
+    }
     const uint8_t *wu = W + (int64_t)e * expert_bytes + (int64_t)row0 * rb + sb * kQ4KBytes;
     u32x4 hdr[R], qa[R], qb[R];
 #pragma unroll
@@ -259,7 +281,8 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
       while (mask) {
         const int p = 64 * w + __builtin_ctzll(mask);
         mask &= mask - 1;
-        const uint8_t *xr = act + (int64_t)(act_per_token ? p / top_k : p) * act_row_bytes;
+        const int arow = STAGE ? __builtin_amdgcn_readlane(tok[w], p - 64 * w) : act_per_token ? p / top_k : p;
+        const uint8_t *xr = act + (int64_t)arow * act_row_bytes;
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_persistent(
           int S0 = 0, S1 = 0;
           float da0, da1;
           if constexpr (STAGE) {
-            const u32x4n *base = xs + (p / top_k) * 5 * U;
+            const u32x4n *base = xs + arow * 5 * U;
             const u32x4n x0 = base[u], x1 = base[U + u], x2 = base[2 * U + u], x3 = base[3 * U + u];
             const u32x4n rec = base[4 * U + u];
             A[1] = x0.x; A[2] = x0.y; A[3] = x0.z; A[4] = x0.w;
@@ -374,10 +397,8 @@ static void launch_expert_gemv(const uint8_t *W, const uint8_t *act, const int32
                      rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles);
 }
 
-// Rows per lane group of the expert GEMVs.
+// Rows per lane group of the grid-form expert GEMV.
 constexpr int kMoeRows = 2;
-// Workgroups of the persistent expert GEMV (four per CU on 256 CUs).
-constexpr int kMoePersistentBlocks = 1024;
 
 // Lanes per row: the smallest power of two >= the row's unit count, capped at
 // 64 (lanes past the last unit idle); each lane then keeps ceil(U/L) units'
@@ -386,25 +407,43 @@ constexpr int kMoePersistentBlocks = 1024;
 // of each row.  Up to this much, four workgroups still fit on a CU.
 constexpr size_t kMoeStageBytes = 40 * 1024;
 
-template <int L, int R>
+// Launch shape of the persistent expert GEMV: workgroup size, rows per lane
+// group, and the waves per SIMD its register allocation must leave room for.
+// The staged gate/up call is held to four workgroups per CU by its LDS; the
+// down call fits five.  The grid is the number of workgroups resident at once.
+constexpr int kGuThreads = 256, kGuRows = 2, kGuWaves = 4;
+constexpr int kDnThreads = 256, kDnRows = 2, kDnWaves = 5;
+
+template <int L, int R, bool STAGE, int NT, int WPE>
+static void launch_persistent_shape(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights,
+                                    float *out, int rows, int nsb, int npairs, int top_k, int act_per_token,
+                                    int64_t expert_bytes, int64_t act_row_bytes, int n_expert, int n_act,
+                                    size_t stage, hipStream_t stream) {
+  constexpr auto kern = moe_expert_gemv_persistent<L, R, STAGE, NT, WPE>;
+  const int rows_per_block = (NT / 64) * (64 / L) * R;
+  const int tiles = (rows + rows_per_block - 1) / rows_per_block;
+  const int64_t max_items = (int64_t)tiles * n_expert;
+  const int64_t resident = resident_blocks<kern>(NT, stage);
+  const dim3 grid((unsigned)(max_items < resident ? max_items : resident));
+  hipLaunchKernelGGL(kern, grid, dim3(NT), stage, stream, W, act, ids, weights, out, rows, nsb, npairs, top_k,
+                     act_per_token, expert_bytes, act_row_bytes, tiles, n_expert, n_act);
+}
+
+template <int L>
 static void launch_expert_gemv_persistent(const uint8_t *W, const uint8_t *act, const int32_t *ids,
                                           const float *weights, float *out, int rows, int nsb, int npairs,
                                           int top_k, int act_per_token, int64_t expert_bytes,
                                           int64_t act_row_bytes, int n_expert, hipStream_t stream) {
-  const int rows_per_block = 4 * (64 / L) * R;
-  const int tiles = (rows + rows_per_block - 1) / rows_per_block;
-  const int64_t max_items = (int64_t)tiles * n_expert;
-  const dim3 grid((unsigned)(max_items < kMoePersistentBlocks ? max_items : kMoePersistentBlocks));
   const int n_act = act_per_token ? (npairs + top_k - 1) / top_k : npairs;
   const size_t stage = (size_t)n_act * nsb * 4 * 80;
   if (act_per_token && stage <= kMoeStageBytes)
-    hipLaunchKernelGGL((moe_expert_gemv_persistent<L, R, true>), grid, dim3(256), stage, stream, W, act, ids,
-                       weights, out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles,
-                       n_expert, n_act);
+    launch_persistent_shape<L, kGuRows, true, kGuThreads, kGuWaves>(W, act, ids, weights, out, rows, nsb, npairs,
+                                                                    top_k, act_per_token, expert_bytes,
+                                                                    act_row_bytes, n_expert, n_act, stage, stream);
   else
-    hipLaunchKernelGGL((moe_expert_gemv_persistent<L, R, false>), grid, dim3(256), 0, stream, W, act, ids, weights,
-                       out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, tiles, n_expert,
-                       n_act);
+    launch_persistent_shape<L, kDnRows, false, kDnThreads, kDnWaves>(W, act, ids, weights, out, rows, nsb, npairs,
+                                                                     top_k, act_per_token, expert_bytes,
+                                                                     act_row_bytes, n_expert, n_act, 0, stream);
 }
 
 static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights, float *out,
@@ -417,7 +456,7 @@ static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids
   const int upl = (U + L - 1) / L;
   if (upl == 1 && npairs <= 64 * kMaxIdWords && n_expert <= 64 * kMaxExpertWords) {
 #define QG_MOE_PERSIST(LV)                                                                                        \
-  launch_expert_gemv_persistent<LV, kMoeRows>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, \
+  launch_expert_gemv_persistent<LV>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, \
                                               expert_bytes, act_row_bytes, n_expert, stream)
     if (L == 4) QG_MOE_PERSIST(4);
     else if (L == 8) QG_MOE_PERSIST(8);
