@@ -317,6 +317,19 @@ def moe_workspace_regions(workspace, n_tok, top_k, n_ff, n_embd):
     return hq, gu, z
 
 
+def moe_workspace_hx(workspace, n_tok, top_k, n_ff, n_embd):
+    """View of the MoE workspace's fourth region: h^ per pair in the unit-major
+    layout the down GEMV reads, uint8 [P][(n_ff/64)*80]."""
+    import torch
+
+    def up(v):
+        return (v + 255) & ~255
+
+    P = n_tok * top_k
+    off = up(P * row_bytes("q8_1", n_ff)) + up(P * 2 * n_ff * 4) + up(P * n_embd * 4)
+    return workspace[off:off + P * (n_ff // 64) * 80].view(P, (n_ff // 64) * 80)
+
+
 # ------------------------------------------------------- per-block dots (tests)
 def _blockdots_32(fmt, w, xq, n, k, stream):
     import torch

@@ -275,6 +275,7 @@ QG_EXPORT qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, co
   a.ws_hq = ws + lay.hq_off;
   a.ws_gu = reinterpret_cast<float *>(ws + lay.gu_off);
   a.ws_z = reinterpret_cast<float *>(ws + lay.z_off);
+  a.ws_hx = ws + lay.hx_off;
   return launched(qg::launch_moe_q4_k(a, stream));
 }
 

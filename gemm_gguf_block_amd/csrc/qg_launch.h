@@ -71,12 +71,13 @@ struct MoeArgs {
   uint8_t *ws_hq;   // Q8_1 h^ per pair
   float *ws_gu;     // g|u per pair
   float *ws_z;      // weighted down projection per pair
+  uint8_t *ws_hx;   // h^ per pair again, unit-major with {d, sum} records (read by the down GEMV)
 };
 hipError_t launch_moe_q4_k(const MoeArgs &a, hipStream_t stream);
 
 // Workspace region offsets for the MoE call (each 256-byte aligned).
 struct MoeLayout {
-  size_t hq_off, gu_off, z_off, total;
+  size_t hq_off, gu_off, z_off, hx_off, total;
 };
 MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd);
 

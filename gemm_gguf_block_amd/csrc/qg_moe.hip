@@ -149,6 +149,7 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
 // the expert come from ballots over the ids already in registers.
 constexpr int kMaxIdWords = 4;      // up to 256 (token, slot) pairs
 constexpr int kMaxExpertWords = 4;  // up to 256 experts
+static_assert(kMaxIdWords == kMaxExpertWords, "one word count serves both");
 
 //
 // Item bookkeeping stays off the scalar unit's critical path: the expert of an
@@ -158,12 +159,16 @@ constexpr int kMaxExpertWords = 4;  // up to 256 experts
 // v_readlane.  Bit scans and divisions per item and per pair had cost each wave
 // about as many scalar as vector instructions.
 //
+// With UMX (the down call) `act` holds the activation rows in that same
+// unit-major layout in global memory (written by the act kernel), so the pair
+// loop loads aligned 16-byte pieces and ready code sums instead of Q8_1 blocks.
+//
 // With STAGE (the gate/up call when the token rows fit in LDS) the workgroup
 // first stages every activation row, unit-major: piece c of unit u of row t at
 // slot t*5U + c*U + u (16 bytes: half c%2 of block 2u + c/2), and the record
 // {d_a(2u), d_a(2u+1), sum qa(2u), sum qa(2u+1)} at slot t*5U + 4U + u.  The
 // pair loop then reads its activation from LDS instead of L2.
-template <int L, int R, bool STAGE, int NT, int WPE>
+template <int L, int R, bool STAGE, int NT, int WPE, bool UMX, int NW>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void moe_expert_gemv_persistent(
     const uint8_t *__restrict__ W, const uint8_t *__restrict__ act, const int32_t *__restrict__ ids,
     const float *__restrict__ weights, float *__restrict__ out, int rows, int nsb, int npairs, int top_k,
@@ -177,27 +182,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   const int64_t rb = (int64_t)nsb * kQ4KBytes;
   const int U = nsb * 4;
   // routing table in registers: id[w] = ids[64w + lane]
-  int id[kMaxIdWords];
+  int id[NW];
 #pragma unroll
-  for (int w = 0; w < kMaxIdWords; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int p = 64 * w + lane;
     id[w] = p < npairs ? ids[p] : -1;
   }
   // touched[x] bit b  <=>  expert 64x + b has a pair: each lane sets the bits
   // of its ids, then a butterfly ORs the words over the wave
-  uint64_t touched[kMaxExpertWords];
+  uint64_t touched[NW];
 #pragma unroll
-  for (int x = 0; x < kMaxExpertWords; ++x) touched[x] = 0;
+  for (int x = 0; x < NW; ++x) touched[x] = 0;
 #pragma unroll
-  for (int w = 0; w < kMaxIdWords; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int e = id[w];
     const bool ok = e >= 0 && e < n_expert;
 #pragma unroll
-    for (int x = 0; x < kMaxExpertWords; ++x)
+    for (int x = 0; x < NW; ++x)
       if (ok && (e >> 6) == x) touched[x] |= 1ull << (e & 63);
   }
 #pragma unroll
-  for (int x = 0; x < kMaxExpertWords; ++x) {
+  for (int x = 0; x < NW; ++x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) touched[x] |= __shfl_xor(touched[x], off, 64);
     // the same in every lane now: keep it in scalar registers
@@ -207,10 +212,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   // rank[x] = position of expert 64x + lane among the touched experts, or -1
   // if it is untouched; the expert at position k is then the one lane whose
   // rank equals k (one compare and ballot per word)
-  int rank[kMaxExpertWords];
+  int rank[NW];
   int active = 0;
 #pragma unroll
-  for (int x = 0; x < kMaxExpertWords; ++x) {
+  for (int x = 0; x < NW; ++x) {
     const uint64_t t = touched[x];
     const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(t >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)t, 0u));
     rank[x] = ((t >> lane) & 1) ? active + below : -1;
@@ -218,9 +223,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   }
   const int items = active * tiles;
   // token row of pair 64w + lane (the activation row of the staged form)
-  int tok[kMaxIdWords];
+  int tok[NW];
 #pragma unroll
-  for (int w = 0; w < kMaxIdWords; ++w) tok[w] = STAGE ? (64 * w + lane) / top_k : 0;
+  for (int w = 0; w < NW; ++w) tok[w] = STAGE ? (64 * w + lane) / top_k : 0;
 
   const int u = li;  // this lane's unit (L >= U here, so at most one)
   const int sb = u >> 2, g = u & 3;
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     int e = -1;
 #pragma unroll
-    for (int x = 0; x < kMaxExpertWords; ++x) {
+    for (int x = 0; x < NW; ++x) {
       const uint64_t m = __ballot(rank[x] == ik);
       if (m) e = 64 * x + __builtin_ctzll(m);
     }
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       }
     }
 #pragma unroll
-    for (int w = 0; w < kMaxIdWords; ++w) {
+    for (int w = 0; w < NW; ++w) {
       uint64_t mask = __ballot(id[w] == e);
       while (mask) {
         const int p = 64 * w + __builtin_ctzll(mask);
@@ -290,8 +295,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
           uint32_t A[18];
           int S0 = 0, S1 = 0;
           float da0, da1;
-          if constexpr (STAGE) {
-            const u32x4n *base = xs + arow * 5 * U;
+          if constexpr (STAGE || UMX) {
+            // the unit-major row: staged in LDS, or (UMX) in global memory
+            const u32x4n *base =
+                (STAGE ? xs : reinterpret_cast<const u32x4n *>(act)) + (int64_t)arow * 5 * U;
             const u32x4n x0 = base[u], x1 = base[U + u], x2 = base[2 * U + u], x3 = base[3 * U + u];
             const u32x4n rec = base[4 * U + u];
             A[1] = x0.x; A[2] = x0.y; A[3] = x0.z; A[4] = x0.w;
@@ -341,13 +348,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 }
 
 // Kernel 2: h = silu(g) * u per pair, requantized to Q8_1.  One 8-lane group
-// per 32-value block of h; pairs with an out-of-range id are skipped.
+// per 32-value block of h; pairs with an out-of-range id are skipped.  The
+// block also goes to hx in the unit-major layout the staged gate/up kernel
+// keeps in LDS (unit = blocks 2u, 2u+1: pieces c = 0..3 of 16 bytes, then the
+// record {d(2u), d(2u+1), sum(2u), sum(2u+1)}), which the down GEMV reads.
 __global__ __launch_bounds__(256) void moe_act_quant_kernel(const float *__restrict__ gu,
                                                             const int32_t *__restrict__ ids,
-                                                            uint8_t *__restrict__ hq, int npairs, int n_ff,
-                                                            int n_expert) {
+                                                            uint8_t *__restrict__ hq, uint8_t *__restrict__ hx,
+                                                            int npairs, int n_ff, int n_expert) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int nbp = n_ff / 32;
+  const int nbp = n_ff / 32, U = n_ff / 64;
   const int64_t b = t >> 3;
   const int j = (int)(t & 7);
   const int p = (int)(b / nbp), bi = (int)(b % nbp);
@@ -367,7 +377,20 @@ __global__ __launch_bounds__(256) void moe_act_quant_kernel(const float *__restr
     v.z = g4.z / (1.0f + expf(-g4.z)) * u4.z;
     v.w = g4.w / (1.0f + expf(-g4.w)) * u4.w;
   }
-  quantize_block_q8_1(v, hq + ((int64_t)p * nbp + bi) * kQ8_1Bytes, j, live);
+  const Q81Part q = quantize_part_q8_1(v);
+  if (live) {
+    uint8_t *blk = hq + ((int64_t)p * nbp + bi) * kQ8_1Bytes;
+    const uint32_t hdr = q81_header(q);
+    *reinterpret_cast<uint32_t *>(blk + 4 + 4 * j) = q.packed;
+    if (j == 0) *reinterpret_cast<uint32_t *>(blk) = hdr;
+    uint32_t *row = reinterpret_cast<uint32_t *>(hx + (int64_t)p * U * 80);
+    const int uu = bi >> 1, bb = bi & 1;
+    row[4 * ((2 * bb + (j >> 2)) * U + uu) + (j & 3)] = q.packed;
+    if (j == 0) {
+      row[4 * (4 * U + uu) + bb] = __builtin_bit_cast(uint32_t, h2f(hdr));
+      row[4 * (4 * U + uu) + 2 + bb] = (uint32_t)q.sum;
+    }
+  }
 }
 
 // Kernel 4: out[t][i] = sum over slots s (in order) of z[t*top_k + s][i].
@@ -409,17 +432,18 @@ constexpr size_t kMoeStageBytes = 40 * 1024;
 
 // Launch shape of the persistent expert GEMV: workgroup size, rows per lane
 // group, and the waves per SIMD its register allocation must leave room for.
-// The staged gate/up call is held to four workgroups per CU by its LDS; the
-// down call fits five.  The grid is the number of workgroups resident at once.
+// The staged gate/up call is held to four workgroups per CU by its LDS.  The
+// down call also runs four: held to the 96 VGPRs of five waves it spills.
+// The grid is the number of workgroups resident at once.
 constexpr int kGuThreads = 256, kGuRows = 2, kGuWaves = 4;
-constexpr int kDnThreads = 256, kDnRows = 2, kDnWaves = 5;
+constexpr int kDnThreads = 256, kDnRows = 2, kDnWaves = 4;
 
-template <int L, int R, bool STAGE, int NT, int WPE>
+template <int L, int R, bool STAGE, int NT, int WPE, bool UMX, int NW>
 static void launch_persistent_shape(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights,
                                     float *out, int rows, int nsb, int npairs, int top_k, int act_per_token,
                                     int64_t expert_bytes, int64_t act_row_bytes, int n_expert, int n_act,
                                     size_t stage, hipStream_t stream) {
-  constexpr auto kern = moe_expert_gemv_persistent<L, R, STAGE, NT, WPE>;
+  constexpr auto kern = moe_expert_gemv_persistent<L, R, STAGE, NT, WPE, UMX, NW>;
   const int rows_per_block = (NT / 64) * (64 / L) * R;
   const int tiles = (rows + rows_per_block - 1) / rows_per_block;
   const int64_t max_items = (int64_t)tiles * n_expert;
@@ -429,26 +453,48 @@ static void launch_persistent_shape(const uint8_t *W, const uint8_t *act, const 
                      act_per_token, expert_bytes, act_row_bytes, tiles, n_expert, n_act);
 }
 
-template <int L>
-static void launch_expert_gemv_persistent(const uint8_t *W, const uint8_t *act, const int32_t *ids,
-                                          const float *weights, float *out, int rows, int nsb, int npairs,
-                                          int top_k, int act_per_token, int64_t expert_bytes,
+// act_um (nullable): the activation rows in the unit-major layout, used
+// instead of the Q8_1 rows by the unstaged form.
+template <int L, int NW>
+static void launch_expert_gemv_persistent_nw(const uint8_t *W, const uint8_t *act, const uint8_t *act_um,
+                                          const int32_t *ids, const float *weights, float *out, int rows, int nsb,
+                                          int npairs, int top_k, int act_per_token, int64_t expert_bytes,
                                           int64_t act_row_bytes, int n_expert, hipStream_t stream) {
   const int n_act = act_per_token ? (npairs + top_k - 1) / top_k : npairs;
   const size_t stage = (size_t)n_act * nsb * 4 * 80;
   if (act_per_token && stage <= kMoeStageBytes)
-    launch_persistent_shape<L, kGuRows, true, kGuThreads, kGuWaves>(W, act, ids, weights, out, rows, nsb, npairs,
-                                                                    top_k, act_per_token, expert_bytes,
-                                                                    act_row_bytes, n_expert, n_act, stage, stream);
+    launch_persistent_shape<L, kGuRows, true, kGuThreads, kGuWaves, false, NW>(
+        W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, n_expert,
+        n_act, stage, stream);
+  else if (act_um)
+    launch_persistent_shape<L, kDnRows, false, kDnThreads, kDnWaves, true, NW>(
+        W, act_um, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, (int64_t)nsb * 4 * 80,
+        n_expert, n_act, 0, stream);
   else
-    launch_persistent_shape<L, kDnRows, false, kDnThreads, kDnWaves>(W, act, ids, weights, out, rows, nsb, npairs,
-                                                                     top_k, act_per_token, expert_bytes,
-                                                                     act_row_bytes, n_expert, n_act, 0, stream);
+    launch_persistent_shape<L, kDnRows, false, kDnThreads, kDnWaves, false, NW>(
+        W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, expert_bytes, act_row_bytes, n_expert,
+        n_act, 0, stream);
 }
 
-static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights, float *out,
-                        int rows, int nsb, int npairs, int top_k, int act_per_token, int64_t act_row_bytes,
-                        int n_expert, hipStream_t stream) {
+// Routing tables of up to 128 pairs over up to 128 experts keep two words of
+// ids and of the touched-expert bitmap per lane instead of four: four VGPRs
+// fewer, which the down call needs to hold five waves per SIMD without spills.
+template <int L>
+static void launch_expert_gemv_persistent(const uint8_t *W, const uint8_t *act, const uint8_t *act_um,
+                                          const int32_t *ids, const float *weights, float *out, int rows, int nsb,
+                                          int npairs, int top_k, int act_per_token, int64_t expert_bytes,
+                                          int64_t act_row_bytes, int n_expert, hipStream_t stream) {
+  if (npairs <= 128 && n_expert <= 128)
+    launch_expert_gemv_persistent_nw<L, 2>(W, act, act_um, ids, weights, out, rows, nsb, npairs, top_k,
+                                           act_per_token, expert_bytes, act_row_bytes, n_expert, stream);
+  else
+    launch_expert_gemv_persistent_nw<L, kMaxIdWords>(W, act, act_um, ids, weights, out, rows, nsb, npairs, top_k,
+                                                     act_per_token, expert_bytes, act_row_bytes, n_expert, stream);
+}
+
+static void expert_gemv(const uint8_t *W, const uint8_t *act, const uint8_t *act_um, const int32_t *ids,
+                        const float *weights, float *out, int rows, int nsb, int npairs, int top_k,
+                        int act_per_token, int64_t act_row_bytes, int n_expert, hipStream_t stream) {
   const int64_t expert_bytes = (int64_t)rows * nsb * kQ4KBytes;
   const int U = nsb * 4;
   int L = 4;
@@ -456,7 +502,7 @@ static void expert_gemv(const uint8_t *W, const uint8_t *act, const int32_t *ids
   const int upl = (U + L - 1) / L;
   if (upl == 1 && npairs <= 64 * kMaxIdWords && n_expert <= 64 * kMaxExpertWords) {
 #define QG_MOE_PERSIST(LV)                                                                                        \
-  launch_expert_gemv_persistent<LV>(W, act, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, \
+  launch_expert_gemv_persistent<LV>(W, act, act_um, ids, weights, out, rows, nsb, npairs, top_k, act_per_token, \
                                               expert_bytes, act_row_bytes, n_expert, stream)
     if (L == 4) QG_MOE_PERSIST(4);
     else if (L == 8) QG_MOE_PERSIST(8);
@@ -486,7 +532,8 @@ MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd)
   l.hq_off = 0;
   l.gu_off = up(P * (size_t)(n_ff / 32) * kQ8_1Bytes);
   l.z_off = l.gu_off + up(P * (size_t)(2 * n_ff) * sizeof(float));
-  l.total = l.z_off + up(P * (size_t)n_embd * sizeof(float));
+  l.hx_off = l.z_off + up(P * (size_t)n_embd * sizeof(float));
+  l.total = l.hx_off + up(P * (size_t)(n_ff / 64) * 80);
   return l;
 }
 
@@ -494,16 +541,16 @@ hipError_t launch_moe_q4_k(const MoeArgs &a, hipStream_t stream) {
   const int P = (int)(a.n_tok * a.top_k);
   const int F = (int)a.n_ff, H = (int)a.n_embd, E = (int)a.n_expert, K = (int)a.top_k;
   // 1. gate|up rows [2F] of each touched expert against token rows of xq
-  expert_gemv(static_cast<const uint8_t *>(a.w_gu), static_cast<const uint8_t *>(a.xq), a.ids, nullptr, a.ws_gu,
+  expert_gemv(static_cast<const uint8_t *>(a.w_gu), static_cast<const uint8_t *>(a.xq), nullptr, a.ids, nullptr, a.ws_gu,
               2 * F, H / 256, P, K, 1, (int64_t)(H / 32) * kQ8_1Bytes, E, stream);
   // 2. h^ = Q8_1(silu(g) * u)
   {
     const int64_t threads = (int64_t)P * (F / 32) * 8;
     hipLaunchKernelGGL(moe_act_quant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.ws_gu,
-                       a.ids, a.ws_hq, P, F, E);
+                       a.ids, a.ws_hq, a.ws_hx, P, F, E);
   }
   // 3. z[p] = weights[p] * (Wdown[e] . h^[p])
-  expert_gemv(static_cast<const uint8_t *>(a.w_down), a.ws_hq, a.ids, a.weights, a.ws_z, H, F / 256, P, K, 0,
+  expert_gemv(static_cast<const uint8_t *>(a.w_down), a.ws_hq, a.ws_hx, a.ids, a.weights, a.ws_z, H, F / 256, P, K, 0,
               (int64_t)(F / 32) * kQ8_1Bytes, E, stream);
   // 4. out[t] = sum of its slots
   {

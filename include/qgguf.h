@@ -216,6 +216,11 @@ qg_status qgemm_q5_0_mmq(const void *w, const void *aq, float *c, int64_t m, int
  *                 [0, P*(n_ff/32)*36)            h^ per pair, Q8_1
  *                 then f32 [P][2*n_ff]           g | u per pair
  *                 then f32 [P][n_embd]           weights[p] * (Wdown . h^)
+ *                 then P * (n_ff/64) * 80 bytes  h^ per pair again, unit-major
+ *                   for the down GEMV: per 64 values u of pair p, at
+ *                   p*(n_ff/64)*80: four 16-byte code pieces (c*(n_ff/64) + u)
+ *                   and a 16-byte record {d(2u), d(2u+1) as f32, sum of codes
+ *                   (2u), (2u+1) as int32} at (4*(n_ff/64) + u)
  *               each region starting on a 256-byte boundary.
  *   n_embd, n_ff : multiples of 256, <= 2^20;  top_k in [1, 64];
  *   n_tok * top_k <= 2^20;  n_expert in [1, 2^16]

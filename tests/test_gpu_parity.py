@@ -663,6 +663,22 @@ def _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K):
         e = ids.ravel()[p]
         D, _ = qg.blockdots_q4_k(WDN[e], _gpu(torch, dev, hq_g[p]), H, F)
         assert np.array_equal(_host(D), orc.blockdots("q4_k", w_dn[e], hq_g[p], H, F)[0])
+    # the unit-major copy of h^ the down GEMV reads holds the same codes, d and
+    # exact code sums as the Q8_1 rows
+    hx_g = _host(qg.moe_workspace_hx(ws, T, K, F, H))
+    U = F // 64
+    for p in np.flatnonzero(valid)[:8]:
+        blk = hq_g[p].reshape(F // 32, 36)
+        q = blk[:, 4:].view(np.int8)
+        d = blk[:, :2].copy().view(np.float16)[:, 0].astype(np.float32)
+        pieces = hx_g[p][:U * 64].reshape(4, U, 16)
+        rec = hx_g[p][U * 64:].reshape(U, 16)
+        for u in range(U):
+            for c in range(4):
+                assert np.array_equal(pieces[c, u], blk[2 * u + c // 2, 4 + 16 * (c % 2):20 + 16 * (c % 2)])
+            r = rec[u].copy()
+            assert np.array_equal(r[:8].view(np.float32), d[2 * u:2 * u + 2])
+            assert np.array_equal(r[8:].view(np.int32), q[2 * u:2 * u + 2].astype(np.int32).sum(axis=1))
     ref_own = orc.moe_q4_k(w_gu, w_dn, xq, ids, rw, T, K, E, F, H, hq_in=hq_g)
     assert rel_err(out, ref_own["out"]) <= REL_TOL
     # end to end against the oracle's own h^ (h^ codes may differ by one at a
