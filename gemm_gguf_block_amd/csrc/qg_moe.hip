@@ -432,10 +432,11 @@ constexpr size_t kMoeStageBytes = 40 * 1024;
 
 // Launch shape of the persistent expert GEMV: workgroup size, rows per lane
 // group, and the waves per SIMD its register allocation must leave room for.
-// The staged gate/up call is held to four workgroups per CU by its LDS.  The
-// down call also runs four: held to the 96 VGPRs of five waves it spills.
-// The grid is the number of workgroups resident at once.
-constexpr int kGuThreads = 256, kGuRows = 2, kGuWaves = 4;
+// The staged gate/up call runs 8-wave workgroups, two per CU: 16 waves, as
+// with four 4-wave ones, but each CU stages the token rows twice, not four
+// times.  The down call runs four waves per SIMD: held to the 96 VGPRs of
+// five it spills.  The grid is the number of workgroups resident at once.
+constexpr int kGuThreads = 512, kGuRows = 2, kGuWaves = 4;
 constexpr int kDnThreads = 256, kDnRows = 2, kDnWaves = 4;
 
 template <int L, int R, bool STAGE, int NT, int WPE, bool UMX, int NW>
