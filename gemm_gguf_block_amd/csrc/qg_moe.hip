@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256) void moe_expert_gemv_kernel(const uint8_t *__r
       // UPL > 0: the lane's UPL units were loaded above; UPL == 0: walk the
       // row's units with stride L, loading each unit's weights here
       const int nv = UPL > 0 ? UPL : (U - li + L - 1) / L;
-#pragma unroll
+      // fully unrolled when the count is the constant UPL; a plain loop for long rows
+      constexpr int kUnroll = UPL > 0 ? UPL : 1;
+#pragma unroll kUnroll
       for (int v = 0; v < nv; ++v) {
         const int u = li + v * L;
         if (u < U) {
