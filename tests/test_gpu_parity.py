@@ -681,10 +681,26 @@ def _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K):
             assert np.array_equal(r[8:].view(np.int32), q[2 * u:2 * u + 2].astype(np.int32).sum(axis=1))
     ref_own = orc.moe_q4_k(w_gu, w_dn, xq, ids, rw, T, K, E, F, H, hq_in=hq_g)
     assert rel_err(out, ref_own["out"]) <= REL_TOL
-    # end to end against the oracle's own h^ (h^ codes may differ by one at a
-    # rounding boundary: c.f. the count below)
-    flips = int(np.sum(hq_g[valid] != ref["hq"][valid]))
-    assert rel_err(out, ref["out"]) <= REL_TOL, f"h^ byte flips: {flips}"
+    # Against the oracle's own h^: the GPU sums g and u in another fp32 order,
+    # so a value on a rounding boundary of its block can land one code away.
+    # A single such flip moves a token's output by weights[p] * d times a
+    # column of Wdown, which can exceed REL_TOL end to end; so the end-to-end
+    # path is held to REL_TOL through the GPU's own h^ (above), and the two
+    # h^ are checked to differ only in that way: codes at most one apart, in
+    # few places, with d equal or one binary16 step apart (s = d * sum of the
+    # codes follows the codes; the dots do not read it).
+    g_blk = hq_g[valid].reshape(-1, F // 32, 36)
+    r_blk = ref["hq"][valid].reshape(-1, F // 32, 36)
+    dq = g_blk[..., 4:].view(np.int8).astype(np.int32) - r_blk[..., 4:].view(np.int8).astype(np.int32)
+    assert np.abs(dq).max(initial=0) <= 1
+    flips = int(np.count_nonzero(dq))
+    assert flips <= max(4, dq.size // 200), f"h^ codes that differ from the oracle's: {flips} of {dq.size}"
+    # d >= 0: its binary16 bit patterns are ordered like the values
+    gd = g_blk[..., 0:2].copy().view(np.uint16).astype(np.int32)
+    rd = r_blk[..., 0:2].copy().view(np.uint16).astype(np.int32)
+    assert np.abs(gd - rd).max(initial=0) <= 1
+    if flips == 0:
+        assert rel_err(out, ref["out"]) <= REL_TOL
     return flips
 
 
@@ -708,6 +724,18 @@ def test_moe_shared_experts(env):
     E, F, H, T, K = 3, 512, 256, 9, 2
     w_gu, w_dn, ids, rw, x = _moe_case(63, E, F, H, T, K)
     _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
+
+
+@pytest.mark.parametrize("E,T,K", [(160, 6, 3),    # experts past 128: four words of routing state
+                                   (8, 40, 4),     # 160 pairs: four words of routing state
+                                   (8, 70, 4)])    # 280 pairs: the (expert x tile) grid form
+def test_moe_routing_table_sizes(env, E, T, K):
+    """The persistent form keeps two words of ids and touched-expert bitmap per
+    lane up to 128 pairs and 128 experts, four words up to 256; larger tables
+    run the grid form.  Each size against the oracle, stage by stage."""
+    F, H = 256, 512
+    case = _moe_case(65 + E + T, E, F, H, T, K)
+    _run_moe_stagewise(env, *case, E, F, H, T, K)
 
 
 @pytest.mark.big
