@@ -726,14 +726,16 @@ def test_moe_shared_experts(env):
     _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
 
 
-@pytest.mark.parametrize("E,T,K", [(160, 6, 3),    # experts past 128: four words of routing state
-                                   (8, 40, 4),     # 160 pairs: four words of routing state
-                                   (8, 70, 4)])    # 280 pairs: the (expert x tile) grid form
-def test_moe_routing_table_sizes(env, E, T, K):
+@pytest.mark.parametrize("E,T,K,H", [(160, 6, 3, 512),    # experts past 128: four words of routing state
+                                     (8, 40, 4, 512),     # 160 pairs: four words of routing state
+                                     (8, 70, 4, 512),     # 280 pairs: the (expert x tile) grid form
+                                     (8, 20, 4, 2048)])   # token rows past the 40 KB staging: unstaged gate/up
+def test_moe_routing_table_sizes(env, E, T, K, H):
     """The persistent form keeps two words of ids and touched-expert bitmap per
     lane up to 128 pairs and 128 experts, four words up to 256; larger tables
-    run the grid form.  Each size against the oracle, stage by stage."""
-    F, H = 256, 512
+    run the grid form.  The gate/up call stages the token rows in LDS when they
+    fit in 40 KB.  Each case against the oracle, stage by stage."""
+    F = 256
     case = _moe_case(65 + E + T, E, F, H, T, K)
     _run_moe_stagewise(env, *case, E, F, H, T, K)
 
