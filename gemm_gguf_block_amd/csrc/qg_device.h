@@ -114,17 +114,43 @@ __device__ __forceinline__ float group_sum_last(float v) {
   return v;
 }
 
+// Lane exchange within a row of 16 lanes for the butterflies below (every
+// lane reads a lane of its own row): quad_perm [1,0,3,2] (xor 1), quad_perm
+// [2,3,0,1] (xor 2), row_half_mirror (lane i of 8 <-> 7 - i), row_mirror
+// (lane i of 16 <-> 15 - i).
+template <int STEP>
+__device__ __forceinline__ int dpp_swap(int v) {
+  constexpr int kCtrl = STEP == 1 ? 0xB1 : STEP == 2 ? 0x4E : STEP == 4 ? 0x141 : 0x140;
+  return __builtin_amdgcn_update_dpp(v, v, kCtrl, 0xf, 0xf, false);
+}
+
+// Max / integer sum over aligned groups of L lanes (L a power of two <= 64);
+// every lane of a group gets the result.  Up to 16 lanes the partner values
+// come by DPP (after the quad steps a lane's partner in the other half of its
+// group, by mirror, already holds that half's result); wider groups use
+// cross-lane shuffles for the steps past 16.
 template <int L>
 __device__ __forceinline__ float group_max(float v) {
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "group of 1..64 lanes, a power of two");
 #pragma unroll
-  for (int off = L / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  for (int step = 1; step < L && step <= 8; step <<= 1)
+    v = fmaxf(v, __builtin_bit_cast(float, step == 1   ? dpp_swap<1>(__builtin_bit_cast(int, v))
+                                           : step == 2 ? dpp_swap<2>(__builtin_bit_cast(int, v))
+                                           : step == 4 ? dpp_swap<4>(__builtin_bit_cast(int, v))
+                                                       : dpp_swap<8>(__builtin_bit_cast(int, v))));
+#pragma unroll
+  for (int off = 16; off < L; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
 
 template <int L>
 __device__ __forceinline__ int group_isum(int v) {
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "group of 1..64 lanes, a power of two");
 #pragma unroll
-  for (int off = L / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int step = 1; step < L && step <= 8; step <<= 1)
+    v += step == 1 ? dpp_swap<1>(v) : step == 2 ? dpp_swap<2>(v) : step == 4 ? dpp_swap<4>(v) : dpp_swap<8>(v);
+#pragma unroll
+  for (int off = 16; off < L; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
