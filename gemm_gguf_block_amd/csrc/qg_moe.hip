@@ -3,16 +3,19 @@
 // profiling" and "Paged experts").
 //
 // Four kernels on one stream, no host round trip:
-//   1. gate/up: grid over (expert, row tile).  A workgroup scans the routing
-//      table for its expert and, for each (token, slot) pair routed to it,
-//      runs the Q4_K GEMV rows of its tile against that token's Q8_1 row.  An
-//      expert nobody routed to reads no weights, and a touched expert's
-//      weights are streamed once for all of its pairs (later pairs hit cache).
+//   1. gate/up: work items (touched expert, row tile).  A workgroup finds the
+//      (token, slot) pairs routed to its item's expert and runs the Q4_K GEMV
+//      rows of its tile against each such token's Q8_1 row (staged in LDS).
+//      An expert nobody routed to reads no weights, and a touched expert's
+//      weights are streamed once for all of its pairs.
 //   2. act: per pair, h = silu(g)*u in fp32, requantized to Q8_1 exactly as
-//      quantize_q8_1 does.
-//   3. down: like 1, over the down weights and each pair's h^, scaled by the
-//      pair's routing weight.
+//      quantize_q8_1 does; written as Q8_1 rows and again unit-major with
+//      ready {d, code sum} records for kernel 3.
+//   3. down: like 1, over the down weights and each pair's h^ (the unit-major
+//      copy), scaled by the pair's routing weight.
 //   4. combine: out[t] = sum over t's slots in slot order (deterministic).
+// Large routing tables take the (expert x tile) grid form of 1 and 3 instead
+// of the persistent one, reading the Q8_1 rows.
 #include "qg_blocks.h"
 #include "qg_launch.h"
 #include "qg_quant.h"
