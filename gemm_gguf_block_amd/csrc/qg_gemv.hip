@@ -592,6 +592,9 @@ __global__ __launch_bounds__(256) void gemv_q5_0_kernel(const uint8_t *__restric
 constexpr int kRowsQ8_0 = 2;
 constexpr int kRowsQ4K = 1;
 constexpr int kRowsQ6K = 4;
+// Q6_K grids hold this many workgroups per resident one: the queued ones start
+// as others finish, which evens out the last round of row groups.
+constexpr int64_t kOversubQ6K = 2;
 
 #define QG_LAUNCH(KERNEL, LV, RV, ...)                                                          \
   do {                                                                                          \
@@ -612,16 +615,17 @@ constexpr int kRowsQ6K = 4;
     default: QG_LAUNCH(KERNEL, 1, RV, __VA_ARGS__); break;      \
   }
 
-// Persistent launch: at most the resident workgroups, each striding over the
-// row groups of 4 * (64 / L) * R rows; `xlds` bytes of dynamic LDS.
+// Persistent launch: at most `oversub` times the resident workgroups, each
+// striding over the row groups of 4 * (64 / L) * R rows; `xlds` bytes of
+// dynamic LDS.
 #define QG_LAUNCH_PERSISTENT(KERNEL, LV, RV, ...)                                               \
   do {                                                                                          \
     const int64_t groups = (n + 4 * (64 / LV) * RV - 1) / (4 * (64 / LV) * RV);                 \
     if (dump) {                                                                                 \
-      const int64_t g = std::min(groups, resident_blocks<KERNEL<LV, RV, true>>(256, xlds));          \
+      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, true>>(256, xlds)); \
       hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
     } else {                                                                                    \
-      const int64_t g = std::min(groups, resident_blocks<KERNEL<LV, RV, false>>(256, xlds));         \
+      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, false>>(256, xlds)); \
       hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
     }                                                                                           \
   } while (0)
@@ -662,6 +666,7 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
+    const int64_t oversub = 1;
     QG_GEMV_SWITCH_PERSISTENT(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else if (fmt == 4 || fmt == 5) {
     const int npair = (int)(k / 64);
@@ -676,11 +681,13 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
+    const int64_t oversub = 1;
     QG_GEMV_SWITCH_PERSISTENT(gemv_q5k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
+    const int64_t oversub = kOversubQ6K;
     QG_GEMV_SWITCH_PERSISTENT(gemv_q6k_kernel, kRowsQ6K, W, X, y, D, ni, nsb)
   }
   return hipGetLastError();
