@@ -97,7 +97,7 @@ __device__ __forceinline__ void stage_x(XView x, const uint8_t *__restrict__ XQ,
 // The K-quants with a min term share this kernel.  Q5_K (FMT 3) is Q4_K's
 // block with qh[32] between the header and qs: element 32j + l of a
 // superblock takes bit j of qh[l] as its fifth code bit.
-template <int L, int R, bool DUMP, int FMT>
+template <int L, int R, bool DUMP, int FMT, int NWV>
 __device__ __forceinline__ void gemv_kmin(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
                                           float *__restrict__ Y, int32_t *__restrict__ Dd,
                                           int32_t *__restrict__ Sd, int n, int nsb) {
@@ -107,7 +107,7 @@ __device__ __forceinline__ void gemv_kmin(const uint8_t *__restrict__ W, const u
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
   constexpr int kChunkSb = kXBlocks / 8;
-  constexpr int kGroupRows = 4 * G * R;  // rows per workgroup per group
+  constexpr int kGroupRows = NWV * G * R;  // rows per workgroup per group
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
   const int64_t rb = (int64_t)nsb * kBlockBytes;
@@ -115,7 +115,7 @@ __device__ __forceinline__ void gemv_kmin(const uint8_t *__restrict__ W, const u
   int staged = -1;  // first superblock of the chunk in xs
   // persistent over row groups, like the Q6_K kernel
   for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const int64_t row0 = ((grp * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+    const int64_t row0 = ((grp * NWV + (threadIdx.x >> 6)) * G + lane / L) * R;
     const uint8_t *wrow = W + row0 * rb;
     float acc[R];
 #pragma unroll
@@ -216,18 +216,23 @@ __device__ __forceinline__ void gemv_kmin(const uint8_t *__restrict__ W, const u
   }
 }
 
+// Waves per workgroup of the Q4_K / Q5_K GEMV.
+constexpr int kWavesQ4K = 4;
+
 template <int L, int R, bool DUMP>
-__global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
-                                                       float *__restrict__ Y, int32_t *__restrict__ Dd,
-                                                       int32_t *__restrict__ Sd, int n, int nsb) {
-  gemv_kmin<L, R, DUMP, 1>(W, XQ, Y, Dd, Sd, n, nsb);
+__global__ __launch_bounds__(64 * kWavesQ4K) void gemv_q4k_kernel(const uint8_t *__restrict__ W,
+                                                                  const uint8_t *__restrict__ XQ,
+                                                                  float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                                                  int32_t *__restrict__ Sd, int n, int nsb) {
+  gemv_kmin<L, R, DUMP, 1, kWavesQ4K>(W, XQ, Y, Dd, Sd, n, nsb);
 }
 
 template <int L, int R, bool DUMP>
-__global__ __launch_bounds__(256) void gemv_q5k_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ XQ,
-                                                       float *__restrict__ Y, int32_t *__restrict__ Dd,
-                                                       int32_t *__restrict__ Sd, int n, int nsb) {
-  gemv_kmin<L, R, DUMP, 3>(W, XQ, Y, Dd, Sd, n, nsb);
+__global__ __launch_bounds__(64 * kWavesQ4K) void gemv_q5k_kernel(const uint8_t *__restrict__ W,
+                                                                  const uint8_t *__restrict__ XQ,
+                                                                  float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                                                  int32_t *__restrict__ Sd, int n, int nsb) {
+  gemv_kmin<L, R, DUMP, 3, kWavesQ4K>(W, XQ, Y, Dd, Sd, n, nsb);
 }
 
 // ---------------------------------------------------------------- Q6_K
@@ -615,18 +620,18 @@ constexpr int64_t kOversubQ6K = 2;
     default: QG_LAUNCH(KERNEL, 1, RV, __VA_ARGS__); break;      \
   }
 
-// Persistent launch: at most `oversub` times the resident workgroups, each
-// striding over the row groups of 4 * (64 / L) * R rows; `xlds` bytes of
-// dynamic LDS.
+// Persistent launch: at most `oversub` times the resident workgroups of
+// `waves` waves, each striding over the row groups of waves * (64 / L) * R
+// rows; `xlds` bytes of dynamic LDS.
 #define QG_LAUNCH_PERSISTENT(KERNEL, LV, RV, ...)                                               \
   do {                                                                                          \
-    const int64_t groups = (n + 4 * (64 / LV) * RV - 1) / (4 * (64 / LV) * RV);                 \
+    const int64_t groups = (n + waves * (64 / LV) * RV - 1) / (waves * (64 / LV) * RV);                 \
     if (dump) {                                                                                 \
-      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, true>>(256, xlds)); \
-      hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
+      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, true>>(64 * waves, xlds)); \
+      hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(64 * waves), xlds, stream, __VA_ARGS__); \
     } else {                                                                                    \
-      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, false>>(256, xlds)); \
-      hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(256), xlds, stream, __VA_ARGS__); \
+      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, false>>(64 * waves, xlds)); \
+      hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(64 * waves), xlds, stream, __VA_ARGS__); \
     }                                                                                           \
   } while (0)
 
@@ -667,6 +672,7 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
     const int64_t oversub = 1;
+    const int waves = kWavesQ4K;
     QG_GEMV_SWITCH_PERSISTENT(gemv_q4k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else if (fmt == 4 || fmt == 5) {
     const int npair = (int)(k / 64);
@@ -682,12 +688,14 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
     const int64_t oversub = 1;
+    const int waves = kWavesQ4K;
     QG_GEMV_SWITCH_PERSISTENT(gemv_q5k_kernel, kRowsQ4K, W, X, y, D, S, ni, nsb)
   } else {
     const int nsb = (int)(k / 256);
     const int L = lanes_per_row((int64_t)nsb * 4);
     const size_t xlds = x_chunk_bytes(k / 32);
     const int64_t oversub = kOversubQ6K;
+    const int waves = 4;
     QG_GEMV_SWITCH_PERSISTENT(gemv_q6k_kernel, kRowsQ6K, W, X, y, D, ni, nsb)
   }
   return hipGetLastError();
