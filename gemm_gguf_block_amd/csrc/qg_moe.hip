@@ -439,10 +439,11 @@ constexpr size_t kMoeStageBytes = 40 * 1024;
 // group, and the waves per SIMD its register allocation must leave room for.
 // The staged gate/up call runs 8-wave workgroups, two per CU: 16 waves, as
 // with four 4-wave ones, but each CU stages the token rows twice, not four
-// times.  The down call runs four waves per SIMD: held to the 96 VGPRs of
-// five it spills.  The grid is the number of workgroups resident at once.
+// times.  The down call runs four waves per SIMD (held to the 96 VGPRs of
+// five it spills) and three rows per lane group.  The grid is the number of
+// workgroups resident at once.
 constexpr int kGuThreads = 512, kGuRows = 2, kGuWaves = 4;
-constexpr int kDnThreads = 256, kDnRows = 2, kDnWaves = 4;
+constexpr int kDnThreads = 256, kDnRows = 3, kDnWaves = 4;
 
 template <int L, int R, bool STAGE, int NT, int WPE, bool UMX, int NW>
 static void launch_persistent_shape(const uint8_t *W, const uint8_t *act, const int32_t *ids, const float *weights,
