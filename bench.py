@@ -18,7 +18,14 @@ copies, so the 256 MB Infinity Cache cannot serve them (--warm disables this).
 
 Printed per workload: one JSON line with the step throughput (`value`), the
 dominant kernel's roofline position measured with HIP events on the launch
-stream, and the CPU oracle's throughput on a bounded sample of the same work.
+stream, and the CPU oracle's throughput on a bounded sample of the same work
+(the median of three runs on all the oracle's threads, and of three on one).
+
+The default run (the Q4_K GEMV line) also carries `configs`: the same figures
+for the five headline workloads (Q4_K, Q8_0 and Q6_K GEMVs, the Q4_K mmq and
+the MoE), each against the published peak and against a peak measured in the
+same run -- the best streaming read of the workload's own byte count (HBM) or
+a loop of int8 MFMAs (mmq) -- listed under `peaks`.
 """
 from __future__ import annotations
 
@@ -44,9 +51,41 @@ def q81_bytes(k):
     return (k // 32) * 36
 
 
-def _cpu_threads():
-    v = os.environ.get("OMP_NUM_THREADS")
-    return int(v) if v and v.isdigit() else (os.cpu_count() or 1)
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, run_s):
+    """The oracle on the host cores: three runs on all its OpenMP threads and
+    three on one; each run repeats the workload's bounded sample for at least
+    run_s seconds.  `value` is the median over the all-threads runs."""
+    import statistics
+
+    import oracle
+    fn, work, unit, sample = wl.cpu_sample()
+    all_threads = oracle.max_threads()
+    out = {}
+    for threads in (all_threads, 1):
+        oracle.set_threads(threads)
+        rates, reps_done, secs = [], 0, 0.0
+        for _ in range(3):
+            reps, t = _repeat(fn, run_s)
+            rates.append(reps * work / t / (1e9 if unit == "GB/s" else 1e12))
+            reps_done, secs = reps_done + reps, secs + t
+        out[threads] = (statistics.median(rates), reps_done, secs)
+    oracle.set_threads(all_threads)
+    v, reps, secs = out[all_threads]
+    v1, reps1, secs1 = out[1]
+    return dict(value=v, unit=unit, cores=all_threads, kind="oracle",
+                sample=f"{sample}; median of 3 runs of >= {run_s:g} s ({reps} repetitions, {secs:.1f} s)",
+                single_thread={"value": v1, "cores": 1, "repetitions": reps1, "seconds": round(secs1, 2)},
+                nproc=os.cpu_count(), cpu_model=_cpu_model())
 
 
 KERNEL_SOURCES = {
@@ -160,16 +199,15 @@ class Gemv(Workload):
     def kernel_rate(self, sec):
         return self.kernel_bytes / sec / 1e9
 
-    def cpu_baseline(self, budget_s):
+    def cpu_sample(self):
         import numpy as np
 
         import oracle
         xq = oracle.quantize_q8_1(self.x_host[None])[0]
         sel = np.arange(min(self.n, 16384), dtype=np.int64)
-        reps, t = _repeat(lambda: oracle.qgemv(self.fmt, self.w_host, xq, self.n, self.k, rows=sel), budget_s)
-        nb = reps * (sel.size * self.w_host.shape[1] + q81_bytes(self.k) + 4 * sel.size)
-        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"rows 0..{sel.size - 1} of {self.n} (plain double dequant-and-dot) x {reps}, {t:.1f} s")
+        nb = sel.size * self.w_host.shape[1] + q81_bytes(self.k) + 4 * sel.size
+        return (lambda: oracle.qgemv(self.fmt, self.w_host, xq, self.n, self.k, rows=sel), nb, "GB/s",
+                f"rows 0..{sel.size - 1} of {self.n} (plain double dequant-and-dot)")
 
 
 class GemvBatch(Gemv):
@@ -202,7 +240,7 @@ class GemvBatch(Gemv):
     def dominant_call(self, i):
         self.fn(self.W[i % self.copies], self.xq, self.b, self.n, self.k, y=self.y)
 
-    def cpu_baseline(self, budget_s):
+    def cpu_sample(self):
         import numpy as np
 
         import oracle
@@ -212,11 +250,9 @@ class GemvBatch(Gemv):
         def once():
             for i in range(self.b):
                 oracle.qgemv(self.fmt, self.w_host, xq[i], self.n, self.k, rows=sel)
-        reps, t = _repeat(once, budget_s)
-        nb = reps * (sel.size * self.w_host.shape[1] + self.b * (q81_bytes(self.k) + 4 * sel.size))
-        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"rows 0..{sel.size - 1} of {self.n} against {self.b} activation rows (plain double "
-                           f"dequant-and-dot per row) x {reps}, {t:.1f} s")
+        nb = sel.size * self.w_host.shape[1] + self.b * (q81_bytes(self.k) + 4 * sel.size)
+        return (once, nb, "GB/s", f"rows 0..{sel.size - 1} of {self.n} against {self.b} activation rows "
+                                  f"(plain double dequant-and-dot per row)")
 
 
 class RmsnormQ81(Workload):
@@ -262,7 +298,7 @@ class RmsnormQ81(Workload):
     def kernel_rate(self, sec):
         return self.kernel_bytes / sec / 1e9
 
-    def cpu_baseline(self, budget_s):
+    def cpu_sample(self):
         import numpy as np
 
         import oracle
@@ -272,11 +308,8 @@ class RmsnormQ81(Workload):
         def once():
             r = oracle.rms_scale(x, self.eps).astype(np.float32)
             oracle.quantize_q8_1((x * r[:, None]) * self.g_host[None, :])
-        reps, t = _repeat(once, budget_s)
-        nb = reps * rows * (4 * self.k + q81_bytes(self.k))
-        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"rows 0..{rows - 1} of {self.rows} (double RMS scale, f32 products, quantize) x {reps}, "
-                           f"{t:.1f} s")
+        return (once, rows * (4 * self.k + q81_bytes(self.k)), "GB/s",
+                f"rows 0..{rows - 1} of {self.rows} (double RMS scale, f32 products, quantize)")
 
 
 class Mmq(Workload):
@@ -315,19 +348,17 @@ class Mmq(Workload):
     def kernel_rate(self, sec):
         return self.ops / sec / 1e12
 
-    def cpu_baseline(self, budget_s):
+    def cpu_sample(self):
         import numpy as np
 
         import oracle
         aq = oracle.quantize_q8_1(self.a_host)
         g = np.random.default_rng(0)
-        cnt = 1 << 18
+        cnt = 1 << 14
         pairs = np.stack([g.integers(0, self.m, cnt), g.integers(0, self.n, cnt)], 1)
-        reps, t = _repeat(lambda: oracle.qgemm(self.fmt, self.w_host, aq, self.m, self.n, self.k, pairs=pairs),
-                          budget_s)
-        return dict(value=2.0 * reps * cnt * self.k / t / 1e12, unit="TOPS", cores=_cpu_threads(), kind="oracle",
-                    sample=f"{cnt} random entries of C[{self.m}][{self.n}] (plain double dequant-and-dot) x {reps}, "
-                           f"{t:.1f} s")
+        return (lambda: oracle.qgemm(self.fmt, self.w_host, aq, self.m, self.n, self.k, pairs=pairs),
+                2.0 * cnt * self.k, "TOPS", f"{cnt} random entries of C[{self.m}][{self.n}] (plain double "
+                                            f"dequant-and-dot)")
 
 
 class Moe(Workload):
@@ -380,16 +411,15 @@ class Moe(Workload):
     def kernel_rate(self, sec):
         return self.kernel_bytes / sec / 1e9
 
-    def cpu_baseline(self, budget_s):
+    def cpu_sample(self):
         import oracle
         inp = self.inp
         T = self.T
         xq = oracle.quantize_q8_1(inp["x"])
-        reps, t = _repeat(lambda: oracle.moe_q4_k(inp["w_gu"], inp["w_down"], xq, inp["ids"], inp["weights"], T,
-                                                  self.K, self.E, self.F, self.H), budget_s)
-        nb = reps * self.distinct * (inp["w_gu"].nbytes + inp["w_down"].nbytes) // self.E
-        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"all {T} tokens ({self.distinct} distinct experts) x {reps}, {t:.1f} s")
+        nb = self.distinct * (inp["w_gu"].nbytes + inp["w_down"].nbytes) // self.E
+        return (lambda: oracle.moe_q4_k(inp["w_gu"], inp["w_down"], xq, inp["ids"], inp["weights"], T, self.K,
+                                        self.E, self.F, self.H), nb, "GB/s",
+                f"all {T} tokens ({self.distinct} distinct experts)")
 
 
 class Router(Workload):
@@ -430,16 +460,13 @@ class Router(Workload):
     def kernel_rate(self, sec):
         return self.kernel_bytes / sec / 1e9
 
-    def cpu_baseline(self, budget_s):
+    def cpu_sample(self):
         import oracle
         inp = self.inp
 
         def once():
             oracle.route_topk(oracle.router_logits(inp["w_router"], inp["x"]).astype("float32"), self.K)
-        reps, t = _repeat(once, budget_s)
-        nb = reps * self.kernel_bytes
-        return dict(value=nb / t / 1e9, unit="GB/s", cores=_cpu_threads(), kind="oracle",
-                    sample=f"all {self.T} tokens (double logits, top-k, softmax) x {reps}, {t:.1f} s")
+        return once, self.kernel_bytes, "GB/s", f"all {self.T} tokens (double logits, top-k, softmax)"
 
 
 def make(name, qg, torch, warm):
@@ -516,7 +543,7 @@ def run(wl, steps, warmup, torch, graph, spinup):
     return ms_step, ms_kernel
 
 
-def bench_one(name, args, qg, torch):
+def bench_one(name, args, qg, torch, cpu_run_s=None):
     t_setup = time.time()
     wl = make(name, qg, torch, args.warm)
     torch.cuda.synchronize()
@@ -565,10 +592,85 @@ def bench_one(name, args, qg, torch):
         ms_alt = _time(wl.alt_call, args.warmup, args.steps, args.warmup, torch, not args.no_graph, args.spinup)
         rec["comparison"] = {"what": wl.alt_what, "ms_per_step": round(ms_alt, 6)}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_run if cpu_run_s is None else cpu_run_s)
     print(f"[bench] {name}: setup {setup_s:.1f} s, step {ms_step * 1e3:.2f} us, "
           f"{wl.dominant} {ms_kernel * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
+    del wl
+    torch.cuda.empty_cache()
     return rec
+
+
+# ------------------------------------------------------------ measured peaks
+# Launch shapes of the streaming-read reference: grid x threads, loads in
+# flight per thread, non-temporal or plain.
+READ_SWEEP = [(g, t, l, nt) for g in (256, 512, 1024) for t in (256, 512) for l in (4, 8) for nt in (1, 0)]
+
+
+def peak_read(qg, torch, nbytes, args):
+    """Best rate (GB/s) of the streaming-read reference over READ_SWEEP for a
+    buffer of nbytes (rounded up to 16), on copies rotating past the Infinity
+    Cache like the weights of the workloads; each shape timed as a HIP graph of
+    args.steps launches after args.spinup seconds of untimed replays."""
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = 1 if args.warm else max(1, math.ceil(COLD_BYTES / nbytes))
+    dev = torch.device("cuda:0")
+    bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.empty(max(g for g, _, _, _ in READ_SWEEP), dtype=torch.int32, device=dev)
+    best = None
+    for j, (g, t, l, nt) in enumerate(READ_SWEEP):
+        def call(i):
+            qg.peak_read(bufs[i % copies], g, t, l, nt, sink)
+        # the first shape spins the clock up; the rest follow back to back
+        ms = _time(call, args.warmup, args.steps, args.warmup, torch, not args.no_graph,
+                   args.spinup if j == 0 else min(args.spinup, 0.05))
+        rate = nbytes / (ms / 1e3) / 1e9
+        if best is None or rate > best["GB/s"]:
+            best = {"GB/s": round(rate, 1), "us": round(ms * 1e3, 3), "grid": g, "threads": t, "loads": l,
+                    "nontemporal": bool(nt)}
+    del bufs
+    torch.cuda.empty_cache()
+    best["bytes"] = nbytes
+    best["copies"] = copies
+    return best
+
+
+def peak_mfma_i8(qg, torch, args, iters=1000):
+    """Rate (TOP/s) of a loop of int8 MFMAs filling every SIMD."""
+    dev = torch.device("cuda:0")
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    ops = qg.peak_mfma_i8(iters, sink)
+    ms = _time(lambda i: qg.peak_mfma_i8(iters, sink), args.warmup, args.steps, args.warmup, torch,
+               not args.no_graph, args.spinup)
+    return {"TOP/s": round(ops / (ms / 1e3) / 1e12, 1), "us": round(ms * 1e3, 3), "ops_per_launch": ops}
+
+
+HEADLINE = ["q4_k_gemv", "q8_0_gemv", "q6_k_gemv", "q4_k_mmq", "moe_q4_k"]
+
+
+def config_entry(rec, peak):
+    """The compact per-workload figures of the `configs` list."""
+    rf = rec["roofline"]
+    meas = peak["GB/s"] if rf["unit"] == "GB/s" else peak["TOP/s"]
+    e = {
+        "workload": rec["config"]["workload"],
+        "config": {k: v for k, v in rec["config"].items() if k not in ("workload", "hip_graph", "spinup_s")},
+        "kernel": rf["kernel"],
+        "us_per_launch": round(rf["ms_per_launch"] * 1e3, 3),
+        "us_per_step": round(rec["ms_per_step"] * 1e3, 3),
+        "achieved": rf["achieved"],
+        "unit": rf["unit"],
+        "frac_of_published_peak": rf["frac"],
+        "measured_peak": meas,
+        "frac_of_measured_peak": round(rf["achieved"] / meas, 4),
+        "step_value": rec["value"],
+        "step_unit": rec["unit"],
+        "tokens_per_s_equiv": rec["tokens_per_s_equiv"],
+        "algorithmic_per_launch": rf["algorithmic_per_launch"],
+        "traffic": rf["traffic"],
+    }
+    if "cpu_baseline" in rec:
+        e["cpu_baseline"] = rec["cpu_baseline"]
+    return e
 
 
 def main():
@@ -579,14 +681,20 @@ def main():
     ap.add_argument("--spinup", type=float, default=1.0,
                     help="minimum seconds of untimed back-to-back calls before each timed region")
     ap.add_argument("--workload", default="q4_k_gemv",
-                    help="q4_k_gemv (default), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, all (these five), "
+                    help="q4_k_gemv (default; with the `configs` list), q8_0_gemv, q6_k_gemv, q4_k_mmq, moe_q4_k, "
+                         "all (these five, one line each), "
                          "q6_k_mmq, q8_0_mmq, rmsnorm_q8_1, q5_k_gemv, q5_k_mmq, router_topk, q4_0_gemv, q5_0_gemv, "
                          "q4_0_mmq, q5_0_mmq, "
                          "a small-batch GEMV <fmt>_gemv_b<B> (B <= 8), or batch (" + ", ".join(BATCH_WORKLOADS) + ")")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload only: leave out the `configs` list and the measured peaks")
     ap.add_argument("--warm", action="store_true", help="one weight copy (Infinity-Cache-resident for small ones)")
     ap.add_argument("--no-graph", action="store_true", help="launch every call from the host (no HIP graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work per workload")
+    ap.add_argument("--cpu-run", type=float, default=1.5,
+                    help="seconds per oracle timing run of the printed workload (3 runs on all threads, 3 on one)")
+    ap.add_argument("--cpu-run-configs", type=float, default=0.4,
+                    help="seconds per oracle timing run of each other entry of the `configs` list")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="instead of benchmarking, run 10 plain device copies of MiB mebibytes (a kernel of known "
                          "traffic, to scale HBM counters by) and exit")
@@ -612,12 +720,37 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 10}))
         return
-    names = (["q4_k_gemv", "q8_0_gemv", "q6_k_gemv", "q4_k_mmq", "moe_q4_k"] if args.workload == "all"
+    if args.workload == "q4_k_gemv" and not args.no_configs:
+        t0 = time.time()
+        recs = {}
+        for name in HEADLINE:
+            run_s = args.cpu_run if name == "q4_k_gemv" else args.cpu_run_configs
+            recs[name] = bench_one(name, args, qg, torch, cpu_run_s=run_s)
+        peaks = {"hbm_read": {}, "mfma_i8": peak_mfma_i8(qg, torch, args)}
+        entries = []
+        for name in HEADLINE:
+            rec = recs[name]
+            if rec["roofline"]["unit"] == "GB/s":
+                nb = rec["roofline"]["algorithmic_per_launch"]
+                pk = peaks["hbm_read"].setdefault(name, peak_read(qg, torch, nb, args))
+            else:
+                pk = peaks["mfma_i8"]
+            entries.append(config_entry(rec, pk))
+            print(f"[bench] {name}: {entries[-1]['frac_of_published_peak']:.3f} of published, "
+                  f"{entries[-1]['frac_of_measured_peak']:.3f} of measured peak", file=sys.stderr, flush=True)
+        head = recs["q4_k_gemv"]
+        head["configs"] = entries
+        head["peaks"] = peaks
+        head["roofline"]["measured_peak"] = entries[0]["measured_peak"]
+        head["roofline"]["frac_of_measured_peak"] = entries[0]["frac_of_measured_peak"]
+        head["bench_wall_s"] = round(time.time() - t0, 1)
+        print(json.dumps(head), flush=True)
+        return
+    names = (HEADLINE if args.workload == "all"
              else BATCH_WORKLOADS if args.workload == "batch" else [args.workload])
     for name in names:
         rec = bench_one(name, args, qg, torch)
         print(json.dumps(rec), flush=True)
-        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

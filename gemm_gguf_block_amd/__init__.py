@@ -60,6 +60,11 @@ SIGNATURES = {
     "qg_blockdots_q5_0": [_P, _P, _P, _I, _I, _P],
     "qg_blockdots_q4_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q5_0_mmq": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_blockdots_q6_k_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "qg_peak_read": [_P, _I, _P, _I, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P],
+    "qg_peak_mfma_i8": [_P, _I, _I, _P, _P],
 }
 
 
@@ -415,3 +420,36 @@ def blockdots_q5_0_mmq(w, aq, m, n, k, stream=None):
 
 def blockdots_q5_k_mmq(w, aq, m, n, k, stream=None):
     return _blockdots_mmq("q5_k", w, aq, m, n, k, stream)
+
+
+def blockdots_batch(fmt, w, xq, b, n, k, stream=None):
+    """[b][n][k/32] (Q6_K: [b][n][k/16]) exact dots from the kernel that
+    qgemv_<fmt>_batch runs for b rows, on its launch grid."""
+    import torch
+    D = _empty((b, n, k // (16 if fmt == "q6_k" else 32)), torch.int32, w)
+    name = f"qg_blockdots_{fmt}_batch"
+    _check(name, getattr(lib(), name)(
+        _need(w, torch.uint8, n * row_bytes(fmt, k), "w"), _need(xq, torch.uint8, b * row_bytes("q8_1", k), "xq"),
+        _need(D, torch.int32, D.numel() * 4, "D"), b, n, k, _stream(stream)))
+    return D
+
+
+# ------------------------------------------------ measurement references (bench)
+def peak_read(src, grid, threads, loads, nontemporal, sink, stream=None):
+    """Streaming read of every 16-byte word of the uint8 tensor src (its whole
+    size, a multiple of 16); sink: uint32/int32 tensor of >= grid entries."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    _check("qg_peak_read", lib().qg_peak_read(
+        _need(src, src.dtype, nbytes, "src"), nbytes, _need(sink, sink.dtype, grid * 4, "sink"), sink.numel(),
+        grid, threads, loads, int(bool(nontemporal)), _stream(stream)))
+
+
+def peak_mfma_i8(iters, sink, stream=None):
+    """Loop of int8 MFMAs; returns the int8 operation count of the launch.
+    sink: int32 tensor of >= 8 * CUs entries."""
+    import torch
+    ops = ctypes.c_int64(0)
+    _check("qg_peak_mfma_i8", lib().qg_peak_mfma_i8(_need(sink, torch.int32, 4, "sink"), sink.numel(), iters,
+                                                    ctypes.byref(ops), _stream(stream)))
+    return ops.value

@@ -73,13 +73,16 @@ qg_status check_gemv_batch(int fmt, const void *w, const void *xq, const void *o
   return QG_OK;
 }
 
-qg_status run_gemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                         hipStream_t stream) {
-  qg_status st = check_gemv_batch(fmt, w, xq, y, nb, n, k);
-  if (st != QG_OK || nb == 0 || n == 0) return st;  // k == 0 runs: the kernel writes y = 0
+// D non-null: the per-block dot dump of the kernel the product call would run.
+qg_status run_gemv_batch(int fmt, const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                         int64_t k, hipStream_t stream) {
+  qg_status st = check_gemv_batch(fmt, w, xq, y ? static_cast<const void *>(y) : D, nb, n, k);
+  if (st != QG_OK) return st;
+  if (D && k > 0 && nb * n > (int64_t(1) << 29) / (k / (fmt == 2 ? 16 : 32))) return QG_ERR_SHAPE;
+  if (nb == 0 || n == 0 || (D && k == 0)) return QG_OK;  // k == 0 runs for y: the kernel writes y = 0
   st = check_device();
   if (st != QG_OK) return st;
-  return launched(qg::launch_qgemv_batch(fmt, w, xq, y, nb, n, k, stream));
+  return launched(qg::launch_qgemv_batch(fmt, w, xq, y, D, nb, n, k, stream));
 }
 
 qg_status check_mmq(int fmt, const void *w, const void *aq, const void *out, int64_t m, int64_t n, int64_t k) {
@@ -163,17 +166,32 @@ QG_EXPORT qg_status qgemv_q5_0(const void *w, const void *xq, float *y, int64_t 
 
 QG_EXPORT qg_status qgemv_q8_0_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
                                      hipStream_t stream) {
-  return run_gemv_batch(0, w, xq, y, b, n, k, stream);
+  return run_gemv_batch(0, w, xq, y, nullptr, b, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q8_0_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_gemv_batch(0, w, xq, nullptr, D, b, n, k, stream);
 }
 
 QG_EXPORT qg_status qgemv_q4_k_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
                                      hipStream_t stream) {
-  return run_gemv_batch(1, w, xq, y, b, n, k, stream);
+  return run_gemv_batch(1, w, xq, y, nullptr, b, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q4_k_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_gemv_batch(1, w, xq, nullptr, D, b, n, k, stream);
 }
 
 QG_EXPORT qg_status qgemv_q6_k_batch(const void *w, const void *xq, float *y, int64_t b, int64_t n, int64_t k,
                                      hipStream_t stream) {
-  return run_gemv_batch(2, w, xq, y, b, n, k, stream);
+  return run_gemv_batch(2, w, xq, y, nullptr, b, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_blockdots_q6_k_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
+                                          hipStream_t stream) {
+  return run_gemv_batch(2, w, xq, nullptr, D, b, n, k, stream);
 }
 
 static qg_status run_mmq(int fmt, const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n, int64_t k,
@@ -347,4 +365,31 @@ QG_EXPORT qg_status qg_blockdots_q5_k_mmq(const void *w, const void *aq, int32_t
 QG_EXPORT qg_status qg_blockdots_q6_k_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                           hipStream_t stream) {
   return run_mmq(2, w, aq, nullptr, D, m, n, k, stream);
+}
+
+QG_EXPORT qg_status qg_peak_read(const void *src, int64_t bytes, uint32_t *sink, int64_t sink_entries, int32_t grid,
+                                 int32_t threads, int32_t loads, int32_t nontemporal, hipStream_t stream) {
+  if (!src || !sink) return QG_ERR_NULL;
+  if (bytes <= 0 || bytes % 16 != 0 || grid < 1 || grid > (1 << 20) || threads < 64 || threads > 1024 ||
+      threads % 64 != 0 || (loads != 4 && loads != 8) || sink_entries < grid)
+    return QG_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return QG_ERR_ALIGN;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  return launched(qg::launch_peak_read(src, bytes, sink, grid, threads, loads, nontemporal != 0, stream));
+}
+
+QG_EXPORT qg_status qg_peak_mfma_i8(int32_t *sink, int64_t sink_entries, int64_t iters, int64_t *ops,
+                                    hipStream_t stream) {
+  if (!sink || !ops) return QG_ERR_NULL;
+  if (iters < 1 || iters > (int64_t(1) << 24)) return QG_ERR_SHAPE;
+  if (!aligned(sink, 4)) return QG_ERR_ALIGN;
+  qg_status st = check_device();
+  if (st != QG_OK) return st;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess)
+    return QG_ERR_NO_DEVICE;
+  if (sink_entries < (int64_t)cus * 8) return QG_ERR_SHAPE;
+  return launched(qg::launch_peak_mfma_i8(sink, iters, ops, stream));
 }

@@ -622,17 +622,17 @@ constexpr int64_t kOversubQ6K = 2;
 
 // Persistent launch: at most `oversub` times the resident workgroups of
 // `waves` waves, each striding over the row groups of waves * (64 / L) * R
-// rows; `xlds` bytes of dynamic LDS.
+// rows; `xlds` bytes of dynamic LDS.  The dump instance runs on the grid of
+// the product instance (sized from the product kernel's occupancy), so a dump
+// walks the row groups exactly as the product launch of that shape does.
 #define QG_LAUNCH_PERSISTENT(KERNEL, LV, RV, ...)                                               \
   do {                                                                                          \
     const int64_t groups = (n + waves * (64 / LV) * RV - 1) / (waves * (64 / LV) * RV);                 \
-    if (dump) {                                                                                 \
-      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, true>>(64 * waves, xlds)); \
+    const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, false>>(64 * waves, xlds)); \
+    if (dump)                                                                                   \
       hipLaunchKernelGGL((KERNEL<LV, RV, true>), dim3((unsigned)g), dim3(64 * waves), xlds, stream, __VA_ARGS__); \
-    } else {                                                                                    \
-      const int64_t g = std::min(groups, oversub * resident_blocks<KERNEL<LV, RV, false>>(64 * waves, xlds)); \
+    else                                                                                        \
       hipLaunchKernelGGL((KERNEL<LV, RV, false>), dim3((unsigned)g), dim3(64 * waves), xlds, stream, __VA_ARGS__); \
-    }                                                                                           \
   } while (0)
 
 #define QG_GEMV_SWITCH_PERSISTENT(KERNEL, RV, ...)                         \

@@ -21,6 +21,10 @@
 //   Q8_0  recf[i * U + u]  = d_a
 //   Q4_K  rec4[i * U + u]  = {d_a(2u), d_a(2u+1), d_a*sum q (2u), d_a*sum q (2u+1)}
 //   Q6_K  rec4[2(i * U + u)] = d_a of pieces 0..3, [+1] = sum of each piece's 16 qs
+//
+// With DUMP the same code writes the exact per-block int32 dots instead of Y:
+// D[i][r][block] per 32-value block (Q8_0, Q4_K) or per 16-value sub-block
+// (Q6_K).
 #include <algorithm>
 
 #include "qg_blocks.h"
@@ -108,10 +112,10 @@ __device__ __forceinline__ void stage_batch(uint8_t *lds, const uint8_t *__restr
 // One workgroup of 8 waves strides over groups of 8 * (64/L) * R rows; the
 // activation is staged per chunk of chunk_blocks<B>() Q8_1 blocks (c0 counts
 // blocks for every format).
-template <int FMT, int L, int B, int R>
+template <int FMT, int L, int B, int R, bool DUMP>
 __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__restrict__ W,
                                                               const uint8_t *__restrict__ XQ, float *__restrict__ Y,
-                                                              int nb, int n, int nblk) {
+                                                              int32_t *__restrict__ Dd, int nb, int n, int nblk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
   constexpr int NP = Unit<FMT>::kPieces;
@@ -237,7 +241,11 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__r
               int D = 0;
 #pragma unroll
               for (int j = 0; j < 8; ++j) D = dot4(q[r][j], a[j], D);
-              acc[r][i] += f[r][0] * da * (float)D;
+              if (DUMP) {
+                if (row0 + r < n && i < nb) Dd[((int64_t)i * n + row0 + r) * nblk + c0 + u] = D;
+              } else {
+                acc[r][i] += f[r][0] * da * (float)D;
+              }
             }
           } else if (FMT == kFmtQ4K) {
             const u32x4n rv = reinterpret_cast<const u32x4n *>(rec)[i * U + u];
@@ -249,6 +257,14 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__r
               for (int j = 0; j < 8; ++j) {
                 D0 = dot4(q[r][j], a[j], D0);
                 D1 = dot4(q[r][8 + j], a[8 + j], D1);
+              }
+              if (DUMP) {
+                if (row0 + r < n && i < nb) {
+                  int32_t *dp = Dd + ((int64_t)i * n + row0 + r) * nblk + c0 + 2 * u;  // blocks 8sb + 2g, + 1
+                  dp[0] = D0;
+                  dp[1] = D1;
+                }
+                continue;
               }
               const float t = da0 * (f[r][2] * (float)D0) + da1 * (f[r][3] * (float)D1);
               const float mm = dS0 * (float)mi[r][0] + dS1 * (float)mi[r][1];
@@ -268,7 +284,14 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__r
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Dg = dot4(q[r][4 * g + j], a[4 * g + j], Dg);
                 Dg -= 32 * (int)ss[g];  // sum (q-32)*qa
-                t += as_f32(dd[g]) * (f[r][g] * (float)Dg);
+                if (DUMP) {
+                  // sub-block 8h + 2g + l of superblock c0/8 + u/4
+                  if (row0 + r < n && i < nb)
+                    Dd[((int64_t)i * n + row0 + r) * (2 * (int64_t)nblk) + 2 * c0 + 4 * (u & ~3) + 8 * ((u >> 1) & 1) +
+                       2 * g + (u & 1)] = Dg;
+                } else {
+                  t += as_f32(dd[g]) * (f[r][g] * (float)Dg);
+                }
               }
               acc[r][i] += t;
             }
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__r
         }
       }
     }
-    if (row0 < n) {
+    if (!DUMP && row0 < n) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -290,59 +313,65 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__r
 
 template <int FMT> constexpr int rows_per_lane() { return FMT == kFmtQ6K ? 2 : 1; }
 
+// The dump instance runs on the grid of the product instance.
 template <int FMT, int L, int B>
-hipError_t launch_fmt_lb(const uint8_t *W, const uint8_t *X, float *y, int nb, int64_t n, int nblk,
+hipError_t launch_fmt_lb(const uint8_t *W, const uint8_t *X, float *y, int32_t *D, int nb, int64_t n, int nblk,
                          hipStream_t stream) {
   constexpr int R = rows_per_lane<FMT>();
   constexpr int kGroupRows = kWaves * (64 / L) * R;
   const size_t lds = batch_lds_bytes<FMT, B>(nblk);
   const int64_t groups = (n + kGroupRows - 1) / kGroupRows;
-  const int64_t g = std::min(groups, resident_blocks<gemv_batch_kernel<FMT, L, B, R>>(kThreads, lds));
-  hipLaunchKernelGGL((gemv_batch_kernel<FMT, L, B, R>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, nb,
-                     (int)n, nblk);
+  const int64_t g = std::min(groups, resident_blocks<gemv_batch_kernel<FMT, L, B, R, false>>(kThreads, lds));
+  if (D)
+    hipLaunchKernelGGL((gemv_batch_kernel<FMT, L, B, R, true>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X,
+                       y, D, nb, (int)n, nblk);
+  else
+    hipLaunchKernelGGL((gemv_batch_kernel<FMT, L, B, R, false>), dim3((unsigned)g), dim3(kThreads), lds, stream, W,
+                       X, y, D, nb, (int)n, nblk);
   return hipGetLastError();
 }
 
 template <int FMT, int B>
-hipError_t launch_fmt_b(const uint8_t *W, const uint8_t *X, float *y, int nb, int64_t n, int nblk, int L,
+hipError_t launch_fmt_b(const uint8_t *W, const uint8_t *X, float *y, int32_t *D, int nb, int64_t n, int nblk, int L,
                         hipStream_t stream) {
   switch (L) {
-    case 64: return launch_fmt_lb<FMT, 64, B>(W, X, y, nb, n, nblk, stream);
-    case 16: return launch_fmt_lb<FMT, 16, B>(W, X, y, nb, n, nblk, stream);
-    case 4: return launch_fmt_lb<FMT, 4, B>(W, X, y, nb, n, nblk, stream);
-    default: return launch_fmt_lb<FMT, 1, B>(W, X, y, nb, n, nblk, stream);
+    case 64: return launch_fmt_lb<FMT, 64, B>(W, X, y, D, nb, n, nblk, stream);
+    case 16: return launch_fmt_lb<FMT, 16, B>(W, X, y, D, nb, n, nblk, stream);
+    case 4: return launch_fmt_lb<FMT, 4, B>(W, X, y, D, nb, n, nblk, stream);
+    default: return launch_fmt_lb<FMT, 1, B>(W, X, y, D, nb, n, nblk, stream);
   }
 }
 
 template <int FMT>
-hipError_t launch_fmt(const uint8_t *W, const uint8_t *X, float *y, int nb, int64_t n, int nblk, hipStream_t stream) {
+hipError_t launch_fmt(const uint8_t *W, const uint8_t *X, float *y, int32_t *D, int nb, int64_t n, int nblk,
+                      hipStream_t stream) {
   // lanes per row: the largest of 64, 16, 4, 1 dividing both the row's unit
   // count and a full chunk's (so every chunk's unit count too)
   const int units = nblk * 32 / Unit<FMT>::kValues;
   int L = 64;
   while (L > 1 && units % L != 0) L /= 4;
-  if (nb <= 2) return launch_fmt_b<FMT, 2>(W, X, y, nb, n, nblk, L, stream);
-  if (nb <= 4) return launch_fmt_b<FMT, 4>(W, X, y, nb, n, nblk, L, stream);
-  return launch_fmt_b<FMT, 8>(W, X, y, nb, n, nblk, L, stream);
+  if (nb <= 2) return launch_fmt_b<FMT, 2>(W, X, y, D, nb, n, nblk, L, stream);
+  if (nb <= 4) return launch_fmt_b<FMT, 4>(W, X, y, D, nb, n, nblk, L, stream);
+  return launch_fmt_b<FMT, 8>(W, X, y, D, nb, n, nblk, L, stream);
 }
 
 }  // namespace
 
-hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                              hipStream_t stream) {
+hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                              int64_t k, hipStream_t stream) {
   const uint8_t *W = static_cast<const uint8_t *>(w);
   const uint8_t *X = static_cast<const uint8_t *>(xq);
   const int nblk = (int)(k / 32);
-  if (fmt == 0) return launch_fmt<kFmtQ8_0>(W, X, y, (int)nb, n, nblk, stream);
+  if (fmt == 0) return launch_fmt<kFmtQ8_0>(W, X, y, D, (int)nb, n, nblk, stream);
   // Measured on MI355X: v_dot4 is faster up to 4 rows; from 5 rows (where it
   // runs its 8-row instance) the matrix-core kernels are.  8 rows, k = 4096:
   // Q4_K 14336 rows 13.8 vs 16.0 us, Q6_K 128256 rows 108 vs 138 us.
   if (fmt == 1) {
-    if (nb > 4) return launch_qgemv_batch_mfma_q4k(w, xq, y, nb, n, k, stream);
-    return launch_fmt<kFmtQ4K>(W, X, y, (int)nb, n, nblk, stream);
+    if (nb > 4) return launch_qgemv_batch_mfma_q4k(w, xq, y, D, nb, n, k, stream);
+    return launch_fmt<kFmtQ4K>(W, X, y, D, (int)nb, n, nblk, stream);
   }
-  if (nb > 4) return launch_qgemv_batch_mfma_q6k(w, xq, y, nb, n, k, stream);
-  return launch_fmt<kFmtQ6K>(W, X, y, (int)nb, n, nblk, stream);
+  if (nb > 4) return launch_qgemv_batch_mfma_q6k(w, xq, y, D, nb, n, k, stream);
+  return launch_fmt<kFmtQ6K>(W, X, y, D, (int)nb, n, nblk, stream);
 }
 
 }  // namespace qg

@@ -18,6 +18,9 @@
 // matrix core.  The 8 waves' partial tiles are summed through LDS at the end.
 // Two such workgroups fit on a CU, so 14336 rows (448 tiles) run in one pass.
 // For b <= 8 only registers r = 0..3 carry rows (4(lane/32) + r).
+//
+// With DUMP the same code writes the exact int32 dots of every MFMA instead of
+// Y: D[i][r][block] per 32-value block (Q4_K) or per 16-value sub-block (Q6_K).
 #include "qg_blocks.h"
 #include "qg_launch.h"
 
@@ -48,9 +51,11 @@ inline size_t lds_bytes(int nb) {
   return (size_t)kChunkBlk * bp * 32 + 2 * (size_t)kChunkBlk * bp * 4 + (size_t)kWaves * 64 * 16;
 }
 
+template <bool DUMP>
 __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q4k(const uint8_t *__restrict__ W,
                                                                 const uint8_t *__restrict__ XQ,
-                                                                float *__restrict__ Y, int nb, int n, int nsb) {
+                                                                float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                                                int nb, int n, int nsb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int bp = rows_padded(nb);
   u32x4n *act = reinterpret_cast<u32x4n *>(lds);
@@ -120,6 +125,15 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q4k(const uint8_t *_
         v4i a = {0, 0, 0, 0};
         if (nl < nb) a = __builtin_bit_cast(v4i, act[(blk * bp + nl) * 2 + lh]);
         const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
+        if (DUMP) {
+          // register r: activation row 4*lh + r, weight row `row`
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * lh + r < nb && live_row)
+              Dd[((int64_t)(4 * lh + r) * n + row) * (8 * (int64_t)nsb) + 8 * (c0 + sbl) + j] = D[r];
+          asm volatile("" ::: "memory");
+          continue;
+        }
         // activation rows 4*lh + r, r = 0..3 (broadcast reads; rows >= nb
         // only reach registers that are never stored)
         f32x4n a4 = {0.f, 0.f, 0.f, 0.f}, s4 = a4;
@@ -138,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q4k(const uint8_t *_
       }
     }
   }
+  if (DUMP) return;
   // sum the waves' partial tiles; thread t < 32 * nb owns output (m, nl) with
   // m = t / 32: lane nl + 32 * (m / 4), register m % 4 of every wave
   part[wv * 64 + lane] = f32x4n{acc[0], acc[1], acc[2], acc[3]};
@@ -206,10 +221,11 @@ __device__ __forceinline__ void load_sb(const uint8_t *p, int lh, Sb &s) {
   s.d = ld2(p + 208);
 }
 
-template <int BP>
+template <int BP, bool DUMP>
 __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *__restrict__ W,
                                                                 const uint8_t *__restrict__ XQ,
-                                                                float *__restrict__ Y, int nb, int n, int nsb) {
+                                                                float *__restrict__ Y, int32_t *__restrict__ Dd,
+                                                                int nb, int n, int nsb) {
   constexpr int S = unit_stride(BP);
   constexpr int NJ = BP / 2;  // activation rows per lane
   typedef float fNJ __attribute__((ext_vector_type(NJ)));
@@ -235,6 +251,8 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
     for (int m = nb; m < 8; ++m) da[t * 8 + pos(m)] = 0.f;
   }
 
+  // c0 and tile of the superblock being run, for the dump
+  int dump_c0 = 0, dump_tile = 0;
   auto step = [&](const Sb &w, int sbl, fNJ &acc) {
     fNJ p = {};
 #pragma unroll
@@ -246,6 +264,22 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
                      q6k_codes4(lo.z >> ls, hi.z >> hs), q6k_codes4(lo.w >> ls, hi.w >> hs)};
       const v4i a = __builtin_bit_cast(v4i, act[blk * S + aunit]);
       const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
+      if (DUMP) {
+        // registers 2q + h: activation row 4(q/2) + 2lh + q%2, k half h =
+        // sub-block 2j + h of the superblock
+        const int64_t r = (int64_t)dump_tile * 32 + nl;
+#pragma unroll
+        for (int q = 0; q < NJ; ++q) {
+          const int m = 4 * (q >> 1) + 2 * lh + (q & 1);
+          if (m < nb && r < n) {
+            int32_t *dp = Dd + ((int64_t)m * n + r) * (16 * (int64_t)nsb) + 16 * (dump_c0 + sbl) + 2 * j;
+            dp[0] = D[2 * q];
+            dp[1] = D[2 * q + 1];
+          }
+        }
+        asm volatile("" ::: "memory");
+        continue;
+      }
       const uint32_t scw = w.sc[j >> 1];
       const float sc0 = (float)sbyte(scw, 16u * (uint32_t)(j & 1));
       const float sc1 = (float)sbyte(scw, 16u * (uint32_t)(j & 1) + 8u);
@@ -263,8 +297,10 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
   for (int rnd = 0; tile < ntiles; ++rnd, tile += (int)gridDim.x) {  // tile is uniform in the workgroup
     const uint8_t *wr = wrow(tile);
     fNJ acc = {};
+    dump_tile = tile;
     for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
       const int csb = min(kChunkSb, nsb - c0);
+      dump_c0 = c0;
       if (c0 > 0 && wv < csb) load_sb(wr + (int64_t)(c0 + wv) * kQ6KBytes, lh, cur);
       if (nchunk > 1 || rnd == 0) {
         if (rnd > 0 || c0 > 0) __syncthreads();  // the previous chunk is no longer read
@@ -290,6 +326,7 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
     }
     const int next = tile + (int)gridDim.x;
     if (next < ntiles && wv < min(kChunkSb, nsb)) load_sb(wrow(next) + (int64_t)wv * kQ6KBytes, lh, cur);
+    if (DUMP) continue;  // tile is uniform in the workgroup: no barrier is skipped by part of it
     // sum the waves' partial tiles: thread t < 32 * nb owns activation row
     // m = t / 32, weight row nn = t % 32, held by lane nn + 32 * ((m / 2) % 2),
     // element (m % 2) + 2 * (m / 4) of every wave
@@ -310,14 +347,20 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
   }
 }
 
+// The dump instance runs on the grid of the product instance.
 template <int BP>
-hipError_t launch_bp(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k, hipStream_t stream) {
+hipError_t launch_bp(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n, int64_t k,
+                     hipStream_t stream) {
   const size_t lds = lds_bytes(BP);
   const int64_t groups = (n + 31) / 32;
-  const int64_t g = std::min(groups, resident_blocks<gemv_batch_mfma_q6k<BP>>(kThreads, lds));
-  hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP>), dim3((unsigned)g), dim3(kThreads), lds, stream,
-                     static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(xq), y, (int)nb, (int)n,
-                     (int)(k / 256));
+  const int64_t g = std::min(groups, resident_blocks<gemv_batch_mfma_q6k<BP, false>>(kThreads, lds));
+  const uint8_t *W = static_cast<const uint8_t *>(w), *X = static_cast<const uint8_t *>(xq);
+  if (D)
+    hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP, true>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, D,
+                       (int)nb, (int)n, (int)(k / 256));
+  else
+    hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP, false>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, D,
+                       (int)nb, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
@@ -325,19 +368,23 @@ hipError_t launch_bp(const void *w, const void *xq, float *y, int64_t nb, int64_
 
 }  // namespace
 
-hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                                       hipStream_t stream) {
+hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                                       int64_t k, hipStream_t stream) {
   const dim3 grid((unsigned)((n + 31) / 32));
-  hipLaunchKernelGGL(gemv_batch_mfma_q4k, grid, dim3(kThreads), lds_bytes((int)nb), stream,
-                     static_cast<const uint8_t *>(w),
-                     static_cast<const uint8_t *>(xq), y, (int)nb, (int)n, (int)(k / 256));
+  const uint8_t *W = static_cast<const uint8_t *>(w), *X = static_cast<const uint8_t *>(xq);
+  if (D)
+    hipLaunchKernelGGL(gemv_batch_mfma_q4k<true>, grid, dim3(kThreads), lds_bytes((int)nb), stream, W, X, y, D,
+                       (int)nb, (int)n, (int)(k / 256));
+  else
+    hipLaunchKernelGGL(gemv_batch_mfma_q4k<false>, grid, dim3(kThreads), lds_bytes((int)nb), stream, W, X, y, D,
+                       (int)nb, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
-hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                                       hipStream_t stream) {
+hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                                       int64_t k, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  return nb <= 4 ? q6::launch_bp<4>(w, xq, y, nb, n, k, stream) : q6::launch_bp<8>(w, xq, y, nb, n, k, stream);
+  return nb <= 4 ? q6::launch_bp<4>(w, xq, y, D, nb, n, k, stream) : q6::launch_bp<8>(w, xq, y, D, nb, n, k, stream);
 }
 
 }  // namespace qg

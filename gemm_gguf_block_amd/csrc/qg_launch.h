@@ -43,15 +43,17 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
 hipError_t launch_rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *xq, float *r_out,
                                         int64_t rows, int64_t k, hipStream_t stream);
 
-// Small-batch GEMV: nb (1..8) Q8_1 rows [nb][k/32] against the weights; y is [nb][n].
-hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                              hipStream_t stream);
+// Small-batch GEMV: nb (1..8) Q8_1 rows [nb][k/32] against the weights; y is
+// [nb][n].  D non-null selects the per-block dot dump of the kernel the
+// product call dispatches to for this nb: D[nb][n][k/32] (Q6_K: [k/16]).
+hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                              int64_t k, hipStream_t stream);
 
-// Small-batch Q4_K / Q6_K GEMV on the int8 matrix cores (nb <= 8).
-hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                                       hipStream_t stream);
-hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int64_t nb, int64_t n, int64_t k,
-                                       hipStream_t stream);
+// Small-batch Q4_K / Q6_K GEMV on the int8 matrix cores (nb <= 8); D as above.
+hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                                       int64_t k, hipStream_t stream);
+hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                                       int64_t k, hipStream_t stream);
 
 // Prefill product on the int8 matrix cores; fmt as for launch_qgemv.  D
 // non-null selects the per-block (Q6_K: per 16-value sub-block) dot dump.
@@ -61,6 +63,15 @@ hipError_t launch_qgemm_mmq(int fmt, const void *w, const void *aq, float *c, in
 // MoE router: logits, top-k, softmax per token (validated arguments).
 hipError_t launch_router_topk(const float *w_router, const float *x, int32_t *ids, float *weights, float *logits,
                               int64_t n_tok, int64_t n_expert, int64_t n_embd, int64_t top_k, hipStream_t stream);
+
+// Measurement references (not part of the product): a streaming read of
+// `bytes` (a multiple of 16) with `grid` x `threads` threads and `loads` (4 or
+// 8) loads in flight per thread, plain or non-temporal; and a loop of int8
+// MFMAs on eight 4-wave workgroups per CU, whose int8 operation count is
+// returned in *ops.  sink: grid entries (read) or 8 * CUs entries (MFMA).
+hipError_t launch_peak_read(const void *src, int64_t bytes, uint32_t *sink, int grid, int threads, int loads, bool nt,
+                            hipStream_t stream);
+hipError_t launch_peak_mfma_i8(int32_t *sink, int64_t iters, int64_t *ops, hipStream_t stream);
 
 struct MoeArgs {
   const void *w_gu, *w_down, *xq;

@@ -64,6 +64,10 @@ const char *qg_status_str(qg_status s);
 
 /*
  * quantize_q8_1 -- activations f32 -> Q8_1 (the activation side of every dot).
+ * Defining passage: the integer-dot kernels the blazr README names ("Model
+ * Formats > GGUF": dp4a kernels for Q4_K, Q6_K and Q8_0) take 8-bit codes on
+ * both sides, so the activation is quantized to GGUF's 32-value Q8_1 block;
+ * the pages name the integer dot, not the block, and this is the reading.
  * Per block of 32 values: amax = max|x|; d = amax/127 (fp32, correctly
  * rounded); q = round-half-away-from-zero(x/d), computed from the fp32 d and
  * clamped to [-127, 127]; s = d*sum(q) as an fp32 product.  d and s are stored
@@ -77,6 +81,10 @@ qg_status quantize_q8_1(const float *x, void *xq, int64_t rows, int64_t k, hipSt
 
 /*
  * qgemv_q8_0 / qgemv_q4_k / qgemv_q6_k -- batch-1 decode GEMV, y = W . x^.
+ * Defining passages: blazr README, "Model Formats > GGUF" (the three weight
+ * types with dedicated dp4a dot kernels on the GPU); infr page, "Benchmarks
+ * you can compare" and "Per-op device profiling" (decode time is spent in the
+ * GEMV buckets, reported per kernel and per shape).
  * y[r] = sum_j w^[r][j] * x^[j] with w^ dequantized from the weight blocks and
  * x^ from the Q8_1 activation.  Computed from exact per-block int32 dots
  * (Q8_0 and Q4_K: per 32 values; Q6_K: per 16 values) scaled in fp32.
@@ -151,6 +159,10 @@ qg_status rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, v
 
 /*
  * qgemm_q4_k_mmq -- prefill product on int8 matrix cores.
+ * Defining passages: infr page, "models" (in-shader dequantization feeding an
+ * integer-dot mmq) and "Vulkan-first, Metal too" (cooperative-matrix matmul on
+ * AMD); infr page, "llama.cpp-compatible refs" (Q4_K_M, the default quant,
+ * whose bulk is Q4_K weights).
  * c[i][r] = sum_j a^[i][j] * w^[r][j]: each 32-wide slice of k is one int8
  * 32x32x32 MFMA tile of exact per-block dots, rescaled in fp32 by d*sc_j*d_a
  * with the min term -dmin*m_j*d_a*sum(qa) of that Q8_1 block.
@@ -196,8 +208,13 @@ qg_status qgemm_q5_0_mmq(const void *w, const void *aq, float *c, int64_t m, int
                          hipStream_t stream);
 
 /*
- * MoE expert FFN with Q4_K experts (the expert_gateup + down calls of an MoE
- * layer).  For token t and each routed slot i with expert e = ids[t][i]:
+ * moe_qgemv_q4_k_workspace_size / moe_qgemv_q4_k -- MoE expert FFN with Q4_K
+ * experts (the expert_gateup + down calls of an MoE layer).  Defining
+ * passages: infr page, "Per-op device profiling" (expert_gateup, a dispatch
+ * role of its own), "Paged experts, spillable KV" (MoE experts streamed from
+ * VRAM) and "install" (a Qwen3-30B-A3B Q4_K_M MoE model).  The pages do not
+ * write the FFN out; the reading is the gated-SiLU expert FFN of those MoE
+ * models.  For token t and each routed slot i with expert e = ids[t][i]:
  *   g = Wgu[e][0:n_ff] . x^_t, u = Wgu[e][n_ff:2n_ff] . x^_t       (fp32)
  *   h = silu(g) * u, silu(g) = g / (1 + exp(-g))                   (fp32)
  *   h^ = Q8_1(h) exactly as quantize_q8_1
@@ -271,6 +288,13 @@ qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *
  *                       qgemm_q4_0_mmq and qgemm_q5_0_mmq
  *   qg_blockdots_q6_k_mmq : D int32 [m][n][k/16] per 16-value sub-block, from
  *                       qgemm_q6_k_mmq; m*n*(k/16) <= 2^28
+ *   qg_blockdots_q8_0_batch, qg_blockdots_q4_k_batch, qg_blockdots_q6_k_batch :
+ *                       D int32 [b][n][k/32] (Q6_K: [b][n][k/16] per 16-value
+ *                       sub-block) from the kernel qgemv_*_batch runs for b
+ *                       rows (v_dot4 or matrix cores), on its launch grid;
+ *                       b*n*(k/32) (Q6_K: b*n*(k/16)) <= 2^29
+ * The GEMV and small-batch dumps run on the grid the product call of the same
+ * shape uses, so a dump walks the rows exactly as that launch does.
  * Same validation rules and limits as the corresponding products.
  */
 qg_status qg_blockdots_q8_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k, hipStream_t stream);
@@ -293,6 +317,33 @@ qg_status qg_blockdots_q4_0_mmq(const void *w, const void *aq, int32_t *D, int64
                                 hipStream_t stream);
 qg_status qg_blockdots_q5_0_mmq(const void *w, const void *aq, int32_t *D, int64_t m, int64_t n, int64_t k,
                                 hipStream_t stream);
+qg_status qg_blockdots_q8_0_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
+                                  hipStream_t stream);
+qg_status qg_blockdots_q4_k_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
+                                  hipStream_t stream);
+qg_status qg_blockdots_q6_k_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
+                                  hipStream_t stream);
+
+/*
+ * Measurement references (for the roofline fractions the benchmark reports;
+ * the per-kernel accounting of infr page, "Per-op device profiling").  They
+ * compute nothing of the products above.
+ *   qg_peak_read : reads every 16-byte word of src (bytes, a multiple of 16,
+ *                  16-byte aligned) once, with grid workgroups of threads
+ *                  (64..1024, a multiple of 64) keeping loads (4 or 8) loads
+ *                  in flight per thread, non-temporal if nontemporal != 0.
+ *                  sink: uint32 [sink_entries >= grid], practically never
+ *                  written (it only keeps the loads from being dropped).
+ *   qg_peak_mfma_i8 : iters (1..2^24) rounds of four independent
+ *                  v_mfma_i32_32x32x32_i8 per wave, eight 4-wave workgroups
+ *                  per CU; *ops (host pointer) receives the int8 operation
+ *                  count of the launch (2*32*32*32 per MFMA).  sink: int32
+ *                  [sink_entries >= 8 * CUs].
+ * Same validation and error rules as the products.
+ */
+qg_status qg_peak_read(const void *src, int64_t bytes, uint32_t *sink, int64_t sink_entries, int32_t grid,
+                       int32_t threads, int32_t loads, int32_t nontemporal, hipStream_t stream);
+qg_status qg_peak_mfma_i8(int32_t *sink, int64_t sink_entries, int64_t iters, int64_t *ops, hipStream_t stream);
 
 #ifdef __cplusplus
 }

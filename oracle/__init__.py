@@ -53,6 +53,10 @@ _I = ctypes.c_int64
 
 
 def _declare(L):
+    L.orc_set_threads.restype = None
+    L.orc_set_threads.argtypes = [ctypes.c_int]
+    L.orc_max_threads.restype = ctypes.c_int
+    L.orc_max_threads.argtypes = []
     L.orc_f16_to_f32.restype = ctypes.c_float
     L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
     L.orc_f32_to_f16.restype = ctypes.c_uint16
@@ -117,6 +121,15 @@ def _c(a, dtype):
 
 
 # ---------------------------------------------------------------- fp16 codec
+def set_threads(n):
+    """OpenMP threads of the oracle's routines (for the CPU-baseline timing)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
 def f16_bits_to_f32(bits):
     bits = _c(bits, np.uint16)
     out = np.empty(bits.shape, np.float32)

@@ -25,6 +25,7 @@
  * other (no shared element-extraction helper), so their agreement is a check.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -42,6 +43,11 @@
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format definition.       */
 /* ------------------------------------------------------------------------ */
+
+/* OpenMP threads the routines below use (the CPU-baseline timing runs them
+ * on one thread and on all threads); no arithmetic depends on it. */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 float orc_f16_to_f32(uint16_t h)
 {

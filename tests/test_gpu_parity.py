@@ -305,48 +305,89 @@ def test_gemv_batch_empty_and_zero_k(env):
         y.fill_(7.0)
 
 
+def _blockdots_ref(orc, fmt, w, xq, n, k):
+    D = orc.blockdots(fmt, w, xq, n, k)
+    return D[0] if fmt in ("q4_k", "q5_k") else D
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("b", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("n,k", [(65, 256), (130, 768), (33, 14336), (5, 33536)])
+def test_gemv_batch_block_dots_exact(env, fmt, b, n, k):
+    """Exact int32 dots of the kernel each b dispatches to (v_dot4 up to 4
+    rows; matrix cores from 5 rows for the K-quants), on fully random bytes."""
+    qg, orc, torch, dev = env
+    w = synth.random_blocks(fmt, n, k, seed=7 * n + b)
+    xq = synth.random_blocks("q8_1", b, k, seed=11 * n + b)
+    D = _host(qg.blockdots_batch(fmt, _gpu(torch, dev, w), _gpu(torch, dev, xq), b, n, k))
+    for i in range(b):
+        assert np.array_equal(D[i], _blockdots_ref(orc, fmt, w, xq[i], n, k)), f"activation row {i}"
+
+
 @pytest.mark.big
 @pytest.mark.parametrize("name,b", [("q8_0_gemv", 8), ("q4_k_gemv", 8), ("q4_k_gemv", 3), ("q6_k_gemv", 4),
                                     ("q6_k_gemv", 8)])
 def test_gemv_batch_full_size(env, name, b):
-    """The workload shapes with b activation rows, on sampled output rows."""
+    """The workload shapes with b activation rows: every output against the
+    oracle, and the exact dots of the whole product from its launch grid."""
     qg, orc, torch, dev = env
     p = synth.WORKLOADS[name]
     fmt, n, k = p["fmt"], p["n"], p["k"]
     w = synth.weights(fmt, n, k, p["seed"])
     x = synth.normal(p["seed"], synth.T_X, (b, k))
     X = qg.quantize_q8_1(_gpu(torch, dev, x))
-    y = _host(getattr(qg, GEMV_BATCH[fmt])(_gpu(torch, dev, w), X, b, n, k))
+    W = _gpu(torch, dev, w)
+    y = _host(getattr(qg, GEMV_BATCH[fmt])(W, X, b, n, k))
     xq = orc.quantize_q8_1(x)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
-                                     np.random.default_rng(2).integers(0, n, 1024)]))
     for i in range(b):
-        assert rel_err(y[i][rows], orc.qgemv(fmt, w, xq[i], n, k, rows=rows)) <= REL_TOL, f"row {i}"
+        assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"activation row {i}"
+    D = qg.blockdots_batch(fmt, W, X, b, n, k)
+    for i in range(b):
+        assert np.array_equal(_host(D[i]), _blockdots_ref(orc, fmt, w, xq[i], n, k)), f"activation row {i}"
 
 
 @pytest.mark.big
 @pytest.mark.parametrize("name", ["q8_0_gemv", "q4_k_gemv", "q6_k_gemv", "q5_k_gemv", "q4_0_gemv", "q5_0_gemv"])
 def test_gemv_full_size(env, name):
-    """The full workload sizes in the launch configuration the bench times."""
+    """The full workload sizes in the launch configuration the bench times:
+    every output row against the oracle, and the exact dots of the whole
+    matrix from a dump that runs on the product launch's grid."""
     qg, orc, torch, dev = env
     p = synth.WORKLOADS[name]
     fmt, n, k = p["fmt"], p["n"], p["k"]
     w = synth.weights(fmt, n, k, p["seed"])
     x = synth.normal(p["seed"], synth.T_X, (k,))
     X = qg.quantize_q8_1(_gpu(torch, dev, x))
-    y = _host(getattr(qg, GEMV[fmt])(_gpu(torch, dev, w), X, n, k))
+    W = _gpu(torch, dev, w)
+    y = _host(getattr(qg, GEMV[fmt])(W, X, n, k))
     xq = orc.quantize_q8_1(x[None])[0]
     assert np.array_equal(_host(X).ravel(), xq)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
-                                     np.random.default_rng(1).integers(0, n, 4096)]))
-    r = orc.qgemv(fmt, w, xq, n, k, rows=rows)
-    # the floor of the metric is the RMS over the sampled rows
-    assert rel_err(y[rows], r) <= REL_TOL
-    D = getattr(qg, "blockdots_" + fmt)(_gpu(torch, dev, w[rows[:256]]), X, 256, k)
+    assert rel_err(y, orc.qgemv(fmt, w, xq, n, k)) <= REL_TOL
+    D = getattr(qg, "blockdots_" + fmt)(W, X, n, k)
     D = D[0] if fmt in ("q4_k", "q5_k") else D
-    Dr = orc.blockdots(fmt, w[rows[:256]], xq, 256, k)
-    Dr = Dr[0] if fmt in ("q4_k", "q5_k") else Dr
-    assert np.array_equal(_host(D), Dr)
+    assert np.array_equal(_host(D), _blockdots_ref(orc, fmt, w, xq, n, k))
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("fmt,n", [("q4_k", 10000), ("q5_k", 10000), ("q6_k", 52000)])
+def test_gemv_chunked_k_multi_round(env, fmt, n):
+    """k = 20480 runs the activation in two LDS chunks (16384 + 4096 values),
+    and n is large enough that the persistent workgroups take more than one
+    round of row groups (at most 6 resident per CU by LDS, 4 or 16 rows per
+    group, Q6_K on twice the resident grid), so a workgroup restages chunk 0
+    after chunk 1 of its previous round.  Every row and every block dot."""
+    qg, orc, torch, dev = env
+    k = 20480
+    w = synth.random_blocks(fmt, n, k, seed=n + 3)
+    x = synth.normal(n + 4, synth.T_X, (k,))
+    X = qg.quantize_q8_1(_gpu(torch, dev, x))
+    xq = orc.quantize_q8_1(x[None])[0]
+    W = _gpu(torch, dev, w)
+    y = _host(getattr(qg, GEMV[fmt])(W, X, n, k))
+    assert rel_err(y, orc.qgemv(fmt, w, xq, n, k)) <= REL_TOL
+    D = getattr(qg, "blockdots_" + fmt)(W, X, n, k)
+    D = D[0] if fmt in ("q4_k", "q5_k") else D
+    assert np.array_equal(_host(D), _blockdots_ref(orc, fmt, w, xq, n, k))
 
 
 # ------------------------------------------------------------------------ mmq
@@ -399,14 +440,10 @@ def test_mmq_full_size(env):
     C = _host(qg.qgemm_q4_k_mmq(_gpu(torch, dev, w), AQ, m, n, k))
     aq = orc.quantize_q8_1(a)
     assert np.array_equal(_host(AQ), aq)
-    g = np.random.default_rng(3)
-    pairs = np.concatenate([np.stack([g.integers(0, m, 4096), g.integers(0, n, 4096)], 1),
-                            np.stack([np.zeros(n, int), np.arange(n)], 1),          # a full row
-                            np.stack([np.arange(m), np.full(m, n - 1)], 1)])        # a full column
-    r = orc.qgemm_q4_k(w, aq, m, n, k, pairs=pairs)
-    assert rel_err(C[pairs[:, 0], pairs[:, 1]], r) <= REL_TOL
-    D = qg.blockdots_q4_k_mmq(_gpu(torch, dev, w[:96]), AQ[:80].contiguous(), 80, 96, k)
-    assert np.array_equal(_host(D), orc.blockdots_q4_k_mmq(w[:96], aq[:80], 80, 96, k))
+    assert rel_err(C, orc.qgemm_q4_k(w, aq, m, n, k)) <= REL_TOL
+    # the exact dots of the whole product (m * n * k/32 = 2^28), same grid
+    D = _host(qg.blockdots_q4_k_mmq(_gpu(torch, dev, w), AQ, m, n, k))
+    assert np.array_equal(D, orc.blockdots_q4_k_mmq(w, aq, m, n, k))
 
 
 # ------------------------------------------------- activation prologue fusion
@@ -552,14 +589,12 @@ def test_mmq_full_size_other_formats(env, name):
     C = _host(getattr(qg, f"qgemm_{fmt}_mmq")(_gpu(torch, dev, w), AQ, m, n, k))
     aq = orc.quantize_q8_1(a)
     assert np.array_equal(_host(AQ), aq)
-    g = np.random.default_rng(4)
-    pairs = np.concatenate([np.stack([g.integers(0, m, 4096), g.integers(0, n, 4096)], 1),
-                            np.stack([np.zeros(n, int), np.arange(n)], 1),          # a full row
-                            np.stack([np.arange(m), np.full(m, n - 1)], 1)])        # a full column
-    r = orc.qgemm(fmt, w, aq, m, n, k, pairs=pairs)
-    assert rel_err(C[pairs[:, 0], pairs[:, 1]], r) <= REL_TOL
-    D = getattr(qg, f"blockdots_{fmt}_mmq")(_gpu(torch, dev, w[:96]), AQ[:80].contiguous(), 80, 96, k)
-    assert np.array_equal(_host(D), orc.blockdots_mmq(fmt, w[:96], aq[:80], 80, 96, k))
+    assert rel_err(C, orc.qgemm(fmt, w, aq, m, n, k)) <= REL_TOL
+    # exact dots of every token row against the first 512 weight rows: the
+    # workgroups of the first four column tiles of the launch, whole
+    nd = 512
+    D = _host(getattr(qg, f"blockdots_{fmt}_mmq")(_gpu(torch, dev, w[:nd]), AQ, m, nd, k))
+    assert np.array_equal(D, orc.blockdots_mmq(fmt, w[:nd], aq, m, nd, k))
 
 
 # --------------------------------------------------------------------- router
@@ -683,25 +718,59 @@ def _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K):
     assert rel_err(out, ref_own["out"]) <= REL_TOL
     # Against the oracle's own h^: the GPU sums g and u in another fp32 order,
     # so a value on a rounding boundary of its block can land one code away.
-    # A single such flip moves a token's output by weights[p] * d times a
-    # column of Wdown, which can exceed REL_TOL end to end; so the end-to-end
-    # path is held to REL_TOL through the GPU's own h^ (above), and the two
-    # h^ are checked to differ only in that way: codes at most one apart, in
-    # few places, with d equal or one binary16 step apart (s = d * sum of the
-    # codes follows the codes; the dots do not read it).
+    # Every such difference must be a tie of the quantizer under the oracle's
+    # own h (|h/d| within 1e-3 of k + 1/2), and a stored d that differs must be
+    # a tie of its binary16 rounding; the end-to-end error is then held to
+    # REL_TOL plus the oracle's own measure of what those tie-breaks change.
+    stats = _check_hq_ties(orc, ref, hq_g, valid, F)
+    e2e = rel_err(out, ref["out"])
+    tie_effect = rel_err(ref_own["out"], ref["out"])
+    assert e2e <= REL_TOL + tie_effect, (e2e, tie_effect, stats)
+    if stats["code_flips"] == 0 and stats["d_flips"] == 0:
+        assert e2e <= REL_TOL
+    return dict(stats, e2e_rel_err=e2e, tie_effect=tie_effect)
+
+
+def _check_hq_ties(orc, ref, hq_g, valid, F):
+    """Compares the GPU's h^ with the oracle's block by block; see the caller."""
     g_blk = hq_g[valid].reshape(-1, F // 32, 36)
     r_blk = ref["hq"][valid].reshape(-1, F // 32, 36)
     dq = g_blk[..., 4:].view(np.int8).astype(np.int32) - r_blk[..., 4:].view(np.int8).astype(np.int32)
     assert np.abs(dq).max(initial=0) <= 1
-    flips = int(np.count_nonzero(dq))
-    assert flips <= max(4, dq.size // 200), f"h^ codes that differ from the oracle's: {flips} of {dq.size}"
-    # d >= 0: its binary16 bit patterns are ordered like the values
-    gd = g_blk[..., 0:2].copy().view(np.uint16).astype(np.int32)
-    rd = r_blk[..., 0:2].copy().view(np.uint16).astype(np.int32)
-    assert np.abs(gd - rd).max(initial=0) <= 1
-    if flips == 0:
-        assert rel_err(out, ref["out"]) <= REL_TOL
-    return flips
+    gd = g_blk[..., 0:2].copy().view(np.uint16).astype(np.int32)[..., 0]
+    rd = r_blk[..., 0:2].copy().view(np.uint16).astype(np.int32)[..., 0]
+    assert np.abs(gd - rd).max(initial=0) <= 1  # d >= 0: bit patterns are ordered like the values
+    # the oracle's h (double silu(g) * u rounded once to f32) and its fp32 d
+    gu = ref["gu"][valid]
+    g, u = gu[:, :F], gu[:, F:]
+    h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32).reshape(-1, F // 32, 32)
+    d32 = (np.abs(h).max(axis=2) / np.float32(127.0)).astype(np.float32)
+    where = np.argwhere(dq != 0)
+    for pi, b, i in where:
+        x = abs(float(np.float32(h[pi, b, i]) / d32[pi, b]))
+        assert abs(x - np.floor(x) - 0.5) <= 1e-3, f"h^ code differs off a tie: pair {pi} block {b} value {i}: {x}"
+    for pi, b in np.argwhere(gd != rd):
+        dv = float(d32[pi, b])
+        lo = float(np.float16(dv))
+        hi = float(np.nextafter(np.float16(dv), np.float16(np.inf if lo <= dv else -np.inf)))
+        ulp = abs(hi - lo)
+        assert abs(abs(dv - lo) - ulp / 2) <= 1e-2 * ulp, f"d differs off a binary16 tie: pair {pi} block {b}"
+    return {"code_flips": int(len(where)), "codes": int(dq.size), "d_flips": int(np.count_nonzero(gd != rd)),
+            "blocks": int(gd.size)}
+
+
+def _record(name, rec):
+    """Keeps a parity measurement: in gpurun_out/ when that folder exists, and
+    as a warning (pytest prints those in its summary)."""
+    import json
+    import os
+    import warnings
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = os.path.join(root, "gpurun_out")
+    if os.path.isdir(out):
+        with open(os.path.join(out, f"parity_{name}.json"), "w") as f:
+            json.dump(rec, f)
+    warnings.warn(f"{name}: {json.dumps(rec)}")
 
 
 def test_moe_small(env):
@@ -745,8 +814,8 @@ def test_moe_full_size(env):
     p = synth.WORKLOADS["moe_q4_k"]
     E, F, H, T, K = p["n_expert"], p["n_ff"], p["n_embd"], p["n_tok"], p["top_k"]
     case = _moe_case(p["seed"], E, F, H, T, K)
-    flips = _run_moe_stagewise(env, *case, E, F, H, T, K)
-    print(f"MoE full size: h^ bytes that differ from the oracle's h^: {flips}")
+    rec = _run_moe_stagewise(env, *case, E, F, H, T, K)
+    _record("moe_full_size", rec)
 
 
 # ---------------------------------------------------------------- HIP graphs
