@@ -63,6 +63,8 @@ SIGNATURES = {
     "qg_blockdots_q8_0_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q4_k_batch": [_P, _P, _P, _I, _I, _I, _P],
     "qg_blockdots_q6_k_batch": [_P, _P, _P, _I, _I, _I, _P],
+    "moe_qgemv_q4_k_noalloc": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P],
+    "moe_qgemv_q4_k_noalloc_max_workspace": [],
     "qg_peak_read": [_P, _I, _P, _I, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P],
     "qg_peak_mfma_i8": [_P, _I, _I, _P, _P],
 }
@@ -89,6 +91,7 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.moe_qgemv_q4_k_workspace_size.restype = ctypes.c_size_t
+        L.moe_qgemv_q4_k_noalloc_max_workspace.restype = ctypes.c_size_t
         L.qg_status_str.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -302,6 +305,28 @@ def moe_qgemv_q4_k(w_gate_up, w_down, xq, ids, weights, n_tok, top_k, n_expert, 
     _check("moe_qgemv_q4_k", lib().moe_qgemv_q4_k(pgu, pdn, pq, pid, pwt, po, n_tok, top_k, n_expert, n_ff, n_embd,
                                                   pws, workspace.numel(), _stream(stream)))
     return out
+
+
+def moe_qgemv_q4_k_noalloc(w_gate_up, w_down, xq, ids, weights, n_tok, top_k, n_expert, n_ff, n_embd, out=None,
+                           stream=None):
+    """moe_qgemv_q4_k on the library's own per-GPU workspace: no allocation
+    beyond `out` (none when `out` is given)."""
+    import torch
+    if out is None:
+        out = _empty((n_tok, n_embd), torch.float32, xq)
+    pgu = _need(w_gate_up, torch.uint8, n_expert * 2 * n_ff * row_bytes("q4_k", n_embd), "w_gate_up")
+    pdn = _need(w_down, torch.uint8, n_expert * n_embd * row_bytes("q4_k", n_ff), "w_down")
+    pq = _need(xq, torch.uint8, n_tok * row_bytes("q8_1", n_embd), "xq")
+    pid = _need(ids, torch.int32, n_tok * top_k * 4, "ids")
+    pwt = _need(weights, torch.float32, n_tok * top_k * 4, "weights")
+    po = _need(out, torch.float32, n_tok * n_embd * 4, "out")
+    _check("moe_qgemv_q4_k_noalloc", lib().moe_qgemv_q4_k_noalloc(pgu, pdn, pq, pid, pwt, po, n_tok, top_k, n_expert,
+                                                                  n_ff, n_embd, _stream(stream)))
+    return out
+
+
+def moe_qgemv_q4_k_noalloc_max_workspace() -> int:
+    return int(lib().moe_qgemv_q4_k_noalloc_max_workspace())
 
 
 def moe_workspace_regions(workspace, n_tok, top_k, n_ff, n_embd):

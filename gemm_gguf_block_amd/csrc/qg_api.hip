@@ -259,26 +259,33 @@ QG_EXPORT size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int
   return qg::moe_layout(n_tok, top_k, n_ff, n_embd).total;
 }
 
-QG_EXPORT qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
-                                   const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
-                                   int64_t n_ff, int64_t n_embd, void *workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
-  if (!w_gate_up || !w_down || !xq || !ids || !weights || !out || !workspace) return QG_ERR_NULL;
+namespace qg {
+
+qg_status check_gfx950() { return check_device(); }
+
+// Arguments of the MoE call other than the workspace: nulls, shapes, alignment.
+qg_status moe_check(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                    const float *weights, const float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
+                    int64_t n_ff, int64_t n_embd) {
+  if (!w_gate_up || !w_down || !xq || !ids || !weights || !out) return QG_ERR_NULL;
   if (n_tok < 0 || top_k < 1 || top_k > 64 || n_expert < 1 || n_expert > (1 << 16) || n_ff < 0 || n_embd < 0)
     return QG_ERR_SHAPE;
   if (n_ff % 256 != 0 || n_embd % 256 != 0 || n_ff > (1 << 20) || n_embd > (1 << 20)) return QG_ERR_SHAPE;
   if (n_tok * top_k > (1 << 20)) return QG_ERR_SHAPE;
   if (n_ff == 0 || n_embd == 0) return QG_ERR_SHAPE;
   if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(xq, 16) || !aligned(ids, 4) ||
-      !aligned(weights, 4) || !aligned(out, 4) || !aligned(workspace, 256))
+      !aligned(weights, 4) || !aligned(out, 4))
     return QG_ERR_ALIGN;
-  const qg::MoeLayout lay = qg::moe_layout(n_tok, top_k, n_ff, n_embd);
-  if (workspace_bytes < lay.total) return QG_ERR_WORKSPACE;
-  if (n_tok == 0) return QG_OK;
-  qg_status st = check_device();
-  if (st != QG_OK) return st;
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  qg::MoeArgs a;
+  return QG_OK;
+}
+
+// Enqueues the MoE kernels with the workspace at ws (checked arguments, a
+// workspace of at least moe_layout().total bytes, 256-byte aligned).
+qg_status moe_enqueue(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                      const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
+                      int64_t n_embd, uint8_t *ws, hipStream_t stream) {
+  const MoeLayout lay = moe_layout(n_tok, top_k, n_ff, n_embd);
+  MoeArgs a;
   a.w_gu = w_gate_up;
   a.w_down = w_down;
   a.xq = xq;
@@ -294,7 +301,25 @@ QG_EXPORT qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, co
   a.ws_gu = reinterpret_cast<float *>(ws + lay.gu_off);
   a.ws_z = reinterpret_cast<float *>(ws + lay.z_off);
   a.ws_hx = ws + lay.hx_off;
-  return launched(qg::launch_moe_q4_k(a, stream));
+  return launched(launch_moe_q4_k(a, stream));
+}
+
+}  // namespace qg
+
+QG_EXPORT qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                                   const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
+                                   int64_t n_ff, int64_t n_embd, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  qg_status st = qg::moe_check(w_gate_up, w_down, xq, ids, weights, out, n_tok, top_k, n_expert, n_ff, n_embd);
+  if (st != QG_OK) return st;
+  if (!workspace) return QG_ERR_NULL;
+  if (!aligned(workspace, 256)) return QG_ERR_ALIGN;
+  if (workspace_bytes < qg::moe_layout(n_tok, top_k, n_ff, n_embd).total) return QG_ERR_WORKSPACE;
+  if (n_tok == 0) return QG_OK;
+  st = check_device();
+  if (st != QG_OK) return st;
+  return qg::moe_enqueue(w_gate_up, w_down, xq, ids, weights, out, n_tok, top_k, n_expert, n_ff, n_embd,
+                         static_cast<uint8_t *>(workspace), stream);
 }
 
 QG_EXPORT qg_status qg_blockdots_q8_0(const void *w, const void *xq, int32_t *D, int64_t n, int64_t k,

@@ -93,3 +93,21 @@ struct MoeLayout {
 MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd);
 
 }  // namespace qg
+
+#include "../../include/qgguf.h"
+
+namespace qg {
+
+// The C ABI's shared checks (qg_api.hip): the current device is gfx950; the
+// MoE call's arguments other than its workspace.  moe_enqueue launches the
+// MoE kernels with the workspace at ws (checked arguments; ws 256-byte aligned
+// and at least moe_layout().total bytes).
+qg_status check_gfx950();
+qg_status moe_check(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                    const float *weights, const float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
+                    int64_t n_ff, int64_t n_embd);
+qg_status moe_enqueue(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                      const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
+                      int64_t n_embd, uint8_t *ws, hipStream_t stream);
+
+}  // namespace qg

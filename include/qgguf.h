@@ -272,6 +272,25 @@ qg_status moe_qgemv_q4_k(const void *w_gate_up, const void *w_down, const void *
                          hipStream_t stream);
 
 /*
+ * moe_qgemv_q4_k_noalloc -- moe_qgemv_q4_k without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  It allocates
+ * nothing: the workspace is a device array of the library, one copy per GPU,
+ * moe_qgemv_q4_k_noalloc_max_workspace() bytes (32 MiB), held until the
+ * process ends.  Same computation, arguments, limits and errors as
+ * moe_qgemv_q4_k (its kernels are the same), except:
+ *   - a call whose moe_qgemv_q4_k_workspace_size() exceeds the maximum
+ *     returns QG_ERR_WORKSPACE and launches nothing;
+ *   - all calls on one GPU share that GPU's array: calls that overlap on one
+ *     GPU (streams with no ordering between them) race.  Calls ordered on a
+ *     stream do not: every workspace byte a call reads it has written first.
+ */
+size_t moe_qgemv_q4_k_noalloc_max_workspace(void);
+qg_status moe_qgemv_q4_k_noalloc(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                                 const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert,
+                                 int64_t n_ff, int64_t n_embd, hipStream_t stream);
+
+/*
  * Test access to the exact per-block int32 dots, computed by the same device
  * unpack and dot code the products above run (not for production use).
  *   qg_blockdots_q8_0 : D int32 [n][k/32],  D[r][b] = sum_i qw*qa over block b
