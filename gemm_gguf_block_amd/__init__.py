@@ -65,6 +65,8 @@ SIGNATURES = {
     "qg_blockdots_q6_k_batch": [_P, _P, _P, _I, _I, _I, _P],
     "moe_qgemv_q4_k_noalloc": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P],
     "moe_qgemv_q4_k_noalloc_max_workspace": [],
+    "qg_blockdots_moe_q4_k": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P, _P, _P],
+    "qg_moe_q4_k_launches": [_I, _I, _I, _I, _I],
     "qg_peak_read": [_P, _I, _P, _I, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P],
     "qg_peak_mfma_i8": [_P, _I, _I, _P, _P],
 }
@@ -330,8 +332,9 @@ def moe_qgemv_q4_k_noalloc_max_workspace() -> int:
 
 
 def moe_workspace_regions(workspace, n_tok, top_k, n_ff, n_embd):
-    """Views of the MoE workspace regions: (h^ Q8_1 [P][n_ff/32*36] uint8,
-    g|u f32 [P][2*n_ff], weighted down f32 [P][n_embd]) -- the documented layout."""
+    """Views of the first three MoE workspace regions: (h^ Q8_1 [P][n_ff/32*36]
+    uint8, g|u f32 [P][2*n_ff], weighted down f32 [P][n_embd]) -- the
+    documented layout."""
     import torch
 
     def up(v):
@@ -345,19 +348,6 @@ def moe_workspace_regions(workspace, n_tok, top_k, n_ff, n_embd):
     gu = workspace[gu_off:gu_off + P * 2 * n_ff * 4].view(torch.float32).view(P, 2 * n_ff)
     z = workspace[z_off:z_off + P * n_embd * 4].view(torch.float32).view(P, n_embd)
     return hq, gu, z
-
-
-def moe_workspace_hx(workspace, n_tok, top_k, n_ff, n_embd):
-    """View of the MoE workspace's fourth region: h^ per pair in the unit-major
-    layout the down GEMV reads, uint8 [P][(n_ff/64)*80]."""
-    import torch
-
-    def up(v):
-        return (v + 255) & ~255
-
-    P = n_tok * top_k
-    off = up(P * row_bytes("q8_1", n_ff)) + up(P * 2 * n_ff * 4) + up(P * n_embd * 4)
-    return workspace[off:off + P * (n_ff // 64) * 80].view(P, (n_ff // 64) * 80)
 
 
 # ------------------------------------------------------- per-block dots (tests)
@@ -478,3 +468,31 @@ def peak_mfma_i8(iters, sink, stream=None):
     _check("qg_peak_mfma_i8", lib().qg_peak_mfma_i8(_need(sink, torch.int32, 4, "sink"), sink.numel(), iters,
                                                     ctypes.byref(ops), _stream(stream)))
     return ops.value
+
+
+def blockdots_moe_q4_k(w_gate_up, w_down, xq, ids, weights, n_tok, top_k, n_expert, n_ff, n_embd, workspace,
+                       stream=None):
+    """Exact dots of the MoE call's expert GEMVs, from their dump instances:
+    (D_gu int32 [P][2*n_ff][n_embd/32], D_dn int32 [P][n_embd][n_ff/32]).
+    The gate/up product runs first (its g|u feeds the down dump); the
+    workspace then holds h^ as the product call would.  Rows of pairs with an
+    out-of-range id are not written."""
+    import torch
+    P = n_tok * top_k
+    D_gu = torch.zeros((P, 2 * n_ff, n_embd // 32), dtype=torch.int32, device=xq.device)
+    D_dn = torch.zeros((P, n_embd, n_ff // 32), dtype=torch.int32, device=xq.device)
+    ws_bytes = moe_qgemv_q4_k_workspace_size(n_tok, top_k, n_expert, n_ff, n_embd)
+    _check("qg_blockdots_moe_q4_k", lib().qg_blockdots_moe_q4_k(
+        _need(w_gate_up, torch.uint8, n_expert * 2 * n_ff * row_bytes("q4_k", n_embd), "w_gate_up"),
+        _need(w_down, torch.uint8, n_expert * n_embd * row_bytes("q4_k", n_ff), "w_down"),
+        _need(xq, torch.uint8, n_tok * row_bytes("q8_1", n_embd), "xq"), _need(ids, torch.int32, P * 4, "ids"),
+        _need(weights, torch.float32, P * 4, "weights"), n_tok, top_k, n_expert, n_ff, n_embd,
+        _need(workspace, torch.uint8, ws_bytes, "workspace"), workspace.numel(),
+        _need(D_gu, torch.int32, D_gu.numel() * 4, "D_gu"), _need(D_dn, torch.int32, D_dn.numel() * 4, "D_dn"),
+        _stream(stream)))
+    return D_gu, D_dn
+
+
+def moe_launches(n_tok, top_k, n_expert, n_ff, n_embd) -> int:
+    """Kernel launches moe_qgemv_q4_k makes for this shape (2 or 4)."""
+    return int(lib().qg_moe_q4_k_launches(n_tok, top_k, n_expert, n_ff, n_embd))

@@ -283,7 +283,7 @@ qg_status moe_check(const void *w_gate_up, const void *w_down, const void *xq, c
 // workspace of at least moe_layout().total bytes, 256-byte aligned).
 qg_status moe_enqueue(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
                       const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
-                      int64_t n_embd, uint8_t *ws, hipStream_t stream) {
+                      int64_t n_embd, uint8_t *ws, hipStream_t stream, int32_t *D_gu, int32_t *D_dn) {
   const MoeLayout lay = moe_layout(n_tok, top_k, n_ff, n_embd);
   MoeArgs a;
   a.w_gu = w_gate_up;
@@ -300,7 +300,7 @@ qg_status moe_enqueue(const void *w_gate_up, const void *w_down, const void *xq,
   a.ws_hq = ws + lay.hq_off;
   a.ws_gu = reinterpret_cast<float *>(ws + lay.gu_off);
   a.ws_z = reinterpret_cast<float *>(ws + lay.z_off);
-  a.ws_hx = ws + lay.hx_off;
+  if (D_gu) return launched(launch_moe_q4_k_dump(a, D_gu, D_dn, stream));
   return launched(launch_moe_q4_k(a, stream));
 }
 
@@ -417,4 +417,36 @@ QG_EXPORT qg_status qg_peak_mfma_i8(int32_t *sink, int64_t sink_entries, int64_t
     return QG_ERR_NO_DEVICE;
   if (sink_entries < (int64_t)cus * 8) return QG_ERR_SHAPE;
   return launched(qg::launch_peak_mfma_i8(sink, iters, ops, stream));
+}
+
+QG_EXPORT qg_status qg_blockdots_moe_q4_k(const void *w_gate_up, const void *w_down, const void *xq,
+                                          const int32_t *ids, const float *weights, int64_t n_tok, int64_t top_k,
+                                          int64_t n_expert, int64_t n_ff, int64_t n_embd, void *workspace,
+                                          size_t workspace_bytes, int32_t *D_gu, int32_t *D_dn, hipStream_t stream) {
+  // D_gu stands in for out (checked for null and alignment; out is not written)
+  qg_status st = qg::moe_check(w_gate_up, w_down, xq, ids, weights, reinterpret_cast<const float *>(D_gu), n_tok,
+                               top_k, n_expert, n_ff, n_embd);
+  if (st != QG_OK) return st;
+  if (!workspace || !D_dn) return QG_ERR_NULL;
+  if (!aligned(workspace, 256) || !aligned(D_dn, 4)) return QG_ERR_ALIGN;
+  if (workspace_bytes < qg::moe_layout(n_tok, top_k, n_ff, n_embd).total) return QG_ERR_WORKSPACE;
+  const int64_t P = n_tok * top_k;
+  if (P * 2 * n_ff > (int64_t(1) << 29) / (n_embd / 32) || P * n_embd > (int64_t(1) << 29) / (n_ff / 32))
+    return QG_ERR_SHAPE;
+  if (n_tok == 0) return QG_OK;
+  st = check_device();
+  if (st != QG_OK) return st;
+  return qg::moe_enqueue(w_gate_up, w_down, xq, ids, weights, nullptr, n_tok, top_k, n_expert, n_ff, n_embd,
+                         static_cast<uint8_t *>(workspace), stream, D_gu, D_dn);
+}
+
+QG_EXPORT int qg_moe_q4_k_launches(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff, int64_t n_embd) {
+  if (n_tok <= 0 || top_k < 1 || n_expert < 1 || n_ff <= 0 || n_embd <= 0 || n_ff % 256 || n_embd % 256) return 0;
+  qg::MoeArgs a{};
+  a.n_tok = n_tok;
+  a.top_k = top_k;
+  a.n_expert = n_expert;
+  a.n_ff = n_ff;
+  a.n_embd = n_embd;
+  return qg::moe_two_kernel_path(a) ? 2 : 4;
 }

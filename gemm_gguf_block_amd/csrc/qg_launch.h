@@ -79,16 +79,21 @@ struct MoeArgs {
   const float *weights;
   float *out;
   int64_t n_tok, top_k, n_expert, n_ff, n_embd;
-  uint8_t *ws_hq;   // Q8_1 h^ per pair
-  float *ws_gu;     // g|u per pair
-  float *ws_z;      // weighted down projection per pair
-  uint8_t *ws_hx;   // h^ per pair again, unit-major with {d, sum} records (read by the down GEMV)
+  uint8_t *ws_hq;    // Q8_1 h^ per pair
+  float *ws_gu;      // g|u per pair
+  float *ws_z;       // weighted down projection per pair (four-kernel path)
 };
 hipError_t launch_moe_q4_k(const MoeArgs &a, hipStream_t stream);
+// The same kernels' dump instances: exact dots of gate/up D_gu [P][2F][H/32]
+// and of down D_dn [P][H][F/32] (after the gate/up product, which the down
+// dump needs); out and z are not written.
+hipError_t launch_moe_q4_k_dump(const MoeArgs &a, int32_t *D_gu, int32_t *D_dn, hipStream_t stream);
+// True when the call runs the two-kernel path, false for the four-kernel one.
+bool moe_two_kernel_path(const MoeArgs &a);
 
 // Workspace region offsets for the MoE call (each 256-byte aligned).
 struct MoeLayout {
-  size_t hq_off, gu_off, z_off, hx_off, total;
+  size_t hq_off, gu_off, z_off, total;
 };
 MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd);
 
@@ -108,6 +113,7 @@ qg_status moe_check(const void *w_gate_up, const void *w_down, const void *xq, c
                     int64_t n_ff, int64_t n_embd);
 qg_status moe_enqueue(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
                       const float *weights, float *out, int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
-                      int64_t n_embd, uint8_t *ws, hipStream_t stream);
+                      int64_t n_embd, uint8_t *ws, hipStream_t stream, int32_t *D_gu = nullptr,
+                      int32_t *D_dn = nullptr);
 
 }  // namespace qg

@@ -233,12 +233,14 @@ qg_status qgemm_q5_0_mmq(const void *w, const void *aq, float *c, int64_t m, int
  *                 [0, P*(n_ff/32)*36)            h^ per pair, Q8_1
  *                 then f32 [P][2*n_ff]           g | u per pair
  *                 then f32 [P][n_embd]           weights[p] * (Wdown . h^)
- *                 then P * (n_ff/64) * 80 bytes  h^ per pair again, unit-major
- *                   for the down GEMV: per 64 values u of pair p, at
- *                   p*(n_ff/64)*80: four 16-byte code pieces (c*(n_ff/64) + u)
- *                   and a 16-byte record {d(2u), d(2u+1) as f32, sum of codes
- *                   (2u), (2u+1) as int32} at (4*(n_ff/64) + u)
- *               each region starting on a 256-byte boundary.
+ *                                                (four-kernel path only)
+ *               each region starting on a 256-byte boundary.  Every byte the
+ *               call reads it has written first in the same call.
+ * Small routing tables (n_tok*top_k <= 256 over <= 256 experts, n_embd <=
+ * 4096, n_ff/64 a power of two in 4..64 times 1, 2 or 3, top_k*n_ff*1.25 <=
+ * 32 KiB) run two kernels: gate/up, then a token-major down that forms h^
+ * first and sums the slots itself; other shapes run four (gate/up,
+ * activation, down, routed sum).
  *   n_embd, n_ff : multiples of 256, <= 2^20;  top_k in [1, 64];
  *   n_tok * top_k <= 2^20;  n_expert in [1, 2^16]
  */
@@ -342,6 +344,25 @@ qg_status qg_blockdots_q4_k_batch(const void *w, const void *xq, int32_t *D, int
                                   hipStream_t stream);
 qg_status qg_blockdots_q6_k_batch(const void *w, const void *xq, int32_t *D, int64_t b, int64_t n, int64_t k,
                                   hipStream_t stream);
+/*
+ * qg_blockdots_moe_q4_k : the exact dots of moe_qgemv_q4_k's expert GEMVs,
+ *                       from their dump instances on the product's grids:
+ *                       D_gu int32 [P][2*n_ff][n_embd/32] (gate/up rows
+ *                       against the token's Q8_1 row) and D_dn int32
+ *                       [P][n_embd][n_ff/32] (down rows against the pair's
+ *                       h^, which the call leaves in the workspace as the
+ *                       product does); rows of pairs with an out-of-range id
+ *                       are not written.  out is not written.  Same arguments
+ *                       and errors as moe_qgemv_q4_k; P*2*n_ff*(n_embd/32) and
+ *                       P*n_embd*(n_ff/32) <= 2^29.
+ * qg_moe_q4_k_launches : kernel launches moe_qgemv_q4_k makes for a shape
+ *                       (2 or 4; 0 for an invalid shape).
+ */
+qg_status qg_blockdots_moe_q4_k(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,
+                                const float *weights, int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff,
+                                int64_t n_embd, void *workspace, size_t workspace_bytes, int32_t *D_gu,
+                                int32_t *D_dn, hipStream_t stream);
+int qg_moe_q4_k_launches(int64_t n_tok, int64_t top_k, int64_t n_expert, int64_t n_ff, int64_t n_embd);
 
 /*
  * Measurement references (for the roofline fractions the benchmark reports;

@@ -18,7 +18,7 @@ OK, NULL, SHAPE, ALIGN, WORKSPACE, NO_DEVICE = 0, 1, 2, 3, 4, 5
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:qg_status|size_t|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:qg_status|size_t|char|int)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -156,7 +156,7 @@ def test_moe_validation(lib):
     T, K, E, F, H = 16, 8, 128, 768, 2048
     need = lib.moe_qgemv_q4_k_workspace_size(T, K, E, F, H)
     P_ = T * K
-    assert need >= P_ * (F // 32) * 36 + P_ * 2 * F * 4 + P_ * H * 4 + P_ * (F // 64) * 80
+    assert need >= P_ * (F // 32) * 36 + P_ * 2 * F * 4 + P_ * H * 4
     assert need % 256 == 0
     ws = P(1 << 24)
     ids, wts, out = P((1 << 20) + 64), P((1 << 20) + 128), P((1 << 20) + 256)

@@ -686,34 +686,20 @@ def _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K):
     hq_g, gu_g = _host(hq_g), _host(gu_g)
     ref = orc.moe_q4_k(w_gu, w_dn, xq, ids, rw, T, K, E, F, H)
     valid = (ids.ravel() >= 0) & (ids.ravel() < E)
-    # stage 1: gate/up values, and their block dots exactly (same device code)
+    # stage 1: gate/up values
     assert rel_err(gu_g[valid], ref["gu"][valid]) <= REL_TOL
-    for p in np.flatnonzero(valid)[:4]:
+    # exact dots of both expert GEMVs, every valid pair, from the call's own
+    # kernels (dump instances on the product's grids): gate/up against the
+    # token's Q8_1 row, down against the pair's h^ as the call formed it
+    ws2 = torch.empty_like(ws)
+    D_gu, D_dn = qg.blockdots_moe_q4_k(WGU, WDN, XQ, IDS, RW, T, K, E, F, H, ws2)
+    hq_d = _host(qg.moe_workspace_regions(ws2, T, K, F, H)[0])
+    assert np.array_equal(hq_d[valid], hq_g[valid])
+    D_gu, D_dn = _host(D_gu), _host(D_dn)
+    for p in np.flatnonzero(valid):
         e, t = ids.ravel()[p], p // K
-        D, S = qg.blockdots_q4_k(WGU[e], XQ[t], 2 * F, H)
-        Dr, Sr = orc.blockdots("q4_k", w_gu[e], xq[t], 2 * F, H)
-        assert np.array_equal(_host(D), Dr) and np.array_equal(_host(S), Sr)
-    # stage 2: down projection from the GPU's own h^ -- exact block dots, then out
-    for p in np.flatnonzero(valid)[:4]:
-        e = ids.ravel()[p]
-        D, _ = qg.blockdots_q4_k(WDN[e], _gpu(torch, dev, hq_g[p]), H, F)
-        assert np.array_equal(_host(D), orc.blockdots("q4_k", w_dn[e], hq_g[p], H, F)[0])
-    # the unit-major copy of h^ the down GEMV reads holds the same codes, d and
-    # exact code sums as the Q8_1 rows
-    hx_g = _host(qg.moe_workspace_hx(ws, T, K, F, H))
-    U = F // 64
-    for p in np.flatnonzero(valid)[:8]:
-        blk = hq_g[p].reshape(F // 32, 36)
-        q = blk[:, 4:].view(np.int8)
-        d = blk[:, :2].copy().view(np.float16)[:, 0].astype(np.float32)
-        pieces = hx_g[p][:U * 64].reshape(4, U, 16)
-        rec = hx_g[p][U * 64:].reshape(U, 16)
-        for u in range(U):
-            for c in range(4):
-                assert np.array_equal(pieces[c, u], blk[2 * u + c // 2, 4 + 16 * (c % 2):20 + 16 * (c % 2)])
-            r = rec[u].copy()
-            assert np.array_equal(r[:8].view(np.float32), d[2 * u:2 * u + 2])
-            assert np.array_equal(r[8:].view(np.int32), q[2 * u:2 * u + 2].astype(np.int32).sum(axis=1))
+        assert np.array_equal(D_gu[p], orc.blockdots("q4_k", w_gu[e], xq[t], 2 * F, H)[0]), f"gate/up pair {p}"
+        assert np.array_equal(D_dn[p], orc.blockdots("q4_k", w_dn[e], hq_g[p], H, F)[0]), f"down pair {p}"
     ref_own = orc.moe_q4_k(w_gu, w_dn, xq, ids, rw, T, K, E, F, H, hq_in=hq_g)
     assert rel_err(out, ref_own["out"]) <= REL_TOL
     # Against the oracle's own h^: the GPU sums g and u in another fp32 order,
@@ -788,6 +774,31 @@ def test_moe_invalid_ids_skipped(env):
     _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
 
 
+def test_moe_token_without_valid_slots_and_repeated_experts(env):
+    """A token whose slots are all out of range gets zeros (no slot arrives
+    for it); a token routed twice to one expert counts both slots."""
+    E, F, H, T, K = 5, 256, 512, 4, 2
+    w_gu, w_dn, ids, rw, x = _moe_case(66, E, F, H, T, K)
+    ids = ids.copy()
+    ids[2, :] = [-1, E]
+    ids[1, :] = [3, 3]
+    qg = env[0]
+    assert qg.moe_launches(T, K, E, F, H) == 2
+    _run_moe_stagewise(env, w_gu, w_dn, ids, rw, x, E, F, H, T, K)
+
+
+@pytest.mark.parametrize("E,F,H,T,K,launches", [(6, 1536, 512, 5, 3, 2),    # 24 down units: 8 lanes x 3 units
+                                                (3, 8192, 256, 2, 2, 2),    # 128 down units: 64 lanes x 2 units
+                                                (4, 1280, 512, 3, 2, 4)])   # 20 down units: the four-kernel path
+def test_moe_down_row_splits(env, E, F, H, T, K, launches):
+    """Down rows of n_ff/64 units split over L lanes with 1, 2 or 3 units each
+    (two kernels), or not at all (four kernels)."""
+    qg = env[0]
+    assert qg.moe_launches(T, K, E, F, H) == launches
+    case = _moe_case(67 + F, E, F, H, T, K)
+    _run_moe_stagewise(env, *case, E, F, H, T, K)
+
+
 def test_moe_shared_experts(env):
     """Several tokens on one expert: the expert's rows are reused across pairs."""
     E, F, H, T, K = 3, 512, 256, 9, 2
@@ -802,9 +813,11 @@ def test_moe_shared_experts(env):
 def test_moe_routing_table_sizes(env, E, T, K, H):
     """The persistent form keeps two words of ids and touched-expert bitmap per
     lane up to 128 pairs and 128 experts, four words up to 256; larger tables
-    run the grid form.  The gate/up call stages the token rows in LDS when they
-    fit in 40 KB.  Each case against the oracle, stage by stage."""
+    run the grid form (four kernels).  The gate/up call stages the token rows
+    in LDS when they fit in 40 KB.  Each case against the oracle, stage by
+    stage."""
     F = 256
+    assert env[0].moe_launches(T, K, E, F, H) == (2 if T * K <= 256 else 4)
     case = _moe_case(65 + E + T, E, F, H, T, K)
     _run_moe_stagewise(env, *case, E, F, H, T, K)
 
@@ -813,6 +826,7 @@ def test_moe_routing_table_sizes(env, E, T, K, H):
 def test_moe_full_size(env):
     p = synth.WORKLOADS["moe_q4_k"]
     E, F, H, T, K = p["n_expert"], p["n_ff"], p["n_embd"], p["n_tok"], p["top_k"]
+    assert env[0].moe_launches(T, K, E, F, H) == 2
     case = _moe_case(p["seed"], E, F, H, T, K)
     rec = _run_moe_stagewise(env, *case, E, F, H, T, K)
     _record("moe_full_size", rec)
