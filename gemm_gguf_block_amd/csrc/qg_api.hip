@@ -97,7 +97,11 @@ qg_status check_mmq(int fmt, const void *w, const void *aq, const void *out, int
 }  // namespace
 
 QG_EXPORT const char *qg_status_str(qg_status s) {
-  switch (s) {
+  // read as an int: a C caller may pass any int, which as a C++ enum of this
+  // range would be undefined
+  int v = 0;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
     case QG_ERR_SHAPE: return "invalid shape (negative, not a multiple of the block size, or too large)";
@@ -262,6 +266,17 @@ QG_EXPORT size_t moe_qgemv_q4_k_workspace_size(int64_t n_tok, int64_t top_k, int
 namespace qg {
 
 qg_status check_gfx950() { return check_device(); }
+
+MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t P = (size_t)(n_tok * top_k);
+  MoeLayout l;
+  l.hq_off = 0;
+  l.gu_off = up(P * (size_t)(n_ff / 32) * 36);  // Q8_1: 36 bytes per 32 values
+  l.z_off = l.gu_off + up(P * (size_t)(2 * n_ff) * sizeof(float));
+  l.total = l.z_off + up(P * (size_t)n_embd * sizeof(float));
+  return l;
+}
 
 // Arguments of the MoE call other than the workspace: nulls, shapes, alignment.
 qg_status moe_check(const void *w_gate_up, const void *w_down, const void *xq, const int32_t *ids,

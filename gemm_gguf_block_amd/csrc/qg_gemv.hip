@@ -351,64 +351,90 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t *__restrict
 
 // ---------------------------------------------------------------- Q8_0
 // Rows with an even block count: unit = block pair at a dword-aligned offset.
+// Persistent like the K-quant kernels: the workgroup stages the Q8_1
+// activation in LDS once per chunk, unit-major exactly as for Q4_K (a unit is
+// two 32-value blocks there too), so a lane group reads its activation slice
+// from LDS instead of every lane group fetching it from L2.
 template <int L, int R, bool DUMP>
 __global__ __launch_bounds__(256) void gemv_q8_0_pair_kernel(const uint8_t *__restrict__ W,
                                                              const uint8_t *__restrict__ XQ, float *__restrict__ Y,
                                                              int32_t *__restrict__ Dd, int n, int npair) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
+  constexpr int kChunkU = kXBlocks / 2;  // units (block pairs) per staged chunk
+  constexpr int kGroupRows = 4 * G * R;  // rows per workgroup per group
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
-  const int64_t row0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
   const int64_t rb = (int64_t)npair * (2 * kQ8_0Bytes);
-  const uint8_t *wrow = W + row0 * rb;
-  float acc[R];
+  const int64_t ngroups = ((int64_t)n + kGroupRows - 1) / kGroupRows;
+  int staged = -1;  // first unit of the chunk in xs
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t row0 = ((grp * 4 + (threadIdx.x >> 6)) * G + lane / L) * R;
+    const uint8_t *wrow = W + row0 * rb;
+    float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  if (row0 < n) {
-    for (int u = li; u < npair; u += L) {
-      uint32_t Wd[R][17];
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int c0 = 0; c0 < npair; c0 += kChunkU) {
+      const int U = min(kChunkU, npair - c0);
+      const XView xs = x_view(lds, U);
+      // L divides npair and kChunkU, so every lane of the workgroup runs the
+      // same number of units per chunk (rows past n included, masked): the
+      // staging barrier sits in the first one, after its weight loads
+      for (int u = li; u < U; u += L) {
+        uint32_t Wd[R][17];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (row0 + r < n) {
-          const uint8_t *bp = wrow + r * rb + u * (2 * kQ8_0Bytes);
-          const u32x4 w0 = ld16(bp), w1 = ld16(bp + 16), w2 = ld16(bp + 32), w3 = ld16(bp + 48);
-          Wd[r][0] = w0.x; Wd[r][1] = w0.y; Wd[r][2] = w0.z; Wd[r][3] = w0.w;
-          Wd[r][4] = w1.x; Wd[r][5] = w1.y; Wd[r][6] = w1.z; Wd[r][7] = w1.w;
-          Wd[r][8] = w2.x; Wd[r][9] = w2.y; Wd[r][10] = w2.z; Wd[r][11] = w2.w;
-          Wd[r][12] = w3.x; Wd[r][13] = w3.y; Wd[r][14] = w3.z; Wd[r][15] = w3.w;
-          Wd[r][16] = ld4(bp + 64);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 17; ++i) Wd[r][i] = 0u;
-        }
-      }
-      uint32_t A[18];
-      load_q8_1_pair(XQ + (int64_t)(2 * u) * kQ8_1Bytes, A);
-      const float da0 = h2f(A[0]), da1 = h2f(A[9]);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        int D0 = 0, D1 = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          D0 = dot4(align_bytes(Wd[r][i + 1], Wd[r][i], 2), A[1 + i], D0);  // qs of block 0: bytes 2..33
-          D1 = dot4(Wd[r][9 + i], A[10 + i], D1);                            // qs of block 1: bytes 36..67
-        }
-        if (DUMP) {
+        for (int r = 0; r < R; ++r) {
           if (row0 + r < n) {
-            Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * u] = D0;
-            Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * u + 1] = D1;
+            const uint8_t *bp = wrow + r * rb + (int64_t)(c0 + u) * (2 * kQ8_0Bytes);
+            const u32x4 w0 = ld16(bp), w1 = ld16(bp + 16), w2 = ld16(bp + 32), w3 = ld16(bp + 48);
+            Wd[r][0] = w0.x; Wd[r][1] = w0.y; Wd[r][2] = w0.z; Wd[r][3] = w0.w;
+            Wd[r][4] = w1.x; Wd[r][5] = w1.y; Wd[r][6] = w1.z; Wd[r][7] = w1.w;
+            Wd[r][8] = w2.x; Wd[r][9] = w2.y; Wd[r][10] = w2.z; Wd[r][11] = w2.w;
+            Wd[r][12] = w3.x; Wd[r][13] = w3.y; Wd[r][14] = w3.z; Wd[r][15] = w3.w;
+            Wd[r][16] = ld4(bp + 64);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 17; ++i) Wd[r][i] = 0u;
           }
-        } else {
-          acc[r] += h2f(Wd[r][0]) * da0 * (float)D0 + h2f(Wd[r][8] >> 16) * da1 * (float)D1;
+        }
+        if (staged != c0) {
+          if (staged >= 0) __syncthreads();  // the previous chunk is no longer read
+          stage_x<kXQ4K>(xs, XQ, 2 * (int64_t)c0, 2 * U);
+          __syncthreads();
+          staged = c0;
+        }
+        if (row0 >= n) continue;
+        // blocks 2u (pieces 0, 1) and 2u + 1 (pieces 2, 3) of the chunk
+        const u32x4n x0 = xs.qs[u], x1 = xs.qs[U + u], x2 = xs.qs[2 * U + u], x3 = xs.qs[3 * U + u];
+        const u32x4n rec = xs.rec[u];
+        const uint32_t A0[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const uint32_t A1[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+        const float da0 = as_f32(rec.x), da1 = as_f32(rec.y);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          int D0 = 0, D1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            D0 = dot4(align_bytes(Wd[r][i + 1], Wd[r][i], 2), A0[i], D0);  // qs of block 0: bytes 2..33
+            D1 = dot4(Wd[r][9 + i], A1[i], D1);                            // qs of block 1: bytes 36..67
+          }
+          if (DUMP) {
+            if (row0 + r < n) {
+              Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * (c0 + u)] = D0;
+              Dd[(row0 + r) * (int64_t)(2 * npair) + 2 * (c0 + u) + 1] = D1;
+            }
+          } else {
+            acc[r] += h2f(Wd[r][0]) * da0 * (float)D0 + h2f(Wd[r][8] >> 16) * da1 * (float)D1;
+          }
         }
       }
     }
-  }
-  if (!DUMP) {
+    if (!DUMP && row0 < n) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = group_sum_last<L>(acc[r]);
-      if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
+      for (int r = 0; r < R; ++r) {
+        const float v = group_sum_last<L>(acc[r]);
+        if (li == L - 1 && row0 + r < n) Y[row0 + r] = v;
+      }
     }
   }
 }
@@ -600,6 +626,7 @@ constexpr int kRowsQ6K = 4;
 // Q6_K grids hold this many workgroups per resident one: the queued ones start
 // as others finish, which evens out the last round of row groups.
 constexpr int64_t kOversubQ6K = 2;
+constexpr int64_t kOversubQ8_0 = 1;
 
 #define QG_LAUNCH(KERNEL, LV, RV, ...)                                                          \
   do {                                                                                          \
@@ -660,8 +687,10 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
   if (fmt == 0 && ((k / 32) % 2) == 0) {
     const int npair = (int)(k / 64);
     const int L = lanes_per_row(npair);
-    const dim3 grid = gemv_grid(n, L, kRowsQ8_0);
-    QG_GEMV_SWITCH(gemv_q8_0_pair_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
+    const size_t xlds = x_chunk_bytes(k / 32);
+    const int64_t oversub = kOversubQ8_0;
+    const int waves = 4;
+    QG_GEMV_SWITCH_PERSISTENT(gemv_q8_0_pair_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
   } else if (fmt == 0) {
     const int nb = (int)(k / 32);
     const int L = lanes_per_row(nb);

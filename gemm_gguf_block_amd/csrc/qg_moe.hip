@@ -787,17 +787,6 @@ static void launch_down_token(const MoeArgs &a, int32_t *D, int L, int upl, hipS
 #undef QG_DT
 }
 
-MoeLayout moe_layout(int64_t n_tok, int64_t top_k, int64_t n_ff, int64_t n_embd) {
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  const size_t P = (size_t)(n_tok * top_k);
-  MoeLayout l;
-  l.hq_off = 0;
-  l.gu_off = up(P * (size_t)(n_ff / 32) * kQ8_1Bytes);
-  l.z_off = l.gu_off + up(P * (size_t)(2 * n_ff) * sizeof(float));
-  l.total = l.z_off + up(P * (size_t)n_embd * sizeof(float));
-  return l;
-}
-
 // Which path a call takes: the two-kernel one needs the small-table
 // persistent gate/up and a down row that splits evenly over lane groups.
 static bool two_kernel_path(const MoeArgs &a, int *L, int *upl) {
