@@ -620,7 +620,8 @@ __global__ __launch_bounds__(256) void gemv_q5_0_kernel(const uint8_t *__restric
 // ---------------------------------------------------------------- dispatch
 // Rows per lane group (R): each lane reuses its activation slice across R
 // rows and keeps R rows' worth of weight loads in flight.
-constexpr int kRowsQ8_0 = 2;
+constexpr int kRowsQ8_0 = 1;    // the staged block-pair kernel (R = 2: 5.35 us, R = 1: 5.22 us at 4096 x 4096)
+constexpr int kRowsLegacy = 2;  // Q4_0 / Q5_0 (R = 1: 8.00 us, R = 2: 7.22 us at 14336 x 4096)
 constexpr int kRowsQ4K = 1;
 constexpr int kRowsQ6K = 4;
 // Q6_K grids hold this many workgroups per resident one: the queued ones start
@@ -706,11 +707,11 @@ hipError_t launch_qgemv(int fmt, const void *w, const void *xq, float *y, int32_
   } else if (fmt == 4 || fmt == 5) {
     const int npair = (int)(k / 64);
     const int L = lanes_per_row(npair);
-    const dim3 grid = gemv_grid(n, L, kRowsQ8_0);
+    const dim3 grid = gemv_grid(n, L, kRowsLegacy);
     if (fmt == 4) {
-      QG_GEMV_SWITCH(gemv_q4_0_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
+      QG_GEMV_SWITCH(gemv_q4_0_kernel, kRowsLegacy, W, X, y, D, ni, npair)
     } else {
-      QG_GEMV_SWITCH(gemv_q5_0_kernel, kRowsQ8_0, W, X, y, D, ni, npair)
+      QG_GEMV_SWITCH(gemv_q5_0_kernel, kRowsLegacy, W, X, y, D, ni, npair)
     }
   } else if (fmt == 3) {
     const int nsb = (int)(k / 256);
