@@ -36,9 +36,18 @@ namespace {
 
 typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));  // 16-byte aligned: ds_read/write_b128
 
-constexpr int kThreads = 512;  // 8 waves: one LDS copy of the activations serves more waves
-constexpr int kWaves = kThreads / 64;
 enum { kFmtQ8_0 = 0, kFmtQ4K = 1, kFmtQ6K = 2 };
+
+// Waves per workgroup.  Every workgroup stages all activation rows, so larger
+// workgroups stage them fewer times; for Q8_0 with 5-8 rows that staging
+// outweighs the workgroup's share of weight bytes, and 16 waves measured
+// faster (8 rows at 4096 x 4096: 8.49 -> 7.78 us; 6 rows 8.18 -> 7.56), while
+// 2 and 4 rows and the K-quants measured slower with 16 (Q8_0 b = 2: 6.63 ->
+// 6.73 us; Q4_K b = 4: 11.1 -> 12.3; Q6_K b = 4: 99.1 -> 102.0).
+template <int FMT, int B>
+__host__ __device__ constexpr int batch_waves() {
+  return FMT == kFmtQ8_0 && B == 8 ? 16 : 8;
+}
 
 // Values per unit and 16-value pieces per unit.
 template <int FMT> struct Unit {
@@ -70,7 +79,7 @@ __device__ __forceinline__ void stage_batch(uint8_t *lds, const uint8_t *__restr
   const int U = cb * 32 / Unit<FMT>::kValues;
   u32x4n *qs = reinterpret_cast<u32x4n *>(lds);
   uint8_t *rec = lds + (size_t)B * NP * U * 16;
-  for (int t = threadIdx.x; t < B * cb; t += kThreads) {
+  for (int t = threadIdx.x; t < B * cb; t += 64 * batch_waves<FMT, B>()) {
     const int i = t / cb, blk = t - i * cb;
     u32x4n lo = {0u, 0u, 0u, 0u}, hi = lo;
     float d = 0.f;
@@ -109,16 +118,17 @@ __device__ __forceinline__ void stage_batch(uint8_t *lds, const uint8_t *__restr
   }
 }
 
-// One workgroup of 8 waves strides over groups of 8 * (64/L) * R rows; the
-// activation is staged per chunk of chunk_blocks<B>() Q8_1 blocks (c0 counts
-// blocks for every format).
+// One workgroup of W = batch_waves waves strides over groups of W * (64/L) * R
+// rows; the activation is staged per chunk of chunk_blocks<B>() Q8_1 blocks
+// (c0 counts blocks for every format).
 template <int FMT, int L, int B, int R, bool DUMP>
-__global__ __launch_bounds__(kThreads) void gemv_batch_kernel(const uint8_t *__restrict__ W,
+__global__ __launch_bounds__((64 * batch_waves<FMT, B>())) void gemv_batch_kernel(const uint8_t *__restrict__ W,
                                                               const uint8_t *__restrict__ XQ, float *__restrict__ Y,
                                                               int32_t *__restrict__ Dd, int nb, int n, int nblk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int G = 64 / L;
   constexpr int NP = Unit<FMT>::kPieces;
+  constexpr int kWaves = batch_waves<FMT, B>();
   constexpr int kGroupRows = kWaves * G * R;
   constexpr int CB = chunk_blocks<B>();  // activation blocks per chunk
   const int lane = threadIdx.x & 63;
@@ -318,7 +328,8 @@ template <int FMT, int L, int B>
 hipError_t launch_fmt_lb(const uint8_t *W, const uint8_t *X, float *y, int32_t *D, int nb, int64_t n, int nblk,
                          hipStream_t stream) {
   constexpr int R = rows_per_lane<FMT>();
-  constexpr int kGroupRows = kWaves * (64 / L) * R;
+  constexpr int kThreads = 64 * batch_waves<FMT, B>();
+  constexpr int kGroupRows = batch_waves<FMT, B>() * (64 / L) * R;
   const size_t lds = batch_lds_bytes<FMT, B>(nblk);
   const int64_t groups = (n + kGroupRows - 1) / kGroupRows;
   const int64_t g = std::min(groups, resident_blocks<gemv_batch_kernel<FMT, L, B, R, false>>(kThreads, lds));
