@@ -13,9 +13,9 @@
 //   B  the weight codes as int8 (Q4_K nibbles, Q6_K q - 32, Q8_0 qs, Q4_0
 //      q - 8, Q5_0 q - 16), plus per (weight row, scale group) the group's
 //      factor (d*sc_j, d*sc_j, d) and for Q4_K -dmin*m_j
-// double-buffered: the global loads of step s+2 are in flight while the MFMAs
-// of step s run.  (The 32-value types run an 8-wave form of the same scheme;
-// see mmq8_kernel.)  Each 32-wide block of k is one v_mfma_i32_32x32x32_i8 -> the
+// double-buffered: the global loads of step s+1 are in flight while the MFMAs
+// of step s run (the 8-wave form of the 32-value types loads two steps ahead;
+// see mmq8_kernel).  Each 32-wide block of k is one v_mfma_i32_32x32x32_i8 -> the
 // exact int32 dots D of that block for the wave's 32x32 tile; Q6_K's 16-wide
 // sub-blocks are two v_mfma_i32_32x32x16_i8.  A dot's fp32 rescale is
 // acc += F * D with F[m][n] = d_a[m] * f[n], a rank-1 outer product that the
@@ -422,9 +422,12 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
     fzero[r] = 0.f;
   }
 
-  // Step s is staged from registers R[s & 1]: its global loads are issued two
-  // steps ahead, so two compute phases cover their latency.
-  MmqRegs<FMT> R0, R1;
+  // Step s + 1's global loads are issued at the start of step s and staged at
+  // its end: one compute phase (about 2 us at 512 x 4096 x 4096) covers their
+  // latency, and a single register set leaves room for the compute phase's
+  // operand lookahead.  (Loading two steps ahead from two register sets
+  // measured slower with the lookahead dropped: 34.3 against 32.7 us.)
+  MmqRegs<FMT> R0;
   auto load = [&](MmqRegs<FMT> &g, int s) {
     if (act)
       load_act<FMT>(g, AQ, M, nblk, m0, s, st);
@@ -468,14 +471,13 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sv, mv, acc, 0, 0, 0);
       }
     }
+    if constexpr (FMT == kMQ6K) {
 #pragma unroll
-    for (int jj = 0; jj < kJ; ++jj) {
-      const int j = j0 + jj;
-      if (MmqFmt<FMT>::kBlk32 && 8 * s + j >= nblk) break;  // ragged last step (wave-uniform)
-      const uint32_t *pa = cur.fa[j][wm * 32 + lr];
-      const u32x4n av = *reinterpret_cast<const u32x4n *>(arow + 32 * jj);
-      const u32x4n bv = *reinterpret_cast<const u32x4n *>(brow + 32 * jj);
-      if constexpr (FMT == kMQ6K) {
+      for (int jj = 0; jj < kJ; ++jj) {
+        const int j = j0 + jj;
+        const uint32_t *pa = cur.fa[j][wm * 32 + lr];
+        const u32x4n av = *reinterpret_cast<const u32x4n *>(arow + 32 * jj);
+        const u32x4n bv = *reinterpret_cast<const u32x4n *>(brow + 32 * jj);
         // sub-blocks 2j and 2j+1: the lane's 8-byte slices are (x, y) and (z, w)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -492,43 +494,68 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
           }
           asm volatile("" : "+v"(acc)::"memory");  // one sub-block's D and F live at a time
         }
-      } else {
-        // D = exact int32 dots of block j; F2 = 2F for its rescale: lanes
-        // 32-63 (k = 4..7) of the bf16 MFMA repeat the four parts of lanes
-        // 0-31, so it returns exactly twice the outer product
-        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, av),
-                                                              __builtin_bit_cast(v4i, bv), zero, 0, 0, 0);
+        asm volatile("" : "+v"(acc)::"memory");
+      }
+    } else {
+      // Block j + 1's LDS operands are read before block j's rescale, so their
+      // latency runs under that vector work; its products are issued after it.
+      struct Opnd {
+        u32x4n a, b;
+        u32x2 fa, fb;
+      };
+      auto rd = [&](int jj, Opnd &o) {
+        const int j = j0 + jj;
+        o.a = *reinterpret_cast<const u32x4n *>(arow + 32 * jj);
+        o.b = *reinterpret_cast<const u32x4n *>(brow + 32 * jj);
+        const uint32_t *pa = cur.fa[j][wm * 32 + lr];
+        const uint32_t *pb = cur.fb[j][wn * 32 + lr];
+        o.fa = u32x2{pa[0], pa[1]};
+        o.fb = u32x2{pb[0], pb[1]};
+      };
+      const int nj = MmqFmt<FMT>::kBlk32 ? max(0, min(kJ, nblk - 8 * s - j0)) : kJ;  // ragged last step
+      Opnd o0, o1;
+      if (nj > 0) rd(0, o0);
+#pragma unroll
+      for (int jj = 0; jj < kJ; ++jj) {
+        if (jj >= nj) break;
+        Opnd &oc = (jj & 1) ? o1 : o0;
+        Opnd &on = (jj & 1) ? o0 : o1;
+        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, oc.a),
+                                                              __builtin_bit_cast(v4i, oc.b), zero, 0, 0, 0);
+        v16f F2;
+        if (!DUMP) {
+          const v4s fav = __builtin_bit_cast(v4s, oc.fa), fbv = __builtin_bit_cast(v4s, oc.fb);
+          F2 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fav, fbv, fzero, 0, 0, 0);
+        }
+        if (jj + 1 < nj) rd(jj + 1, on);
         if (DUMP) {
-          dump(D, 8 * s + j, nblk);
+          dump(D, 8 * s + j0 + jj, nblk);
         } else {
-          const v16f F2 = factor(pa, cur.fb[j][wn * 32 + lr]);
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] += F2[r] * (float)D[r];
         }
+        // Fence: block j + 1's products stay after block j's rescale
+        asm volatile("" : "+v"(acc), "+v"(on.a), "+v"(on.b), "+v"(on.fa), "+v"(on.fb)::"memory");
       }
-      // Fence: the MFMA builtins carry no memory dependence, so without it
-      // every block's products would be hoisted to the top of the step, with
-      // all their results live at once.
-      asm volatile("" : "+v"(acc)::"memory");
     }
   };
-  // One step: step s+2 loads into `mine` (free: it held s, staged one step
-  // earlier), s computes from `cur`, and s+1 (loaded one step earlier, in
-  // `next`) is staged into `other`, which nobody reads during this step.
-  auto step = [&](int s, MmqRegs<FMT> &mine, const MmqRegs<FMT> &next, MmqStage<FMT> &cur,
-                  MmqStage<FMT> &other) {
-    if (s + 2 < nsteps) load(mine, s + 2);
+  // One step: s + 1 loads into R0 (free: it held s, staged one step earlier),
+  // s computes from `cur`, and s + 1 is then staged into `other`, which
+  // nobody reads during this step.
+  auto step = [&](int s, MmqStage<FMT> &cur, MmqStage<FMT> &other) {
+    if (s + 1 < nsteps) load(R0, s + 1);
     compute(cur, s);
-    if (s + 1 < nsteps) store(next, other);
+    if (s + 1 < nsteps) store(R0, other);
     __syncthreads();
   };
-  if (nsteps > 0) load(R0, 0);
-  if (nsteps > 1) load(R1, 1);
-  if (nsteps > 0) store(R0, stage[0]);
+  if (nsteps > 0) {
+    load(R0, 0);
+    store(R0, stage[0]);
+  }
   __syncthreads();
   for (int s = 0; s < nsteps; s += 2) {
-    step(s, R0, R1, stage[0], stage[1]);
-    if (s + 1 < nsteps) step(s + 1, R1, R0, stage[1], stage[0]);
+    step(s, stage[0], stage[1]);
+    if (s + 1 < nsteps) step(s + 1, stage[1], stage[0]);
   }
 
   if (!DUMP) {
