@@ -330,9 +330,7 @@ class Mmq(Workload):
         self.a = torch.from_numpy(self.a_host).to(dev)
         self.aq = torch.empty((self.m, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
         self.c = torch.empty((self.m, self.n), dtype=torch.float32, device=dev)
-        # the 32-value types run the 8-wave form of the kernel
-        self.dominant = (f"mmq8_kernel<{self.fmt}>" if self.fmt in ("q8_0", "q4_0", "q5_0")
-                         else f"mmq_kernel<{self.fmt}>")
+        self.dominant = f"mmq_kernel<{self.fmt}>"
         self.ops = 2.0 * self.m * self.n * self.k
         self.kernel_bytes = w.nbytes + self.m * q81_bytes(self.k) + 4 * self.m * self.n
         self.tokens_per_step = self.m

@@ -14,8 +14,7 @@
 //      q - 8, Q5_0 q - 16), plus per (weight row, scale group) the group's
 //      factor (d*sc_j, d*sc_j, d) and for Q4_K -dmin*m_j
 // double-buffered: the global loads of step s+1 are in flight while the MFMAs
-// of step s run (the 8-wave form of the 32-value types loads two steps ahead;
-// see mmq8_kernel).  Each 32-wide block of k is one v_mfma_i32_32x32x32_i8 -> the
+// of step s run.  Each 32-wide block of k is one v_mfma_i32_32x32x32_i8 -> the
 // exact int32 dots D of that block for the wave's 32x32 tile; Q6_K's 16-wide
 // sub-blocks are two v_mfma_i32_32x32x16_i8.  A dot's fp32 rescale is
 // acc += F * D with F[m][n] = d_a[m] * f[n], a rank-1 outer product that the
@@ -584,157 +583,18 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
   }
 }
 
-// 8-wave form (two waves per SIMD, so up to 256 registers a wave): wave w
-// owns output tile (w / 4, w % 4) of the 64 x 128 workgroup tile over all
-// eight blocks of a step, and every thread stages one activation block and
-// one weight part per step.  A wave's blocks run one ahead: block j + 1's LDS
-// reads and MFMAs are issued before block j's rescale, so one wave overlaps
-// its own matrix-core and LDS latency with vector work instead of relying on
-// other waves of its SIMD.  Q4_K, Q5_K and the 32-value types (one MFMA per
-// 32-wide block).
-template <int FMT, bool DUMP>
-__global__ __launch_bounds__(512) void mmq8_kernel(const uint8_t *__restrict__ W, const uint8_t *__restrict__ AQ,
-                                                   float *__restrict__ C, int32_t *__restrict__ Dd, int M, int N,
-                                                   int nblk) {
-  static_assert(FMT != kMQ6K, "one MFMA per 32-wide block");
-  __shared__ MmqStage<FMT> stage[2];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 2, wn = wv & 3;  // 2 x 4 tiles of 32x32
-  const int tiles_n = (N + kBN - 1) / kBN;
-  const int m0 = (int)(blockIdx.x / tiles_n) * kBM, n0 = (int)(blockIdx.x % tiles_n) * kBN;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int nsteps = (nblk + 7) / 8;
-  const bool al = MmqFmt<FMT>::kBlk32 && (nblk & 1) == 0;
-
-  v16f acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  v16i zero;
-  v16f fzero;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    zero[r] = 0;
-    fzero[r] = 0.f;
-  }
-  // step s is staged from RA[s & 1] / RB[s & 1], loaded two steps ahead
-  MmqRegs<FMT> RA0, RA1, RB0, RB1;
-  auto load = [&](MmqRegs<FMT> &ga, MmqRegs<FMT> &gb, int s) {
-    load_act<FMT>(ga, AQ, M, nblk, m0, s, tid);
-    load_wgt<FMT>(gb, W, N, nblk, n0, s, tid, al);
-  };
-  auto store = [&](const MmqRegs<FMT> &ga, const MmqRegs<FMT> &gb, MmqStage<FMT> &dst) {
-    store_act<FMT>(ga, dst, tid);
-    store_wgt<FMT>(gb, dst, tid, al);
-  };
-  auto dump = [&](const v16i &D, int idx) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4), gn = n0 + wn * 32 + lr;
-      if (gm < M && gn < N) Dd[((int64_t)gm * N + gn) * nblk + idx] = D[r];
-    }
-  };
-  auto factor = [&](const uint32_t *pa, const uint32_t *pb) {
-    const v4s fav = __builtin_bit_cast(v4s, u32x2{pa[0], pa[1]});
-    const v4s fbv = __builtin_bit_cast(v4s, u32x2{pb[0], pb[1]});
-    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fav, fbv, fzero, 0, 0, 0);
-  };
-  auto compute = [&](MmqStage<FMT> &cur, int s) {
-    const uint8_t *arow = cur.a + (wm * 32 + lr) * kRow + 16 * lh;
-    const uint8_t *brow = cur.b + (wn * 32 + lr) * kRow + 16 * lh;
-    if constexpr (MmqFmt<FMT>::kMin) {
-      if (!DUMP) {
-        // min term of the step's eight blocks, four per MFMA (see mmq_kernel)
-        constexpr int sA = (kBM + 1) * 2, sB = (kBN + 1) * 2;
-#pragma unroll
-        for (int j0 = 0; j0 < 8; j0 += 4) {
-          const uint32_t *ps = cur.fs[j0 + 2 * lh][wm * 32 + lr];
-          const uint32_t *pm = cur.fm[j0 + 2 * lh][wn * 32 + lr];
-          const v8bf sv = __builtin_bit_cast(v8bf, u32x4{ps[0], ps[1], ps[sA], ps[sA + 1]});
-          const v8bf mv = __builtin_bit_cast(v8bf, u32x4{pm[0], pm[1], pm[sB], pm[sB + 1]});
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sv, mv, acc, 0, 0, 0);
-        }
-      }
-    }
-    // blocks of this step (32-value types: fewer in a ragged last step; uniform)
-    const int nbs = MmqFmt<FMT>::kBlk32 ? min(8, nblk - 8 * s) : 8;
-    auto issue = [&](int j, v16i &D, v16f &F) {
-      const u32x4n av = *reinterpret_cast<const u32x4n *>(arow + 32 * j);
-      const u32x4n bv = *reinterpret_cast<const u32x4n *>(brow + 32 * j);
-      D = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, av), __builtin_bit_cast(v4i, bv), zero, 0,
-                                                0, 0);
-      if (!DUMP) F = factor(cur.fa[j][wm * 32 + lr], cur.fb[j][wn * 32 + lr]);
-    };
-    v16i D0, D1;
-    v16f F0, F1;
-    issue(0, D0, F0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= nbs) break;
-      v16i &Dc = (j & 1) ? D1 : D0;
-      v16f &Fc = (j & 1) ? F1 : F0;
-      v16i &Dn = (j & 1) ? D0 : D1;
-      v16f &Fn = (j & 1) ? F0 : F1;
-      if (j + 1 < nbs) issue(j + 1, Dn, Fn);
-      if (DUMP) {
-        dump(Dc, 8 * s + j);
-      } else {
-        // F2 = 2F (see mmq_kernel): the sum is halved at the end
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += Fc[r] * (float)Dc[r];
-      }
-      // Fence: block j + 2's LDS reads and MFMAs stay after block j's rescale
-      asm volatile("" : "+v"(acc), "+v"(Dn), "+v"(Fn)::"memory");
-    }
-  };
-  auto step = [&](int s, MmqRegs<FMT> &ma, MmqRegs<FMT> &mb, const MmqRegs<FMT> &na, const MmqRegs<FMT> &nb,
-                  MmqStage<FMT> &cur, MmqStage<FMT> &other) {
-    if (s + 2 < nsteps) load(ma, mb, s + 2);
-    compute(cur, s);
-    if (s + 1 < nsteps) store(na, nb, other);
-    __syncthreads();
-  };
-  if (nsteps > 0) load(RA0, RB0, 0);
-  if (nsteps > 1) load(RA1, RB1, 1);
-  if (nsteps > 0) store(RA0, RB0, stage[0]);
-  __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, RA0, RB0, RA1, RB1, stage[0], stage[1]);
-    if (s + 1 < nsteps) step(s + 1, RA1, RB1, RA0, RB0, stage[1], stage[0]);
-  }
-  if (!DUMP) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int gm = m0 + wm * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-      const int gn = n0 + wn * 32 + lr;
-      if (gm < M && gn < N) C[(int64_t)gm * N + gn] = 0.5f * acc[r];
-    }
-  }
-}
-
-// Which form runs, per format, measured on MI355X at 512 x 4096 x 4096
-// (us per launch, 16-wave form / 8-wave form): Q8_0 54.4 / 46.4, Q4_0 43.5 /
-// 38.9, Q5_0 55.8 / 42.1, Q4_K 34.5 / 36.5, Q5_K 39.4 / 40.9.  The 32-value
-// types take the 8-wave form; the K-quants with a min term (two more MFMAs
-// and heavier weight staging per step) keep four waves per SIMD.
-template <int FMT>
-constexpr bool kMmq8Waves = MmqFmt<FMT>::kBlk32;
-
+// One kernel for every format.  An 8-wave form (two waves per SIMD, each
+// wave a 32x32 tile over all eight blocks of a step, one block of MFMA
+// lookahead, loads two steps ahead) ran the 32-value types faster than this
+// kernel did before its operand lookahead (us at 512 x 4096 x 4096: Q8_0 46.4
+// against 54.4), and slower since (Q8_0 46.1 against 33.9, Q4_0 38.6 against
+// 32.8, Q5_0 42.0 against 35.1), so it was retired.
 template <int FMT>
 static hipError_t launch_fmt(const void *w, const void *aq, float *c, int32_t *D, int64_t m, int64_t n, int64_t k,
                              hipStream_t stream) {
   const dim3 grid((unsigned)(((n + kBN - 1) / kBN) * ((m + kBM - 1) / kBM)));
   const uint8_t *W = static_cast<const uint8_t *>(w);
   const uint8_t *A = static_cast<const uint8_t *>(aq);
-  if constexpr (FMT != kMQ6K && kMmq8Waves<FMT>) {
-    if (D)
-      hipLaunchKernelGGL((mmq8_kernel<FMT, true>), grid, dim3(512), 0, stream, W, A, c, D, (int)m, (int)n,
-                         (int)(k / 32));
-    else
-      hipLaunchKernelGGL((mmq8_kernel<FMT, false>), grid, dim3(512), 0, stream, W, A, c, D, (int)m, (int)n,
-                         (int)(k / 32));
-    return hipGetLastError();
-  }
   if (D)
     hipLaunchKernelGGL((mmq_kernel<FMT, true>), grid, dim3(1024), 0, stream, W, A, c, D, (int)m, (int)n,
                        (int)(k / 32));
