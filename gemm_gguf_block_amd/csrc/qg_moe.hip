@@ -33,12 +33,13 @@ typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));  // 16-byte aligned
 
 // R rows of one lane unit (64 weights: superblock sb, group g) of a Q4_K row
 // against one activation unit: A[1..8] / A[10..17] the qs of Q8_1 blocks 2u
-// and 2u + 1, da0/da1 their d, S0/S1 their code sums.  D0/D1 are the exact
-// block dots of each row.
+// and 2u + 1, da0/da1 their d, dS0/dS1 their d times their code sum (formed
+// once per activation unit, for the min term).  D0/D1 are the exact block dots
+// of each row.
 struct ActUnit {
   uint32_t A[18];
   float da0, da1;
-  int S0, S1;
+  float dS0, dS1;
 };
 
 __device__ __forceinline__ void unit_dots(const u32x4 &qa, const u32x4 &qb, const ActUnit &x, int &D0, int &D1) {
@@ -56,27 +57,27 @@ __device__ __forceinline__ float unit_value(const u32x4 &hdr, int g, const ActUn
   int sc0, sc1, m0, m1;
   q4k_scales(hdr.y, hdr.z, hdr.w, g, sc0, sc1, m0, m1);
   const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-  const float dS0 = x.da0 * (float)x.S0, dS1 = x.da1 * (float)x.S1;
-  return d * (x.da0 * (float)(sc0 * D0) + x.da1 * (float)(sc1 * D1)) - dmin * (dS0 * (float)m0 + dS1 * (float)m1);
+  return d * (x.da0 * (float)(sc0 * D0) + x.da1 * (float)(sc1 * D1)) - dmin * (x.dS0 * (float)m0 + x.dS1 * (float)m1);
 }
 
 // Activation unit from Q8_1 blocks 2u, 2u + 1 at p.
 __device__ __forceinline__ void act_from_q8_1(const uint8_t *p, ActUnit &x) {
   load_q8_1_pair(p, x.A);
-  x.S0 = 0;
-  x.S1 = 0;
+  int S0 = 0, S1 = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    x.S0 = bsum4(x.A[1 + i], x.S0);
-    x.S1 = bsum4(x.A[10 + i], x.S1);
+    S0 = bsum4(x.A[1 + i], S0);
+    S1 = bsum4(x.A[10 + i], S1);
   }
   x.da0 = h2f(x.A[0]);
   x.da1 = h2f(x.A[9]);
+  x.dS0 = x.da0 * (float)S0;
+  x.dS1 = x.da1 * (float)S1;
 }
 
 // Activation unit u from a unit-major row of U units at base: piece c of unit
 // u at base[c*U + u] (16 bytes: half c%2 of block 2u + c/2), the record
-// {d(2u), d(2u+1), sum(2u), sum(2u+1)} at base[4U + u].
+// {d(2u), d(2u+1), d*sum(2u), d*sum(2u+1)} at base[4U + u] (sum: the block's code sum).
 __device__ __forceinline__ void act_from_unit_major(const u32x4n *base, int U, int u, ActUnit &x) {
   const u32x4n x0 = base[u], x1 = base[U + u], x2 = base[2 * U + u], x3 = base[3 * U + u];
   const u32x4n rec = base[4 * U + u];
@@ -86,8 +87,8 @@ __device__ __forceinline__ void act_from_unit_major(const u32x4n *base, int U, i
   x.A[14] = x3.x; x.A[15] = x3.y; x.A[16] = x3.z; x.A[17] = x3.w;
   x.da0 = as_f32(rec.x);
   x.da1 = as_f32(rec.y);
-  x.S0 = (int)rec.z;
-  x.S1 = (int)rec.w;
+  x.dS0 = as_f32(rec.z);
+  x.dS1 = as_f32(rec.w);
 }
 
 // Writes the two block dots of unit u (blocks 2u, 2u + 1) of row `row` of
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       base[2 * U + uu] = u32x4n{x.A[10], x.A[11], x.A[12], x.A[13]};
       base[3 * U + uu] = u32x4n{x.A[14], x.A[15], x.A[16], x.A[17]};
       base[4 * U + uu] = u32x4n{__builtin_bit_cast(uint32_t, x.da0), __builtin_bit_cast(uint32_t, x.da1),
-                                (uint32_t)x.S0, (uint32_t)x.S1};
+                                __builtin_bit_cast(uint32_t, x.dS0), __builtin_bit_cast(uint32_t, x.dS1)};
     }
     __syncthreads();
   }
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 //   2. each wave's first slot's weight loads are issued;
 //   3. for every valid slot, h = silu(g) * u from g|u of its pair, quantized
 //      to Q8_1 (8 lanes per 32-value block, the rule of quantize_q8_1) into
-//      LDS, unit-major with the record {d(2u), d(2u+1), sum(2u), sum(2u+1)};
+//      LDS, unit-major with the record {d(2u), d(2u+1), d*sum(2u), d*sum(2u+1)};
 //      row tile 0 also writes the Q8_1 rows to hq;
 //   4. each wave runs its slots in order (its next slot's weights loading
 //      during this one's dots), acc += weights[p] * (Wdown[e] . h^_p); then
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(512) void moe_down_token_kernel(
       const uint32_t head = q81_header(qp);
       if (j8 == 0) {
         xr[4 * (4 * U + uu) + bb] = __builtin_bit_cast(uint32_t, h2f(head));
-        xr[4 * (4 * U + uu) + 2 + bb] = (uint32_t)qp.sum;
+        xr[4 * (4 * U + uu) + 2 + bb] = __builtin_bit_cast(uint32_t, h2f(head) * (float)qp.sum);
       }
       if (tile == 0) {
         uint8_t *qb8 = hq + ((int64_t)p * (F / 32) + blk) * kQ8_1Bytes;
