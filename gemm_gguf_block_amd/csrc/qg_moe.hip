@@ -547,9 +547,7 @@ __global__ __launch_bounds__(512) void moe_down_token_kernel(
   // 4. this wave's slots (parity sp) in order, the next one's weights loading
   // during each; then the odd slots' sum joins the even slots' in LDS
   float acc = 0.f;
-  for (int j = sp; j < nv; j += 2) {
-    u32x4 nxt[3 * UPL];
-    if (j + 2 < nv) load_w(nxt, j + 2);
+  auto run_slot = [&](const u32x4 (&w)[3 * UPL], int j) __attribute__((always_inline)) {
     const int p = t * top_k + vs[j];
     const u32x4n *base = xs + j * 5 * U;
     float pt = 0.f;
@@ -559,16 +557,23 @@ __global__ __launch_bounds__(512) void moe_down_token_kernel(
       ActUnit x;
       act_from_unit_major(base, U, u, x);
       int D0, D1;
-      unit_dots(cur[3 * v + 1], cur[3 * v + 2], x, D0, D1);
+      unit_dots(w[3 * v + 1], w[3 * v + 2], x, D0, D1);
       if (DUMP) {
         if (row < H) dump_unit(Dd, p, H, row, U, u, D0, D1);
       } else {
-        pt += unit_value(cur[3 * v], g, x, D0, D1);
+        pt += unit_value(w[3 * v], g, x, D0, D1);
       }
     }
     if (!DUMP) acc += vw[j] * group_sum_last<L>(pt);
-#pragma unroll
-    for (int i = 0; i < 3 * UPL; ++i) cur[i] = nxt[i];
+  };
+  // two register sets in turn (no copies between them)
+  u32x4 nxt[3 * UPL];
+  for (int j = sp; j < nv; j += 4) {
+    if (j + 2 < nv) load_w(nxt, j + 2);
+    run_slot(cur, j);
+    if (j + 2 >= nv) break;
+    if (j + 4 < nv) load_w(cur, j + 4);
+    run_slot(nxt, j + 2);
   }
   if (DUMP) return;
   if (sp == 1) part[rg * 64 + lane] = acc;
