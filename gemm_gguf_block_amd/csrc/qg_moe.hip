@@ -479,19 +479,20 @@ __global__ __launch_bounds__(512) void moe_down_token_kernel(
 
   // weights of valid slot j's expert for this lane's units: w[3v] header,
   // w[3v+1] and w[3v+2] the unit's two 16-byte qs pieces
+  // A slot's 3 * UPL loads are issued by every lane (rows past H read row
+  // H - 1 and are never stored): without a per-lane branch around them the
+  // compiler's waits for one slot leave more of the next slot's loads in
+  // flight (53.6 -> 52.2 us).
+  const int64_t row_off = (int64_t)min(row, H - 1) * rb;
   auto load_w = [&](u32x4 (&w)[3 * UPL], int j) __attribute__((always_inline)) {
-    const int e = ve[j];
+    const uint8_t *we = W + (int64_t)ve[j] * expert_bytes + row_off;
 #pragma unroll
     for (int v = 0; v < UPL; ++v) {
       const int u = li + v * L, sb = u >> 2, g = u & 3;
-      if (row < H) {
-        const uint8_t *bp = W + (int64_t)e * expert_bytes + (int64_t)row * rb + sb * kQ4KBytes;
-        w[3 * v] = ld16(bp);
-        w[3 * v + 1] = ld16(bp + 16 + 32 * g);
-        w[3 * v + 2] = ld16(bp + 32 + 32 * g);
-      } else {
-        w[3 * v] = w[3 * v + 1] = w[3 * v + 2] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const uint8_t *bp = we + sb * kQ4KBytes;
+      w[3 * v] = ld16(bp);
+      w[3 * v + 1] = ld16(bp + 16 + 32 * g);
+      w[3 * v + 2] = ld16(bp + 32 + 32 * g);
     }
   };
   // 2. this wave's first slot's weights in flight during the activation step
@@ -566,7 +567,9 @@ __global__ __launch_bounds__(512) void moe_down_token_kernel(
     }
     if (!DUMP) acc += vw[j] * group_sum_last<L>(pt);
   };
-  // two register sets in turn (no copies between them)
+  // Two register sets in turn (no copies between them).  (Issuing the next
+  // slot's loads even when there is none, repeating the last slot, so that
+  // every wait is a fixed count, measured slower: 55.3 against 53.0 us.)
   u32x4 nxt[3 * UPL];
   for (int j = sp; j < nv; j += 4) {
     if (j + 2 < nv) load_w(nxt, j + 2);
