@@ -2,22 +2,14 @@
 //
 // With b <= 8 activation rows the dot4 kernels spend VALU per (row, block,
 // activation row).  Here the activation rows form the M side of
-// v_mfma_i32_32x32x32_i8 (unused rows are zero) and 32 weight rows the N side,
-// so one MFMA gives the exact int32 block dots of 32 weight rows against all
-// activation rows, and the fp32 rescale costs the same few VALU per block
-// whatever b is.
+// v_mfma_i32_32x32x32_i8 and 32 weight rows the N side, so one MFMA gives the
+// exact int32 block dots of 32 weight rows against all activation rows, and
+// the fp32 rescale costs the same few VALU per block whatever b is.
 //
 // MFMA 32x32 output layout: register r of lane l holds row 8(r/4) + 4(l/32) +
 // r%4, column l%32.  The A operand of lane l is row l%32, k half l/32; the B
-// operand of lane l is column l%32, the same k half.
-//
-// Q4_K: a workgroup of 8 waves owns a tile of 32 weight rows.  k is walked in
-// chunks of 16 superblocks: the workgroup stages the chunk's activation blocks
-// in LDS, wave w takes superblocks w and w + 8 of the chunk (32 rows x 144
-// bytes each, loaded before the staging barrier), and runs their blocks on the
-// matrix core.  The 8 waves' partial tiles are summed through LDS at the end.
-// Two such workgroups fit on a CU, so 14336 rows (448 tiles) run in one pass.
-// For b <= 8 only registers r = 0..3 carry rows (4(lane/32) + r).
+// operand of lane l is column l%32, the same k half.  For b <= 8 only
+// registers r = 0..3 carry rows (4(lane/32) + r).
 //
 // With DUMP the same code writes the exact int32 dots of every MFMA instead of
 // Y: D[i][r][block] per 32-value block (Q4_K) or per 16-value sub-block (Q6_K).
@@ -34,139 +26,285 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
 typedef float f32x4n __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+
+// ---------------------------------------------------------------------------
+// Q4_K.  A workgroup of 8 waves owns a tile of 32 weight rows; two fit on a
+// CU, so 14336 rows (448 tiles) run in one pass.  k is walked in chunks of 16
+// superblocks, and wave w takes superblocks w and w + 8 of a chunk.
+//
+// Weights: the tile's 32 rows of one superblock are 288 16-byte pieces.  A
+// wave reads them in address order (lane l: pieces l + 64q, q = 0..4), which
+// touches a third as many cache lines per load instruction as reading them
+// straight in the MFMA B layout, writes them to its own LDS buffer as
+// [piece][row], and reads back the B layout (header of row l%32, code piece
+// 1 + 2g + l/32).  One superblock is in flight per wave: the next one is
+// loaded as soon as the current one has gone through LDS.
+//
+// Activations: the chunk's Q8_1 blocks are staged once per workgroup:
+//   act  [blk][m][half]  16 B  int8 codes, the A operand;
+//   da   [blk][m]        f32   d_a;
+//   mina [sb][m][half]   16 B  bf16 (hi, lo) of d_a * sum(qa) for blocks
+//                              4 half .. 4 half + 3 of superblock sb.
+// Their loads are issued before the weights', and the staging writes wait
+// for them alone.
+//
+// Per superblock the int8 MFMAs give the block dots D_j; the lane's four
+// activation rows take d * sum_j d_a (sc_j D_j) on the VALU, with block j+1's
+// MFMA issued before block j's rescale, and the min term dmin * sum_j
+// (d_a sum qa)_j m_j on the matrix core: one bf16 MFMA over the (hi, lo)
+// split of d_a sum(qa) (2^-16 relative) against the integer m_j, lanes 0-31
+// carrying blocks 0-3 and lanes 32-63 blocks 4-7 (k slots 2i, 2i + 1 of
+// block 4 l/32 + i).  The 8 waves' partial tiles are summed through LDS.
+namespace q4 {
+
 constexpr int kSbPerWave = 2;
 constexpr int kChunkSb = kWaves * kSbPerWave;  // superblocks per chunk
 constexpr int kChunkBlk = 8 * kChunkSb;
-constexpr int kMaxB = 8;
+constexpr int kWbUnits = 9 * 33;  // per wave: [piece][row], rows padded to 33 units of 16 bytes
+constexpr size_t kDaOff = (size_t)kChunkBlk * 8 * 32;
+constexpr size_t kMinOff = kDaOff + (size_t)kChunkBlk * 8 * 4;
+constexpr size_t kWbOff = kMinOff + (size_t)kChunkSb * 8 * 2 * 16;
+constexpr size_t kPartOff = kWbOff;  // the partial tiles reuse the weight buffers
+constexpr size_t kLds = kWbOff + (size_t)kWaves * kWbUnits * 16;
+static_assert(kWaves * 64 <= kWaves * kWbUnits, "the partial tiles fit in the weight buffers");
+static_assert(2 * kLds <= 160 * 1024, "two workgroups per CU");
+constexpr int kStageIters = (8 * kChunkBlk + kThreads - 1) / kThreads;
 
-// Dynamic LDS for b activation rows: qs [blk][m][half] (16 B), d_a [blk][m],
-// d_a*sum(qa) [blk][m] (rows padded to 4 so lanes read 16-byte groups), then
-// the waves' partial tiles [wave][lane] (16 B).
-__host__ __device__ constexpr int rows_padded(int nb) { return nb <= 4 ? 4 : 8; }
-inline size_t lds_bytes(int nb) {
-  const int bp = rows_padded(nb);
-  return (size_t)kChunkBlk * bp * 32 + 2 * (size_t)kChunkBlk * bp * 4 + (size_t)kWaves * 64 * 16;
+// One superblock of one weight row as lane half lh needs it: the 16-byte
+// header and the 16 code bytes of each 32-byte group that fall in half lh.
+struct Sb {
+  u32x4 hdr, q[4];
+};
+
+// bf16 bits of x with the low mantissa bits cut off (hi) and of the rest
+// rounded to nearest (lo), packed lo << 16 | hi: x = hi + lo to 2^-16.
+__device__ __forceinline__ uint32_t bf16_hilo(float x) {
+  const uint32_t hb = __builtin_bit_cast(uint32_t, x) & 0xFFFF0000u;
+  const uint32_t lb = __builtin_bit_cast(uint32_t, x - __builtin_bit_cast(float, hb));
+  const uint32_t lr = (lb + 0x7FFFu + ((lb >> 16) & 1u)) >> 16;
+  return (hb >> 16) | (lr << 16);
 }
 
+// W and XQ are not declared __restrict__: that keeps the activation loads
+// ahead of the weight loads and both ahead of the staging barrier (loads the
+// compiler may treat as invariant are otherwise scheduled next to their uses).
 template <bool DUMP>
-__global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q4k(const uint8_t *__restrict__ W,
-                                                                const uint8_t *__restrict__ XQ,
-                                                                float *__restrict__ Y, int32_t *__restrict__ Dd,
-                                                                int nb, int n, int nsb) {
+__global__ __launch_bounds__(kThreads, 4) void gemv_batch_mfma_q4k(const uint8_t *W, const uint8_t *XQ, float *Y,
+                                                                   int32_t *Dd, int nb, int n, int nsb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int bp = rows_padded(nb);
   u32x4n *act = reinterpret_cast<u32x4n *>(lds);
-  float *da = reinterpret_cast<float *>(lds + (size_t)kChunkBlk * bp * 32);
-  float *das = da + kChunkBlk * bp;
-  f32x4n *part = reinterpret_cast<f32x4n *>(das + kChunkBlk * bp);
+  float *da = reinterpret_cast<float *>(lds + kDaOff);
+  const u32x4n *mina = reinterpret_cast<const u32x4n *>(lds + kMinOff);
+  uint32_t *minw = reinterpret_cast<uint32_t *>(lds + kMinOff);
+  f32x4n *part = reinterpret_cast<f32x4n *>(lds + kPartOff);
+  u32x4n *wb = reinterpret_cast<u32x4n *>(lds + kWbOff) + (threadIdx.x >> 6) * kWbUnits;
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int nl = lane & 31, lh = lane >> 5;  // weight row in the tile / k half; also activation row (A side)
-  const int64_t row = (int64_t)blockIdx.x * 32 + nl;
-  const bool live_row = row < n;
+  const int tile = (int)blockIdx.x;
   const int64_t rb = (int64_t)nsb * kQ4KBytes;
   const int64_t xrb = (int64_t)nsb * 8 * kQ8_1Bytes;
+  const int nchunk = (nsb + kChunkSb - 1) / kChunkSb;
   const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const v16f fzero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
-    const int csb = min(kChunkSb, nsb - c0);
-    // this wave's superblocks wv and wv + kWaves of the chunk; weights first,
-    // so their latency overlaps the staging
-    u32x4 hdr[kSbPerWave], q[kSbPerWave][4];
+  // Byte offsets of this lane's pieces from the tile's first row (rows past n
+  // read row n - 1; the last 32 lanes of q = 4 repeat piece 287), and their
+  // LDS units.  k <= 2^24 keeps 32 rows of offsets within 31 bits.
+  uint32_t off[5], wbi[5];
+  {
+    const int rowlim = n - 1 - tile * 32;
 #pragma unroll
-    for (int s = 0; s < kSbPerWave; ++s) {
-      const int sbl = wv + kWaves * s;
-      hdr[s] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int g = 0; g < 4; ++g) q[s][g] = hdr[s];
-      if (sbl < csb && live_row) {
-        const uint8_t *bp8 = W + row * rb + (int64_t)(c0 + sbl) * kQ4KBytes;
-        hdr[s] = ld16(bp8);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) q[s][g] = ld16(bp8 + 16 + 32 * g + 16 * lh);
-      }
+    for (int q = 0; q < 5; ++q) {
+      const int pc = min(lane + 64 * q, 287), pr = pc / 9, pp = pc - 9 * pr;
+      off[q] = (uint32_t)(min(pr, rowlim) * (int)rb + 16 * pp);
+      wbi[q] = (uint32_t)(pp * 33 + pr);
     }
-    if (c0 > 0) __syncthreads();  // the previous chunk is no longer read
-    for (int t = tid; t < nb * 8 * csb; t += kThreads) {
+  }
+  const uint8_t *tw = W + (int64_t)tile * 32 * rb;
+  // superblock i of this wave in chunk c (past the chunk's end: its last one,
+  // never used)
+  auto load_sb = [&](Sb &R, int c, int i) __attribute__((always_inline)) {
+    const int c0 = c * kChunkSb, last = min(kChunkSb, nsb - c0) - 1;
+    const uint8_t *p = tw + (int64_t)(c0 + min(wv + kWaves * i, last)) * kQ4KBytes;
+    R.hdr = ld16(p + off[0]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) R.q[g] = ld16(p + off[g + 1]);
+  };
+  // R through this wave's LDS buffer into the B layout (a wave's LDS
+  // accesses complete in order, so no barrier is needed)
+  auto to_mfma = [&](const Sb &R) __attribute__((always_inline)) {
+    const u32x4 v[5] = {R.hdr, R.q[0], R.q[1], R.q[2], R.q[3]};
+#pragma unroll
+    for (int q = 0; q < 5; ++q) wb[wbi[q]] = u32x4n{v[q].x, v[q].y, v[q].z, v[q].w};
+    Sb O;
+    const u32x4n h = wb[nl];
+    O.hdr = u32x4{h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4n t = wb[(1 + 2 * g + lh) * 33 + nl];
+      O.q[g] = u32x4{t.x, t.y, t.z, t.w};
+    }
+    return O;
+  };
+
+  // Activation staging of chunk c: all loads first (threads past the last
+  // block repeat it, so the loads are a fixed sequence), then the writes.
+  u32x4 sv0[kStageIters], sv1[kStageIters];
+  uint32_t sv2[kStageIters];
+  auto stage_load = [&](int c) __attribute__((always_inline)) {
+    const int c0 = c * kChunkSb, csb = min(kChunkSb, nsb - c0), items = nb * 8 * csb;
+#pragma unroll
+    for (int it = 0; it < kStageIters; ++it) {
+      const int t = min(tid + it * kThreads, items - 1);
       const int m = t / (8 * csb), blk = t - m * (8 * csb);
       const uint8_t *ap = XQ + m * xrb + (int64_t)(8 * c0 + blk) * kQ8_1Bytes;
-      const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
-      const uint32_t v2 = ld4(ap + 32);
-      const u32x4n lo = {v0.y, v0.z, v0.w, v1.x}, hi = {v1.y, v1.z, v1.w, v2};
-      act[(blk * bp + m) * 2] = lo;
-      act[(blk * bp + m) * 2 + 1] = hi;
+      sv0[it] = ld16(ap);
+      sv1[it] = ld16(ap + 16);
+      sv2[it] = ld4(ap + 32);
+    }
+  };
+  auto stage_write = [&](int c) __attribute__((always_inline)) {
+    const int c0 = c * kChunkSb, csb = min(kChunkSb, nsb - c0), items = nb * 8 * csb;
+#pragma unroll
+    for (int it = 0; it < kStageIters; ++it) {
+      const int t = min(tid + it * kThreads, items - 1);
+      const int m = t / (8 * csb), blk = t - m * (8 * csb);
+      const u32x4 v0 = sv0[it], v1 = sv1[it];
+      const u32x4n lo = {v0.y, v0.z, v0.w, v1.x}, hi = {v1.y, v1.z, v1.w, sv2[it]};
+      act[(blk * 8 + m) * 2] = lo;
+      act[(blk * 8 + m) * 2 + 1] = hi;
       const int S = bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x,
                     bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0))))))));
       const float d = h2f(v0.x);
-      da[blk * bp + m] = d;
-      das[blk * bp + m] = d * (float)S;
+      da[blk * 8 + m] = d;
+      const int sbl = blk >> 3, j = blk & 7;
+      minw[((sbl * 8 + m) * 2 + (j >> 2)) * 4 + (j & 3)] = bf16_hilo(d * (float)S);
     }
-    __syncthreads();
+  };
+
+  f32x4n acc = {0.f, 0.f, 0.f, 0.f};
+  // superblock sbl of chunk c0, accumulated into acc
+  auto run_sb = [&](const Sb &w, int sbl, int c0) __attribute__((always_inline)) {
+    int sc[8], mn[8];
 #pragma unroll
-    for (int s = 0; s < kSbPerWave; ++s) {
-      const int sbl = wv + kWaves * s;
-      if (sbl >= csb) break;
-      int sc[8], mn[8];
+    for (int g = 0; g < 4; ++g)
+      q4k_scales(w.hdr.y, w.hdr.z, w.hdr.w, g, sc[2 * g], sc[2 * g + 1], mn[2 * g], mn[2 * g + 1]);
+    // A rows 8..31 reach only output registers 4..15, which are never read,
+    // so those lanes take rows nl % 8; rows nb..7 are never stored
+    const u32x4n *ap = act + (64 * sbl + (nl & 7)) * 2 + lh;
+    const f32x4n *dp = reinterpret_cast<const f32x4n *>(da + 64 * sbl + 4 * lh);
+    auto bops = [&](int j) __attribute__((always_inline)) {
+      const u32x4 qg = w.q[j >> 1];
+      const uint32_t sh = 4u * (uint32_t)(j & 1);  // sub-block 2g: low nibbles, 2g+1: high
+      return v4i{(int)((qg.x >> sh) & 0x0F0F0F0Fu), (int)((qg.y >> sh) & 0x0F0F0F0Fu),
+                 (int)((qg.z >> sh) & 0x0F0F0F0Fu), (int)((qg.w >> sh) & 0x0F0F0F0Fu)};
+    };
+    f32x4n t = {0.f, 0.f, 0.f, 0.f};
+    v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, ap[0]), bops(0), zero, 0, 0, 0);
+    f32x4n a4c = dp[0], a4n = dp[2];
+    v4i an = __builtin_bit_cast(v4i, ap[16]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        q4k_scales(hdr[s].y, hdr[s].z, hdr[s].w, g, sc[2 * g], sc[2 * g + 1], mn[2 * g], mn[2 * g + 1]);
-      const float d = h2f(hdr[s].x), dmin = h2f(hdr[s].x >> 16);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int blk = 8 * sbl + j;
-        const u32x4 qg = q[s][j >> 1];
-        const uint32_t sh = 4u * (uint32_t)(j & 1);  // sub-block 2g: low nibbles, 2g+1: high
-        const v4i b = {(int)((qg.x >> sh) & 0x0F0F0F0Fu), (int)((qg.y >> sh) & 0x0F0F0F0Fu),
-                       (int)((qg.z >> sh) & 0x0F0F0F0Fu), (int)((qg.w >> sh) & 0x0F0F0F0Fu)};
-        v4i a = {0, 0, 0, 0};
-        if (nl < nb) a = __builtin_bit_cast(v4i, act[(blk * bp + nl) * 2 + lh]);
-        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
-        if (DUMP) {
-          // register r: activation row 4*lh + r, weight row `row`
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * lh + r < nb && live_row)
-              Dd[((int64_t)(4 * lh + r) * n + row) * (8 * (int64_t)nsb) + 8 * (c0 + sbl) + j] = D[r];
-          asm volatile("" ::: "memory");
-          continue;
-        }
-        // activation rows 4*lh + r, r = 0..3 (broadcast reads; rows >= nb
-        // only reach registers that are never stored)
-        f32x4n a4 = {0.f, 0.f, 0.f, 0.f}, s4 = a4;
-        if (4 * lh < bp) {
-          a4 = *reinterpret_cast<const f32x4n *>(da + blk * bp + 4 * lh);
-          s4 = *reinterpret_cast<const f32x4n *>(das + blk * bp + 4 * lh);
-        }
-        const float dsc = d * (float)sc[j], dm = dmin * (float)mn[j];
-        acc[0] += (a4.x * dsc) * (float)D[0] - s4.x * dm;
-        acc[1] += (a4.y * dsc) * (float)D[1] - s4.y * dm;
-        acc[2] += (a4.z * dsc) * (float)D[2] - s4.z * dm;
-        acc[3] += (a4.w * dsc) * (float)D[3] - s4.w * dm;
-        // Fence: MFMA builtins carry no memory dependence; without it every
-        // block's MFMA is hoisted with all results live at once.
-        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])::"memory");
+    for (int j = 0; j < 8; ++j) {
+      v16i Dn = zero;
+      if (j + 1 < 8) Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(an, bops(j + 1), zero, 0, 0, 0);
+      const f32x4n a4 = a4c;  // d_a of activation rows 4 lh + r (broadcast read)
+      a4c = a4n;
+      if (j + 2 < 8) {
+        an = __builtin_bit_cast(v4i, ap[(j + 2) * 16]);
+        a4n = dp[2 * (j + 2)];
       }
+      if (DUMP) {
+        const int64_t row = (int64_t)tile * 32 + nl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * lh + r < nb && row < n)
+            Dd[((int64_t)(4 * lh + r) * n + row) * (8 * (int64_t)nsb) + 8 * (c0 + sbl) + j] = D[r];
+      } else {
+        t.x = fmaf(a4.x, (float)__mul24(sc[j], D[0]), t.x);
+        t.y = fmaf(a4.y, (float)__mul24(sc[j], D[1]), t.y);
+        t.z = fmaf(a4.z, (float)__mul24(sc[j], D[2]), t.z);
+        t.w = fmaf(a4.w, (float)__mul24(sc[j], D[3]), t.w);
+      }
+      // Fence: MFMA builtins carry no memory dependence; without it every
+      // block's MFMA is hoisted with all results live at once.
+      asm volatile("" : "+v"(t)::"memory");
+      D = Dn;
+    }
+    if (DUMP) return;
+    // min term: B k slots 2i, 2i + 1 hold m of block 4lh + i as bf16 (exact)
+    uint32_t bm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h = __builtin_bit_cast(uint32_t, (float)(lh ? mn[4 + i] : mn[i])) >> 16;
+      bm[i] = h | (h << 16);
+    }
+    const v16f M = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(v8bf, mina[(sbl * 8 + (nl & 7)) * 2 + lh]),
+        __builtin_bit_cast(v8bf, u32x4n{bm[0], bm[1], bm[2], bm[3]}), fzero, 0, 0, 0);
+    const float d = h2f(w.hdr.x), dmin = h2f(w.hdr.x >> 16);
+    acc.x = fmaf(d, t.x, fmaf(-dmin, M[0], acc.x));
+    acc.y = fmaf(d, t.y, fmaf(-dmin, M[1], acc.y));
+    acc.z = fmaf(d, t.z, fmaf(-dmin, M[2], acc.z));
+    acc.w = fmaf(d, t.w, fmaf(-dmin, M[3], acc.w));
+  };
+
+  // (k = 0 runs no chunk and stores zeros)
+  // prologue: the first chunk's activation loads, then the first superblock
+  // of weights, then the staging writes
+  Sb cur;
+  if (nchunk > 0) {  // uniform in the workgroup
+    stage_load(0);
+    asm volatile("" ::: "memory");
+    load_sb(cur, 0, 0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);  // nothing that waits for the activation moves above the weight loads
+    stage_write(0);
+    __syncthreads();
+  }
+  for (int c = 0; c < nchunk; ++c) {
+    const int c0 = c * kChunkSb, csb = min(kChunkSb, nsb - c0);
+    if (c > 0) {         // uniform in the workgroup
+      __syncthreads();   // the previous chunk is no longer read
+      stage_load(c);
+      stage_write(c);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < kSbPerWave; ++i) {
+      // cur goes through LDS, then the next superblock is loaded into it
+      // while this one runs
+      const Sb O = to_mfma(cur);
+      if (i + 1 < kSbPerWave) load_sb(cur, c, i + 1);
+      else if (c + 1 < nchunk) load_sb(cur, c + 1, 0);
+      if (wv + kWaves * i < csb) run_sb(O, wv + kWaves * i, c0);
     }
   }
   if (DUMP) return;
-  // sum the waves' partial tiles; thread t < 32 * nb owns output (m, nl) with
-  // m = t / 32: lane nl + 32 * (m / 4), register m % 4 of every wave
-  part[wv * 64 + lane] = f32x4n{acc[0], acc[1], acc[2], acc[3]};
+  // sum the waves' partial tiles; thread t < 32 * nb owns output (m, nn) with
+  // m = t / 32: lane nn + 32 * (m / 4), register m % 4 of every wave.  part
+  // overlays the weight buffers, so every wave first finishes with them.
+  __syncthreads();
+  part[wv * 64 + lane] = acc;
   __syncthreads();
   if (tid < 32 * nb) {
     const int m = tid >> 5, nn = tid & 31;
-    const int64_t r = (int64_t)blockIdx.x * 32 + nn;
+    const int64_t r = (int64_t)tile * 32 + nn;
     if (r < n) {
-      float s = 0.f;
-      for (int w = 0; w < kWaves; ++w) s += part[w * 64 + nn + 32 * (m >> 2)][m & 3];
-      Y[(int64_t)m * n + r] = s;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += part[w * 64 + nn + 32 * (m >> 2)][m & 3];
+      Y[(int64_t)m * n + r] = sum;
     }
   }
 }
+
+}  // namespace q4
 
 // ---------------------------------------------------------------------------
 // Q6_K.  A scale covers 16 values, half a Q8_1 block, so a block's MFMA
@@ -370,14 +508,15 @@ hipError_t launch_bp(const void *w, const void *xq, float *y, int32_t *D, int64_
 
 hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
                                        int64_t k, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 31) / 32));
   const uint8_t *W = static_cast<const uint8_t *>(w), *X = static_cast<const uint8_t *>(xq);
   if (D)
-    hipLaunchKernelGGL(gemv_batch_mfma_q4k<true>, grid, dim3(kThreads), lds_bytes((int)nb), stream, W, X, y, D,
-                       (int)nb, (int)n, (int)(k / 256));
+    hipLaunchKernelGGL(q4::gemv_batch_mfma_q4k<true>, grid, dim3(kThreads), q4::kLds, stream, W, X, y, D, (int)nb,
+                       (int)n, (int)(k / 256));
   else
-    hipLaunchKernelGGL(gemv_batch_mfma_q4k<false>, grid, dim3(kThreads), lds_bytes((int)nb), stream, W, X, y, D,
-                       (int)nb, (int)n, (int)(k / 256));
+    hipLaunchKernelGGL(q4::gemv_batch_mfma_q4k<false>, grid, dim3(kThreads), q4::kLds, stream, W, X, y, D, (int)nb,
+                       (int)n, (int)(k / 256));
   return hipGetLastError();
 }
 
