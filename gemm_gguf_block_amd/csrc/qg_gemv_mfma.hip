@@ -311,66 +311,58 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_batch_mfma_q4k(const uint8_t
 // carries each activation row twice: A row 2m + h holds activation row m in k
 // half h and zeros in the other half (those lanes read a zero unit in LDS).
 // Output registers 2j and 2j + 1 then hold the two sub-block dots of one
-// activation row.  They are combined with the sub-blocks' int8 scales in fp32:
-// each product is exact (a sub-block dot is at most 16 * 32 * 128 in
-// magnitude), so the pair's sum is rounded once, and not at all below 2^24.
-// (The MFMA results are read by compiler-generated code only: an inline-asm
-// reader gets none of the wait states an MFMA result needs.)
+// activation row.  They are combined with the sub-blocks' int8 scales in
+// integers (exact, at most 2^24, so the fp32 convert is exact too).  (The
+// MFMA results are read by compiler-generated code only: an inline-asm reader
+// gets none of the wait states an MFMA result needs.)
 //
 // B takes the codes as q - 32 in int8 (q6k_codes4).
 //
-// A persistent workgroup of 8 waves takes one 32-row tile at a time; wave w
-// runs superblocks w, w + 8, ... of it (all of a 4096-wide row's superblocks
-// are in flight at once), the 8 partial tiles are summed through LDS, and the
-// next tile's first superblock is loaded before that reduction.  The
-// activation rows are staged in LDS once when k fits a chunk (7168 values),
-// else once per chunk and tile.
+// Workgroups of 16 waves, one per CU, persistent; every wave owns whole
+// 32-row tiles and walks all superblocks of its tile itself, so there is no
+// reduction across waves.  The tile's 32 rows of a superblock (210 bytes
+// each, 2-byte aligned) are read as 448 16-byte pieces in address order, 14
+// per row starting at the row's superblock (the last one at byte 194, so
+// that it ends with d inside the superblock): a third as many cache lines per
+// load instruction as reading the MFMA layout straight from memory.  They go
+// to the wave's LDS buffer as [piece][row], where every field the B layout
+// needs starts a piece.  The next superblock is loaded while the current one
+// runs.  The activation rows are staged in LDS once when k fits a chunk
+// (16 superblocks), else once per chunk and round of tiles.
 namespace q6 {
 
-constexpr int kChunkBlk = 224;           // Q8_1 blocks per LDS chunk
-constexpr int kChunkSb = kChunkBlk / 8;  // superblocks per chunk
+constexpr int kWaves6 = 16;
+constexpr int kThreads6 = 64 * kWaves6;
+constexpr int kChunkSb = kWaves6;       // superblocks per chunk: one per wave
+constexpr int kChunkBlk = 8 * kChunkSb;  // Q8_1 blocks per LDS chunk
+constexpr int kPieces = 14;             // 16-byte pieces per superblock row (the last one at byte 194)
+constexpr int kWbUnits = kPieces * 33;  // per wave: [piece][row], rows padded to 33 units
 
 // Per chunk block: 2 * BP units of 16 bytes (activation row m, k half h at
 // unit 2m + h) and a zero unit; after all units, 8 d_a per block, row m at
 // position pos(m) so that lane half lh reads rows {2lh, 2lh+1, 2lh+4, 2lh+5}
-// as one group at 4 * lh; then the waves' partial tiles, BP / 2 floats per
-// lane.
+// as one group at 4 * lh; then the waves' weight buffers.
 __host__ __device__ constexpr int unit_stride(int bp) { return 2 * bp + 1; }
 __device__ __forceinline__ int pos(int m) { return (m & 1) | ((m & 2) << 1) | ((m & 4) >> 1); }
-__host__ __device__ constexpr size_t part_offset(int bp) { return (size_t)kChunkBlk * ((size_t)unit_stride(bp) * 16 + 32); }
-inline size_t lds_bytes(int bp) { return part_offset(bp) + (size_t)kWaves * 64 * (bp / 2) * 4; }
+__host__ __device__ constexpr size_t wb_offset(int bp) { return (size_t)kChunkBlk * ((size_t)unit_stride(bp) * 16 + 32); }
+inline size_t lds_bytes(int bp) { return wb_offset(bp) + (size_t)kWaves6 * kWbUnits * 16; }
 
-// One superblock as lane half lh needs it: block j (k 32j..32j+31) takes its
-// half-lh codes from ql[2(j/4) + j%2] (nibble (j/2)%2) and qh[j/4] (bit pair
-// j%4); all 16 scales and d are read by both halves.
-struct Sb {
-  u32x4 ql[4];
-  u32x4 qh[2];
-  u32x4 sc;
-  uint32_t d;
+// The same superblock of the tile's 32 rows as loaded: 448 pieces in address
+// order, lane l holding pieces l + 64q (q = 0..6).
+struct Raw {
+  u32x4 v[7];
 };
 
-__device__ __forceinline__ void load_sb(const uint8_t *p, int lh, Sb &s) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s.ql[i] = ld16_a2(p + 64 * (i >> 1) + 32 * (i & 1) + 16 * lh);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) s.qh[h] = ld16_a2(p + 128 + 32 * h + 16 * lh);
-  s.sc = ld16_a2(p + 192);
-  s.d = ld2(p + 208);
-}
-
 template <int BP, bool DUMP>
-__global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *__restrict__ W,
-                                                                const uint8_t *__restrict__ XQ,
-                                                                float *__restrict__ Y, int32_t *__restrict__ Dd,
-                                                                int nb, int n, int nsb) {
+__global__ __launch_bounds__(kThreads6) void gemv_batch_mfma_q6k(const uint8_t *W, const uint8_t *XQ, float *Y,
+                                                                 int32_t *Dd, int nb, int n, int nsb) {
   constexpr int S = unit_stride(BP);
   constexpr int NJ = BP / 2;  // activation rows per lane
   typedef float fNJ __attribute__((ext_vector_type(NJ)));
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   u32x4n *act = reinterpret_cast<u32x4n *>(lds);
   float *da = reinterpret_cast<float *>(lds + (size_t)kChunkBlk * S * 16);
-  fNJ *part = reinterpret_cast<fNJ *>(lds + part_offset(BP));
+  u32x4n *wb = reinterpret_cast<u32x4n *>(lds + wb_offset(BP)) + (threadIdx.x >> 6) * kWbUnits;
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int nl = lane & 31, lh = lane >> 5;
@@ -381,31 +373,86 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
   const int ntiles = (n + 31) / 32;
   const int nchunk = (nsb + kChunkSb - 1) / kChunkSb;
   const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  auto wrow = [&](int tile) { return W + min((int64_t)tile * 32 + nl, (int64_t)n - 1) * rb; };
+
+  // A tile's first row: the last tile is moved back to end at row n - 1
+  // (its rows that the previous tile also has come out bit-identical, and
+  // both store them), so every row read is a row of W; with n < 32 the rows
+  // past n - 1 read row n - 1 instead.
+  auto row0 = [&](int tile) __attribute__((always_inline)) { return n >= 32 ? min(tile * 32, n - 32) : 0; };
+  // this lane's pieces pc = lane + 64q: row pc / 14 of the tile, byte 16 *
+  // (pc % 14) of its superblock (the last piece at 194, so that it ends with
+  // d and stays inside the superblock); poff[q] is its byte offset from the
+  // tile's first row (k <= 2^24 keeps it within 31 bits)
+  uint32_t poff[7];
+#pragma unroll
+  for (int q = 0; q < 7; ++q) {
+    const int pc = lane + 64 * q, pr = pc / kPieces, pp = pc - kPieces * pr;
+    poff[q] = (uint32_t)(min(pr, n - 1) * (int)rb + (pp == kPieces - 1 ? 194 : 16 * pp));
+  }
+  // superblock sb of `tile` (both wave-uniform: p is a scalar base)
+  auto load_raw = [&](Raw &R, int tile, int sb) __attribute__((always_inline)) {
+    const uint8_t *p = W + (int64_t)row0(tile) * rb + (int64_t)sb * kQ6KBytes;
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      uint32_t o = poff[q];
+      asm volatile("" : "+v"(o));  // one scalar base plus a 32-bit offset per load, not hoisted 64-bit addresses
+      R.v[q] = ld16_a2(p + o);
+    }
+  };
+  // R into this wave's LDS buffer as [piece][row]; the B layout is read back
+  // from there as the blocks need it (piece pp of row nl)
+  auto put_raw = [&](const Raw &R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      const int pc = lane + 64 * q, pr = pc / kPieces, pp = pc - kPieces * pr;
+      wb[pp * 33 + pr] = u32x4n{R.v[q].x, R.v[q].y, R.v[q].z, R.v[q].w};
+    }
+  };
+  auto rd = [&](int pp) __attribute__((always_inline)) {
+    const u32x4n t = wb[pp * 33 + nl];
+    return u32x4{t.x, t.y, t.z, t.w};
+  };
 
   // zero units and the d_a of rows >= nb; never written by the staging
-  for (int t = tid; t < kChunkBlk; t += kThreads) {
+  for (int t = tid; t < kChunkBlk; t += kThreads6) {
     act[t * S + 2 * BP] = u32x4n{0u, 0u, 0u, 0u};
     for (int m = nb; m < 8; ++m) da[t * 8 + pos(m)] = 0.f;
   }
 
   // c0 and tile of the superblock being run, for the dump
   int dump_c0 = 0, dump_tile = 0;
-  auto step = [&](const Sb &w, int sbl, fNJ &acc) {
+  // One superblock of this wave's tile from its LDS buffer.  Block j + 1's
+  // MFMA is issued before block j's rescale; the code pieces of blocks 4..7
+  // replace those of blocks 0..3 once block 3's operand is built.
+  auto step = [&](int sbl, fNJ &acc) {
     fNJ p = {};
+    const u32x4 scv = rd(12);
+    const uint32_t dw = rd(13).w >> 16;
+    u32x4 ql0 = rd(lh), ql1 = rd(2 + lh), qh = rd(8 + lh);
+    auto bops = [&](int j) __attribute__((always_inline)) {
+      const u32x4 lo = (j & 1) ? ql1 : ql0, hi = qh;
+      const uint32_t ls = 4u * (uint32_t)((j >> 1) & 1), hs = 2u * (uint32_t)(j & 3);
+      return v4i{q6k_codes4(lo.x >> ls, hi.x >> hs), q6k_codes4(lo.y >> ls, hi.y >> hs),
+                 q6k_codes4(lo.z >> ls, hi.z >> hs), q6k_codes4(lo.w >> ls, hi.w >> hs)};
+    };
+    auto aops = [&](int j) __attribute__((always_inline)) {
+      return __builtin_bit_cast(v4i, act[(8 * sbl + j) * S + aunit]);
+    };
+    v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aops(0), bops(0), zero, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int blk = 8 * sbl + j;
-      const u32x4 lo = w.ql[2 * (j >> 2) + (j & 1)], hi = w.qh[j >> 2];
-      const uint32_t ls = 4u * (uint32_t)((j >> 1) & 1), hs = 2u * (uint32_t)(j & 3);
-      const v4i b = {q6k_codes4(lo.x >> ls, hi.x >> hs), q6k_codes4(lo.y >> ls, hi.y >> hs),
-                     q6k_codes4(lo.z >> ls, hi.z >> hs), q6k_codes4(lo.w >> ls, hi.w >> hs)};
-      const v4i a = __builtin_bit_cast(v4i, act[blk * S + aunit]);
-      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
+      if (j == 3) {
+        ql0 = rd(4 + lh);
+        ql1 = rd(6 + lh);
+        qh = rd(10 + lh);
+      }
+      v16i Dn = zero;
+      if (j + 1 < 8) Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(aops(j + 1), bops(j + 1), zero, 0, 0, 0);
       if (DUMP) {
         // registers 2q + h: activation row 4(q/2) + 2lh + q%2, k half h =
         // sub-block 2j + h of the superblock
-        const int64_t r = (int64_t)dump_tile * 32 + nl;
+        const int64_t r = (int64_t)row0(dump_tile) + nl;
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
           const int m = 4 * (q >> 1) + 2 * lh + (q & 1);
@@ -415,34 +462,46 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
             dp[1] = D[2 * q + 1];
           }
         }
-        asm volatile("" ::: "memory");
-        continue;
-      }
-      const uint32_t scw = w.sc[j >> 1];
-      const float sc0 = (float)sbyte(scw, 16u * (uint32_t)(j & 1));
-      const float sc1 = (float)sbyte(scw, 16u * (uint32_t)(j & 1) + 8u);
-      const fNJ dv = *reinterpret_cast<const fNJ *>(da + blk * 8 + 4 * lh);
+      } else {
+        // sc0 D0 + sc1 D1 in integers: |D| <= 16 * 32 * 128, |sc| <= 128, so
+        // the sum is at most 2^24 and exact in int32 and in its fp32 convert
+        const uint32_t scw = scv[j >> 1];
+        const int sc0 = sbyte(scw, 16u * (uint32_t)(j & 1));
+        const int sc1 = sbyte(scw, 16u * (uint32_t)(j & 1) + 8u);
+        const fNJ dv = *reinterpret_cast<const fNJ *>(da + blk * 8 + 4 * lh);
 #pragma unroll
-      for (int q = 0; q < NJ; ++q) p[q] = fmaf(dv[q], fmaf((float)D[2 * q + 1], sc1, (float)D[2 * q] * sc0), p[q]);
+        for (int q = 0; q < NJ; ++q)
+          p[q] = fmaf(dv[q], (float)(__mul24(D[2 * q + 1], sc1) + __mul24(D[2 * q], sc0)), p[q]);
+      }
       asm volatile("" : "+v"(p)::"memory");
+      D = Dn;
     }
-    acc += h2f(w.d) * p;
+    acc += h2f(dw) * p;
   };
 
-  Sb cur, nxt;
-  int tile = (int)blockIdx.x;
-  if (tile < ntiles && wv < min(kChunkSb, nsb)) load_sb(wrow(tile) + (int64_t)wv * kQ6KBytes, lh, cur);
-  for (int rnd = 0; tile < ntiles; ++rnd, tile += (int)gridDim.x) {  // tile is uniform in the workgroup
-    const uint8_t *wr = wrow(tile);
+  // Every wave owns whole tiles: wave gw = 16 blockIdx.x + wv of the grid
+  // takes tiles gw, gw + TW, ... (TW waves in the grid), one round at a time,
+  // and walks all superblocks of its tile itself, the next one loaded while
+  // the current one runs.  Past the last tile a wave repeats it and stores
+  // nothing (the rounds are uniform in the workgroup, for the staging
+  // barriers).
+  const int gw = (int)blockIdx.x * kWaves6 + __builtin_amdgcn_readfirstlane(wv);
+  const int TW = (int)gridDim.x * kWaves6;
+  const int rounds = (ntiles + TW - 1) / TW;
+  auto round_tile = [&](int r) __attribute__((always_inline)) { return min(gw + r * TW, ntiles - 1); };
+  Raw cur;
+  if (rounds > 0) load_raw(cur, round_tile(0), 0);
+  for (int r = 0; r < rounds; ++r) {
+    const int tile = round_tile(r);
+    const bool live = gw + r * TW < ntiles;
     fNJ acc = {};
     dump_tile = tile;
     for (int c0 = 0; c0 < nsb; c0 += kChunkSb) {
       const int csb = min(kChunkSb, nsb - c0);
       dump_c0 = c0;
-      if (c0 > 0 && wv < csb) load_sb(wr + (int64_t)(c0 + wv) * kQ6KBytes, lh, cur);
-      if (nchunk > 1 || rnd == 0) {
-        if (rnd > 0 || c0 > 0) __syncthreads();  // the previous chunk is no longer read
-        for (int t = tid; t < nb * 8 * csb; t += kThreads) {
+      if (nchunk > 1 || r == 0) {
+        if (r > 0 || c0 > 0) __syncthreads();  // the previous chunk is no longer read
+        for (int t = tid; t < nb * 8 * csb; t += kThreads6) {
           const int m = t / (8 * csb), blk = t - m * (8 * csb);
           const uint8_t *ap = XQ + m * xrb + (int64_t)(8 * c0 + blk) * kQ8_1Bytes;
           const u32x4 v0 = ld16(ap), v1 = ld16(ap + 16);
@@ -453,35 +512,24 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_mfma_q6k(const uint8_t *_
         }
         __syncthreads();
       }
-      // superblocks wv, wv + 8, ... of the chunk, the next one loaded ahead
-      for (int s = wv; s < csb; s += 2 * kWaves) {
-        if (s + kWaves < csb) load_sb(wr + (int64_t)(c0 + s + kWaves) * kQ6KBytes, lh, nxt);
-        step(cur, s, acc);
-        if (s + kWaves >= csb) break;
-        if (s + 2 * kWaves < csb) load_sb(wr + (int64_t)(c0 + s + 2 * kWaves) * kQ6KBytes, lh, cur);
-        step(nxt, s + kWaves, acc);
+#pragma unroll 1
+      for (int sl = 0; sl < csb; ++sl) {
+        put_raw(cur);
+        // the next superblock of this wave: this tile's next, else the next round's first
+        if (c0 + sl + 1 < nsb) load_raw(cur, tile, c0 + sl + 1);
+        else if (r + 1 < rounds) load_raw(cur, round_tile(r + 1), 0);
+        step(sl, acc);
       }
     }
-    const int next = tile + (int)gridDim.x;
-    if (next < ntiles && wv < min(kChunkSb, nsb)) load_sb(wrow(next) + (int64_t)wv * kQ6KBytes, lh, cur);
-    if (DUMP) continue;  // tile is uniform in the workgroup: no barrier is skipped by part of it
-    // sum the waves' partial tiles: thread t < 32 * nb owns activation row
-    // m = t / 32, weight row nn = t % 32, held by lane nn + 32 * ((m / 2) % 2),
-    // element (m % 2) + 2 * (m / 4) of every wave
-    part[wv * 64 + lane] = acc;
-    __syncthreads();
-    if (tid < 32 * nb) {
-      const int m = tid >> 5, nn = tid & 31;
-      const int src = nn + 32 * ((m >> 1) & 1), q = (m & 1) + 2 * (m >> 2);
-      const int64_t r = (int64_t)tile * 32 + nn;
-      if (r < n) {
-        float sum = 0.f;
+    if (DUMP || !live) continue;
+    // element q of acc: activation row 4(q/2) + 2lh + q%2, weight row
+    // row0(tile) + nl
+    const int64_t row = (int64_t)row0(tile) + nl;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += part[w * 64 + src][q];
-        Y[(int64_t)m * n + r] = sum;
-      }
+    for (int q = 0; q < NJ; ++q) {
+      const int m = 4 * (q >> 1) + 2 * lh + (q & 1);
+      if (m < nb && row < n) Y[(int64_t)m * n + row] = acc[q];
     }
-    __syncthreads();  // part is rewritten next round
   }
 }
 
@@ -490,14 +538,15 @@ template <int BP>
 hipError_t launch_bp(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n, int64_t k,
                      hipStream_t stream) {
   const size_t lds = lds_bytes(BP);
-  const int64_t groups = (n + 31) / 32;
-  const int64_t g = std::min(groups, resident_blocks<gemv_batch_mfma_q6k<BP, false>>(kThreads, lds));
+  const int64_t waves = (n + 31) / 32;  // one per tile at most
+  const int64_t g = std::min((waves + kWaves6 - 1) / kWaves6,
+                             resident_blocks<gemv_batch_mfma_q6k<BP, false>>(kThreads6, lds));
   const uint8_t *W = static_cast<const uint8_t *>(w), *X = static_cast<const uint8_t *>(xq);
   if (D)
-    hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP, true>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, D,
+    hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP, true>), dim3((unsigned)g), dim3(kThreads6), lds, stream, W, X, y, D,
                        (int)nb, (int)n, (int)(k / 256));
   else
-    hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP, false>), dim3((unsigned)g), dim3(kThreads), lds, stream, W, X, y, D,
+    hipLaunchKernelGGL((gemv_batch_mfma_q6k<BP, false>), dim3((unsigned)g), dim3(kThreads6), lds, stream, W, X, y, D,
                        (int)nb, (int)n, (int)(k / 256));
   return hipGetLastError();
 }
