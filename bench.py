@@ -226,8 +226,9 @@ class GemvBatch(Gemv):
         self.xq = torch.empty((self.b, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
         self.y = torch.empty((self.b, self.n), dtype=torch.float32, device=dev)
         self.fn = getattr(qg, "qgemv_" + self.fmt + "_batch")
-        # the kernel the library dispatches to (matrix cores for K-quants above 4 rows)
-        self.dominant = (f"gemv_batch_mfma_{self.fmt.replace('_', '')}" if self.b > 4 and self.fmt != "q8_0"
+        # the kernel the library dispatches to (matrix cores for Q4_K from 5 rows, Q6_K from 3)
+        mfma = (self.fmt == "q4_k" and self.b > 4) or (self.fmt == "q6_k" and self.b > 2)
+        self.dominant = (f"gemv_batch_mfma_{self.fmt.replace('_', '')}" if mfma
                          else "gemv_batch_kernel")
         wbytes = self.w_host.nbytes
         self.kernel_bytes = wbytes + self.b * (q81_bytes(self.k) + 4 * self.n)

@@ -315,7 +315,7 @@ def _blockdots_ref(orc, fmt, w, xq, n, k):
 @pytest.mark.parametrize("n,k", [(65, 256), (130, 768), (33, 14336), (5, 33536)])
 def test_gemv_batch_block_dots_exact(env, fmt, b, n, k):
     """Exact int32 dots of the kernel each b dispatches to (v_dot4 up to 4
-    rows; matrix cores from 5 rows for the K-quants), on fully random bytes."""
+    rows; matrix cores from 5 rows for Q4_K and from 3 for Q6_K), on fully random bytes."""
     qg, orc, torch, dev = env
     w = synth.random_blocks(fmt, n, k, seed=7 * n + b)
     xq = synth.random_blocks("q8_1", b, k, seed=11 * n + b)
