@@ -240,6 +240,26 @@ def test_gemv_batch_values(env, fmt, b, n, k):
         assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
 
 
+@pytest.mark.parametrize("b", [2, 4, 8])
+@pytest.mark.parametrize("n,k", [(9, 96), (70, 800), (33, 4128)])
+def test_gemv_batch_q8_0_odd_block_count(env, b, n, k):
+    """Q8_0 rows with an odd block count take the single-block path (an even
+    count is read in block pairs): values against the oracle and exact dots."""
+    qg, orc, torch, dev = env
+    assert (k // 32) % 2 == 1
+    w = synth.weights("q8_0", n, k, seed=5 * n + k)
+    x = synth.normal(3 * n + k + b, 1, (b, k))
+    X = qg.quantize_q8_1(_gpu(torch, dev, x))
+    W = _gpu(torch, dev, w)
+    y = _host(qg.qgemv_q8_0_batch(W, X, b, n, k))
+    xq = orc.quantize_q8_1(x)
+    for i in range(b):
+        assert rel_err(y[i], orc.qgemv("q8_0", w, xq[i], n, k)) <= REL_TOL, f"row {i}"
+    D = _host(qg.blockdots_batch("q8_0", W, X, b, n, k))
+    for i in range(b):
+        assert np.array_equal(D[i], orc.blockdots("q8_0", w, xq[i], n, k)), f"activation row {i}"
+
+
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
 def test_gemv_batch_values_random_bytes(env, fmt):
     qg, orc, torch, dev = env
