@@ -94,8 +94,10 @@ __device__ __forceinline__ void stage_batch(uint8_t *lds, const uint8_t *__restr
       hi = u32x4n{v1.y, v1.z, v1.w, v2};
       d = h2f(v0.x);
     }
-    const int slo = bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0))));
-    const int shi = bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x, 0))));
+    // code sums (the min and offset terms of the K-quants; Q8_0 has none)
+    const bool sums = FMT == kFmtQ4K || FMT == kFmtQ6K;
+    const int slo = sums ? bsum4(lo.w, bsum4(lo.z, bsum4(lo.y, bsum4(lo.x, 0)))) : 0;
+    const int shi = sums ? bsum4(hi.w, bsum4(hi.z, bsum4(hi.y, bsum4(hi.x, 0)))) : 0;
     if (FMT == kFmtQ8_0) {
       qs[(i * NP + 0) * U + blk] = lo;
       qs[(i * NP + 1) * U + blk] = hi;
@@ -106,7 +108,7 @@ __device__ __forceinline__ void stage_batch(uint8_t *lds, const uint8_t *__restr
       qs[(i * NP + 2 * bb + 1) * U + u] = hi;
       float *r = reinterpret_cast<float *>(rec) + 4 * (i * U + u);
       r[bb] = d;
-      r[2 + bb] = d * (float)(slo + shi);
+      if (FMT == kFmtQ4K) r[2 + bb] = d * (float)(slo + shi);
     } else {
       const int sbl = blk >> 3, h = (blk >> 2) & 1, g = blk & 3;
       const int u0 = 4 * sbl + 2 * h;  // unit of half 0; half 1 is u0 + 1
