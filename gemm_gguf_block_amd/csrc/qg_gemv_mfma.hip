@@ -75,8 +75,10 @@ static_assert(kWaves * 64 <= kWaves * kWbUnits, "the partial tiles fit in the we
 static_assert(2 * kLds <= 160 * 1024, "two workgroups per CU");
 constexpr int kStageIters = (8 * kChunkBlk + kThreads - 1) / kThreads;
 
-// One superblock of one weight row as lane half lh needs it: the 16-byte
-// header and the 16 code bytes of each 32-byte group that fall in half lh.
+// Five 16-byte pieces of one superblock.  As loaded (load_sb): the lane's
+// address-ordered pieces l + 64q of the tile's 32 rows.  After to_mfma: what
+// lane l needs in the B layout, the header of row l%32 and, per 32-byte code
+// group, the 16 bytes that fall in k half l/32.
 struct Sb {
   u32x4 hdr, q[4];
 };
