@@ -331,7 +331,7 @@ def _blockdots_ref(orc, fmt, w, xq, n, k):
 
 
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_k", "q6_k"])
-@pytest.mark.parametrize("b", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(65, 256), (130, 768), (33, 14336), (5, 33536)])
 def test_gemv_batch_block_dots_exact(env, fmt, b, n, k):
     """Exact int32 dots of the kernel each b dispatches to (v_dot4 up to 4
