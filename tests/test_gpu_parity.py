@@ -766,8 +766,9 @@ def _check_hq_ties(orc, ref, hq_g, valid, F):
 
 
 def _record(name, rec):
-    """Keeps a parity measurement: in gpurun_out/ when that folder exists, and
-    as a warning (pytest prints those in its summary)."""
+    """Keeps a parity measurement: as a JSON file in the repository's run-output
+    folder when that folder exists, and as a warning (pytest prints those in
+    its summary)."""
     import json
     import os
     import warnings
