@@ -481,8 +481,10 @@ def _check_rmsnorm_stagewise(orc, x, gamma, eps, xq_gpu, r_gpu):
     assert np.array_equal(xq_gpu, orc.quantize_q8_1(v))
 
 
-@pytest.mark.parametrize("rows,k,std", [(1, 32, 1.0), (3, 4096, 1.0), (2, 14336, 1e-3), (5, 768, 30.0),
-                                        (2, 33536, 1.0)])
+# k <= 4096 keeps the row in registers; 4128 and up read it again, 4128 with a
+# remainder past the four-load rounds of the first step
+@pytest.mark.parametrize("rows,k,std", [(1, 32, 1.0), (2, 64, 1.0), (3, 4096, 1.0), (2, 4128, 1.0),
+                                        (2, 14336, 1e-3), (5, 768, 30.0), (2, 33536, 1.0)])
 def test_rmsnorm_quantize_stagewise(env, rows, k, std):
     qg, orc, torch, dev = env
     x = synth.normal(rows + k, 4, (rows, k), std=std)
