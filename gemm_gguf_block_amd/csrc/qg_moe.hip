@@ -503,7 +503,7 @@ __global__ __launch_bounds__(512) void moe_down_token_kernel(
   // thread takes up to kActUnroll quads per round, all their g|u loads issued
   // before any is used (a round is uniform over each 8-thread group: the
   // quad count and the thread stride are multiples of 8).
-  constexpr int kActUnroll = 2;
+  constexpr int kActUnroll = 3;  // 8 slots of 768 values: every quad of a thread in one round
   for (int q0 = tid; q0 < nv * nq; q0 += kActUnroll * NT) {
     float4 g4[kActUnroll], u4[kActUnroll];
 #pragma unroll
