@@ -105,7 +105,7 @@ BATCH_WORKLOADS = ["q8_0_gemv_b8", "q4_k_gemv_b2", "q4_k_gemv_b4", "q4_k_gemv_b8
 
 def _sources(workload):
     if "_gemv_b" in workload:
-        return ["qg_gemv_batch.hip"] if workload.startswith("q8_0") else ["qg_gemv_batch.hip", "qg_gemv_mfma.hip"]
+        return ["qg_gemv_batch.hip", "qg_gemv_mfma.hip"]
     return KERNEL_SOURCES[workload]
 
 
@@ -227,9 +227,10 @@ class GemvBatch(Gemv):
         self.y = torch.empty((self.b, self.n), dtype=torch.float32, device=dev)
         self.fn = getattr(qg, "qgemv_" + self.fmt + "_batch")
         # the kernel the library dispatches to (matrix cores for Q4_K from 5 rows, Q6_K from 3)
-        mfma = (self.fmt == "q4_k" and self.b > 4) or (self.fmt == "q6_k" and self.b > 2)
-        self.dominant = (f"gemv_batch_mfma_{self.fmt.replace('_', '')}" if mfma
-                         else "gemv_batch_kernel")
+        # the kernel the batch call dispatches to at these shapes (k a multiple of 256)
+        mfma = (self.fmt in ("q8_0", "q4_k") and self.b > 4) or (self.fmt == "q6_k" and self.b > 2)
+        self.dominant = ({"q8_0": "gemv_batch_mfma_q8_0", "q4_k": "gemv_batch_mfma_q4k",
+                          "q6_k": "gemv_batch_mfma_q6k"}[self.fmt] if mfma else "gemv_batch_kernel")
         wbytes = self.w_host.nbytes
         self.kernel_bytes = wbytes + self.b * (q81_bytes(self.k) + 4 * self.n)
         self.step_bytes = self.kernel_bytes + self.b * (4 * self.k + q81_bytes(self.k))

@@ -1,4 +1,5 @@
-// qg_gemv_mfma.hip -- small-batch Q4_K and Q6_K GEMV on the int8 matrix cores.
+// qg_gemv_mfma.hip -- small-batch Q4_K, Q6_K and Q8_0 GEMV on the int8 matrix
+// cores.
 //
 // With b <= 8 activation rows the dot4 kernels spend VALU per (row, block,
 // activation row).  Here the activation rows form the M side of
@@ -12,7 +13,8 @@
 // registers r = 0..3 carry rows (4(lane/32) + r).
 //
 // With DUMP the same code writes the exact int32 dots of every MFMA instead of
-// Y: D[i][r][block] per 32-value block (Q4_K) or per 16-value sub-block (Q6_K).
+// Y: D[i][r][block] per 32-value block (Q4_K, Q8_0) or per 16-value sub-block
+// (Q6_K).  (Q8_0 runs 16-row tiles on v_mfma_i32_16x16x64_i8; see below.)
 #include "qg_blocks.h"
 #include "qg_launch.h"
 
@@ -555,6 +557,196 @@ hipError_t launch_bp(const void *w, const void *xq, float *y, int32_t *D, int64_
 
 }  // namespace q6
 
+// ---------------------------------------------------------------------------
+// Q8_0 (k a multiple of 256).  A workgroup of 16 waves owns a tile of 16
+// weight rows: 4096 rows give 256 workgroups.  v_mfma_i32_16x16x64_i8 takes
+// two blocks per instruction: A rows 0-7 hold the activation rows in k 0..31
+// (block j) and zeros in k 32..63, rows 8-15 the same rows in k 32..63 (block
+// j + 1) and zeros below, so output rows 0-7 are block j's dots and 8-15 block
+// j + 1's.  Register r of lane l is output row 4(l/16) + r, column l%16: the
+// lane holds activation rows 4((l/16)%2) + r of block j + l/32 against weight
+// row l%16, and its B operand is that same weight row and block (16 of the
+// code bytes, k half (l/16)%2).
+//
+// Weights: 8 blocks of a row are 272 bytes, 16-byte aligned; the tile's 16
+// rows of them are 272 pieces of 16 bytes.  Wave w takes blocks 8w..8w+7 of
+// every 128-block activation chunk, loads the pieces in address order (lane l:
+// pieces l + 64q), and writes them to its LDS buffer as [dword][row] (rows
+// padded to 17).  A block's 32 code bytes start 2 bytes past its d, so a lane
+// reads its 16 bytes as five dwords and realigns them with v_alignbyte.
+namespace q8 {
+
+constexpr int kWaves8 = 16;
+constexpr int kThreads8 = 64 * kWaves8;
+constexpr int kChunkBlk = 8 * kWaves8;       // activation blocks per staged chunk
+constexpr int kRowPad = 17;                  // 16 rows + 1
+constexpr int kWbDwords = 68 * kRowPad;      // per wave: 68 dwords of each of 16 rows
+constexpr size_t kZeroUnit = (size_t)kChunkBlk * 8 * 2;  // act unit index of a zero unit
+constexpr size_t kDaOff = (kZeroUnit + 1) * 16;
+constexpr size_t kWbOff = kDaOff + (size_t)kChunkBlk * 8 * 4;
+constexpr size_t kPartOff = kWbOff;  // the partial tiles reuse the weight buffers
+constexpr size_t kLds = kWbOff + (size_t)kWaves8 * kWbDwords * 4;
+static_assert(kWaves8 * 64 * 16 <= kWaves8 * kWbDwords * 4, "the partial tiles fit in the weight buffers");
+static_assert(kLds <= 160 * 1024, "one workgroup per CU");
+
+// W and XQ are not declared __restrict__, as in the Q4_K kernel: the loads
+// then stay in the order written around the staging barrier.
+template <bool DUMP>
+__global__ __launch_bounds__(kThreads8) void gemv_batch_mfma_q8_0(const uint8_t *W, const uint8_t *XQ, float *Y,
+                                                                  int32_t *Dd, int nb, int n, int nblk) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  u32x4n *act = reinterpret_cast<u32x4n *>(lds);  // [blk][m][half], 16 bytes
+  float *da = reinterpret_cast<float *>(lds + kDaOff);
+  uint32_t *wb = reinterpret_cast<uint32_t *>(lds + kWbOff) + (threadIdx.x >> 6) * kWbDwords;
+  f32x4n *part = reinterpret_cast<f32x4n *>(lds + kPartOff);
+
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int nl = lane & 15, sl = lane >> 4;  // weight row in the tile (B column) / k slice; A row is nl too
+  const int tile = (int)blockIdx.x;
+  const int64_t rb = (int64_t)nblk * kQ8_0Bytes;
+  const int64_t xrb = (int64_t)nblk * kQ8_1Bytes;
+  const int nsub = nblk / 8;  // 8-block pieces of a row
+  const int nchunk = (nblk + kChunkBlk - 1) / kChunkBlk;
+  const v4i izero = {0, 0, 0, 0};
+
+  // this lane's pieces: pc = lane + 64q (the last 48 lanes of q = 4 repeat
+  // piece 271), row pc / 17, piece pc % 17; rows past n read row n - 1.
+  // Offsets from the tile's first row, k <= 2^24 keeping them in 32 bits.
+  uint32_t goff[5];
+  {
+    const int rowlim = n - 1 - tile * 16;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int pc = min(lane + 64 * q, 271), pr = pc / 17, pp = pc - 17 * pr;
+      goff[q] = (uint32_t)(min(pr, rowlim) * (int)rb + 16 * pp);
+    }
+  }
+  const uint8_t *tw = W + (int64_t)tile * 16 * rb;
+  u32x4 P[5];
+  // the wave's 8 blocks of chunk c (past the row's end: its last 8, never used)
+  auto load_w = [&](int c) __attribute__((always_inline)) {
+    const uint8_t *p = tw + (int64_t)min(c * kWaves8 + wv, nsub - 1) * 272;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) P[q] = ld16(p + goff[q]);
+  };
+  auto put_w = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int pc = lane + 64 * q;
+      if (pc < 272) {
+        const int pr = pc / 17, pp = pc - 17 * pr;
+        uint32_t *d = wb + (4 * pp) * kRowPad + pr;
+        d[0] = P[q].x;
+        d[kRowPad] = P[q].y;
+        d[2 * kRowPad] = P[q].z;
+        d[3 * kRowPad] = P[q].w;
+      }
+    }
+  };
+
+  // Activation staging of chunk c: item t = (row m, block) with its loads first.
+  constexpr int kStageIters = (8 * kChunkBlk + kThreads8 - 1) / kThreads8;
+  u32x4 sv0[kStageIters], sv1[kStageIters];
+  uint32_t sv2[kStageIters];
+  auto stage_load = [&](int c) __attribute__((always_inline)) {
+    const int b0 = c * kChunkBlk, cb = min(kChunkBlk, nblk - b0), items = nb * cb;
+#pragma unroll
+    for (int it = 0; it < kStageIters; ++it) {
+      const int t = min(tid + it * kThreads8, items - 1);
+      const int m = t / cb, blk = t - m * cb;
+      const uint8_t *ap = XQ + m * xrb + (int64_t)(b0 + blk) * kQ8_1Bytes;
+      sv0[it] = ld16(ap);
+      sv1[it] = ld16(ap + 16);
+      sv2[it] = ld4(ap + 32);
+    }
+  };
+  auto stage_write = [&](int c) __attribute__((always_inline)) {
+    const int b0 = c * kChunkBlk, cb = min(kChunkBlk, nblk - b0), items = nb * cb;
+#pragma unroll
+    for (int it = 0; it < kStageIters; ++it) {
+      const int t = min(tid + it * kThreads8, items - 1);
+      const int m = t / cb, blk = t - m * cb;
+      const u32x4 v0 = sv0[it], v1 = sv1[it];
+      act[(blk * 8 + m) * 2] = u32x4n{v0.y, v0.z, v0.w, v1.x};
+      act[(blk * 8 + m) * 2 + 1] = u32x4n{v1.y, v1.z, v1.w, sv2[it]};
+      da[blk * 8 + m] = h2f(v0.x);
+    }
+  };
+
+  f32x4n acc = {0.f, 0.f, 0.f, 0.f};
+  // the wave's 8 blocks (chunk-local blocks 8wv .. 8wv + 7) from its buffer
+  auto run = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+      // B: weight row nl, block jj = 2jp + sl/2, k half sl%2
+      const int jj = 2 * jp + (sl >> 1);
+      const int o = 34 * jj + 2 + 16 * (sl & 1), w0 = o >> 2;
+      const uint32_t sh = (uint32_t)(o & 3);
+      uint32_t x[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) x[i] = wb[min(w0 + i, 67) * kRowPad + nl];
+      const v4i bv = {(int)align_bytes(x[1], x[0], sh), (int)align_bytes(x[2], x[1], sh),
+                      (int)align_bytes(x[3], x[2], sh), (int)align_bytes(x[4], x[3], sh)};
+      const uint32_t dword = wb[((34 * jj) >> 2) * kRowPad + nl];
+      const float dw = h2f((jj & 1) ? (dword >> 16) : dword);
+      // A: row nl = activation row nl % 8 of block 2jp + nl/8, nonzero in
+      // the k slices of that block only
+      const bool av = (sl >> 1) == (nl >> 3);
+      const int ab = 8 * wv + 2 * jp + (nl >> 3);
+      const u32x4n a = act[av ? (size_t)((ab * 8 + (nl & 7)) * 2 + (sl & 1)) : kZeroUnit];
+      const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), bv, izero, 0, 0, 0);
+      const int bo = 8 * wv + 2 * jp + (lane >> 5);  // this lane's output block (chunk-local)
+      const int m0 = 4 * (sl & 1);
+      if (DUMP) {
+        const int64_t row = (int64_t)tile * 16 + nl;
+        const int64_t blk = (int64_t)c * kChunkBlk + bo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (m0 + r < nb && row < n) Dd[((int64_t)(m0 + r) * n + row) * nblk + blk] = D[r];
+      } else {
+        const f32x4n a4 = *reinterpret_cast<const f32x4n *>(da + bo * 8 + m0);
+        acc.x = fmaf(dw * a4.x, (float)D[0], acc.x);
+        acc.y = fmaf(dw * a4.y, (float)D[1], acc.y);
+        acc.z = fmaf(dw * a4.z, (float)D[2], acc.z);
+        acc.w = fmaf(dw * a4.w, (float)D[3], acc.w);
+      }
+    }
+  };
+
+  if (tid == 0) act[kZeroUnit] = u32x4n{0u, 0u, 0u, 0u};
+  for (int c = 0; c < nchunk; ++c) {
+    if (c > 0) __syncthreads();  // the previous chunk is no longer read
+    stage_load(c);
+    asm volatile("" ::: "memory");
+    load_w(c);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);  // nothing that waits for the activation moves above the weight loads
+    stage_write(c);
+    __syncthreads();
+    put_w();  // the wave's own buffer: its LDS accesses complete in order
+    if (c * kWaves8 + wv < nsub) run(c);
+  }
+  if (DUMP) return;
+  // sum the waves' partial tiles and both block parities: output (m, row
+  // nn) is register m%4 of lanes nn + 16(m/4) and nn + 16(m/4) + 32
+  __syncthreads();
+  part[wv * 64 + lane] = acc;
+  __syncthreads();
+  if (tid < 16 * nb) {
+    const int m = tid >> 4, nn = tid & 15;
+    const int64_t r = (int64_t)tile * 16 + nn;
+    if (r < n) {
+      const int l0 = nn + 16 * (m >> 2);
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves8; ++w) sum += part[w * 64 + l0][m & 3] + part[w * 64 + l0 + 32][m & 3];
+      Y[(int64_t)m * n + r] = sum;
+    }
+  }
+}
+
+}  // namespace q8
+
 }  // namespace
 
 hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
@@ -568,6 +760,20 @@ hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, 
   else
     hipLaunchKernelGGL(q4::gemv_batch_mfma_q4k<false>, grid, dim3(kThreads), q4::kLds, stream, W, X, y, D, (int)nb,
                        (int)n, (int)(k / 256));
+  return hipGetLastError();
+}
+
+hipError_t launch_qgemv_batch_mfma_q8_0(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                                        int64_t k, hipStream_t stream) {
+  if (n == 0 || nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 15) / 16));
+  const uint8_t *W = static_cast<const uint8_t *>(w), *X = static_cast<const uint8_t *>(xq);
+  if (D)
+    hipLaunchKernelGGL(q8::gemv_batch_mfma_q8_0<true>, grid, dim3(q8::kThreads8), q8::kLds, stream, W, X, y, D,
+                       (int)nb, (int)n, (int)(k / 32));
+  else
+    hipLaunchKernelGGL(q8::gemv_batch_mfma_q8_0<false>, grid, dim3(q8::kThreads8), q8::kLds, stream, W, X, y, D,
+                       (int)nb, (int)n, (int)(k / 32));
   return hipGetLastError();
 }
 

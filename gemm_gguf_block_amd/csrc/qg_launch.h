@@ -50,6 +50,8 @@ hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, 
                               int64_t k, hipStream_t stream);
 
 // Small-batch Q4_K / Q6_K GEMV on the int8 matrix cores (nb <= 8); D as above.
+hipError_t launch_qgemv_batch_mfma_q8_0(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
+                                        int64_t k, hipStream_t stream);
 hipError_t launch_qgemv_batch_mfma_q4k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,
                                        int64_t k, hipStream_t stream);
 hipError_t launch_qgemv_batch_mfma_q6k(const void *w, const void *xq, float *y, int32_t *D, int64_t nb, int64_t n,

@@ -240,13 +240,15 @@ def test_gemv_batch_values(env, fmt, b, n, k):
         assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
 
 
-@pytest.mark.parametrize("b", [2, 4, 8])
-@pytest.mark.parametrize("n,k", [(9, 96), (70, 800), (33, 4128)])
-def test_gemv_batch_q8_0_odd_block_count(env, b, n, k):
-    """Q8_0 rows with an odd block count take the single-block path (an even
-    count is read in block pairs): values against the oracle and exact dots."""
+@pytest.mark.parametrize("b", [2, 4, 5, 8])
+@pytest.mark.parametrize("n,k", [(9, 96), (70, 800), (33, 4128), (40, 320), (33, 4160)])
+def test_gemv_batch_q8_0_block_counts(env, b, n, k):
+    """Q8_0 rows whose block count is odd take the single-block path, and an
+    even count that is not a multiple of 8 the block-pair path at every b (the
+    matrix-core kernel needs k to be a multiple of 256): values against the
+    oracle and exact dots."""
     qg, orc, torch, dev = env
-    assert (k // 32) % 2 == 1
+    assert (k // 32) % 8 != 0
     w = synth.weights("q8_0", n, k, seed=5 * n + k)
     x = synth.normal(3 * n + k + b, 1, (b, k))
     X = qg.quantize_q8_1(_gpu(torch, dev, x))
@@ -335,7 +337,8 @@ def _blockdots_ref(orc, fmt, w, xq, n, k):
 @pytest.mark.parametrize("n,k", [(65, 256), (130, 768), (33, 14336), (5, 33536)])
 def test_gemv_batch_block_dots_exact(env, fmt, b, n, k):
     """Exact int32 dots of the kernel each b dispatches to (v_dot4 up to 4
-    rows; matrix cores from 5 rows for Q4_K and from 3 for Q6_K), on fully random bytes."""
+    rows; matrix cores from 5 rows for Q8_0 and Q4_K and from 3 for Q6_K), on
+    fully random bytes."""
     qg, orc, torch, dev = env
     w = synth.random_blocks(fmt, n, k, seed=7 * n + b)
     xq = synth.random_blocks("q8_1", b, k, seed=11 * n + b)
