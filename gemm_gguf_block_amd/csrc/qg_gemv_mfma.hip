@@ -571,16 +571,18 @@ hipError_t launch_bp(const void *w, const void *xq, float *y, int32_t *D, int64_
 // Weights: 8 blocks of a row are 272 bytes, 16-byte aligned; the tile's 16
 // rows of them are 272 pieces of 16 bytes.  Wave w takes blocks 8w..8w+7 of
 // every 128-block activation chunk, loads the pieces in address order (lane l:
-// pieces l + 64q), and writes them to its LDS buffer as [dword][row] (rows
+// pieces l + 64q), and writes them to its LDS buffer as [piece][row] (rows
 // padded to 17).  A block's 32 code bytes start 2 bytes past its d, so a lane
-// reads its 16 bytes as five dwords and realigns them with v_alignbyte.
+// reads the two pieces its 16 bytes fall in and shifts them into place: by a
+// whole number of dwords for an odd block, with v_alignbyte for an even one
+// (the offsets are fixed per block pair, one choice per lane half).
 namespace q8 {
 
 constexpr int kWaves8 = 16;
 constexpr int kThreads8 = 64 * kWaves8;
 constexpr int kChunkBlk = 8 * kWaves8;       // activation blocks per staged chunk
 constexpr int kRowPad = 17;                  // 16 rows + 1
-constexpr int kWbDwords = 68 * kRowPad;      // per wave: 68 dwords of each of 16 rows
+constexpr int kWbDwords = 68 * kRowPad;      // per wave: 17 pieces (68 dwords) of each of 16 rows
 constexpr size_t kZeroUnit = (size_t)kChunkBlk * 8 * 2;  // act unit index of a zero unit
 constexpr size_t kDaOff = (kZeroUnit + 1) * 16;
 constexpr size_t kWbOff = kDaOff + (size_t)kChunkBlk * 8 * 4;
@@ -635,11 +637,7 @@ __global__ __launch_bounds__(kThreads8) void gemv_batch_mfma_q8_0(const uint8_t 
       const int pc = lane + 64 * q;
       if (pc < 272) {
         const int pr = pc / 17, pp = pc - 17 * pr;
-        uint32_t *d = wb + (4 * pp) * kRowPad + pr;
-        d[0] = P[q].x;
-        d[kRowPad] = P[q].y;
-        d[2 * kRowPad] = P[q].z;
-        d[3 * kRowPad] = P[q].w;
+        reinterpret_cast<u32x4n *>(wb)[pp * kRowPad + pr] = u32x4n{P[q].x, P[q].y, P[q].z, P[q].w};
       }
     }
   };
@@ -680,14 +678,21 @@ __global__ __launch_bounds__(kThreads8) void gemv_batch_mfma_q8_0(const uint8_t 
     for (int jp = 0; jp < 4; ++jp) {
       // B: weight row nl, block jj = 2jp + sl/2, k half sl%2
       const int jj = 2 * jp + (sl >> 1);
-      const int o = 34 * jj + 2 + 16 * (sl & 1), w0 = o >> 2;
-      const uint32_t sh = (uint32_t)(o & 3);
-      uint32_t x[5];
+      const int o = 34 * jj + 2 + 16 * (sl & 1), p0 = o >> 4;
+      const u32x4n *wu = reinterpret_cast<const u32x4n *>(wb);
+      const u32x4n u0 = wu[p0 * kRowPad + nl], u1 = wu[min(p0 + 1, 16) * kRowPad + nl];
+      const uint32_t X[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      // the byte shift within the two pieces: (4jp + 2) mod 16 for the even
+      // block (lanes with sl < 2), (4jp + 4) mod 16 for the odd one
+      const int se = (4 * jp + 2) & 15, so = (4 * jp + 4) & 15;
+      v4i bv;
 #pragma unroll
-      for (int i = 0; i < 5; ++i) x[i] = wb[min(w0 + i, 67) * kRowPad + nl];
-      const v4i bv = {(int)align_bytes(x[1], x[0], sh), (int)align_bytes(x[2], x[1], sh),
-                      (int)align_bytes(x[3], x[2], sh), (int)align_bytes(x[4], x[3], sh)};
-      const uint32_t dword = wb[((34 * jj) >> 2) * kRowPad + nl];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t ev = align_bytes(X[(se >> 2) + i + 1], X[(se >> 2) + i], 2);
+        const uint32_t od = X[(so >> 2) + i];
+        bv[i] = (int)((sl >> 1) ? od : ev);
+      }
+      const uint32_t dword = wb[(((34 * jj) >> 4) * kRowPad + nl) * 4 + (((34 * jj) & 15) >> 2)];
       const float dw = h2f((jj & 1) ? (dword >> 16) : dword);
       // A: row nl = activation row nl % 8 of block 2jp + nl/8, nonzero in
       // the k slices of that block only
