@@ -422,13 +422,13 @@ hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, 
   const uint8_t *W = static_cast<const uint8_t *>(w);
   const uint8_t *X = static_cast<const uint8_t *>(xq);
   const int nblk = (int)(k / 32);
-  // Q8_0: int8 MFMA from 5 rows when k is a multiple of 256 and the weights
-  // 16-byte aligned (same process, us at 4096 x 4096: b = 8 7.67 -> 7.14; b =
-  // 4 6.58 against 7.12 and b = 2 5.69 against 7.07 stay on v_dot4); else
-  // aligned block pairs against single 2-byte-aligned blocks (b = 2 6.65 ->
-  // 5.72, b = 4 6.98 -> 6.81, b = 8 7.79 -> 7.69)
-  if (fmt == 0 && nb > 4 && nblk % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0)
-    return launch_qgemv_batch_mfma_q8_0(w, xq, y, D, nb, n, k, stream);
+  // Q8_0: int8 MFMA from 5 rows when k is a multiple of 256, so that 8 blocks
+  // of a row are 16-byte aligned (the entry points require w to be) (same
+  // process, us at 4096 x 4096: b = 8 7.67 -> 6.73; b = 4 6.58 against 7.12
+  // and b = 2 5.69 against 7.07 stay on v_dot4); else aligned block pairs
+  // against single 2-byte-aligned blocks (b = 2 6.65 -> 5.72, b = 4 6.98 ->
+  // 6.81, b = 8 7.79 -> 7.69)
+  if (fmt == 0 && nb > 4 && nblk % 8 == 0) return launch_qgemv_batch_mfma_q8_0(w, xq, y, D, nb, n, k, stream);
   if (fmt == 0 && nblk % 2 == 0) return launch_fmt<kFmtQ8P>(W, X, y, D, (int)nb, n, nblk, stream);
   if (fmt == 0) return launch_fmt<kFmtQ8_0>(W, X, y, D, (int)nb, n, nblk, stream);
   // Measured on MI355X (k = 4096, us per call): Q4_K 14336 rows takes
