@@ -226,9 +226,9 @@ class GemvBatch(Gemv):
         self.xq = torch.empty((self.b, q81_bytes(self.k)), dtype=torch.uint8, device=dev)
         self.y = torch.empty((self.b, self.n), dtype=torch.float32, device=dev)
         self.fn = getattr(qg, "qgemv_" + self.fmt + "_batch")
-        # the kernel the library dispatches to (matrix cores for Q4_K from 5 rows, Q6_K from 3)
-        # the kernel the batch call dispatches to at these shapes (k a multiple of 256)
-        mfma = (self.fmt in ("q8_0", "q4_k") and self.b > 4) or (self.fmt == "q6_k" and self.b > 2)
+        # the kernel the batch call dispatches to at these shapes (k a multiple of 256): the
+        # matrix cores for Q4_K and Q6_K from 3 rows, for Q8_0 from 5
+        mfma = (self.fmt == "q8_0" and self.b > 4) or (self.fmt in ("q4_k", "q6_k") and self.b > 2)
         self.dominant = ({"q8_0": "gemv_batch_mfma_q8_0", "q4_k": "gemv_batch_mfma_q4k",
                           "q6_k": "gemv_batch_mfma_q6k"}[self.fmt] if mfma else "gemv_batch_kernel")
         wbytes = self.w_host.nbytes
