@@ -227,8 +227,8 @@ class GemvBatch(Gemv):
         self.y = torch.empty((self.b, self.n), dtype=torch.float32, device=dev)
         self.fn = getattr(qg, "qgemv_" + self.fmt + "_batch")
         # the kernel the batch call dispatches to at these shapes (k a multiple of 256): the
-        # matrix cores for Q4_K and Q6_K from 3 rows, for Q8_0 from 5
-        mfma = (self.fmt == "q8_0" and self.b > 4) or (self.fmt in ("q4_k", "q6_k") and self.b > 2)
+        # matrix cores for Q4_K from 2 rows, Q6_K from 3, Q8_0 from 5
+        mfma = self.b > {"q4_k": 1, "q6_k": 2, "q8_0": 4}[self.fmt]
         self.dominant = ({"q8_0": "gemv_batch_mfma_q8_0", "q4_k": "gemv_batch_mfma_q4k",
                           "q6_k": "gemv_batch_mfma_q6k"}[self.fmt] if mfma else "gemv_batch_kernel")
         wbytes = self.w_host.nbytes

@@ -431,14 +431,14 @@ hipError_t launch_qgemv_batch(int fmt, const void *w, const void *xq, float *y, 
   if (fmt == 0 && nb > 4 && nblk % 8 == 0) return launch_qgemv_batch_mfma_q8_0(w, xq, y, D, nb, n, k, stream);
   if (fmt == 0 && nblk % 2 == 0) return launch_fmt<kFmtQ8P>(W, X, y, D, (int)nb, n, nblk, stream);
   if (fmt == 0) return launch_fmt<kFmtQ8_0>(W, X, y, D, (int)nb, n, nblk, stream);
-  // Measured on MI355X (k = 4096, us per call): Q4_K 14336 rows takes
-  // v_dot4 up to 2 rows (b = 2: 9.69 against 9.70 on the matrix cores) and
-  // the matrix cores from 3 (b = 3: 9.57 against 10.59, b = 4: 10.18 against
-  // 10.75, b = 8: 10.3 against 16.0); Q6_K 128256 rows takes v_dot4 up to 2
-  // rows (b = 2: 86.1 against 87.2) and the matrix cores from 3 (b = 3: 88.2
-  // against 95.8, b = 4: 88.7 against 98.3).
+  // Measured on MI355X (k = 4096, us per call): Q4_K 14336 rows takes v_dot4
+  // for one row and the matrix cores from 2 (b = 2: 9.28 against 9.69, b = 3:
+  // 9.57 against 10.59, b = 4: 10.18 against 10.75, b = 8: 10.3 against 16.0);
+  // Q6_K 128256 rows takes v_dot4 up to 2 rows (b = 2: 86.1 against 87.2) and
+  // the matrix cores from 3 (b = 3: 88.2 against 95.8, b = 4: 88.7 against
+  // 98.3).
   if (fmt == 1) {
-    if (nb > 2) return launch_qgemv_batch_mfma_q4k(w, xq, y, D, nb, n, k, stream);
+    if (nb > 1) return launch_qgemv_batch_mfma_q4k(w, xq, y, D, nb, n, k, stream);
     return launch_fmt<kFmtQ4K>(W, X, y, D, (int)nb, n, nblk, stream);
   }
   if (nb > 2) return launch_qgemv_batch_mfma_q6k(w, xq, y, D, nb, n, k, stream);

@@ -273,7 +273,8 @@ def test_gemv_batch_values_random_bytes(env, fmt):
         assert rel_err(y[i], orc.qgemv(fmt, w, xq[i], n, k)) <= REL_TOL, f"row {i}"
 
 
-@pytest.mark.parametrize("b", [2, 3, 5])  # K-quants: the v_dot4 kernels up to 2 rows, the matrix-core ones above
+# b = 2: Q4_K on the matrix cores, Q6_K on v_dot4; b = 3 and 5: both on the matrix cores
+@pytest.mark.parametrize("b", [2, 3, 5])
 def test_gemv_batch_hand_superblock_exact(env, b):
     """Rows with different power-of-two d_a and shifted codes: every
     intermediate is exact in fp32, so each y[i] equals its hand-computed dot."""
@@ -336,9 +337,9 @@ def _blockdots_ref(orc, fmt, w, xq, n, k):
 @pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(65, 256), (130, 768), (33, 14336), (5, 33536)])
 def test_gemv_batch_block_dots_exact(env, fmt, b, n, k):
-    """Exact int32 dots of the kernel each b dispatches to (v_dot4 up to 2 or 4
-    rows; matrix cores from 3 rows for Q4_K and Q6_K and from 5 for Q8_0), on
-    fully random bytes."""
+    """Exact int32 dots of the kernel each b dispatches to (matrix cores from 2
+    rows for Q4_K, from 3 for Q6_K and from 5 for Q8_0, v_dot4 below), on fully
+    random bytes."""
     qg, orc, torch, dev = env
     w = synth.random_blocks(fmt, n, k, seed=7 * n + b)
     xq = synth.random_blocks("q8_1", b, k, seed=11 * n + b)
