@@ -512,13 +512,16 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
         o.fb = u32x2{pb[0], pb[1]};
       };
       const int nj = MmqFmt<FMT>::kBlk32 ? max(0, min(kJ, nblk - 8 * s - j0)) : kJ;  // ragged last step
+      // Q5_K's fifth staging register leaves no room for the lookahead
+      constexpr bool kLook = FMT != kMQ5K;
       Opnd o0, o1;
       if (nj > 0) rd(0, o0);
 #pragma unroll
       for (int jj = 0; jj < kJ; ++jj) {
         if (jj >= nj) break;
-        Opnd &oc = (jj & 1) ? o1 : o0;
-        Opnd &on = (jj & 1) ? o0 : o1;
+        Opnd &oc = (!kLook || (jj & 1) == 0) ? o0 : o1;
+        Opnd &on = (!kLook || (jj & 1) == 0) ? o1 : o0;
+        if (!kLook && jj > 0) rd(jj, oc);
         const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, oc.a),
                                                               __builtin_bit_cast(v4i, oc.b), zero, 0, 0, 0);
         v16f F2;
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(1024) void mmq_kernel(const uint8_t *__restrict__ W
           const v4s fav = __builtin_bit_cast(v4s, oc.fa), fbv = __builtin_bit_cast(v4s, oc.fb);
           F2 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fav, fbv, fzero, 0, 0, 0);
         }
-        if (jj + 1 < nj) rd(jj + 1, on);
+        if (kLook && jj + 1 < nj) rd(jj + 1, on);
         if (DUMP) {
           dump(D, 8 * s + j0 + jj, nblk);
         } else {
